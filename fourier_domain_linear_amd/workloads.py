@@ -1,0 +1,72 @@
+"""Seeded synthetic workloads for the EQ-Linear forward.
+
+This module holds no arithmetic of the layer itself: it only names the workload shapes and draws
+seeded random inputs. It is the one module that both the GPU path's callers (tests, benchmark) and
+the fp64 oracle's callers use, so that both sides see the same values.
+
+Shapes. Token counts are flattened vision feature maps (batch x H x W), the activations an EQ-ViT /
+EQ-Swin stage feeds its linear layers (Flash EQ-Linear page, "A Nivel de Red"); the pages measured
+real networks on ImageNet, which synthetic Gaussian inputs of the same shapes stand in for here.
+The group sizes are p4 (G=4, "Especialización para el Grupo de Rotación p4") and its p8 extension
+(G=8, 45-degree rotations, the EQ-VMamba page's section 5.2).
+
+Distributions. x ~ N(0, 1); W ~ N(0, 1/(C_in*G)) and b ~ N(0, 0.01), reading the second argument
+as the variance, so W has standard deviation (C_in*G)**-0.5 (outputs then have about unit variance)
+and b has standard deviation 0.1. Draw order: x, then W, then b, from one ``torch.Generator`` seeded
+with ``seed`` (0 by default), in fp32 on the CPU; bf16 workloads are then rounded to bf16 with
+round-to-nearest-even, once, and those rounded values are what both the GPU and the oracle see.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    G: int
+    C_in: int
+    C_out: int
+    N: int
+    dtype: str  # "f32" or "bf16"
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+# The five workloads. The first is the tiny fp32 case the oracle finishes in well under a second;
+# the second is the benchmark's workload (p4, 96 channels, 8x56x56 tokens).
+WORKLOADS = [
+    Workload("p4_c16_n64_f32", G=4, C_in=16, C_out=16, N=64, dtype="f32"),
+    Workload("p4_c96_n25088_bf16", G=4, C_in=96, C_out=96, N=8 * 56 * 56, dtype="bf16"),
+    Workload("p8_c64_n25088_bf16", G=8, C_in=64, C_out=64, N=32 * 28 * 28, dtype="bf16"),
+    Workload("p4_c192x768_n12544_bf16", G=4, C_in=192, C_out=768, N=16 * 28 * 28, dtype="bf16"),
+    Workload("p8_c256x1024_n12544_bf16", G=8, C_in=256, C_out=1024, N=64 * 14 * 14, dtype="bf16"),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+BENCH_WORKLOAD = WORKLOADS[1]
+
+
+def make_inputs(G: int, C_in: int, C_out: int, N: int, dtype: str = "bf16", seed: int = 0):
+    """Return CPU tensors (x[N, C_in, G], W[C_out, C_in, G], b[C_out]) in the workload dtype."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    gen = torch.Generator().manual_seed(int(seed))
+    x = torch.randn((N, C_in, G), generator=gen, dtype=torch.float32)
+    W = torch.randn((C_out, C_in, G), generator=gen, dtype=torch.float32) * (C_in * G) ** -0.5
+    b = torch.randn((C_out,), generator=gen, dtype=torch.float32) * 0.1
+    if dtype == "bf16":
+        x, W, b = x.to(torch.bfloat16), W.to(torch.bfloat16), b.to(torch.bfloat16)
+    return x, W, b
+
+
+def workload_inputs(w: Workload, seed: int = 0, N: int | None = None):
+    """Inputs of workload ``w`` (optionally with a different token count N)."""
+    return make_inputs(w.G, w.C_in, w.C_out, w.N if N is None else N, w.dtype, seed)

@@ -1,0 +1,138 @@
+"""fp64 CPU oracle for the cyclic-group equivariant linear layer (EQ-Linear).
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the benchmark's
+CPU-baseline leg are the only callers. The GPU library never imports, links or runs anything here,
+and nothing here imports the GPU library.
+
+Source followed: "Flash EQ-Linear: Accelerating Equivariant Linear Layers via Group-wise Discrete
+Fourier Transform" (explainer page, gist.science/es/paper/2607.21271):
+
+* ``forward`` -- sections "Declaración del Problema" and "Percepción Central": the layer is the
+  dense product with the unrolled group-circulant weight E[o*G+h, i*G+g] = W[o, i, (h-g) mod G],
+  plus a bias b[o] broadcast over the output group index h. Plain fp64 loops in C
+  (``eqlin_oracle.c``); the result the fast method must reproduce ("Principales Contribuciones":
+  exact up to floating point).
+* ``expand`` -- the unrolled matrix E itself (same section).
+* ``dft_weights`` -- section "Enfoque Algorítmico": the DFT of W along the group axis, kept for the
+  non-redundant half k = 0..G/2 (conjugate symmetry of a real signal's spectrum).
+
+All three are pinned in ``tests/test_oracle.py`` against things other than themselves (an
+independent Kronecker construction of the block-circulant matrix, numpy's FFT convolution theorem,
+closed forms for delta / constant / alternating inputs, equivariance, the G=1 plain linear layer).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "eqlin_oracle.c")
+_LIB_DIR = os.path.join(_HERE, "_build")
+_LIB = os.path.join(_LIB_DIR, "libeqlin_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (generic x86-64, -O2, OpenMP). Returns the library path."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    os.makedirs(_LIB_DIR, exist_ok=True)
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.eqlin_oracle_forward.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int]
+    lib.eqlin_oracle_forward.restype = ctypes.c_int
+    lib.eqlin_oracle_expand.argtypes = [dp, i64, i64, i64, dp]
+    lib.eqlin_oracle_expand.restype = ctypes.c_int
+    lib.eqlin_oracle_dft_weights.argtypes = [dp, i64, i64, i64, dp, dp]
+    lib.eqlin_oracle_dft_weights.restype = ctypes.c_int
+    lib.eqlin_oracle_max_threads.argtypes = []
+    lib.eqlin_oracle_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    """Any array-like (numpy or a CPU torch tensor) -> C-contiguous float64 numpy array."""
+    if hasattr(a, "detach"):  # torch tensor: widen exactly on the torch side (bf16 has no numpy dtype)
+        import torch
+
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def max_threads() -> int:
+    return int(_load().eqlin_oracle_max_threads())
+
+
+def forward(x, W, b=None, threads: int = 0) -> np.ndarray:
+    """y[n, o, h] = b[o] + sum_{i, g} W[o, i, (h-g) mod G] * x[n, i, g], in fp64.
+
+    x: [N, C_in, G]; W: [C_out, C_in, G]; b: [C_out] or None. ``threads`` = 0 uses OpenMP's default.
+    """
+    lib = _load()
+    W = _f64(W)
+    x = _f64(x)
+    C_out, C_in, G = W.shape
+    if x.ndim != 3 or x.shape[1:] != (C_in, G):
+        raise ValueError(f"x shape {x.shape} does not match W shape {W.shape}")
+    N = x.shape[0]
+    y = np.empty((N, C_out, G), dtype=np.float64)
+    bp = None
+    if b is not None:
+        b = _f64(b)
+        if b.shape != (C_out,):
+            raise ValueError(f"b shape {b.shape} != ({C_out},)")
+        bp = _ptr(b)
+    rc = lib.eqlin_oracle_forward(_ptr(x) if N else None, _ptr(W), bp, _ptr(y) if N else None,
+                                  N, C_out, C_in, G, int(threads))
+    if rc != 0:
+        raise RuntimeError(f"eqlin_oracle_forward failed with code {rc}")
+    return y
+
+
+def expand(W) -> np.ndarray:
+    """The unrolled block-circulant matrix E[(o*G+h), (i*G+g)] = W[o, i, (h-g) mod G] (fp64)."""
+    lib = _load()
+    W = _f64(W)
+    C_out, C_in, G = W.shape
+    E = np.empty((C_out * G, C_in * G), dtype=np.float64)
+    rc = lib.eqlin_oracle_expand(_ptr(W), C_out, C_in, G, _ptr(E))
+    if rc != 0:
+        raise RuntimeError(f"eqlin_oracle_expand failed with code {rc}")
+    return E
+
+
+def dft_weights(W) -> np.ndarray:
+    """What[o, i, k] = sum_d W[o, i, d] exp(-2 pi i d k / G) for k = 0..G/2 (complex128)."""
+    lib = _load()
+    W = _f64(W)
+    C_out, C_in, G = W.shape
+    K = G // 2 + 1
+    re = np.empty((C_out, C_in, K), dtype=np.float64)
+    im = np.empty((C_out, C_in, K), dtype=np.float64)
+    rc = lib.eqlin_oracle_dft_weights(_ptr(W), C_out, C_in, G, _ptr(re), _ptr(im))
+    if rc != 0:
+        raise RuntimeError(f"eqlin_oracle_dft_weights failed with code {rc}")
+    return re + 1j * im
