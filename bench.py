@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the EQ-Linear spectral forward on one MI355X.
+
+A step is one eqlin_forward over one batch of the workload (the whole hot path: load, group DFT,
+per-frequency products, inverse DFT + bias, store -- one fused kernel). Default workload: p4
+(G = 4), C_in = C_out = 96, N = 8x56x56 = 25088 tokens, bf16 in/out, synthetic seeded inputs.
+
+Timing. Inputs are resident in HBM before the timed region. W warmup steps run eagerly; then K steps
+are captured into one HIP graph (so the ~6 us kernels are not bounded by host launch latency) and
+replayed once untimed and once timed, between HIP events on the launch stream, with
+torch.cuda.synchronize() on both sides. The K steps rotate over R buffer sets totalling >= 1 GiB,
+more than the 256 MB Infinity Cache, so x is read from HBM, not from the cache.
+ms_per_step = event time / K; value = tokens / (ms_per_step / 1e3).
+
+The same is done for eqlin_forward_expanded (the unrolled dense product, the comparator), and the
+fp64 oracle is timed on the host cores over a bounded sample (cpu_baseline).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "EQ-Linear fwd tokens/s + % of bf16 MFMA/HBM roofline vs expanded dense GEMM"
+KERNEL_SOURCES = ["fourier_domain_linear_amd/csrc/fwd_bf16.hip", "fourier_domain_linear_amd/csrc/device_common.h",
+                  "fourier_domain_linear_amd/csrc/dft.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        log(f"[bench] {path} was taken on other kernel sources: traffic = null")
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def time_graph(torch, launch, K: int, R: int):
+    """Capture K launches (launch(i) uses buffer set i % R) into one graph; replay once untimed and
+    once timed. Returns ms per launch."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            launch(i % R)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / K
+
+
+def time_eager(torch, launch, K: int, R: int):
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        launch(i % R)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / K
+
+
+def cpu_baseline(w, x, W, b, budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on the host cores over a bounded sample of the workload."""
+    import oracle
+
+    threads = oracle.max_threads()
+    pilot = min(w.N, 256)
+    t0 = time.perf_counter()
+    oracle.forward(x[:pilot], W, b)
+    t_pilot = time.perf_counter() - t0
+    per_token = t_pilot / pilot
+    if per_token * w.N <= budget_s:
+        passes = max(1, int(budget_s / max(per_token * w.N, 1e-9)))
+        passes = min(passes, 50)
+        t0 = time.perf_counter()
+        for _ in range(passes):
+            oracle.forward(x, W, b)
+        dt = time.perf_counter() - t0
+        tokens = passes * w.N
+        sample = f"{passes} pass(es) over all {w.N} tokens of the workload"
+    else:
+        n = max(pilot, int(budget_s / per_token))
+        n = min(n, w.N)
+        t0 = time.perf_counter()
+        oracle.forward(x[:n], W, b)
+        dt = time.perf_counter() - t0
+        tokens = n
+        sample = f"first {n} of {w.N} tokens of the workload"
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=None, help="workload name (default: the p4, 96-channel one)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-expanded", action="store_true")
+    ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer is token-parallel "
+              "with no communication: N GPUs would each run this on N-th of the tokens).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fourier_domain_linear_amd as eq
+    from fourier_domain_linear_amd import roofline as rl
+    from fourier_domain_linear_amd.workloads import BENCH_WORKLOAD, BY_NAME, workload_inputs
+
+    w = BY_NAME[args.workload] if args.workload else BENCH_WORKLOAD
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    eq.load_library()
+
+    log(f"[bench] workload {w.name}: G={w.G} C_in={w.C_in} C_out={w.C_out} N={w.N} {w.dtype}")
+    x, W, b = workload_inputs(w, seed=0)
+    eb = w.elem_bytes
+    set_bytes = w.N * (w.C_in + w.C_out) * w.G * eb
+    R = max(3, math.ceil((1 << 30) / set_bytes))
+    xd0 = x.to(dev)
+    xs = [xd0] + [xd0.clone() for _ in range(R - 1)]
+    ys = [torch.empty((w.N, w.C_out, w.G), dtype=w.torch_dtype, device=dev) for _ in range(R)]
+    bd = b.to(dev)
+    h = eq.prepare_weights(W.to(dev), expanded=not args.no_expanded)
+    torch.cuda.synchronize()
+    log(f"[bench] {h.describe()}  rotating buffer sets: {R} ({R * set_bytes / 2**20:.0f} MiB)")
+
+    def spectral(i):
+        eq.forward(h, xs[i], bd, ys[i])
+
+    def expanded(i):
+        eq.forward_expanded(h, xs[i], bd, ys[i])
+
+    K, Wm = args.steps, args.warmup
+    timer = time_eager if args.no_graph else time_graph
+    for i in range(Wm):
+        spectral(i % R)
+    torch.cuda.synchronize()
+    ms = timer(torch, spectral, K, R)
+    log(f"[bench] spectral: {ms * 1e3:.2f} us/step")
+
+    F = rl.spectral_flops(w.N, w.C_in, w.C_out, w.G)
+    B = rl.spectral_bytes(w.N, w.C_in, w.C_out, w.G, eb)
+    peak_c = rl.PEAK_BF16_TFLOPS if w.dtype == "bf16" else rl.PEAK_FP32_TFLOPS
+    _, bound = rl.roof_time_s(F, B, peak_c)
+    t = ms / 1e3
+    if bound == "hbm":
+        achieved, peak, unit = B / t / 1e9, rl.PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = F / t / 1e12, peak_c, "TFLOP/s"
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name),
+            "kernel": "spectral forward (one launch per step)",
+            "algorithmic_bytes_per_launch": B, "algorithmic_flops_per_launch": F,
+            "mfma_frac": round(F / t / 1e12 / peak_c, 4), "hbm_frac": round(B / t / 1e9 / rl.PEAK_HBM_GBS, 4)}
+
+    extra = {}
+    if not args.no_expanded:
+        for i in range(Wm):
+            expanded(i % R)
+        torch.cuda.synchronize()
+        ms_e = timer(torch, expanded, K, R)
+        Fd = rl.dense_flops(w.N, w.C_in, w.C_out, w.G)
+        Bd = rl.dense_bytes(w.N, w.C_in, w.C_out, w.G, eb)
+        te = ms_e / 1e3
+        tr, bd_ = rl.roof_time_s(Fd, Bd, peak_c)
+        extra["expanded_baseline"] = {
+            "ms_per_step": round(ms_e, 6), "tokens_per_s": w.N / te, "bound": bd_,
+            "roof_frac": round(tr / te, 4), "mfma_frac": round(Fd / te / 1e12 / peak_c, 4),
+            "hbm_frac": round(Bd / te / 1e9 / rl.PEAK_HBM_GBS, 4), "effective_tflops": round(Fd / te / 1e12, 2)}
+        extra["speedup_vs_expanded"] = round(ms_e / ms, 3)
+        log(f"[bench] expanded: {ms_e * 1e3:.2f} us/step  speedup {ms_e / ms:.2f}x")
+    extra["effective_tflops"] = round(rl.dense_flops(w.N, w.C_in, w.C_out, w.G) / t / 1e12, 2)
+    extra["useful_tflops"] = round(F / t / 1e12, 2)
+
+    line = {
+        "metric": METRIC, "value": w.N / t, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded Gaussian x, W, b; see fourier_domain_linear_amd/workloads.py)",
+        "config": {"workload": w.name, "G": w.G, "C_in": w.C_in, "C_out": w.C_out, "tokens": w.N,
+                   "timing": ("eager launches" if args.no_graph else "one HIP graph of K launches")
+                   + f", {R} rotating buffer sets"},
+        "roofline": roof,
+    }
+    line.update(extra)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host cores ...")
+        line["cpu_baseline"] = cpu_baseline(w, x, W, b)
+    out = json.dumps(line)
+    print(out, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(out + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,222 @@
-"""MI355X-native EQ-Linear forward (placeholder; the binding is added with the HIP library)."""
+"""MI355X-native EQ-Linear forward: a thin ctypes binding over libeqlin.so (include/eqlin.h).
+
+The binding only marshals arguments (shape/dtype/device checks, pointers, the current HIP stream);
+every step of the layer runs in the library's HIP kernels. There is no CPU fallback: if the library
+is missing, every call raises.
+
+    import fourier_domain_linear_amd as eq
+    h = eq.prepare_weights(W)                 # W: cuda tensor [C_out, C_in, G], bf16 or fp32
+    y = eq.forward(h, x, b)                   # x: [N, C_in, G]; b: [C_out] or None
+    y2 = eq.forward_expanded(h, x, b)         # needs prepare_weights(W, expanded=True)
+
+Method: "Flash EQ-Linear: Accelerating Equivariant Linear Layers via Group-wise Discrete Fourier
+Transform" (explainer page, gist.science/es/paper/2607.21271).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libeqlin.so")
+
+EQLIN_OK = 0
+EQLIN_ERR_INVALID_ARG = 1
+EQLIN_ERR_UNSUPPORTED = 2
+EQLIN_ERR_OUT_OF_MEMORY = 3
+EQLIN_ERR_HIP = 4
+EQLIN_F32 = 0
+EQLIN_BF16 = 1
+EQLIN_PREPARE_EXPANDED = 1
+
+# Every symbol include/eqlin.h declares.
+EXPORTED = (
+    "eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_destroy",
+    "eqlin_export_spectral_weights", "eqlin_export_expanded_weight", "eqlin_describe",
+    "eqlin_status_string", "eqlin_last_error", "eqlin_version",
+)
+
+_lib = None
+
+
+class EqlinError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libeqlin.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m fourier_domain_linear_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint
+    lib.eqlin_prepare_weights.argtypes = [vp, i32, i32, i32, i32, u32, vp, ctypes.POINTER(vp)]
+    lib.eqlin_forward.argtypes = [vp, vp, vp, vp, i64, vp]
+    lib.eqlin_forward_expanded.argtypes = [vp, vp, vp, vp, i64, vp]
+    lib.eqlin_destroy.argtypes = [vp]
+    lib.eqlin_export_spectral_weights.argtypes = [vp, vp, vp]
+    lib.eqlin_export_expanded_weight.argtypes = [vp, vp, vp]
+    lib.eqlin_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
+    lib.eqlin_describe.restype = i32
+    lib.eqlin_status_string.argtypes = [i32]
+    lib.eqlin_status_string.restype = ctypes.c_char_p
+    lib.eqlin_last_error.argtypes = []
+    lib.eqlin_last_error.restype = ctypes.c_char_p
+    lib.eqlin_version.argtypes = []
+    lib.eqlin_version.restype = ctypes.c_char_p
+    for name in ("eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_destroy",
+                 "eqlin_export_spectral_weights", "eqlin_export_expanded_weight"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != EQLIN_OK:
+        lib = load_library()
+        name = lib.eqlin_status_string(status).decode()
+        detail = lib.eqlin_last_error().decode()
+        raise EqlinError(status, f"{what}: {name}: {detail}")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return EQLIN_BF16
+    if dt == torch.float32:
+        return EQLIN_F32
+    raise TypeError(f"unsupported dtype {dt} (bfloat16 or float32)")
+
+
+def _need_cuda(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Handle:
+    """Owns an eqlin_handle_t; destroyed with the object (or explicitly via destroy())."""
+
+    def __init__(self, ptr: int, C_out: int, C_in: int, G: int, dtype: torch.dtype, device, expanded: bool):
+        self.ptr = ptr
+        self.C_out, self.C_in, self.G = C_out, C_in, G
+        self.dtype, self.device, self.expanded = dtype, device, expanded
+
+    def destroy(self):
+        if self.ptr:
+            load_library().eqlin_destroy(ctypes.c_void_p(self.ptr))
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    def describe(self) -> str:
+        return describe(self)
+
+
+def prepare_weights(W: torch.Tensor, expanded: bool = False) -> Handle:
+    """eqlin_prepare_weights: W [C_out, C_in, G] (cuda, bf16 or fp32) -> Handle."""
+    lib = load_library()
+    _need_cuda(W, "W")
+    if W.dim() != 3:
+        raise ValueError(f"W must be [C_out, C_in, G], got {tuple(W.shape)}")
+    C_out, C_in, G = W.shape
+    out = ctypes.c_void_p()
+    flags = EQLIN_PREPARE_EXPANDED if expanded else 0
+    with torch.cuda.device(W.device):
+        st = lib.eqlin_prepare_weights(ctypes.c_void_p(W.data_ptr()), C_out, C_in, G, _dtype_code(W.dtype),
+                                       flags, _stream(W), ctypes.byref(out))
+    _check(st, "eqlin_prepare_weights")
+    return Handle(out.value, C_out, C_in, G, W.dtype, W.device, expanded)
+
+
+def _forward(fn, what: str, h: Handle, x: torch.Tensor, b: torch.Tensor | None, y: torch.Tensor | None):
+    _need_cuda(x, "x")
+    if x.dtype != h.dtype:
+        raise TypeError(f"x dtype {x.dtype} != handle dtype {h.dtype}")
+    if x.dim() != 3 or x.shape[1] != h.C_in or x.shape[2] != h.G:
+        raise ValueError(f"x must be [N, {h.C_in}, {h.G}], got {tuple(x.shape)}")
+    N = x.shape[0]
+    if y is None:
+        y = torch.empty((N, h.C_out, h.G), dtype=x.dtype, device=x.device)
+    else:
+        _need_cuda(y, "y")
+        if y.dtype != h.dtype or tuple(y.shape) != (N, h.C_out, h.G):
+            raise ValueError(f"y must be [{N}, {h.C_out}, {h.G}] of {h.dtype}")
+    bp = None
+    if b is not None:
+        _need_cuda(b, "b")
+        if b.dtype != h.dtype or tuple(b.shape) != (h.C_out,):
+            raise ValueError(f"b must be [{h.C_out}] of {h.dtype}")
+        bp = ctypes.c_void_p(b.data_ptr())
+    with torch.cuda.device(x.device):
+        st = fn(ctypes.c_void_p(h.ptr), ctypes.c_void_p(x.data_ptr()), bp, ctypes.c_void_p(y.data_ptr()), N,
+                _stream(x))
+    _check(st, what)
+    return y
+
+
+def forward(h: Handle, x: torch.Tensor, b: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """eqlin_forward: y[n, o, h] = b[o] + sum_{i,g} W[o, i, (h-g) mod G] x[n, i, g] (spectral kernel)."""
+    return _forward(load_library().eqlin_forward, "eqlin_forward", h, x, b, y)
+
+
+def forward_expanded(h: Handle, x: torch.Tensor, b: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """eqlin_forward_expanded: the same layer as one dense product with the unrolled weight."""
+    if not h.expanded:
+        raise ValueError("handle was prepared without expanded=True")
+    return _forward(load_library().eqlin_forward_expanded, "eqlin_forward_expanded", h, x, b, y)
+
+
+def export_spectral_weights(h: Handle) -> torch.Tensor:
+    """eqlin_export_spectral_weights -> float32 [G, C_out, C_in] (plane order in include/eqlin.h)."""
+    out = torch.empty((h.G, h.C_out, h.C_in), dtype=torch.float32, device=h.device)
+    with torch.cuda.device(h.device):
+        st = load_library().eqlin_export_spectral_weights(ctypes.c_void_p(h.ptr), ctypes.c_void_p(out.data_ptr()),
+                                                          _stream(out))
+    _check(st, "eqlin_export_spectral_weights")
+    return out
+
+
+def export_expanded_weight(h: Handle) -> torch.Tensor:
+    """eqlin_export_expanded_weight -> [C_out*G, C_in*G] of the handle's dtype."""
+    out = torch.empty((h.C_out * h.G, h.C_in * h.G), dtype=h.dtype, device=h.device)
+    with torch.cuda.device(h.device):
+        st = load_library().eqlin_export_expanded_weight(ctypes.c_void_p(h.ptr), ctypes.c_void_p(out.data_ptr()),
+                                                         _stream(out))
+    _check(st, "eqlin_export_expanded_weight")
+    return out
+
+
+def describe(h: Handle) -> str:
+    lib = load_library()
+    buf = ctypes.create_string_buffer(512)
+    lib.eqlin_describe(ctypes.c_void_p(h.ptr), buf, len(buf))
+    return buf.value.decode()
+
+
+def version() -> str:
+    return load_library().eqlin_version().decode()
+
+
+def status_string(code: int) -> str:
+    return load_library().eqlin_status_string(code).decode()
+
+
+def destroy(h: Handle):
+    h.destroy()

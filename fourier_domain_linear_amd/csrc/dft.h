@@ -1,0 +1,105 @@
+// dft.h -- G-point real DFT butterflies along the group axis (G in {1, 2, 4, 8}), in registers.
+//
+// Flash EQ-Linear page ("Flash EQ-Linear: Accelerating Equivariant Linear Layers via Group-wise
+// Discrete Fourier Transform", gist.science explainer), section "Enfoque Algorítmico": a DFT along
+// the group axis turns the group convolution into a pointwise product per frequency, and because x
+// and W are real only k = 0..G/2 is kept (conjugate symmetry). Section "Especialización para el Grupo
+// de Rotación p4": for G = 4 both transforms need only additions, subtractions and power-of-two
+// scalings. For G = 8 (the p8 extension) the odd frequencies add the twiddle sqrt(2)/2.
+//
+// Plane order (G real planes per channel, used for x, W and the products alike):
+//   p = 0          : Re X_0                (real)
+//   p = 1          : Re X_{G/2}            (real; G >= 2)
+//   p = 2k, 2k + 1 : Re X_k, Im X_k        (k = 1 .. G/2 - 1)
+// with X_k = sum_g x_g exp(-2 pi i g k / G).
+//
+// Inverse. With Y_k = What_k X_k, the real inverse over the half spectrum is
+//   y_h = (1/G) [ Y_0 + (-1)^h Y_{G/2} + 2 sum_{k=1}^{G/2-1} Re(Y_k exp(+2 pi i h k / G)) ].
+// The library folds the 1/G (real planes) and 2/G (complex planes) factors into the stored weight
+// planes (exact: powers of two), so inverse_planes() below takes the already-scaled products and is
+// additions only for G <= 4. plane_scale() gives those factors.
+//
+// This header is plain C++ so the host test suite can compile it and check it against numpy's FFT.
+#pragma once
+
+#if defined(__HIPCC__)
+#define EQLIN_HD __host__ __device__ __forceinline__
+#else
+#define EQLIN_HD inline
+#endif
+
+namespace eqlin {
+
+constexpr float kSqrtHalf = 0.70710678118654752440f;
+
+// Scale folded into weight plane p (see above).
+EQLIN_HD float plane_scale(int G, int p) {
+    if (G == 1) return 1.0f;
+    return (p < 2) ? 1.0f / (float)G : 2.0f / (float)G;
+}
+
+// Forward: v[0..G-1] (group samples) -> P[0..G-1] (planes, order above).
+template <int G>
+EQLIN_HD void forward_planes(const float *v, float *P) {
+    if constexpr (G == 1) {
+        P[0] = v[0];
+    } else if constexpr (G == 2) {
+        P[0] = v[0] + v[1];
+        P[1] = v[0] - v[1];
+    } else if constexpr (G == 4) {
+        const float a = v[0] + v[2], c = v[0] - v[2];
+        const float b = v[1] + v[3], d = v[1] - v[3];
+        P[0] = a + b;  // X0
+        P[1] = a - b;  // X2
+        P[2] = c;      // Re X1 = v0 - v2
+        P[3] = -d;     // Im X1 = v3 - v1
+    } else {
+        static_assert(G == 8, "G must be 1, 2, 4 or 8");
+        const float a0 = v[0] + v[4], a1 = v[1] + v[5], a2 = v[2] + v[6], a3 = v[3] + v[7];
+        const float d0 = v[0] - v[4], d1 = v[1] - v[5], d2 = v[2] - v[6], d3 = v[3] - v[7];
+        const float e0 = a0 + a2, e1 = a1 + a3, f0 = a0 - a2, f1 = a1 - a3;
+        const float t1 = d1 - d3, t2 = d1 + d3;
+        P[0] = e0 + e1;                      // X0
+        P[1] = e0 - e1;                      // X4
+        P[2] = d0 + kSqrtHalf * t1;          // Re X1
+        P[3] = -(d2 + kSqrtHalf * t2);       // Im X1
+        P[4] = f0;                           // Re X2
+        P[5] = -f1;                          // Im X2
+        P[6] = d0 - kSqrtHalf * t1;          // Re X3
+        P[7] = d2 - kSqrtHalf * t2;          // Im X3
+    }
+}
+
+// Inverse: scaled products Y[0..G-1] (plane order) -> y[0..G-1] (group samples).
+template <int G>
+EQLIN_HD void inverse_planes(const float *Y, float *y) {
+    if constexpr (G == 1) {
+        y[0] = Y[0];
+    } else if constexpr (G == 2) {
+        y[0] = Y[0] + Y[1];
+        y[1] = Y[0] - Y[1];
+    } else if constexpr (G == 4) {
+        const float u = Y[0] + Y[1], w = Y[0] - Y[1];
+        y[0] = u + Y[2];
+        y[1] = w - Y[3];
+        y[2] = u - Y[2];
+        y[3] = w + Y[3];
+    } else {
+        static_assert(G == 8, "G must be 1, 2, 4 or 8");
+        // even part (period 4 in h): Y0, Y4, Y2
+        const float u = Y[0] + Y[1], w = Y[0] - Y[1];
+        const float E0 = u + Y[4], E1 = w - Y[5], E2 = u - Y[4], E3 = w + Y[5];
+        // odd part (antiperiodic, period 8): Y1, Y3
+        const float r1 = Y[2], i1 = Y[3], r3 = Y[6], i3 = Y[7];
+        const float O0 = r1 + r3;
+        const float O1 = kSqrtHalf * ((r1 - i1) - (r3 + i3));
+        const float O2 = i3 - i1;
+        const float O3 = kSqrtHalf * ((r3 - i3) - (r1 + i1));
+        y[0] = E0 + O0; y[4] = E0 - O0;
+        y[1] = E1 + O1; y[5] = E1 - O1;
+        y[2] = E2 + O2; y[6] = E2 - O2;
+        y[3] = E3 + O3; y[7] = E3 - O3;
+    }
+}
+
+}  // namespace eqlin

@@ -1,0 +1,78 @@
+// eqlin_internal.h -- the plan behind an eqlin_handle_t and the kernel launchers the C ABI calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/eqlin.h"
+
+namespace eqlin {
+
+// Forward-kernel families.
+enum KernelKind {
+    KIND_ROWBLOCK = 0,  // bf16, small C: a wave holds 16 tokens x the whole C_out tile; x straight to
+                        // registers, the C_out tile's weights staged once in LDS
+    KIND_TILED = 1,     // bf16, any C: GEMM-style token x C_out tiles, x planes and weights via LDS
+    KIND_F32 = 2        // fp32: vector-ALU spectral kernel
+};
+
+struct Plan;
+
+typedef hipError_t (*LaunchFn)(const Plan *p, const void *x, const void *b, void *y, int64_t N,
+                               hipStream_t s);
+
+// Kernel choice for one plan. The weight layout (padding of C_in and C_out) depends on it.
+struct KernelChoice {
+    int kind = -1;
+    int nb_tile = 1;        // 16-wide output blocks per workgroup tile
+    int tokens_per_block = 0;
+    int block_threads = 0;
+    size_t lds_bytes = 0;
+    LaunchFn launch = nullptr;
+    char name[96] = {0};
+};
+
+struct Plan {
+    int C_out = 0, C_in = 0, G = 0;
+    eqlin_dtype_t dtype = EQLIN_BF16;
+    unsigned flags = 0;
+    int device = 0;
+    int bias_shift = 0;  // the bias index is o >> bias_shift (expanded plans: log2 of the parent's G)
+
+    // spectral weights. bf16: fragment-ordered chunks (see prepare.hip); f32: planes [G][C_out][C_in]
+    void *planes = nullptr;
+    size_t planes_bytes = 0;
+    int KS = 0;        // bf16: 32-channel K-steps (C_in padded up to a multiple of 32)
+    int NB_total = 0;  // bf16: 16-wide output blocks (C_out padded up to a multiple of the tile)
+    KernelChoice fwd;
+
+    // unrolled weight (flags & EQLIN_PREPARE_EXPANDED): a G = 1 plan over E, plus E itself
+    Plan *expanded = nullptr;
+    void *wexp = nullptr;  // [C_out*G][C_in*G] of dtype
+};
+
+// ---- fwd_bf16.hip ----
+bool select_bf16(int G, int C_in, int C_out, KernelChoice *out);
+// ---- fwd_f32.hip ----
+bool select_f32(int G, int C_in, int C_out, KernelChoice *out);
+
+// ---- prepare.hip ----
+// W [C_out][C_in][G] (bf16 bits or fp32) -> fragment-ordered bf16 spectral planes.
+hipError_t launch_prep_frag(const void *W, bool w_is_bf16, int G, int C_out, int C_in, int KS,
+                            int NB_total, void *frag, hipStream_t s);
+// W fp32 -> planes [G][C_out][C_in] fp32.
+hipError_t launch_prep_plain_f32(const float *W, int G, int C_out, int C_in, float *planes,
+                                 hipStream_t s);
+// W -> E[C_out*G][C_in*G] (same element size, 2 or 4 bytes).
+hipError_t launch_expand(const void *W, int elem_bytes, int G, int C_out, int C_in, void *E,
+                         hipStream_t s);
+// stored spectral weights -> canonical fp32 [G][C_out][C_in] with the scaling undone.
+hipError_t launch_export_frag(const void *frag, int G, int C_out, int C_in, int KS, int NB_total,
+                              float *out, hipStream_t s);
+hipError_t launch_export_plain_f32(const float *planes, int G, int C_out, int C_in, float *out,
+                                   hipStream_t s);
+
+}  // namespace eqlin
+
+struct eqlin_plan : public eqlin::Plan {};

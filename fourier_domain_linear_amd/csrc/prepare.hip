@@ -1,0 +1,151 @@
+// prepare.hip -- weight preparation: W -> spectral planes (once per weight set), W -> unrolled E,
+// and the export kernels that read them back in a canonical layout for checking.
+//
+// Spectral weights ("Flash EQ-Linear" explainer, "Enfoque Algorítmico"): What_k = sum_d W_d
+// exp(-2 pi i d k / G) along the group axis for k = 0..G/2, the same DFT as the activations' (a
+// convolution, so no conjugate). Computed in fp32 from the given W (bf16 or fp32), with the inverse
+// transform's 1/G (real planes) and 2/G (complex planes) folded in -- exact power-of-two scalings --
+// then rounded once to bf16 for the matrix-core path.
+//
+// Unrolled weight ("Declaración del Problema": the naive layer replicates and cyclically shifts the
+// shared weights into a dense matrix): E[o*G+h][i*G+g] = W[o][i][(h-g) mod G].
+#include "device_common.h"
+#include "eqlin_internal.h"
+
+namespace eqlin {
+
+__device__ __forceinline__ float load_w(const void *W, bool is_bf16, size_t idx) {
+    return is_bf16 ? __uint_as_float((uint32_t)((const uint16_t *)W)[idx] << 16)
+                   : ((const float *)W)[idx];
+}
+
+// Fragment position of What_p[o][i] in the chunked layout (see fwd_bf16.hip): chunk
+// (nb*KS + ks)*G + p, lane (i%32)/8*16 + o%16, element i%8. Returns a bf16 element index.
+__device__ __forceinline__ size_t frag_index(int G, int KS, int o, int i, int p) {
+    const int nb = o >> 4, ks = i >> 5;
+    const int lane = ((i & 31) >> 3) * 16 + (o & 15);
+    return ((((size_t)nb * KS + ks) * G + p) * 64 + lane) * 8 + (i & 7);
+}
+
+// One thread per (o, i) of the padded domain [NB_total*16] x [KS*32]; padding gets zeros.
+template <int G>
+__global__ void k_prep_frag(const void *__restrict__ W, bool w_is_bf16, int C_out, int C_in, int KS,
+                            int NB_total, uint16_t *__restrict__ frag) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int ipad = KS * 32;
+    if (t >= (int64_t)NB_total * 16 * ipad) return;
+    const int o = (int)(t / ipad), i = (int)(t % ipad);
+    float v[G], P[G];
+    const bool live = o < C_out && i < C_in;
+#pragma unroll
+    for (int d = 0; d < G; ++d) v[d] = live ? load_w(W, w_is_bf16, ((size_t)o * C_in + i) * G + d) : 0.f;
+    forward_planes<G>(v, P);
+#pragma unroll
+    for (int p = 0; p < G; ++p) frag[frag_index(G, KS, o, i, p)] = pack_bf16(P[p] * plane_scale(G, p));
+}
+
+template <int G>
+__global__ void k_export_frag(const uint16_t *__restrict__ frag, int C_out, int C_in, int KS,
+                              float *__restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)C_out * C_in) return;
+    const int o = (int)(t / C_in), i = (int)(t % C_in);
+#pragma unroll
+    for (int p = 0; p < G; ++p) {
+        const float s = __uint_as_float((uint32_t)frag[frag_index(G, KS, o, i, p)] << 16);
+        out[((size_t)p * C_out + o) * C_in + i] = s / plane_scale(G, p);
+    }
+}
+
+template <int G>
+__global__ void k_prep_plain_f32(const float *__restrict__ W, int C_out, int C_in,
+                                 float *__restrict__ planes) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)C_out * C_in) return;
+    float v[G], P[G];
+#pragma unroll
+    for (int d = 0; d < G; ++d) v[d] = W[t * G + d];
+    forward_planes<G>(v, P);
+#pragma unroll
+    for (int p = 0; p < G; ++p) planes[(size_t)p * C_out * C_in + t] = P[p] * plane_scale(G, p);
+}
+
+template <int G>
+__global__ void k_export_plain_f32(const float *__restrict__ planes, int C_out, int C_in,
+                                   float *__restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)C_out * C_in) return;
+#pragma unroll
+    for (int p = 0; p < G; ++p)
+        out[(size_t)p * C_out * C_in + t] = planes[(size_t)p * C_out * C_in + t] / plane_scale(G, p);
+}
+
+// E[o*G+h][i*G+g] = W[o][i][(h-g) mod G]; one thread per element of E.
+template <typename T>
+__global__ void k_expand(const T *__restrict__ W, int G, int C_out, int C_in, T *__restrict__ E) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t cols = (int64_t)C_in * G;
+    if (t >= (int64_t)C_out * G * cols) return;
+    const int64_t r = t / cols, c = t % cols;
+    const int o = (int)(r / G), h = (int)(r % G), i = (int)(c / G), g = (int)(c % G);
+    const int d = (h - g + G) % G;
+    E[t] = W[((int64_t)o * C_in + i) * G + d];
+}
+
+static inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+#define DISPATCH_G(G, CALL)                     \
+    switch (G) {                                \
+        case 1: { constexpr int GG = 1; CALL; } break; \
+        case 2: { constexpr int GG = 2; CALL; } break; \
+        case 4: { constexpr int GG = 4; CALL; } break; \
+        case 8: { constexpr int GG = 8; CALL; } break; \
+        default: return hipErrorInvalidValue;   \
+    }
+
+hipError_t launch_prep_frag(const void *W, bool w_is_bf16, int G, int C_out, int C_in, int KS,
+                            int NB_total, void *frag, hipStream_t s) {
+    const int64_t n = (int64_t)NB_total * 16 * KS * 32;
+    DISPATCH_G(G, hipLaunchKernelGGL(k_prep_frag<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s, W,
+                                     w_is_bf16, C_out, C_in, KS, NB_total, (uint16_t *)frag));
+    return hipGetLastError();
+}
+
+hipError_t launch_export_frag(const void *frag, int G, int C_out, int C_in, int KS, int NB_total,
+                              float *out, hipStream_t s) {
+    (void)NB_total;
+    const int64_t n = (int64_t)C_out * C_in;
+    DISPATCH_G(G, hipLaunchKernelGGL(k_export_frag<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
+                                     (const uint16_t *)frag, C_out, C_in, KS, out));
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_plain_f32(const float *W, int G, int C_out, int C_in, float *planes,
+                                 hipStream_t s) {
+    const int64_t n = (int64_t)C_out * C_in;
+    DISPATCH_G(G, hipLaunchKernelGGL(k_prep_plain_f32<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
+                                     W, C_out, C_in, planes));
+    return hipGetLastError();
+}
+
+hipError_t launch_export_plain_f32(const float *planes, int G, int C_out, int C_in, float *out,
+                                   hipStream_t s) {
+    const int64_t n = (int64_t)C_out * C_in;
+    DISPATCH_G(G, hipLaunchKernelGGL(k_export_plain_f32<GG>, dim3(blocks_for(n, 256)), dim3(256), 0,
+                                     s, planes, C_out, C_in, out));
+    return hipGetLastError();
+}
+
+hipError_t launch_expand(const void *W, int elem_bytes, int G, int C_out, int C_in, void *E,
+                         hipStream_t s) {
+    const int64_t n = (int64_t)C_out * G * C_in * G;
+    if (elem_bytes == 2)
+        hipLaunchKernelGGL(k_expand<uint16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
+                           (const uint16_t *)W, G, C_out, C_in, (uint16_t *)E);
+    else
+        hipLaunchKernelGGL(k_expand<float>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
+                           (const float *)W, G, C_out, C_in, (float *)E);
+    return hipGetLastError();
+}
+
+}  // namespace eqlin

@@ -1,0 +1,145 @@
+/*
+ * eqlin.h -- C ABI of the MI355X (gfx950) EQ-Linear forward library, libeqlin.so.
+ *
+ * The operation. A cyclic-group equivariant linear layer (EQ-Linear) over tokens shaped
+ * [channels, G], G the order of the rotation group (p4: G = 4; p8: G = 8; G = 1 and 2 also work):
+ *
+ *     y[n, o, h] = b[o] + sum_{i < C_in} sum_{g < G} W[o, i, (h - g) mod G] * x[n, i, g]
+ *
+ * Source: "Flash EQ-Linear: Accelerating Equivariant Linear Layers via Group-wise Discrete Fourier
+ * Transform" (explainer page, gist.science/es/paper/2607.21271). Section "Percepción Central": the
+ * layer's unrolled weight is group-circulant (cyclic shifts of one parameter set), i.e. a circular
+ * convolution along the group axis composed with a channel linear map. Section "Enfoque
+ * Algorítmico": a DFT along the group axis turns the convolution into independent per-frequency
+ * channel products, and conjugate symmetry leaves only k = 0..G/2 to compute. The bias b[o] is
+ * broadcast over h (the pages name no bias; this is the only bias that keeps the layer equivariant).
+ *
+ * Layouts (row-major, contiguous, group index innermost):
+ *   x[N][C_in][G], y[N][C_out][G], W[C_out][C_in][G], b[C_out].
+ * Element type: EQLIN_BF16 (bfloat16 in and out, fp32 transforms and accumulation, one
+ * round-to-nearest-even at the store) or EQLIN_F32 (fp32 throughout).
+ *
+ * Memory. Every data pointer is a DEVICE pointer on the current HIP device. The caller owns x, W, b
+ * and y; the handle owns the spectral weights (and the unrolled weight, when asked for) until
+ * eqlin_destroy. x, y and W must be 16-byte aligned; b (optional) 4-byte aligned for f32, 2-byte
+ * for bf16. x and y must not overlap.
+ *
+ * Streams. All device work is enqueued on `stream` (NULL = the legacy default stream) and nothing
+ * synchronises the host, except where an entry point says otherwise. A handle is immutable after
+ * eqlin_prepare_weights returns; forwards on several streams may share it once the preparing stream
+ * has passed the prepare (the caller orders that).
+ *
+ * Errors. Arguments are checked on the host before anything is enqueued; a bad argument returns a
+ * status code and enqueues nothing. A failed HIP call returns EQLIN_ERR_HIP. Nothing throws or aborts
+ * across this ABI. eqlin_last_error() gives a message for the calling thread's most recent failure.
+ * A device-side fault would surface at the caller's next synchronisation, as for any HIP kernel.
+ */
+#ifndef EQLIN_H
+#define EQLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t (HIP defines hipStream_t as struct ihipStream_t*). */
+struct ihipStream_t;
+typedef struct ihipStream_t *eqlin_stream_t;
+
+/* Opaque plan: spectral weights + kernel choice for one weight set. Owned by the library. */
+typedef struct eqlin_plan *eqlin_handle_t;
+
+typedef enum {
+    EQLIN_OK = 0,
+    EQLIN_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, G not in {1,2,4,8}, ... */
+    EQLIN_ERR_UNSUPPORTED = 2,   /* valid layer the kernels do not cover (bf16 with C_in % 8 != 0) */
+    EQLIN_ERR_OUT_OF_MEMORY = 3, /* device allocation failed */
+    EQLIN_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} eqlin_status_t;
+
+typedef enum { EQLIN_F32 = 0, EQLIN_BF16 = 1 } eqlin_dtype_t;
+
+/* flags for eqlin_prepare_weights */
+#define EQLIN_PREPARE_EXPANDED 1u /* also build the unrolled weight for eqlin_forward_expanded */
+
+/*
+ * eqlin_prepare_weights -- W -> spectral weights, once per weight set.
+ *
+ * Computes What[o, i, k] = sum_d W[o, i, d] exp(-2 pi i d k / G) for k = 0..G/2 (the DFT along the
+ * group axis, same sign as the input's, no conjugate; "Enfoque Algorítmico") in fp32 and stores it
+ * as G real planes in the layout the forward kernels read (bf16 for EQLIN_BF16). It takes the very
+ * W a naive EQ-Linear uses: the method is a drop-in replacement that needs no retraining
+ * ("Implementación": training-free, plug-and-play).
+ *
+ *   W      device [C_out][C_in][G] of `dtype`; read once, stream-ordered. The caller may free or
+ *          overwrite W once `stream` has passed this call.
+ *   C_out, C_in >= 1; G in {1, 2, 4, 8}. EQLIN_BF16 needs C_in % 8 == 0 (else UNSUPPORTED).
+ *   flags  EQLIN_PREPARE_EXPANDED to also build the unrolled weight for eqlin_forward_expanded.
+ *   out    receives the new handle (set to NULL on failure).
+ * Allocates device memory (hipMalloc) on the current device; synchronises nothing.
+ */
+eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, eqlin_dtype_t dtype,
+                                     unsigned flags, eqlin_stream_t stream, eqlin_handle_t *out);
+
+/*
+ * eqlin_forward -- the spectral forward, one fused kernel: load a token tile (G contiguous), group
+ * DFT in registers, per-frequency channel products on the matrix cores (bf16 in, fp32 accumulate;
+ * a complex frequency as four real products), inverse DFT + bias in registers, one store
+ * ("Enfoque Algorítmico"; "Implementación": fused dataflow with no intermediate global writes).
+ *
+ *   h      handle from eqlin_prepare_weights.
+ *   x      device [N][C_in][G]; b device [C_out] or NULL (no bias); y device [N][C_out][G].
+ *   N      >= 0 tokens; N == 0 enqueues nothing and returns EQLIN_OK.
+ * Must be called with the handle's device current. Asynchronous on `stream`; allocates nothing.
+ */
+eqlin_status_t eqlin_forward(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N,
+                             eqlin_stream_t stream);
+
+/*
+ * eqlin_forward_expanded -- the naive comparator: y_flat = x_flat E^T + b_exp with the unrolled
+ * block-circulant weight E[o*G+h][i*G+g] = W[o, i, (h-g) mod G] and b_exp[o*G+h] = b[o], as one
+ * dense matrix product on the matrix cores ("Declaración del Problema": replicate the shared
+ * weights into a dense matrix, then multiply densely). Same arguments and rules as eqlin_forward;
+ * needs a handle prepared with EQLIN_PREPARE_EXPANDED (else EQLIN_ERR_INVALID_ARG).
+ */
+eqlin_status_t eqlin_forward_expanded(eqlin_handle_t h, const void *x, const void *b, void *y,
+                                      int64_t N, eqlin_stream_t stream);
+
+/* Frees the handle's device memory (hipFree, which synchronises the device). NULL is a no-op. */
+eqlin_status_t eqlin_destroy(eqlin_handle_t h);
+
+/*
+ * eqlin_export_spectral_weights -- copy the stored spectral weights out, for checking.
+ * out: device float [G][C_out][C_in], plane order: k = 0 (real); k = G/2 (real, when G >= 2);
+ * then Re and Im of each k = 1..G/2-1 in turn. Values are What itself (the forward's internal
+ * 1/G and 2/G scalings are undone exactly), as stored: bf16-rounded for an EQLIN_BF16 handle.
+ */
+eqlin_status_t eqlin_export_spectral_weights(eqlin_handle_t h, float *out, eqlin_stream_t stream);
+
+/*
+ * eqlin_export_expanded_weight -- copy the unrolled weight out, for checking.
+ * out: device [C_out*G][C_in*G] of the handle's dtype. Needs EQLIN_PREPARE_EXPANDED.
+ */
+eqlin_status_t eqlin_export_expanded_weight(eqlin_handle_t h, void *out, eqlin_stream_t stream);
+
+/* Writes a one-line description of the kernels the handle dispatches to (for logs and reports).
+ * Returns the length it wanted to write (like snprintf); buf may be NULL when len == 0. */
+int eqlin_describe(eqlin_handle_t h, char *buf, size_t len);
+
+/* Static text for a status code. */
+const char *eqlin_status_string(eqlin_status_t s);
+
+/* Message for the calling thread's most recent failed call ("" if none). Valid until the thread's
+ * next call into the library. */
+const char *eqlin_last_error(void);
+
+/* Library version string, "major.minor.patch". */
+const char *eqlin_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EQLIN_H */

@@ -1,0 +1,70 @@
+"""The C-ABI library loads and exports every symbol include/eqlin.h declares; host-side argument
+checks return status codes without touching a GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fourier_domain_linear_amd as eq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "eqlin.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(eqlin_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(eq.LIB_PATH):
+        pytest.fail("libeqlin.so is not built: run `python -m fourier_domain_linear_amd.build`")
+    return eq.load_library()
+
+
+def test_header_declares_what_binding_lists():
+    assert _declared() == sorted(eq.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert re.fullmatch(r"\d+\.\d+\.\d+", eq.version())
+    assert eq.status_string(0) == "EQLIN_OK"
+    assert eq.status_string(2) == "EQLIN_ERR_UNSUPPORTED"
+    assert eq.status_string(99) == "EQLIN_ERR_UNKNOWN"
+
+
+def _prepare(lib, W, C_out, C_in, G, dtype=1, flags=0, out=True):
+    h = ctypes.c_void_p()
+    return lib.eqlin_prepare_weights(W, C_out, C_in, G, dtype, flags, None, ctypes.byref(h) if out else None), h
+
+
+def test_prepare_argument_errors(lib):
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails its host-side check first
+    assert _prepare(lib, fake, 4, 8, 4, out=False)[0] == eq.EQLIN_ERR_INVALID_ARG
+    st, h = _prepare(lib, None, 4, 8, 4)
+    assert st == eq.EQLIN_ERR_INVALID_ARG and h.value is None
+    assert _prepare(lib, fake, 4, 8, 3)[0] == eq.EQLIN_ERR_INVALID_ARG         # G not a valid group
+    assert _prepare(lib, fake, 4, 8, 16)[0] == eq.EQLIN_ERR_INVALID_ARG
+    assert _prepare(lib, fake, 0, 8, 4)[0] == eq.EQLIN_ERR_INVALID_ARG         # C_out < 1
+    assert _prepare(lib, fake, 4, -1, 4)[0] == eq.EQLIN_ERR_INVALID_ARG
+    assert _prepare(lib, fake, 4, 8, 4, dtype=7)[0] == eq.EQLIN_ERR_INVALID_ARG
+    assert _prepare(lib, fake, 4, 8, 4, flags=0x10)[0] == eq.EQLIN_ERR_INVALID_ARG
+    assert _prepare(lib, ctypes.c_void_p(0x10008), 4, 8, 4)[0] == eq.EQLIN_ERR_INVALID_ARG  # misaligned
+    assert _prepare(lib, fake, 4, 12, 4, dtype=1)[0] == eq.EQLIN_ERR_UNSUPPORTED  # bf16, C_in % 8
+    assert "C_in" in lib.eqlin_last_error().decode()
+
+
+def test_forward_null_handle(lib):
+    assert lib.eqlin_forward(None, None, None, None, 10, None) == eq.EQLIN_ERR_INVALID_ARG
+    assert lib.eqlin_forward_expanded(None, None, None, None, 10, None) == eq.EQLIN_ERR_INVALID_ARG
+    assert lib.eqlin_destroy(None) == eq.EQLIN_OK
+    assert lib.eqlin_export_spectral_weights(None, None, None) == eq.EQLIN_ERR_INVALID_ARG
+    n = lib.eqlin_describe(None, None, 0)
+    assert n > 0

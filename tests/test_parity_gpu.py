@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Bars (fixed up front for this layer): bf16 path -- relative Frobenius error <= 1e-2 AND max abs
+error <= 3e-2 against the unrounded fp64 oracle fed the same bf16-rounded x, W, b; fp32 path --
+relative Frobenius error <= 1e-5. The oracle is exact arithmetic (fp64) of the unrolled layer, so
+any correct fast path lands within rounding of it ("Flash EQ-Linear" explainer, "Principales
+Contribuciones": the method is exact up to floating point).
+
+Sizes: every workload's channel shape at a ragged token count the oracle finishes in seconds
+(several tiles plus a partial one), and every workload at its full token count, checked on a seeded
+sample of tokens (first, last, tile edges, random) that the oracle computes one by one, in the same
+launch configuration the benchmark times.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import fourier_domain_linear_amd as eq
+import oracle
+from fourier_domain_linear_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+REL_BF16, MAX_BF16, REL_F32 = 1e-2, 3e-2, 1e-5
+
+
+def _errors(y_gpu: torch.Tensor, ref: np.ndarray):
+    y = y_gpu.detach().to("cpu", torch.float64).numpy()
+    diff = y - ref
+    rel = np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300)
+    return float(rel), float(np.max(np.abs(diff))) if diff.size else 0.0
+
+
+def _check(y_gpu, ref, dtype: str, label: str):
+    rel, mx = _errors(y_gpu, ref)
+    print(f"[parity] {label}: rel_frob={rel:.3e} max_abs={mx:.3e}", flush=True)
+    assert np.all(np.isfinite(y_gpu.detach().float().cpu().numpy())), label
+    if dtype == "bf16":
+        assert rel <= REL_BF16 and mx <= MAX_BF16, (label, rel, mx)
+    else:
+        assert rel <= REL_F32, (label, rel)
+
+
+def _run(x, W, b, dev, expanded=False):
+    h = eq.prepare_weights(W.to(dev), expanded=expanded)
+    xd, bd = x.to(dev), (None if b is None else b.to(dev))
+    y = eq.forward_expanded(h, xd, bd) if expanded else eq.forward(h, xd, bd)
+    torch.cuda.synchronize()
+    return h, y
+
+
+def _sample_tokens(N: int, k: int = 192, seed: int = 1):
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 15, 16, 63, 64, 127, 128, N // 2, N - 65, N - 64, N - 2, N - 1]
+    idx = set(i for i in edges if 0 <= i < N)
+    idx.update(rng.choice(N, size=min(k, N), replace=False).tolist())
+    return np.array(sorted(idx))
+
+
+@pytest.mark.parametrize("expanded", [False, True], ids=["spectral", "expanded"])
+@pytest.mark.parametrize("w", WORKLOADS, ids=[w.name for w in WORKLOADS])
+def test_workload_ragged_full_compare(w, expanded, cuda_device):
+    N = w.N if w.N <= 64 else 517
+    x, W, b = make_inputs(w.G, w.C_in, w.C_out, N, w.dtype, seed=0)
+    h, y = _run(x, W, b, cuda_device, expanded)
+    print(f"[kernel] {h.describe()}", flush=True)
+    _check(y, oracle.forward(x, W, b), w.dtype, f"{w.name} N={N} {'expanded' if expanded else 'spectral'}")
+
+
+@pytest.mark.parametrize("expanded", [False, True], ids=["spectral", "expanded"])
+@pytest.mark.parametrize("w", WORKLOADS, ids=[w.name for w in WORKLOADS])
+def test_workload_full_size_sampled(w, expanded, cuda_device):
+    x, W, b = make_inputs(w.G, w.C_in, w.C_out, w.N, w.dtype, seed=0)
+    h, y = _run(x, W, b, cuda_device, expanded)
+    idx = _sample_tokens(w.N)
+    ref = oracle.forward(x[idx], W, b)
+    _check(y[torch.as_tensor(idx, device=y.device)], ref, w.dtype,
+           f"{w.name} full N={w.N} sampled {len(idx)} {'expanded' if expanded else 'spectral'}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("N", [1, 17, 1000])
+def test_edge_token_counts_and_groups(G, N, dtype, cuda_device):
+    C_in, C_out = 32, 48
+    x, W, b = make_inputs(G, C_in, C_out, N, dtype, seed=G * 1000 + N)
+    for bias in (b, None):
+        for expanded in (False, True):
+            _, y = _run(x, W, bias, cuda_device, expanded)
+            _check(y, oracle.forward(x, W, bias), dtype,
+                   f"G={G} N={N} {dtype} bias={bias is not None} expanded={expanded}")
+
+
+@pytest.mark.parametrize("dtype,C_in,C_out", [("bf16", 40, 20), ("bf16", 8, 1), ("bf16", 136, 200),
+                                              ("f32", 5, 3), ("f32", 70, 130)])
+@pytest.mark.parametrize("G", [4, 8])
+def test_ragged_channels(G, dtype, C_in, C_out, cuda_device):
+    N = 203
+    x, W, b = make_inputs(G, C_in, C_out, N, dtype, seed=7)
+    for expanded in (False, True):
+        _, y = _run(x, W, b, cuda_device, expanded)
+        _check(y, oracle.forward(x, W, b), dtype, f"G={G} C_in={C_in} C_out={C_out} {dtype} exp={expanded}")
+
+
+def test_empty_batch(cuda_device):
+    x, W, b = make_inputs(4, 32, 32, 0, "bf16")
+    h, y = _run(x, W, b, cuda_device, expanded=True)
+    assert y.shape == (0, 32, 4)
+    y2 = eq.forward_expanded(h, x.to(cuda_device), b.to(cuda_device))
+    assert y2.shape == (0, 32, 4)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_spectral_weights_match_oracle_dft(G, dtype, cuda_device):
+    C_out, C_in = 40, 48
+    _, W, _ = make_inputs(G, C_in, C_out, 1, dtype, seed=3)
+    h = eq.prepare_weights(W.to(cuda_device))
+    got = eq.export_spectral_weights(h).cpu().double().numpy()
+    Wh = oracle.dft_weights(W)  # [C_out, C_in, G/2+1] complex
+    planes = [Wh[:, :, 0].real]
+    if G >= 2:
+        planes.append(Wh[:, :, G // 2].real)
+    for k in range(1, G // 2):
+        planes += [Wh[:, :, k].real, Wh[:, :, k].imag]
+    ref = np.stack(planes)
+    # The oracle's own fp64 error: its twiddles cos/sin(2 pi d k / G) are not exactly 0 at multiples
+    # of pi/2, so an exactly-zero coefficient comes out near 1e-17 there; bound it by G eps sum|W|.
+    floor = 4 * G * np.finfo(np.float64).eps * np.abs(W.double().numpy()).sum(axis=2)[None]
+    if dtype == "bf16":
+        # one bf16 rounding of an fp32 value: within half a bf16 ulp (2^-8 relative) of the exact DFT
+        tol = np.abs(ref) * 2.0 ** -8 + floor
+    else:
+        tol = np.abs(ref) * 1e-6 + 1e-7
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (int(bad.sum()), got[bad][:5], ref[bad][:5])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_expanded_weight_is_exact_unrolling(G, dtype, cuda_device):
+    _, W, _ = make_inputs(G, 16, 24, 1, dtype, seed=4)
+    h = eq.prepare_weights(W.to(cuda_device), expanded=True)
+    got = eq.export_expanded_weight(h).cpu().double().numpy()
+    np.testing.assert_array_equal(got, oracle.expand(W))
+
+
+def test_equivariance_full_size(cuda_device):
+    # cyclic shift of x along g shifts y along h (holds at any size)
+    w = WORKLOADS[1]
+    x, W, b = make_inputs(w.G, w.C_in, w.C_out, w.N, w.dtype, seed=0)
+    h = eq.prepare_weights(W.to(cuda_device))
+    xd, bd = x.to(cuda_device), b.to(cuda_device)
+    y = eq.forward(h, xd, bd).double()
+    for s in range(1, w.G):
+        ys = eq.forward(h, torch.roll(xd, s, dims=2), bd).double()
+        rel = (torch.linalg.vector_norm(ys - torch.roll(y, s, dims=2)) / torch.linalg.vector_norm(y)).item()
+        print(f"[equivariance] shift={s} rel={rel:.3e}", flush=True)
+        assert rel <= 1e-2
+
+
+@pytest.mark.parametrize("w", WORKLOADS[1:], ids=[w.name for w in WORKLOADS[1:]])
+def test_deterministic(w, cuda_device):
+    x, W, b = make_inputs(w.G, w.C_in, w.C_out, 2048, w.dtype, seed=5)
+    h = eq.prepare_weights(W.to(cuda_device), expanded=True)
+    xd, bd = x.to(cuda_device), b.to(cuda_device)
+    assert torch.equal(eq.forward(h, xd, bd), eq.forward(h, xd, bd))
+    assert torch.equal(eq.forward_expanded(h, xd, bd), eq.forward_expanded(h, xd, bd))
+
+
+def test_abi_rejects_bad_pointers_with_device_tensors(cuda_device):
+    lib = eq.load_library()
+    x, W, b = make_inputs(4, 32, 32, 64, "bf16")
+    h = eq.prepare_weights(W.to(cuda_device), expanded=True)
+    xd = x.to(cuda_device)
+    y = torch.empty((64, 32, 4), dtype=torch.bfloat16, device=cuda_device)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hp = ctypes.c_void_p(h.ptr)
+    mis = ctypes.c_void_p(xd.data_ptr() + 2)
+    assert lib.eqlin_forward(hp, mis, None, ctypes.c_void_p(y.data_ptr()), 63, s) == eq.EQLIN_ERR_INVALID_ARG
+    assert lib.eqlin_forward(hp, ctypes.c_void_p(xd.data_ptr()), None, None, 64, s) == eq.EQLIN_ERR_INVALID_ARG
+    assert lib.eqlin_forward(hp, ctypes.c_void_p(xd.data_ptr()), None, ctypes.c_void_p(y.data_ptr()), -1, s) \
+        == eq.EQLIN_ERR_INVALID_ARG
+    # in-place (x and y overlap) is rejected
+    assert lib.eqlin_forward(hp, ctypes.c_void_p(xd.data_ptr()), None, ctypes.c_void_p(xd.data_ptr()), 64, s) \
+        == eq.EQLIN_ERR_INVALID_ARG
+    h2 = eq.prepare_weights(W.to(cuda_device), expanded=False)
+    assert lib.eqlin_forward_expanded(ctypes.c_void_p(h2.ptr), ctypes.c_void_p(xd.data_ptr()), None,
+                                      ctypes.c_void_p(y.data_ptr()), 64, s) == eq.EQLIN_ERR_INVALID_ARG
+    with pytest.raises(eq.EqlinError):
+        eq.prepare_weights(torch.zeros((4, 12, 4), dtype=torch.bfloat16, device=cuda_device))
+
+
+def test_graph_replay_matches_eager(cuda_device):
+    # The benchmark times HIP-graph replays; every replay must equal the eager result, also with
+    # other eager work and synchronisations between replays.
+    w = WORKLOADS[1]
+    x, W, b = make_inputs(w.G, w.C_in, w.C_out, 4096, w.dtype, seed=9)
+    h = eq.prepare_weights(W.to(cuda_device), expanded=True)
+    x0, x1, bd = x.to(cuda_device), (x.float() * 0.5).to(torch.bfloat16).to(cuda_device), b.to(cuda_device)
+    ref0, ref1 = eq.forward(h, x0, bd), eq.forward_expanded(h, x1, bd)
+    y0, y1 = torch.empty_like(ref0), torch.empty_like(ref1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        eq.forward(h, x0, bd, y0)
+        eq.forward_expanded(h, x1, bd, y1)
+    for r in range(4):
+        y0.zero_()
+        y1.fill_(float("nan"))
+        eq.forward(h, x1, None)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y0, ref0) and torch.equal(y1, ref1), f"replay {r}"
