@@ -60,7 +60,7 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
             return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for spectral weights: %s", p->planes_bytes,
                         hipGetErrorString(e));
         }
-        e = eqlin::launch_prep_frag(W, true, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->planes, s);
+        e = eqlin::launch_prep_frag(W, true, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->fwd.kmap, p->planes, s);
         if (e != hipSuccess) return hip_fail(e, "spectral weight preparation");
     } else {
         if (!eqlin::select_f32(p->G, p->C_in, p->C_out, &p->fwd))
@@ -216,8 +216,8 @@ eqlin_status_t eqlin_export_spectral_weights(eqlin_handle_t h, float *out, eqlin
     if (!h || !out) return fail(EQLIN_ERR_INVALID_ARG, "null handle or out");
     hipError_t e;
     if (h->dtype == EQLIN_BF16)
-        e = eqlin::launch_export_frag(h->planes, h->G, h->C_out, h->C_in, h->KS, h->NB_total, out,
-                                      (hipStream_t)stream);
+        e = eqlin::launch_export_frag(h->planes, h->G, h->C_out, h->C_in, h->KS, h->NB_total, h->fwd.kmap,
+                                      out, (hipStream_t)stream);
     else
         e = eqlin::launch_export_plain_f32((const float *)h->planes, h->G, h->C_out, h->C_in, out,
                                            (hipStream_t)stream);

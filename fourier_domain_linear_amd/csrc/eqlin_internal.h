@@ -11,8 +11,8 @@ namespace eqlin {
 
 // Forward-kernel families.
 enum KernelKind {
-    KIND_ROWBLOCK = 0,  // bf16, small C: a wave holds 16 tokens x the whole C_out tile; x straight to
-                        // registers, the C_out tile's weights staged once in LDS
+    KIND_STREAM = 0,    // bf16, small C_in: persistent workgroup per CU, the C_out tile's weights in
+                        // LDS, 16-token row blocks streamed through the waves, x straight to registers
     KIND_TILED = 1,     // bf16, any C: GEMM-style token x C_out tiles, x planes and weights via LDS
     KIND_F32 = 2        // fp32: vector-ALU spectral kernel
 };
@@ -28,6 +28,8 @@ struct KernelChoice {
     int nb_tile = 1;        // 16-wide output blocks per workgroup tile
     int tokens_per_block = 0;
     int block_threads = 0;
+    int num_cus = 0;        // compute units of the device the plan was made on
+    int kmap = 0;           // k order of the weight fragments: 0 natural, 1 piece-interleaved
     size_t lds_bytes = 0;
     LaunchFn launch = nullptr;
     char name[96] = {0};
@@ -60,7 +62,7 @@ bool select_f32(int G, int C_in, int C_out, KernelChoice *out);
 // ---- prepare.hip ----
 // W [C_out][C_in][G] (bf16 bits or fp32) -> fragment-ordered bf16 spectral planes.
 hipError_t launch_prep_frag(const void *W, bool w_is_bf16, int G, int C_out, int C_in, int KS,
-                            int NB_total, void *frag, hipStream_t s);
+                            int NB_total, int kmap, void *frag, hipStream_t s);
 // W fp32 -> planes [G][C_out][C_in] fp32.
 hipError_t launch_prep_plain_f32(const float *W, int G, int C_out, int C_in, float *planes,
                                  hipStream_t s);
@@ -69,7 +71,7 @@ hipError_t launch_expand(const void *W, int elem_bytes, int G, int C_out, int C_
                          hipStream_t s);
 // stored spectral weights -> canonical fp32 [G][C_out][C_in] with the scaling undone.
 hipError_t launch_export_frag(const void *frag, int G, int C_out, int C_in, int KS, int NB_total,
-                              float *out, hipStream_t s);
+                              int kmap, float *out, hipStream_t s);
 hipError_t launch_export_plain_f32(const float *planes, int G, int C_out, int C_in, float *out,
                                    hipStream_t s);
 

@@ -24,13 +24,16 @@
 // instruction, so a wave's read of a chunk is one linear 1 KB access.
 //
 // Two kernels:
-//   k_rowblock  small channel counts (C_in <= 128): each wave owns 16 tokens x the C_out tile; the
-//               tile's weight chunks are copied to LDS once per workgroup (global_load_lds, no VGPR
-//               staging); x goes straight from global memory into the A operands.
+//   k_stream    small C_in (a row block's x fits in registers): one persistent workgroup per CU
+//               keeps the C_out tile's weight chunks in LDS (copied with global_load_lds, no VGPR
+//               staging) and streams 16-token row blocks through its waves; x goes straight from
+//               global memory into the A operands.
 //   k_tiled     any channel count: workgroup tile BM tokens x BN outputs, 32-channel K steps; the
 //               workgroup DFTs its x slab once into LDS (A operands) and copies the weight chunks of
 //               the step into LDS; each of the 4 waves computes a WM x WN sub-tile for all G planes.
 #include <stdio.h>
+
+#include <algorithm>
 
 #include "device_common.h"
 #include "eqlin_internal.h"
@@ -130,64 +133,289 @@ __device__ __forceinline__ float load_bias(const uint16_t *__restrict__ bias, in
     return bias ? __uint_as_float((uint32_t)bias[idx] << 16) : 0.0f;
 }
 
-// ------------------------------------------------------------------------------------------------
-// k_rowblock<G, KS, NB, NW>: NW waves x 16 tokens per workgroup, NB output blocks of 16 per wave.
-// grid = (ceil(N / (16 NW)), NB_total / NB). Dynamic LDS = NB * KS * G KB (the tile's weights).
-template <int G, int KS, int NB, int NW>
-__global__ __launch_bounds__(NW * 64) void k_rowblock(const uint4 *__restrict__ x4,
-                                                      const uint4 *__restrict__ wfrag,
-                                                      const uint16_t *__restrict__ bias,
-                                                      int bias_shift, uint16_t *__restrict__ y,
-                                                      int64_t N, int C_in, int C_out) {
-    extern __shared__ uint4 lds[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n_base = (int64_t)blockIdx.x * (NW * 16) + wave * 16;
-    const int nb0 = blockIdx.y * NB;
+// Unconditional variant of load_x_step: the token index is clamped to N-1 and the channel group to
+// the last real one, so every lane issues the same G loads (no branches, no zero fill). Rows past N
+// only feed outputs that are never stored; a channel group past C_in only meets zero weight
+// columns (the prepared weights are zero-padded), so its (finite) duplicate data contributes 0.
+template <int G>
+__device__ __forceinline__ void load_x_clamped(const uint4 *__restrict__ x4, int64_t n, int64_t N,
+                                               int C_in, int i0, uint4 (&r)[G]) {
+    const int64_t nc = n < N ? n : N - 1;
+    const int ic = i0 < C_in ? i0 : C_in - 8;
+    const uint4 *p = x4 + ((nc * C_in + ic) >> 3) * G;
+#pragma unroll
+    for (int q = 0; q < G; ++q) r[q] = p[q];
+}
 
-    // 1. this wave's activations: all K steps in flight at once
-    uint4 xr[KS][G];
-    const int64_t n_ld = n_base + (lane & 15);
+// The 2G-2 real products with the weights as the A operand (rows = outputs) and the x planes as
+// the B operand (columns = tokens): D lane l holds outputs 4*(l/16)+v of token l%16.
+template <int G>
+__device__ __forceinline__ void spectral_mfma_wx(const uint4 (&w)[G], const uint4 (&a)[G],
+                                                 const uint4 (&an)[G], f32x4 (&acc)[G]) {
+    acc[0] = mfma16x16x32(w[0], a[0], acc[0]);
+    if constexpr (G >= 2) acc[1] = mfma16x16x32(w[1], a[1], acc[1]);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load_x_step<G>(x4, n_ld, N, C_in, ks * 32 + (lane >> 4) * 8, xr[ks]);
-
-    // 2. the C_out tile's weight chunks -> LDS (contiguous in global memory for a tile)
-    constexpr int CHUNKS = NB * KS * G;
-    const uint4 *src = wfrag + (size_t)nb0 * KS * G * 64;
-    for (int c = wave; c < CHUNKS; c += NW) chunk_to_lds(src + c * 64 + lane, lds + c * 64);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // 3. DFT -> A operands, then the per-frequency products for every output block
-    f32x4 acc[NB][G];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int p = 0; p < G; ++p) acc[nb][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 a[G], an[G];
-        dft_to_frags<G>(xr[ks], a);
-        negate_imag<G>(a, an);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            uint4 bw[G];
-#pragma unroll
-            for (int p = 0; p < G; ++p) bw[p] = lds[((nb * KS + ks) * G + p) * 64 + lane];
-            spectral_mfma<G>(a, an, bw, acc[nb]);
-        }
+    for (int k = 1; k < G / 2; ++k) {
+        const int r = 2 * k, i = 2 * k + 1;
+        acc[r] = mfma16x16x32(w[r], a[r], acc[r]);
+        acc[r] = mfma16x16x32(w[i], an[i], acc[r]);
+        acc[i] = mfma16x16x32(w[i], a[r], acc[i]);
+        acc[i] = mfma16x16x32(w[r], a[i], acc[i]);
     }
+}
 
-    // 4./5. inverse DFT + bias, store
+// Inverse DFT of the 4 consecutive outputs v = 0..3 a lane holds (bias already in plane 0), then
+// one contiguous store of 4*G bf16 at dst (16-byte aligned when G >= 2).
+template <int G>
+__device__ __forceinline__ void store_quad(const f32x4 (&acc)[G], uint16_t *__restrict__ dst) {
+    float out[4 * G];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int o = (nb0 + nb) * 16 + (lane & 15);
-        if (o >= C_out) continue;
-        const float bo = load_bias(bias, o >> bias_shift);
+    for (int v = 0; v < 4; ++v) {
+        float Y[G];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t n = n_base + 4 * (lane >> 4) + v;
-            if (n < N) store_row<G>(acc[nb], v, bo, y, n, C_out, o);
+        for (int p = 0; p < G; ++p) Y[p] = acc[p][v];
+        inverse_planes<G>(Y, out + v * G);
+    }
+    if constexpr (G == 1) {
+        uint2 w;
+        w.x = pack_bf16x2(out[0], out[1]);
+        w.y = pack_bf16x2(out[2], out[3]);
+        *reinterpret_cast<uint2 *>(dst) = w;
+    } else {
+#pragma unroll
+        for (int q = 0; q < G / 2; ++q) reinterpret_cast<uint4 *>(dst)[q] = pack_bf16x8(out + 8 * q);
+    }
+}
+
+// Element-wise tail store for a partial output block or the last token rows: output o0 + v of token n.
+template <int G>
+__device__ __forceinline__ void store_quad_masked(const f32x4 (&acc)[G], uint16_t *__restrict__ y,
+                                                  int64_t n, int64_t N, int o0, int C_out) {
+    if (n >= N) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        if (o0 + v >= C_out) continue;
+        float Y[G], out[G];
+#pragma unroll
+        for (int p = 0; p < G; ++p) Y[p] = acc[p][v];
+        inverse_planes<G>(Y, out);
+        uint16_t *dst = y + (n * C_out + o0 + v) * G;
+#pragma unroll
+        for (int h = 0; h < G; ++h) dst[h] = pack_bf16(out[h]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// k_stream<G, KS>: small C_in (KS 32-channel steps held in registers). One persistent workgroup of
+// NW waves per CU and per C_out tile. The tile's weight chunks are staged in LDS once; the
+// workgroup's token range is an even share of the 16-token row blocks, dealt round-robin to its
+// waves. Per row block a wave: DFTs the block (x already in registers), issues the loads of its
+// next block, then for each 16-output block runs the K-step products and stores the result, so the
+// stores of one output block overlap the products of the next and the next block's loads overlap
+// both.
+// grid = (token workgroups, C_out tiles); dynamic LDS = nb_tile * KS * G KB.
+constexpr int kStreamWaves = 8;
+constexpr int kStreamBiasPerThread = 8;  // bias values staged per thread: tiles of <= 4096 outputs
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory operations are
+// outstanding and all LDS/scalar-memory operations are done; export counter not waited on.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+static_assert(waitcnt_vm_lgkm0(0) == 0x70, "waitcnt encoding");
+
+// Geometry of the stream kernel's data movement for group order G. Every global access moves whole
+// 128-byte lines: x arrives through coalesced non-temporal loads and is re-ordered into matrix-core
+// operands through a small per-wave LDS exchange buffer; y leaves the same way in reverse.
+//   x exchange unit: U K-steps (32 channels each) of 16 rows; PX 16-byte pieces per row.
+//   y store unit: UO 16-output blocks of 16 rows; PPR 16-byte pieces per row.
+// A lane's operand for K-step ks, load q, lane group g = lane/16 is piece 4q + g of the K-step's
+// 4G pieces of its row (whole channels: a piece holds 8/G channels x G samples); the prepared
+// weights use the same k order.
+template <int G>
+struct StreamGeom {
+    static constexpr int U = G == 1 ? 2 : 1;
+    static constexpr int PX = 4 * G * U;
+    static constexpr int XROWS = 64 / PX;   // rows per coalesced load instruction
+    static constexpr int XINST = 16 / XROWS;
+    static constexpr int UO = G >= 4 ? 1 : 4 / G;
+    static constexpr int PPR = UO * 2 * G;
+    static constexpr int OROWS = 64 / PPR;  // rows per store instruction
+    static constexpr int OINST = 16 / OROWS;
+    static constexpr int SCRATCH = 16 * 16 * (PX > PPR ? PX : PPR);  // bytes per wave
+};
+
+// XOR swizzle of a 16-row x P-piece tile in LDS: conflict-free for both the row-major coalesced side
+// and the column-wise (16 rows, one piece) operand side.
+template <int P>
+__device__ __forceinline__ int swz(int r, int p) { return r * P + (p ^ (r & 7)); }
+
+__device__ __forceinline__ uint4 ld_nt(const uint4 *p) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(uint4 *p, const uint4 &v) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
+
+// Coalesced non-temporal loads of one 16-token row block: exchange unit u, instruction i, lane l
+// reads piece u*PX + l%PX of row i*XROWS + l/PX. Tokens past N re-read row N-1 and pieces past the
+// row end re-read its last piece (both discarded: never stored / met by zero weight columns).
+template <int G, int KS>
+__device__ __forceinline__ void load_x_raw(const uint4 *__restrict__ x4, int64_t blk, int64_t N,
+                                           int row_pieces, int lane,
+                                           uint4 (&xr)[KS / StreamGeom<G>::U][StreamGeom<G>::XINST]) {
+    using SG = StreamGeom<G>;
+#pragma unroll
+    for (int u = 0; u < KS / SG::U; ++u)
+#pragma unroll
+        for (int i = 0; i < SG::XINST; ++i) {
+            const int64_t n = blk * 16 + i * SG::XROWS + lane / SG::PX;
+            const int64_t nc = n < N ? n : N - 1;
+            const int pc = min(u * SG::PX + lane % SG::PX, row_pieces - 1);
+            xr[u][i] = ld_nt(x4 + nc * row_pieces + pc);
+        }
+}
+
+template <int G, int KS>
+__global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__restrict__ x4,
+                                                              const uint4 *__restrict__ wfrag,
+                                                              const uint16_t *__restrict__ bias,
+                                                              int bias_shift, uint16_t *__restrict__ y,
+                                                              int64_t N, int C_in, int C_out,
+                                                              int nb_tile) {
+    using SG = StreamGeom<G>;
+    static_assert(KS % SG::U == 0, "KS must be a multiple of the exchange unit");
+    constexpr int NU = KS / SG::U;
+    extern __shared__ uint4 lds[];
+    constexpr int NW = kStreamWaves;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int nb0 = blockIdx.y * nb_tile;
+    const int64_t blocks = (N + 15) >> 4;
+    const int64_t b0 = (int64_t)blockIdx.x * blocks / gridDim.x;
+    const int64_t b1 = (int64_t)(blockIdx.x + 1) * blocks / gridDim.x;
+    const int row_pieces = C_in * G / 8;             // 16-byte pieces per x row
+    const int yrow_pieces = C_out * G / 8;           // 16-byte pieces per y row (when C_out*G % 8 == 0)
+
+    // LDS: [weights: nb_tile*KS*G KB][bias: nb_tile*16 fp32][per-wave scratch: SCRATCH bytes each]
+    const int chunks = nb_tile * KS * G;
+    float *lbias = reinterpret_cast<float *>(lds + chunks * 64);
+    uint4 *scratch = lds + chunks * 64 + nb_tile * 4 + wave * (SG::SCRATCH / 16);
+
+    // Prologue, ordered so that the x loads of the wave's first block are the youngest memory
+    // operations: (1) this thread's share of the tile's bias (raw bf16, clamped unconditional
+    // loads), (2) the tile's weight chunks global -> LDS (contiguous in global memory for a tile),
+    // (3) x. The barrier then waits only for (1) and (2) -- vector-memory counter down to the KS*G
+    // x loads, which complete in order after them -- so each wave starts as soon as its own x has
+    // arrived. s_barrier is issued without the block-wide memory fence of __syncthreads() (which
+    // would wait for the x loads too). Without a bias the loads read the weight buffer instead
+    // (valid memory, discarded), so no loaded value is selected before the wait.
+    const int n_bias = nb_tile * 16;
+    const int bias_len = (C_out + (1 << bias_shift) - 1) >> bias_shift;
+    const uint16_t *bsrc = bias ? bias : reinterpret_cast<const uint16_t *>(wfrag);
+    const int blen = bias ? bias_len : 1;
+    uint32_t braw[kStreamBiasPerThread];
+#pragma unroll
+    for (int k = 0; k < kStreamBiasPerThread; ++k) {
+        const int o = nb0 * 16 + threadIdx.x + k * NW * 64;
+        braw[k] = bsrc[min(o >> bias_shift, blen - 1)];
+    }
+    const uint4 *src = wfrag + (size_t)nb0 * KS * G * 64;
+    for (int c = wave; c < chunks; c += NW) chunk_to_lds(src + c * 64 + lane, lds + c * 64);
+
+    // (a wave without a block of its own loads the workgroup's first block: cache hits, discarded)
+    int64_t blk = b0 + wave;
+    uint4 xr[NU][SG::XINST];
+    __builtin_amdgcn_sched_barrier(0);
+    load_x_raw<G, KS>(x4, blk < b1 ? blk : b0, N, row_pieces, lane, xr);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KS * G));
+#pragma unroll
+    for (int k = 0; k < kStreamBiasPerThread; ++k) {
+        const int t = threadIdx.x + k * NW * 64;
+        if (t < n_bias) lbias[t] = (bias && nb0 * 16 + t < C_out) ? __uint_as_float(braw[k] << 16) : 0.f;
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    asm volatile("s_barrier" ::: "memory");
+
+    const int nb_end = min(nb_tile, (C_out + 15) / 16 - nb0);
+    const bool vec_rows = (C_out * G) % 8 == 0;  // 16-byte pieces tile the y rows exactly
+    for (; blk < b1; blk += NW) {
+        // x: exchange through LDS into operand order, then the group DFT -> bf16 planes
+        uint4 a[KS][G], an[KS][G];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int i = 0; i < SG::XINST; ++i)
+                scratch[swz<SG::PX>(i * SG::XROWS + lane / SG::PX, lane % SG::PX)] = xr[u][i];
+#pragma unroll
+            for (int ku = 0; ku < SG::U; ++ku) {
+                uint4 r[G];
+#pragma unroll
+                for (int q = 0; q < G; ++q) r[q] = scratch[swz<SG::PX>(lane & 15, ku * 4 * G + 4 * q + g)];
+                dft_to_frags<G>(r, a[u * SG::U + ku]);
+                negate_imag<G>(a[u * SG::U + ku], an[u * SG::U + ku]);
+            }
+        }
+        const int64_t nxt = blk + NW;
+        if (nxt < b1) load_x_raw<G, KS>(x4, nxt, N, row_pieces, lane, xr);
+
+        const int64_t nrow0 = blk * 16;
+        for (int nb = 0; nb < nb_end; ++nb) {
+            const float4 bq = reinterpret_cast<const float4 *>(lbias)[nb * 4 + g];
+            f32x4 acc[G];
+            acc[0] = f32x4{bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+            for (int p = 1; p < G; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                uint4 bw[G];
+#pragma unroll
+                for (int p = 0; p < G; ++p) bw[p] = lds[((nb * KS + ks) * G + p) * 64 + lane];
+                spectral_mfma_wx<G>(bw, a[ks], an[ks], acc);
+            }
+            if (!vec_rows) {
+                store_quad_masked<G>(acc, y, nrow0 + (lane & 15), N, (nb0 + nb) * 16 + 4 * g, C_out);
+                continue;
+            }
+            // inverse DFT -> this lane's 4 outputs x G (8G bytes) -> staging row lane%16
+            float out[4 * G];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float Y[G];
+#pragma unroll
+                for (int p = 0; p < G; ++p) Y[p] = acc[p][v];
+                inverse_planes<G>(Y, out + v * G);
+            }
+            const int ub = nb % SG::UO;  // block within the store unit
+            if constexpr (G == 1) {
+                uint2 w;
+                w.x = pack_bf16x2(out[0], out[1]);
+                w.y = pack_bf16x2(out[2], out[3]);
+                // 8 bytes at byte (ub*32 + g*8) of the row's 128-byte unit segment
+                const int piece = ub * 2 + (g >> 1);
+                reinterpret_cast<uint2 *>(scratch + swz<SG::PPR>(lane & 15, piece))[g & 1] = w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < G / 2; ++k)
+                    scratch[swz<SG::PPR>(lane & 15, ub * 2 * G + g * (G / 2) + k)] = pack_bf16x8(out + 8 * k);
+            }
+            if (ub == SG::UO - 1 || nb == nb_end - 1) {
+                // whole 16-byte pieces of the unit's rows, full lines per instruction, non-temporal
+                const int unit_o0 = (nb0 + nb - ub) * 16;                 // first output of the unit
+                const int piece0 = unit_o0 * G / 8;
+#pragma unroll
+                for (int j = 0; j < SG::OINST; ++j) {
+                    const int r = j * SG::OROWS + lane / SG::PPR, pc = lane % SG::PPR;
+                    const uint4 v = scratch[swz<SG::PPR>(r, pc)];
+                    // only the pieces of blocks computed in this unit (a tile's last unit may be
+                    // partial; the rest of its row belongs to the next tile or past C_out)
+                    if (nrow0 + r < N && pc < (ub + 1) * 2 * G && piece0 + pc < yrow_pieces)
+                        st_nt(reinterpret_cast<uint4 *>(y) + (nrow0 + r) * yrow_pieces + piece0 + pc, v);
+                }
+            }
         }
     }
 }
@@ -289,21 +517,38 @@ static hipError_t set_lds_limit(const void *fn, size_t bytes) {
     return e;
 }
 
-template <int G, int KS, int NB>
-static hipError_t launch_rowblock(const Plan *p, const void *x, const void *b, void *y, int64_t N,
-                                  hipStream_t s) {
-    constexpr int NW = 4;
-    const auto fn = k_rowblock<G, KS, NB, NW>;
-    const size_t lds = (size_t)NB * KS * G * 1024;
-    const dim3 grid((unsigned)((N + NW * 16 - 1) / (NW * 16)), (unsigned)(p->NB_total / NB));
-    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, s, (const uint4 *)x, (const uint4 *)p->planes,
-                       (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out);
+static int g_num_cus = 0;
+
+static int num_cus() {
+    if (g_num_cus <= 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            g_num_cus = n;
+        else
+            g_num_cus = 256;
+    }
+    return g_num_cus;
+}
+
+template <int G, int KS>
+static hipError_t launch_stream(const Plan *p, const void *x, const void *b, void *y, int64_t N,
+                                hipStream_t s) {
+    const size_t lds = p->fwd.lds_bytes;
+    const int64_t blocks = (N + 15) / 16;
+    const int tiles = p->NB_total / p->fwd.nb_tile;
+    // one workgroup per CU in total (over all C_out tiles), at least one row block each
+    int64_t wg = std::max<int64_t>(1, p->fwd.num_cus / tiles);
+    wg = std::min<int64_t>(wg, blocks);
+    hipLaunchKernelGGL((k_stream<G, KS>), dim3((unsigned)wg, (unsigned)tiles), dim3(kStreamWaves * 64), lds, s,
+                       (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
+                       (uint16_t *)y, N, p->C_in, p->C_out, p->fwd.nb_tile);
     return hipGetLastError();
 }
 
-template <int G, int KS, int NB>
-static hipError_t init_rowblock() {
-    return set_lds_limit((const void *)k_rowblock<G, KS, NB, 4>, (size_t)NB * KS * G * 1024);
+template <int G, int KS>
+static hipError_t init_stream(size_t lds) {
+    return set_lds_limit((const void *)k_stream<G, KS>, lds);
 }
 
 template <int G, int BM, int BN, int WM, int WN>
@@ -323,20 +568,21 @@ static hipError_t init_tiled() {
                          (size_t)(G * (BM / 16) + (BN / 16) * G) * 1024);
 }
 
-struct RowblockEntry {
-    int G, KS, NB;
+struct StreamEntry {
+    int G, KS;
     LaunchFn launch;
-    hipError_t (*init)();
+    hipError_t (*init)(size_t);
 };
-#define RB(G, KS, NB) {G, KS, NB, launch_rowblock<G, KS, NB>, init_rowblock<G, KS, NB>}
-static const RowblockEntry kRowblock[] = {
-    RB(1, 1, 8), RB(1, 2, 8), RB(1, 3, 8), RB(1, 4, 8),
-    RB(2, 1, 8), RB(2, 2, 8), RB(2, 3, 8), RB(2, 4, 8),
-    RB(4, 1, 4), RB(4, 2, 4), RB(4, 3, 4), RB(4, 4, 4),
-    RB(4, 1, 6), RB(4, 2, 6), RB(4, 3, 6),
-    RB(8, 1, 4), RB(8, 2, 4), RB(8, 3, 2), RB(8, 4, 2),
+#define SE(G, KS) {G, KS, launch_stream<G, KS>, init_stream<G, KS>}
+static const StreamEntry kStream[] = {
+    SE(1, 2), SE(1, 4), SE(1, 6), SE(1, 8), SE(1, 10), SE(1, 12), SE(1, 14), SE(1, 16),
+    SE(2, 1), SE(2, 2), SE(2, 3), SE(2, 4), SE(2, 6), SE(2, 8),
+    SE(4, 1), SE(4, 2), SE(4, 3), SE(4, 4),
+    SE(8, 1), SE(8, 2),
 };
-#undef RB
+#undef SE
+static constexpr size_t kStreamLdsMax = 160 * 1024;
+static constexpr int kStreamMaxTiles = 4;
 
 struct TiledEntry {
     int G, BM, BN;
@@ -352,42 +598,53 @@ static const TiledEntry kTiled[] = {
 };
 #undef TL
 
+static size_t stream_scratch(int G) {
+    switch (G) {
+        case 1: return StreamGeom<1>::SCRATCH;
+        case 2: return StreamGeom<2>::SCRATCH;
+        case 4: return StreamGeom<4>::SCRATCH;
+        default: return StreamGeom<8>::SCRATCH;
+    }
+}
+
 bool select_bf16(int G, int C_in, int C_out, KernelChoice *out) {
     const int KS = (C_in + 31) / 32;
     const int nb_needed = (C_out + 15) / 16;
-    // Rowblock when the whole (or half the) output fits one or two tiles and C_in <= 128: the DFT is
-    // then done at most twice per token and x streams straight into registers.
-    const RowblockEntry *best = nullptr;
-    int best_waste = 1 << 30;
-    for (const auto &e : kRowblock) {
+    // Stream kernel when x of a row block fits in registers (an instantiated KS) and the C_out tiles
+    // whose weights fit LDS number at most kStreamMaxTiles (x is re-read and re-transformed per tile).
+    for (const auto &e : kStream) {
         if (e.G != G || e.KS != KS) continue;
-        const int tiles = (nb_needed + e.NB - 1) / e.NB;
-        if (tiles > 2) continue;
-        const int waste = tiles * e.NB - nb_needed;
-        if (waste < best_waste || (waste == best_waste && best && e.NB > best->NB)) {
-            best = &e;
-            best_waste = waste;
-        }
-    }
-    if (best) {
-        (void)best->init();
-        out->kind = KIND_ROWBLOCK;
-        out->nb_tile = best->NB;
-        out->tokens_per_block = 64;
-        out->block_threads = 256;
-        out->lds_bytes = (size_t)best->NB * KS * G * 1024;
-        out->launch = best->launch;
-        snprintf(out->name, sizeof(out->name), "bf16 rowblock G=%d KS=%d NB=%d waves=4", G, KS, best->NB);
+        const size_t fixed = (size_t)kStreamWaves * stream_scratch(G);
+        const size_t per_nb = (size_t)KS * G * 1024 + 16 * sizeof(float);
+        const int nb_fit = (int)((kStreamLdsMax - fixed) / per_nb);
+        if (nb_fit < 1) break;
+        const int tiles = (nb_needed + nb_fit - 1) / nb_fit;
+        if (tiles > kStreamMaxTiles) break;
+        const int nb_tile = (nb_needed + tiles - 1) / tiles;
+        if (nb_tile * 16 > kStreamBiasPerThread * kStreamWaves * 64) break;
+        out->kind = KIND_STREAM;
+        out->nb_tile = nb_tile;
+        out->tokens_per_block = 16;
+        out->block_threads = kStreamWaves * 64;
+        out->lds_bytes = (size_t)nb_tile * per_nb + fixed;
+        out->num_cus = num_cus();
+        out->kmap = 1;
+        out->launch = e.launch;
+        (void)e.init(out->lds_bytes);
+        snprintf(out->name, sizeof(out->name), "bf16 stream G=%d KS=%d nb_tile=%d tiles=%d waves=%d", G, KS,
+                 nb_tile, tiles, kStreamWaves);
         return true;
     }
     for (const auto &e : kTiled) {
         if (e.G != G) continue;
         (void)e.init();
         out->kind = KIND_TILED;
+        out->kmap = 0;
         out->nb_tile = e.BN / 16;
         out->tokens_per_block = e.BM;
         out->block_threads = 256;
         out->lds_bytes = (size_t)(G * (e.BM / 16) + (e.BN / 16) * G) * 1024;
+        out->num_cus = num_cus();
         out->launch = e.launch;
         snprintf(out->name, sizeof(out->name), "bf16 tiled G=%d BM=%d BN=%d KS=%d", G, e.BM, e.BN, KS);
         return true;

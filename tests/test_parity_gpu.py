@@ -94,6 +94,7 @@ def test_edge_token_counts_and_groups(G, N, dtype, cuda_device):
 
 
 @pytest.mark.parametrize("dtype,C_in,C_out", [("bf16", 40, 20), ("bf16", 8, 1), ("bf16", 136, 200),
+                                              ("bf16", 96, 200), ("bf16", 96, 100), ("bf16", 64, 54),
                                               ("f32", 5, 3), ("f32", 70, 130)])
 @pytest.mark.parametrize("G", [4, 8])
 def test_ragged_channels(G, dtype, C_in, C_out, cuda_device):
