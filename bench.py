@@ -20,7 +20,6 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -31,20 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "EQ-Linear fwd tokens/s + % of bf16 MFMA/HBM roofline vs expanded dense GEMM"
-KERNEL_SOURCES = ["fourier_domain_linear_amd/csrc/fwd_bf16.hip", "fourier_domain_linear_amd/csrc/device_common.h",
-                  "fourier_domain_linear_amd/csrc/dft.h"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
 
 
 def load_traffic(workload: str):
@@ -55,6 +44,8 @@ def load_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
+    from fourier_domain_linear_amd.profiling import kernel_source_hash
+
     if rec.get("source_sha256") != kernel_source_hash():
         log(f"[bench] {path} was taken on other kernel sources: traffic = null")
         return None
@@ -133,7 +124,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-expanded", action="store_true")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (the counter calibration for traffic)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+
+        a = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(max(1, args.steps)):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "launches": max(1, args.steps)}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer is token-parallel "

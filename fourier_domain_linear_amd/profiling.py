@@ -1,0 +1,132 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+    # kernel durations (rocprofv3 --kernel-trace --stats -f csv ...)
+    python -m fourier_domain_linear_amd.profiling stats DIR --cmd "<the rocprofv3 command>" --out FILE.txt
+
+    # HBM traffic per launch from two counter runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
+    # each scaled by what the same counter reads for a plain device copy of known size
+    python -m fourier_domain_linear_amd.profiling traffic --kernel k_stream \
+        --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes B \
+        --workload NAME --cmd "..." --out profiles/traffic_NAME.json
+
+DIR is a rocprofv3 output directory (-d); the CSV files are found by name inside it.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ["fourier_domain_linear_amd/csrc/fwd_bf16.hip", "fourier_domain_linear_amd/csrc/device_common.h",
+                  "fourier_domain_linear_amd/csrc/dft.h"]
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the forward kernel's sources (a counter summary is valid only for these)."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _find(d: str, pattern: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no {pattern} under {d}")
+    return hits[0]
+
+
+def kernel_stats(d: str):
+    """Rows of the rocprofv3 kernel statistics CSV: (name, calls, avg_ns, min_ns, max_ns, total_ns, pct)."""
+    rows = []
+    with open(_find(d, "*kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                         float(r["MaxNs"]), float(r["TotalDurationNs"]), float(r["Percentage"])))
+    return rows
+
+
+def counter_per_dispatch(d: str, kernel: str, counter: str):
+    """Values of `counter` summed over its hardware instances, one per dispatch of kernels whose
+    name contains `kernel`."""
+    per = collections.defaultdict(float)
+    with open(_find(d, "*counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"no {counter} samples for kernels matching {kernel!r} in {d}")
+    return list(per.values())
+
+
+def _avg(v):
+    return sum(v) / len(v)
+
+
+def cmd_stats(a):
+    rows = kernel_stats(a.dir)
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {a.cmd}", "",
+             f"{'kernel':<90} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+    for name, calls, avg, mn, mx, tot, pct in sorted(rows, key=lambda r: -r[5]):
+        lines.append(f"{name[:90]:<90} {calls:>6} {avg / 1e3:>9.3f} {mn / 1e3:>9.3f} {mx / 1e3:>9.3f} {pct:>6.2f}")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
+def cmd_traffic(a):
+    fetch = counter_per_dispatch(a.fetch, a.kernel, "FETCH_SIZE")
+    write = counter_per_dispatch(a.write, a.kernel, "WRITE_SIZE")
+    cfetch = counter_per_dispatch(a.copy_fetch, a.copy_kernel, "FETCH_SIZE")
+    cwrite = counter_per_dispatch(a.copy_write, a.copy_kernel, "WRITE_SIZE")
+    # the copy reads and writes copy_bytes each: bytes per KiB of counter reading
+    f_scale = a.copy_bytes / _avg(cfetch)
+    w_scale = a.copy_bytes / _avg(cwrite)
+    rd, wr = _avg(fetch) * f_scale, _avg(write) * w_scale
+    rec = {
+        "workload": a.workload, "kernel": a.kernel, "source_sha256": kernel_source_hash(),
+        "fetch_kib_per_dispatch": _avg(fetch), "write_kib_per_dispatch": _avg(write),
+        "copy_bytes": a.copy_bytes, "copy_fetch_kib": _avg(cfetch), "copy_write_kib": _avg(cwrite),
+        "fetch_scale_bytes_per_kib": f_scale, "write_scale_bytes_per_kib": w_scale,
+        "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+        "traffic_bytes_per_launch": rd + wr, "dispatches": [len(fetch), len(write)], "command": a.cmd,
+    }
+    with open(a.out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out")
+    t = sub.add_parser("traffic")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-kernel", default="copy")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    {"stats": cmd_stats, "traffic": cmd_traffic}[a.what](a)
+
+
+if __name__ == "__main__":
+    main()
