@@ -12,6 +12,7 @@ namespace eqlin {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -51,6 +52,14 @@ __device__ __forceinline__ uint4 neg_bf16x8(const uint4 &v) {
 // 8*(l/16) .. 8*(l/16)+7; D: lane l holds rows 4*(l/16) + v (v = 0..3) of column l%16.
 __device__ __forceinline__ f32x4 mfma16x16x32(const uint4 &a, const uint4 &b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Operand layout (lane l of 64): A row l%32, B column l%32, both holding the 8 consecutive k values
+// 8*(l/32) .. 8*(l/32)+7; D: lane l holds rows 8*(v/4) + 4*(l/32) + v%4 (v = 0..15) of column l%32.
+__device__ __forceinline__ f32x16 mfma32x32x16(const uint4 &a, const uint4 &b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 

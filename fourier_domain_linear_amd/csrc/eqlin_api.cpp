@@ -50,8 +50,9 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
         if (!eqlin::select_bf16(p->G, p->C_in, p->C_out, &p->fwd))
             return fail(EQLIN_ERR_UNSUPPORTED, "no bf16 kernel for G=%d C_in=%d C_out=%d", p->G, p->C_in,
                         p->C_out);
-        p->KS = (p->C_in + 31) / 32;
-        const int nb = (p->C_out + 15) / 16;
+        const int ks = (p->C_in + p->fwd.kc - 1) / p->fwd.kc;
+        p->KS = (ks + p->fwd.ks_mult - 1) / p->fwd.ks_mult * p->fwd.ks_mult;
+        const int nb = (p->C_out + p->fwd.rows_per_block - 1) / p->fwd.rows_per_block;
         p->NB_total = (nb + p->fwd.nb_tile - 1) / p->fwd.nb_tile * p->fwd.nb_tile;
         p->planes_bytes = (size_t)p->NB_total * p->KS * p->G * 1024;
         e = hipMalloc(&p->planes, p->planes_bytes);
@@ -60,7 +61,7 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
             return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for spectral weights: %s", p->planes_bytes,
                         hipGetErrorString(e));
         }
-        e = eqlin::launch_prep_frag(W, true, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->fwd.kmap, p->planes, s);
+        e = eqlin::launch_prep_frag(W, true, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->fwd.frag_kind, p->planes, s);
         if (e != hipSuccess) return hip_fail(e, "spectral weight preparation");
     } else {
         if (!eqlin::select_f32(p->G, p->C_in, p->C_out, &p->fwd))
@@ -216,7 +217,7 @@ eqlin_status_t eqlin_export_spectral_weights(eqlin_handle_t h, float *out, eqlin
     if (!h || !out) return fail(EQLIN_ERR_INVALID_ARG, "null handle or out");
     hipError_t e;
     if (h->dtype == EQLIN_BF16)
-        e = eqlin::launch_export_frag(h->planes, h->G, h->C_out, h->C_in, h->KS, h->NB_total, h->fwd.kmap,
+        e = eqlin::launch_export_frag(h->planes, h->G, h->C_out, h->C_in, h->KS, h->NB_total, h->fwd.frag_kind,
                                       out, (hipStream_t)stream);
     else
         e = eqlin::launch_export_plain_f32((const float *)h->planes, h->G, h->C_out, h->C_in, out,

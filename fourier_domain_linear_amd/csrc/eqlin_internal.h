@@ -13,7 +13,8 @@ namespace eqlin {
 enum KernelKind {
     KIND_STREAM = 0,    // bf16, small C_in: persistent workgroup per CU, the C_out tile's weights in
                         // LDS, 16-token row blocks streamed through the waves, x straight to registers
-    KIND_TILED = 1,     // bf16, any C: GEMM-style token x C_out tiles, x planes and weights via LDS
+    KIND_TILED = 1,     // bf16, any C: GEMM-style output x token tiles on 32x32x16 matrix cores, x
+                        // planes (transformed once per stage) and weights double-buffered in LDS
     KIND_F32 = 2        // fp32: vector-ALU spectral kernel
 };
 
@@ -29,7 +30,11 @@ struct KernelChoice {
     int tokens_per_block = 0;
     int block_threads = 0;
     int num_cus = 0;        // compute units of the device the plan was made on
-    int kmap = 0;           // k order of the weight fragments: 0 natural, 1 piece-interleaved
+    int frag_kind = 1;      // weight fragment layout (prepare.hip): 1 = 16x32 chunks, stream k order;
+                            // 2 = 32x16 chunks, natural k order
+    int rows_per_block = 16;  // outputs per fragment chunk
+    int kc = 32;            // input channels per K-step (per fragment chunk)
+    int ks_mult = 1;        // K-steps are padded to a multiple of this
     size_t lds_bytes = 0;
     LaunchFn launch = nullptr;
     char name[96] = {0};
@@ -45,8 +50,8 @@ struct Plan {
     // spectral weights. bf16: fragment-ordered chunks (see prepare.hip); f32: planes [G][C_out][C_in]
     void *planes = nullptr;
     size_t planes_bytes = 0;
-    int KS = 0;        // bf16: 32-channel K-steps (C_in padded up to a multiple of 32)
-    int NB_total = 0;  // bf16: 16-wide output blocks (C_out padded up to a multiple of the tile)
+    int KS = 0;        // bf16: K-steps of fwd.kc channels (C_in padded up; a multiple of ks_mult)
+    int NB_total = 0;  // bf16: output blocks of fwd.rows_per_block (C_out padded to the tile)
     KernelChoice fwd;
 
     // unrolled weight (flags & EQLIN_PREPARE_EXPANDED): a G = 1 plan over E, plus E itself
@@ -56,13 +61,15 @@ struct Plan {
 
 // ---- fwd_bf16.hip ----
 bool select_bf16(int G, int C_in, int C_out, KernelChoice *out);
+// ---- fwd_big.hip ----
+bool select_big(int G, int C_in, int C_out, KernelChoice *out);
 // ---- fwd_f32.hip ----
 bool select_f32(int G, int C_in, int C_out, KernelChoice *out);
 
 // ---- prepare.hip ----
 // W [C_out][C_in][G] (bf16 bits or fp32) -> fragment-ordered bf16 spectral planes.
 hipError_t launch_prep_frag(const void *W, bool w_is_bf16, int G, int C_out, int C_in, int KS,
-                            int NB_total, int kmap, void *frag, hipStream_t s);
+                            int NB_total, int frag_kind, void *frag, hipStream_t s);
 // W fp32 -> planes [G][C_out][C_in] fp32.
 hipError_t launch_prep_plain_f32(const float *W, int G, int C_out, int C_in, float *planes,
                                  hipStream_t s);
@@ -71,7 +78,7 @@ hipError_t launch_expand(const void *W, int elem_bytes, int G, int C_out, int C_
                          hipStream_t s);
 // stored spectral weights -> canonical fp32 [G][C_out][C_in] with the scaling undone.
 hipError_t launch_export_frag(const void *frag, int G, int C_out, int C_in, int KS, int NB_total,
-                              int kmap, float *out, hipStream_t s);
+                              int frag_kind, float *out, hipStream_t s);
 hipError_t launch_export_plain_f32(const float *planes, int G, int C_out, int C_in, float *out,
                                    hipStream_t s);
 

@@ -28,9 +28,7 @@
 //               keeps the C_out tile's weight chunks in LDS (copied with global_load_lds, no VGPR
 //               staging) and streams 16-token row blocks through its waves; x goes straight from
 //               global memory into the A operands.
-//   k_tiled     any channel count: workgroup tile BM tokens x BN outputs, 32-channel K steps; the
-//               workgroup DFTs its x slab once into LDS (A operands) and copies the weight chunks of
-//               the step into LDS; each of the 4 waves computes a WM x WN sub-tile for all G planes.
+//   (larger channel counts go to k_big in fwd_big.hip)
 #include <stdio.h>
 
 #include <algorithm>
@@ -47,20 +45,6 @@ typedef const __attribute__((address_space(1))) void gbl_void;
 // the same for every lane of the wave (each lane lands at dst + 16 * lane).
 __device__ __forceinline__ void chunk_to_lds(const uint4 *src_lane, uint4 *dst_wave) {
     __builtin_amdgcn_global_load_lds((gbl_void *)src_lane, (lds_void *)dst_wave, 16, 0, 0);
-}
-
-// One lane's share of a 32-channel step: token n, channels i0..i0+7, all G samples (G uint4).
-template <int G>
-__device__ __forceinline__ void load_x_step(const uint4 *__restrict__ x4, int64_t n, int64_t N,
-                                            int C_in, int i0, uint4 (&r)[G]) {
-    if (n < N && i0 < C_in) {
-        const uint4 *p = x4 + ((n * C_in + i0) >> 3) * G;
-#pragma unroll
-        for (int q = 0; q < G; ++q) r[q] = p[q];
-    } else {
-#pragma unroll
-        for (int q = 0; q < G; ++q) r[q] = make_uint4(0u, 0u, 0u, 0u);
-    }
 }
 
 // G samples of 8 channels (channel-major, sample-minor: element j*G+g) -> G planes of 8 bf16.
@@ -87,54 +71,9 @@ __device__ __forceinline__ void negate_imag(const uint4 (&a)[G], uint4 (&an)[G])
     for (int p = 0; p < G; ++p) an[p] = (p >= 3 && (p & 1)) ? neg_bf16x8(a[p]) : a[p];
 }
 
-// All 2G-2 real products of one (16 tokens x 32 channels) x (32 channels x 16 outputs) block.
-template <int G>
-__device__ __forceinline__ void spectral_mfma(const uint4 (&a)[G], const uint4 (&an)[G],
-                                              const uint4 (&b)[G], f32x4 (&acc)[G]) {
-    acc[0] = mfma16x16x32(a[0], b[0], acc[0]);
-    if constexpr (G >= 2) acc[1] = mfma16x16x32(a[1], b[1], acc[1]);
-#pragma unroll
-    for (int k = 1; k < G / 2; ++k) {
-        const int r = 2 * k, i = 2 * k + 1;
-        acc[r] = mfma16x16x32(a[r], b[r], acc[r]);
-        acc[r] = mfma16x16x32(an[i], b[i], acc[r]);
-        acc[i] = mfma16x16x32(a[r], b[i], acc[i]);
-        acc[i] = mfma16x16x32(a[i], b[r], acc[i]);
-    }
-}
-
-// Inverse DFT + bias of accumulator row v, then one store of G bf16 at y[n][o][0..G-1].
-template <int G>
-__device__ __forceinline__ void store_row(const f32x4 (&acc)[G], int v, float bias,
-                                          uint16_t *__restrict__ y, int64_t n, int C_out, int o) {
-    float Y[G], out[G];
-#pragma unroll
-    for (int p = 0; p < G; ++p) Y[p] = acc[p][v];
-    inverse_planes<G>(Y, out);
-    uint16_t *dst = y + (n * C_out + o) * G;
-    if constexpr (G == 1) {
-        *dst = pack_bf16(out[0] + bias);
-    } else if constexpr (G == 2) {
-        *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(out[0] + bias, out[1] + bias);
-    } else if constexpr (G == 4) {
-        uint2 w;
-        w.x = pack_bf16x2(out[0] + bias, out[1] + bias);
-        w.y = pack_bf16x2(out[2] + bias, out[3] + bias);
-        *reinterpret_cast<uint2 *>(dst) = w;
-    } else {
-        float t[8];
-#pragma unroll
-        for (int h = 0; h < 8; ++h) t[h] = out[h] + bias;
-        *reinterpret_cast<uint4 *>(dst) = pack_bf16x8(t);
-    }
-}
-
-__device__ __forceinline__ float load_bias(const uint16_t *__restrict__ bias, int idx) {
-    return bias ? __uint_as_float((uint32_t)bias[idx] << 16) : 0.0f;
-}
-
-// Unconditional variant of load_x_step: the token index is clamped to N-1 and the channel group to
-// the last real one, so every lane issues the same G loads (no branches, no zero fill). Rows past N
+// One lane's share of a 32-channel step (token n, channels i0..i0+7, all G samples) with the token
+// index clamped to N-1 and the channel group to the last real one, so every lane issues the same G
+// loads (no branches, no zero fill). Rows past N
 // only feed outputs that are never stored; a channel group past C_in only meets zero weight
 // columns (the prepared weights are zero-padded), so its (finite) duplicate data contributes 0.
 template <int G>
@@ -421,91 +360,6 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
 }
 
 // ------------------------------------------------------------------------------------------------
-// k_tiled<G, BM, BN, WM, WN>: 4 waves, (BM/WM) x (BN/WN) == 4. grid = (ceil(N/BM), NB_total/(BN/16)).
-// LDS per K step: A planes [G][BM/16] chunks + B chunks [BN/16][G], 1 KB each.
-template <int G, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void k_tiled(const uint4 *__restrict__ x4,
-                                               const uint4 *__restrict__ wfrag,
-                                               const uint16_t *__restrict__ bias, int bias_shift,
-                                               uint16_t *__restrict__ y, int64_t N, int C_in,
-                                               int C_out, int KS) {
-    static_assert((BM / WM) * (BN / WN) == 4, "4 waves per workgroup");
-    constexpr int MB = BM / 16, WMB = WM / 16, WNB = WN / 16, BNB = BN / 16;
-    constexpr int ITEMS = BM * 4 / 256;  // (token, 8-channel group) items per thread per K step
-    static_assert(ITEMS >= 1 && BM * 4 % 256 == 0, "BM must be a multiple of 64");
-    extern __shared__ uint4 lds[];
-    uint4 *ldsA = lds;                  // [G][MB][64]
-    uint4 *ldsB = lds + G * MB * 64;    // [BNB][G][64]
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / (BN / WN), wn = wave % (BN / WN);
-    const int64_t m0 = (int64_t)blockIdx.x * BM;
-    const int nb0 = blockIdx.y * BNB;
-
-    f32x4 acc[WMB][WNB][G];
-#pragma unroll
-    for (int mi = 0; mi < WMB; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < WNB; ++ni)
-#pragma unroll
-            for (int p = 0; p < G; ++p) acc[mi][ni][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int ks = 0; ks < KS; ++ks) {
-        // weights of this K step -> LDS
-        for (int c = wave; c < BNB * G; c += 4) {
-            const int nbl = c / G, p = c % G;
-            const uint4 *src = wfrag + ((size_t)((nb0 + nbl) * KS + ks) * G + p) * 64;
-            chunk_to_lds(src + lane, ldsB + c * 64);
-        }
-        // activations of this K step: DFT once per workgroup -> A operand chunks in LDS
-#pragma unroll
-        for (int it = 0; it < ITEMS; ++it) {
-            const int item = threadIdx.x + it * 256;
-            const int m = item >> 2, kg = item & 3;
-            uint4 r[G], a[G];
-            load_x_step<G>(x4, m0 + m, N, C_in, ks * 32 + kg * 8, r);
-            dft_to_frags<G>(r, a);
-#pragma unroll
-            for (int p = 0; p < G; ++p) ldsA[(p * MB + (m >> 4)) * 64 + kg * 16 + (m & 15)] = a[p];
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-
-        uint4 a[WMB][G], an[WMB][G];
-#pragma unroll
-        for (int mi = 0; mi < WMB; ++mi) {
-#pragma unroll
-            for (int p = 0; p < G; ++p) a[mi][p] = ldsA[(p * MB + wm * WMB + mi) * 64 + lane];
-            negate_imag<G>(a[mi], an[mi]);
-        }
-#pragma unroll
-        for (int ni = 0; ni < WNB; ++ni) {
-            uint4 bw[G];
-#pragma unroll
-            for (int p = 0; p < G; ++p) bw[p] = ldsB[((wn * WNB + ni) * G + p) * 64 + lane];
-#pragma unroll
-            for (int mi = 0; mi < WMB; ++mi) spectral_mfma<G>(a[mi], an[mi], bw, acc[mi][ni]);
-        }
-        __syncthreads();
-    }
-
-#pragma unroll
-    for (int ni = 0; ni < WNB; ++ni) {
-        const int o = (nb0 + wn * WNB + ni) * 16 + (lane & 15);
-        if (o >= C_out) continue;
-        const float bo = load_bias(bias, o >> bias_shift);
-#pragma unroll
-        for (int mi = 0; mi < WMB; ++mi) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t n = m0 + (wm * WMB + mi) * 16 + 4 * (lane >> 4) + v;
-                if (n < N) store_row<G>(acc[mi][ni], v, bo, y, n, C_out, o);
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------------------------------------------
 // Launchers and selection.
 
 // Raise the kernel's dynamic-LDS limit above 64 KB where needed (gfx950 has 160 KB per CU). A
@@ -551,23 +405,6 @@ static hipError_t init_stream(size_t lds) {
     return set_lds_limit((const void *)k_stream<G, KS>, lds);
 }
 
-template <int G, int BM, int BN, int WM, int WN>
-static hipError_t launch_tiled(const Plan *p, const void *x, const void *b, void *y, int64_t N,
-                               hipStream_t s) {
-    const auto fn = k_tiled<G, BM, BN, WM, WN>;
-    const size_t lds = (size_t)(G * (BM / 16) + (BN / 16) * G) * 1024;
-    const dim3 grid((unsigned)((N + BM - 1) / BM), (unsigned)(p->NB_total / (BN / 16)));
-    hipLaunchKernelGGL(fn, grid, dim3(256), lds, s, (const uint4 *)x, (const uint4 *)p->planes,
-                       (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, p->KS);
-    return hipGetLastError();
-}
-
-template <int G, int BM, int BN, int WM, int WN>
-static hipError_t init_tiled() {
-    return set_lds_limit((const void *)k_tiled<G, BM, BN, WM, WN>,
-                         (size_t)(G * (BM / 16) + (BN / 16) * G) * 1024);
-}
-
 struct StreamEntry {
     int G, KS;
     LaunchFn launch;
@@ -583,20 +420,6 @@ static const StreamEntry kStream[] = {
 #undef SE
 static constexpr size_t kStreamLdsMax = 160 * 1024;
 static constexpr int kStreamMaxTiles = 4;
-
-struct TiledEntry {
-    int G, BM, BN;
-    LaunchFn launch;
-    hipError_t (*init)();
-};
-#define TL(G, BM, BN, WM, WN) {G, BM, BN, launch_tiled<G, BM, BN, WM, WN>, init_tiled<G, BM, BN, WM, WN>}
-static const TiledEntry kTiled[] = {
-    TL(1, 128, 128, 64, 64),
-    TL(2, 128, 128, 64, 64),
-    TL(4, 128, 64, 64, 32),
-    TL(8, 64, 64, 32, 32),
-};
-#undef TL
 
 static size_t stream_scratch(int G) {
     switch (G) {
@@ -628,28 +451,17 @@ bool select_bf16(int G, int C_in, int C_out, KernelChoice *out) {
         out->block_threads = kStreamWaves * 64;
         out->lds_bytes = (size_t)nb_tile * per_nb + fixed;
         out->num_cus = num_cus();
-        out->kmap = 1;
+        out->frag_kind = 1;
+        out->rows_per_block = 16;
+        out->kc = 32;
+        out->ks_mult = 1;
         out->launch = e.launch;
         (void)e.init(out->lds_bytes);
         snprintf(out->name, sizeof(out->name), "bf16 stream G=%d KS=%d nb_tile=%d tiles=%d waves=%d", G, KS,
                  nb_tile, tiles, kStreamWaves);
         return true;
     }
-    for (const auto &e : kTiled) {
-        if (e.G != G) continue;
-        (void)e.init();
-        out->kind = KIND_TILED;
-        out->kmap = 0;
-        out->nb_tile = e.BN / 16;
-        out->tokens_per_block = e.BM;
-        out->block_threads = 256;
-        out->lds_bytes = (size_t)(G * (e.BM / 16) + (e.BN / 16) * G) * 1024;
-        out->num_cus = num_cus();
-        out->launch = e.launch;
-        snprintf(out->name, sizeof(out->name), "bf16 tiled G=%d BM=%d BN=%d KS=%d", G, e.BM, e.BN, KS);
-        return true;
-    }
-    return false;
+    return select_big(G, C_in, C_out, out);
 }
 
 }  // namespace eqlin

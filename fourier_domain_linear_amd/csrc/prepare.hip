@@ -19,36 +19,40 @@ __device__ __forceinline__ float load_w(const void *W, bool is_bf16, size_t idx)
                    : ((const float *)W)[idx];
 }
 
-// Fragment position of What_p[o][i] in the chunked layout (see fwd_bf16.hip): chunk
-// (nb*KS + ks)*G + p holds the operand of output rows nb*16 .. nb*16+15 for K-step ks (32 input
-// channels); lane (g*16 + o%16) holds 8 k-slots j of lane group g. Returns a bf16 element index.
-// kmap 0: k-slot (g, j) is channel 8g + j of the K-step (natural order).
-// kmap 1: the channel of k-slot (g, j) is the one the stream kernel's x operand holds there: load
-//         q = j / (8/G) of lane group g reads 16-byte piece 4q + g of the K-step, and a piece
-//         holds 8/G whole channels; so channel c = piece * (8/G) + t maps to g = piece % 4,
+// Fragment position of What_p[o][i] in the chunked layouts the forward kernels read. Every chunk is
+// 1 KB = one matrix-core operand: 64 lanes x 8 bf16 k-slots; chunk index (ob * KS + ks) * G + p.
+// kind 1 (stream kernel, 16x16x32 operands): ob = o / 16, ks = i / 32; lane (g*16 + o%16) holds the
+//         8 k-slots j of lane group g, and k-slot (g, j) is the channel the stream kernel's x operand
+//         holds there: load q = j / (8/G) of lane group g reads 16-byte piece 4q + g of the K-step and
+//         a piece holds 8/G whole channels, so channel c = piece * (8/G) + t has g = piece % 4,
 //         j = (piece / 4) * (8/G) + t.
-__device__ __forceinline__ size_t frag_index(int G, int KS, int kmap, int o, int i, int p) {
-    const int nb = o >> 4, ks = i >> 5, c = i & 31;
-    int g, j;
-    if (kmap == 0) {
-        g = c >> 3;
-        j = c & 7;
+// kind 2 (large-channel kernel, 32x32x16 operands): ob = o / 32, ks = i / 16; lane (h*32 + o%32)
+//         holds channels 8h + j of the K-step (natural order).
+// Returns a bf16 element index.
+__device__ __forceinline__ size_t frag_index(int G, int KS, int kind, int o, int i, int p) {
+    int ob, ks, lane, j;
+    if (kind == 2) {
+        ob = o >> 5;
+        ks = i >> 4;
+        lane = ((i & 15) >> 3) * 32 + (o & 31);
+        j = i & 7;
     } else {
-        const int w = 8 / G, piece = c / w, t = c % w;
-        g = piece & 3;
+        ob = o >> 4;
+        ks = i >> 5;
+        const int c = i & 31, w = 8 / G, piece = c / w, t = c % w;
+        lane = (piece & 3) * 16 + (o & 15);
         j = (piece >> 2) * w + t;
     }
-    const int lane = g * 16 + (o & 15);
-    return ((((size_t)nb * KS + ks) * G + p) * 64 + lane) * 8 + j;
+    return ((((size_t)ob * KS + ks) * G + p) * 64 + lane) * 8 + j;
 }
 
-// One thread per (o, i) of the padded domain [NB_total*16] x [KS*32]; padding gets zeros.
+// One thread per (o, i) of the padded domain [NB_total * rows] x [KS * kc]; padding gets zeros.
 template <int G>
 __global__ void k_prep_frag(const void *__restrict__ W, bool w_is_bf16, int C_out, int C_in, int KS,
-                            int NB_total, int kmap, uint16_t *__restrict__ frag) {
+                            int NB_total, int kind, uint16_t *__restrict__ frag) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int ipad = KS * 32;
-    if (t >= (int64_t)NB_total * 16 * ipad) return;
+    const int ipad = KS * (kind == 2 ? 16 : 32), rows = kind == 2 ? 32 : 16;
+    if (t >= (int64_t)NB_total * rows * ipad) return;
     const int o = (int)(t / ipad), i = (int)(t % ipad);
     float v[G], P[G];
     const bool live = o < C_out && i < C_in;
@@ -56,18 +60,18 @@ __global__ void k_prep_frag(const void *__restrict__ W, bool w_is_bf16, int C_ou
     for (int d = 0; d < G; ++d) v[d] = live ? load_w(W, w_is_bf16, ((size_t)o * C_in + i) * G + d) : 0.f;
     forward_planes<G>(v, P);
 #pragma unroll
-    for (int p = 0; p < G; ++p) frag[frag_index(G, KS, kmap, o, i, p)] = pack_bf16(P[p] * plane_scale(G, p));
+    for (int p = 0; p < G; ++p) frag[frag_index(G, KS, kind, o, i, p)] = pack_bf16(P[p] * plane_scale(G, p));
 }
 
 template <int G>
-__global__ void k_export_frag(const uint16_t *__restrict__ frag, int C_out, int C_in, int KS, int kmap,
+__global__ void k_export_frag(const uint16_t *__restrict__ frag, int C_out, int C_in, int KS, int kind,
                               float *__restrict__ out) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= (int64_t)C_out * C_in) return;
     const int o = (int)(t / C_in), i = (int)(t % C_in);
 #pragma unroll
     for (int p = 0; p < G; ++p) {
-        const float s = __uint_as_float((uint32_t)frag[frag_index(G, KS, kmap, o, i, p)] << 16);
+        const float s = __uint_as_float((uint32_t)frag[frag_index(G, KS, kind, o, i, p)] << 16);
         out[((size_t)p * C_out + o) * C_in + i] = s / plane_scale(G, p);
     }
 }
@@ -119,19 +123,19 @@ static inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n
     }
 
 hipError_t launch_prep_frag(const void *W, bool w_is_bf16, int G, int C_out, int C_in, int KS,
-                            int NB_total, int kmap, void *frag, hipStream_t s) {
-    const int64_t n = (int64_t)NB_total * 16 * KS * 32;
+                            int NB_total, int kind, void *frag, hipStream_t s) {
+    const int64_t n = (int64_t)NB_total * KS * 512;
     DISPATCH_G(G, hipLaunchKernelGGL(k_prep_frag<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s, W,
-                                     w_is_bf16, C_out, C_in, KS, NB_total, kmap, (uint16_t *)frag));
+                                     w_is_bf16, C_out, C_in, KS, NB_total, kind, (uint16_t *)frag));
     return hipGetLastError();
 }
 
 hipError_t launch_export_frag(const void *frag, int G, int C_out, int C_in, int KS, int NB_total,
-                              int kmap, float *out, hipStream_t s) {
+                              int kind, float *out, hipStream_t s) {
     (void)NB_total;
     const int64_t n = (int64_t)C_out * C_in;
     DISPATCH_G(G, hipLaunchKernelGGL(k_export_frag<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
-                                     (const uint16_t *)frag, C_out, C_in, KS, kmap, out));
+                                     (const uint16_t *)frag, C_out, C_in, KS, kind, out));
     return hipGetLastError();
 }
 
