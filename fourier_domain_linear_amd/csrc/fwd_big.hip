@@ -7,15 +7,20 @@
 //
 // Workgroup tile: BO outputs x BT tokens, all G planes; OW x TW waves, each owning WA x WB blocks of
 // 32 outputs x 32 tokens. The channel (K) loop runs in stages of SC input channels (SC*G*2 bytes per
-// token row: whole 128-byte lines):
-//   - x: raw rows are loaded into registers one stage ahead, transformed (group DFT, fp32) and
-//     written to a three-slot LDS ring as bf16 B operands (32 tokens x 16 channels x 1 plane per
-//     1 KB chunk), shared by every wave of the workgroup;
-//   - weights: fragment chunks (32 outputs x 16 channels x 1 plane per 1 KB) are copied global ->
-//     LDS without VGPR staging, two stages ahead, into the same ring (the VGPR file is needed for
-//     operands and the DFT; the 256 accumulator registers hold the tile);
+// token row: whole 128-byte lines), two stages per loop trip so every register slot is fixed:
+//   - x: raw rows are loaded into a two-slot register ring two stages ahead (HBM latency spans
+//     several stages of products), transformed (group DFT, fp32) one stage ahead and written to one
+//     of two LDS buffers as bf16 B operands (32 tokens x 16 channels x 1 plane per 1 KB chunk),
+//     shared by every wave of the workgroup; each thread transforms distinct (token, 4 or 8
+//     channel) items, so no transform is repeated;
+//   - weights: each wave owns distinct output rows, so LDS staging would buy no reuse: fragment
+//     chunks (32 outputs x 16 channels x 1 plane per 1 KB, one coalesced load per wave) go straight
+//     into a two-slot register ring one stage ahead (they are L2 hits: every token tile of an output
+//     tile reads the same ones);
 //   - products: weights as the A operand (rows = outputs), x planes as B (columns = tokens); a
 //     complex frequency is four real products (Re = WrXr - WiXi via a sign-flipped Xi operand).
+// All global loads are plain loads, so the compiler's waits count exactly the ones in flight; the
+// per-stage barrier waits for LDS only.
 // Epilogue: the bias sits in the k = 0 accumulator from the start; inverse DFT in fp32; each wave
 // stages its 32 x 32 blocks in LDS (XOR-swizzled) and writes whole lines with non-temporal stores.
 #include <stdio.h>
@@ -50,12 +55,11 @@ __device__ __forceinline__ void spectral_mfma32(const uint4 (&w)[G], const uint4
     }
 }
 
-// G samples of 8 channels (element j*G+g) -> G bf16 planes of 8 channels; same as the stream path.
-template <int G>
-__device__ __forceinline__ void dft8(const uint4 (&r)[G], uint4 (&a)[G]) {
-    float pl[G][8];
+// G samples of NCH channels (element j*G+g) -> G planes of NCH bf16 (NCH = 4 or 8).
+template <int G, int NCH>
+__device__ __forceinline__ void dft_ch(const uint4 (&r)[NCH * G / 8], float (&pl)[G][NCH]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         float v[G], P[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -68,19 +72,13 @@ __device__ __forceinline__ void dft8(const uint4 (&r)[G], uint4 (&a)[G]) {
 #pragma unroll
         for (int p = 0; p < G; ++p) pl[p][j] = P[p];
     }
-#pragma unroll
-    for (int p = 0; p < G; ++p) a[p] = pack_bf16x8(pl[p]);
 }
 
-// One 1 KB chunk global -> LDS (lane l's 16 bytes land at lds_byte + 16 l). Issued as inline asm on
-// purpose: the compiler tracks the builtin form as an LDS write and then waits for *all* outstanding
-// vector-memory operations before any later LDS read, which would serialise the prefetch pipeline.
-// Untracked, it is covered by the kernel's own counted waits; an untracked load can only make the
-// compiler's own vmcnt waits stricter (loads complete in issue order), never looser. No register
-// output; M0 is set in the same block (nothing else in these kernels uses M0).
-__device__ __forceinline__ void chunk_dma(const uint4 *src_lane, uint32_t lds_byte) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_byte), "v"(src_lane)
-                 : "memory");
+// Workgroup barrier that orders LDS only: outstanding global loads stay in flight across it (the
+// fence in __syncthreads would wait for them too).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+    asm volatile("s_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ void st_nt16(uint4 *p, const uint4 &v) {
@@ -93,19 +91,20 @@ template <int G, int WA, int WB, int OW, int TW>
 struct BigCfg {
     static constexpr int NW = OW * TW, NT = NW * 64;
     static constexpr int BO = 32 * WA * OW, BT = 32 * WB * TW;
-    static constexpr int KSS = BigStage<G>::KSS, GRP = BigStage<G>::GRP, SA = BigStage<G>::SA;
-    static constexpr int XCH = (BT / 32) * KSS * G;         // x-plane chunks per stage (1 KB each)
-    static constexpr int WCH = (BO / 32) * KSS * G;         // weight chunks per stage
-    static constexpr int DMA_PER_WAVE = WCH / NW;           // weight chunk copies per wave per stage
-    static constexpr int STAGE = (XCH + WCH) * 64;          // uint4 per LDS ring slot
-    static constexpr int RING = 3;                          // LDS ring slots: weights two stages ahead
-    static constexpr int ITEMS = (BT * GRP + NT - 1) / NT;  // x items (token, 8 channels) per thread
+    static constexpr int SC = BigStage<G>::SC, KSS = BigStage<G>::KSS, GRP = BigStage<G>::GRP;
+    static constexpr int SA = BigStage<G>::SA;
+    // x work items: (token, NCH channels); NCH = 4 where 8-channel items would leave threads idle
+    static constexpr int NCH = (G >= 2 && BT * GRP < NT) ? 4 : 8;
+    static constexpr int ITEMS = BT * (SC / NCH) / NT;      // x items per thread per stage
+    static constexpr int XU4 = NCH * G / 8;                 // uint4 of raw x per item
+    static constexpr int XST = (BT / 32) * KSS * G * 64;    // uint4 per x-plane buffer (1 KB chunks)
+    static constexpr int WF = WA * KSS * G;                 // weight fragments per wave per stage
     static constexpr int PR = 4 * SA * G;                   // 16-byte pieces per staged output row
     static constexpr int STG = 32 * PR;                     // uint4 of epilogue staging per wave
-    static constexpr int LDS_U4 = RING * STAGE > NW * STG ? RING * STAGE : NW * STG;
+    static constexpr int LDS_U4 = 2 * XST > NW * STG ? 2 * XST : NW * STG;
     static constexpr size_t LDS = (size_t)LDS_U4 * 16 + BO * 4;
     static_assert(WA % SA == 0, "store unit must divide the wave's output blocks");
-    static_assert(WCH % NW == 0, "weight chunks must split evenly over the waves");
+    static_assert(ITEMS >= 1 && ITEMS * NT == BT * (SC / NCH), "x items must split evenly over the threads");
 };
 
 template <int G, int WA, int WB, int OW, int TW>
@@ -115,69 +114,77 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                                                       uint16_t *__restrict__ y, int64_t N, int C_in,
                                                       int C_out, int n_stages, int KS16, int tiles_t) {
     using C = BigCfg<G, WA, WB, OW, TW>;
-    constexpr int KSS = C::KSS, GRP = C::GRP;
-    extern __shared__ uint4 lds[];
-    float *lbias = reinterpret_cast<float *>(lds + C::LDS_U4);
+    constexpr int KSS = C::KSS, NCH = C::NCH;
+    __shared__ uint4 lds[C::LDS_U4];  // two x-plane buffers; the epilogue's staging afterwards
+    __shared__ float lbias[C::BO];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wo = wave % OW, wt = wave / OW;
     const int tt = blockIdx.x % tiles_t, ot = blockIdx.x / tiles_t;
     const int64_t t0 = (int64_t)tt * C::BT;
     const int o0 = ot * C::BO, ob0 = o0 / 32;
 
-    // LDS ring slot r: [x planes: XCH chunks][weights: WCH chunks]
-    auto slot = [&](int st) { return lds + (st % C::RING) * C::STAGE; };
-
-    // ---- loaders: raw x one stage ahead in registers, weights copied global -> LDS ----
-    uint4 xr[C::ITEMS][G];
-    auto load_x = [&](int stage) {
+    // ---- loaders. Stages past the last one re-load the last stage (valid addresses, unused data),
+    // so the loop body has no branches around loads. ----
+    auto load_x = [&](int stage, uint4 (&dst)[C::ITEMS][C::XU4]) {
+        stage = stage < n_stages ? stage : n_stages - 1;
 #pragma unroll
         for (int k = 0; k < C::ITEMS; ++k) {
-            const int item = (tid + k * C::NT) % (C::BT * GRP);  // duplicates re-load a real item
-            const int tl = item / GRP, c8 = item % GRP;
+            const int item = tid + k * C::NT;
+            const int tl = item / (C::SC / NCH), cq = item % (C::SC / NCH);
             int64_t n = t0 + tl;
             n = n < N ? n : N - 1;
-            int i0 = (stage * GRP + c8) * 8;
-            i0 = i0 < C_in ? i0 : C_in - 8;  // padded channels meet zero weight columns
-            const uint4 *p = x4 + ((n * C_in + i0) >> 3) * G;
+            int i0 = stage * C::SC + cq * NCH;
+            i0 = i0 < C_in ? i0 : C_in - NCH;  // padded channels meet zero weight columns
+            const uint4 *p = x4 + (n * C_in + i0) * G / 8;
 #pragma unroll
-            for (int q = 0; q < G; ++q) xr[k][q] = p[q];
+            for (int q = 0; q < C::XU4; ++q) dst[k][q] = p[q];
         }
     };
-    auto dma_w = [&](int stage) {
-        uint4 *wb = slot(stage) + C::XCH * 64;
+    auto load_w = [&](int stage, uint4 (&dst)[C::WF]) {
+        stage = stage < n_stages ? stage : n_stages - 1;
 #pragma unroll
-        for (int k = 0; k < C::DMA_PER_WAVE; ++k) {
-            const int c = wave + k * C::NW;
-            const int obl = c / (KSS * G), rem = c % (KSS * G);
-            const uint4 *src = wfrag + ((size_t)((ob0 + obl) * KS16 + stage * KSS) * G + rem) * 64;
-            chunk_dma(src + lane, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(wb + c * 64)));
+        for (int a = 0; a < WA; ++a) {
+            const uint4 *src = wfrag + (size_t)((ob0 + wo * WA + a) * KS16 + stage * KSS) * G * 64 + lane;
+#pragma unroll
+            for (int r = 0; r < KSS * G; ++r) dst[a * KSS * G + r] = src[r * 64];
         }
     };
-    auto dft_store = [&](int stage) {
-        uint4 *xb = slot(stage);
+    auto dft_store = [&](const uint4 (&src)[C::ITEMS][C::XU4], uint4 *xb) {
 #pragma unroll
         for (int k = 0; k < C::ITEMS; ++k) {
-            const int item = (tid + k * C::NT) % (C::BT * GRP);
-            const int tl = item / GRP, c8 = item % GRP;
-            uint4 a[G];
-            dft8<G>(xr[k], a);
-            const int sl = (c8 & 1) * 32 + (tl & 31);
+            const int item = tid + k * C::NT;
+            const int tl = item / (C::SC / NCH), cq = item % (C::SC / NCH);
+            const int c0 = cq * NCH;  // first channel of the item within the stage
+            uint4 *dst = xb + ((tl >> 5) * KSS + (c0 >> 4)) * G * 64 + ((c0 >> 3) & 1) * 32 + (tl & 31);
+            float pl[G][NCH];
+            dft_ch<G, NCH>(src[k], pl);
 #pragma unroll
-            for (int p = 0; p < G; ++p) xb[(((tl >> 5) * KSS + (c8 >> 1)) * G + p) * 64 + sl] = a[p];
+            for (int p = 0; p < G; ++p) {
+                if constexpr (NCH == 8) {
+                    dst[p * 64] = pack_bf16x8(pl[p]);
+                } else {
+                    uint2 w;
+                    w.x = pack_bf16x2(pl[p][0], pl[p][1]);
+                    w.y = pack_bf16x2(pl[p][2], pl[p][3]);
+                    reinterpret_cast<uint2 *>(dst + p * 64)[(c0 >> 2) & 1] = w;
+                }
+            }
         }
     };
 
-    // ---- prologue: bias; weights of stages 0 and 1 in flight; x of stage 0 transformed ----
+    // ---- prologue: bias; weights of stage 0 and raw x of stages 0 and 1 requested; x of stage 0
+    // transformed (n_stages is even, so at least 2) ----
+    uint4 xr[2][C::ITEMS][C::XU4];
+    uint4 wr[2][C::WF];
     if (tid < C::BO) {
         const int o = o0 + tid;
         lbias[tid] = (bias && o < C_out) ? __uint_as_float((uint32_t)bias[o >> bias_shift] << 16) : 0.f;
     }
-    dma_w(0);
-    load_x(0);
-    if (n_stages > 1) dma_w(1);
-    dft_store(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    load_w(0, wr[0]);
+    load_x(0, xr[0]);
+    load_x(1, xr[1]);
+    dft_store(xr[0], lds);
+    lds_barrier();
 
     f32x16 acc[WA][WB][G];
 #pragma unroll
@@ -193,44 +200,40 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
         }
     }
 
-    // ---- main loop: stage s consumes ring slot s%3 (x planes transformed at the end of stage s-1,
-    // weights copied since stage s-2). During stage s: request the weights of stage s+2 and the raw x
-    // of stage s+1, run the products, transform x of s+1 into slot (s+1)%3, wait for the weights of
-    // stage s+1 only (older than this stage's requests), barrier. ----
-    for (int s = 0; s < n_stages; ++s) {
-        const bool w_ahead = s + 2 < n_stages, x_ahead = s + 1 < n_stages;
-        // x first: the transform below waits for it, and loads complete in issue order, so the
-        // weight copies of stage s+2 issued after it stay in flight through that wait
-        if (x_ahead) load_x(s + 1);
+    // ---- main loop. Stage s: request the weights of s+1 and the raw x of s+2 (each into the
+    // register slot its stage-s predecessor vacated), run the products of stage s, transform the raw
+    // x of s+1 into the other x-plane buffer, barrier. ----
+    auto step = [&](int s, uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
+                    const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF], const uint4 *planes,
+                    uint4 *planes_next) {
+        load_w(s + 1, w_next);
+        load_x(s + 2, x_free);
+        // keep the requests at the top, in this order: the products below then wait only for the
+        // weights requested a whole stage ago (loads complete in issue order)
         __builtin_amdgcn_sched_barrier(0);
-        if (w_ahead) dma_w(s + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        const uint4 *xb = slot(s), *wb = slot(s) + C::XCH * 64;
 #pragma unroll
         for (int kk = 0; kk < KSS; ++kk)
 #pragma unroll
             for (int b = 0; b < WB; ++b) {
                 uint4 xf[G], xn[G];
 #pragma unroll
-                for (int p = 0; p < G; ++p) xf[p] = xb[(((wt * WB + b) * KSS + kk) * G + p) * 64 + lane];
+                for (int p = 0; p < G; ++p) xf[p] = planes[(((wt * WB + b) * KSS + kk) * G + p) * 64 + lane];
 #pragma unroll
                 for (int p = 0; p < G; ++p) xn[p] = (p >= 3 && (p & 1)) ? neg_bf16x8(xf[p]) : xf[p];
 #pragma unroll
                 for (int a = 0; a < WA; ++a) {
                     uint4 wf[G];
 #pragma unroll
-                    for (int p = 0; p < G; ++p) wf[p] = wb[(((wo * WA + a) * KSS + kk) * G + p) * 64 + lane];
+                    for (int p = 0; p < G; ++p) wf[p] = w_cur[(a * KSS + kk) * G + p];
                     spectral_mfma32<G>(wf, xf, xn, acc[a][b]);
                 }
             }
-        if (x_ahead) dft_store(s + 1);
-        // vector-memory ops younger than the weight copies of stage s+1: only those of stage s+2
-        // (the x loads of s+1, issued before them, were consumed by the transform)
-        if (w_ahead)
-            __builtin_amdgcn_s_waitcnt((C::DMA_PER_WAVE & 15) | ((C::DMA_PER_WAVE >> 4) << 14) | (7 << 4));
-        else
-            __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        dft_store(x_next, planes_next);  // after the last stage: unused planes, harmless
+        lds_barrier();
+    };
+    for (int s = 0; s < n_stages; s += 2) {  // n_stages is even (the channel padding sees to it)
+        step(s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST);
+        step(s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds);
     }
 
     // ---- epilogue: inverse DFT, stage, whole-line non-temporal stores ----
@@ -309,34 +312,22 @@ static hipError_t launch_big(const Plan *p, const void *x, const void *b, void *
     const int tiles_o = p->NB_total / (C::BO / 32);
     const int n_stages = p->KS / C::KSS;
     if (tiles_t * tiles_o > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_big<G, WA, WB, OW, TW>), dim3((unsigned)(tiles_t * tiles_o)), dim3(C::NT), C::LDS, s,
+    hipLaunchKernelGGL((k_big<G, WA, WB, OW, TW>), dim3((unsigned)(tiles_t * tiles_o)), dim3(C::NT), 0, s,
                        (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
                        (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t);
     return hipGetLastError();
-}
-
-template <int G, int WA, int WB, int OW, int TW>
-static hipError_t init_big() {
-    using C = BigCfg<G, WA, WB, OW, TW>;
-    hipError_t e = hipSuccess;
-    if (C::LDS > 65536)
-        e = hipFuncSetAttribute((const void *)k_big<G, WA, WB, OW, TW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)C::LDS);
-    (void)hipGetLastError();
-    return e;
 }
 
 struct BigEntry {
     int G, BO, BT, KSS, NT;
     size_t lds;
     LaunchFn launch;
-    hipError_t (*init)();
     const char *tile;
 };
 #define BE(G, WA, WB, OW, TW)                                                                            \
     {G, BigCfg<G, WA, WB, OW, TW>::BO, BigCfg<G, WA, WB, OW, TW>::BT, BigCfg<G, WA, WB, OW, TW>::KSS,      \
      BigCfg<G, WA, WB, OW, TW>::NT, BigCfg<G, WA, WB, OW, TW>::LDS, launch_big<G, WA, WB, OW, TW>,         \
-     init_big<G, WA, WB, OW, TW>, #WA "x" #WB " blocks/wave, " #OW "x" #TW " waves"}
+     #WA "x" #WB " blocks/wave, " #OW "x" #TW " waves"}
 static const BigEntry kBig[] = {
     BE(1, 2, 4, 4, 1),
     BE(2, 2, 4, 4, 1),
@@ -350,12 +341,11 @@ bool select_big(int G, int C_in, int C_out, KernelChoice *out) {
     (void)C_out;
     for (const auto &e : kBig) {
         if (e.G != G) continue;
-        (void)e.init();
         out->kind = KIND_TILED;
         out->frag_kind = 2;
         out->rows_per_block = 32;
         out->kc = 16;
-        out->ks_mult = e.KSS;
+        out->ks_mult = 2 * e.KSS;  // an even number of stages: the main loop runs them in pairs
         out->nb_tile = e.BO / 32;
         out->tokens_per_block = e.BT;
         out->block_threads = e.NT;
