@@ -61,6 +61,7 @@ struct Plan {
 
 // ---- fwd_bf16.hip ----
 bool select_bf16(int G, int C_in, int C_out, KernelChoice *out);
+int device_num_cus();  // compute units of the current device (queried once)
 // ---- fwd_big.hip ----
 bool select_big(int G, int C_in, int C_out, KernelChoice *out);
 // ---- fwd_f32.hip ----

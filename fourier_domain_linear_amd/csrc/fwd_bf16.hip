@@ -373,7 +373,7 @@ static hipError_t set_lds_limit(const void *fn, size_t bytes) {
 
 static int g_num_cus = 0;
 
-static int num_cus() {
+int device_num_cus() {
     if (g_num_cus <= 0) {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
@@ -450,7 +450,7 @@ bool select_bf16(int G, int C_in, int C_out, KernelChoice *out) {
         out->tokens_per_block = 16;
         out->block_threads = kStreamWaves * 64;
         out->lds_bytes = (size_t)nb_tile * per_nb + fixed;
-        out->num_cus = num_cus();
+        out->num_cus = device_num_cus();
         out->frag_kind = 1;
         out->rows_per_block = 16;
         out->kc = 32;

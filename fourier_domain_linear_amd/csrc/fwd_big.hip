@@ -81,11 +81,32 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Scheduling pattern for one region of a stage: a 32x32x16 product keeps the matrix core busy for
+// 32 cycles while the wave goes on issuing independent instructions, so the region's loads and the
+// transform's vector ALU work are spread over its NM products: the region's NR LDS reads first,
+// then after each product one global load (the first NV products) and up to VPM vector ALU
+// instructions.
+template <int NR, int NM, int NV, int VPM>
+__device__ __forceinline__ void interleave_stage() {
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // LDS reads, as one batch
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // vector ALU
+    }
+}
+
 __device__ __forceinline__ void st_nt16(uint4 *p, const uint4 &v) {
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
 }
+
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
 
 template <int G, int WA, int WB, int OW, int TW>
 struct BigCfg {
@@ -99,6 +120,7 @@ struct BigCfg {
     static constexpr int XU4 = NCH * G / 8;                 // uint4 of raw x per item
     static constexpr int XST = (BT / 32) * KSS * G * 64;    // uint4 per x-plane buffer (1 KB chunks)
     static constexpr int WF = WA * KSS * G;                 // weight fragments per wave per stage
+    static constexpr int VPM = G == 8 ? 10 : G == 2 ? 5 : G == 4 ? 4 : 3;  // transform ALU ops per product
     static constexpr int PR = 4 * SA * G;                   // 16-byte pieces per staged output row
     static constexpr int STG = 32 * PR;                     // uint4 of epilogue staging per wave
     static constexpr int LDS_U4 = 2 * XST > NW * STG ? 2 * XST : NW * STG;
@@ -203,33 +225,43 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     // ---- main loop. Stage s: request the weights of s+1 and the raw x of s+2 (each into the
     // register slot its stage-s predecessor vacated), run the products of stage s, transform the raw
     // x of s+1 into the other x-plane buffer, barrier. ----
+    // products of (K-step kk, token block b) pairs [lo, hi) of the stage, kk major
+    auto products = [&](auto lo, auto hi, const uint4 (&w_cur)[C::WF], const uint4 *planes) {
+#pragma unroll
+        for (int q = decltype(lo)::value; q < decltype(hi)::value; ++q) {
+            const int kk = q / WB, b = q % WB;
+            uint4 xf[G], xn[G];
+#pragma unroll
+            for (int p = 0; p < G; ++p) xf[p] = planes[(((wt * WB + b) * KSS + kk) * G + p) * 64 + lane];
+#pragma unroll
+            for (int p = 0; p < G; ++p) xn[p] = (p >= 3 && (p & 1)) ? neg_bf16x8(xf[p]) : xf[p];
+#pragma unroll
+            for (int a = 0; a < WA; ++a) {
+                uint4 wf[G];
+#pragma unroll
+                for (int p = 0; p < G; ++p) wf[p] = w_cur[(a * KSS + kk) * G + p];
+                spectral_mfma32<G>(wf, xf, xn, acc[a][b]);
+            }
+        }
+    };
+    // One stage in two scheduling regions, so the loads leave in a fixed order: the weights of s+1
+    // under the first half of the products, then the raw x of s+2 and the transform of x(s+1) under
+    // the second half. The next stage's products then wait for the weights only, with the raw x
+    // still in flight (vector-memory operations complete in issue order).
     auto step = [&](int s, uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
                     const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF], const uint4 *planes,
                     uint4 *planes_next) {
+        constexpr int P = KSS * WB, H = P / 2;
         load_w(s + 1, w_next);
-        load_x(s + 2, x_free);
-        // keep the requests at the top, in this order: the products below then wait only for the
-        // weights requested a whole stage ago (loads complete in issue order)
+        products(IC<0>{}, IC<H>{}, w_cur, planes);
+        interleave_stage<H * G, H * WA * real_products(G), C::WF, 1>();
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk < KSS; ++kk)
-#pragma unroll
-            for (int b = 0; b < WB; ++b) {
-                uint4 xf[G], xn[G];
-#pragma unroll
-                for (int p = 0; p < G; ++p) xf[p] = planes[(((wt * WB + b) * KSS + kk) * G + p) * 64 + lane];
-#pragma unroll
-                for (int p = 0; p < G; ++p) xn[p] = (p >= 3 && (p & 1)) ? neg_bf16x8(xf[p]) : xf[p];
-#pragma unroll
-                for (int a = 0; a < WA; ++a) {
-                    uint4 wf[G];
-#pragma unroll
-                    for (int p = 0; p < G; ++p) wf[p] = w_cur[(a * KSS + kk) * G + p];
-                    spectral_mfma32<G>(wf, xf, xn, acc[a][b]);
-                }
-            }
+        load_x(s + 2, x_free);
+        products(IC<H>{}, IC<P>{}, w_cur, planes);
         dft_store(x_next, planes_next);  // after the last stage: unused planes, harmless
+        interleave_stage<(P - H) * G, (P - H) * WA * real_products(G), C::ITEMS * C::XU4, C::VPM>();
         lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);  // each stage is its own scheduling region
     };
     for (int s = 0; s < n_stages; s += 2) {  // n_stages is even (the channel padding sees to it)
         step(s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST);
