@@ -302,18 +302,46 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
         if (nxt < b1) load_x_raw<G, KS>(x4, nxt, N, row_pieces, lane, xr);
 
         const int64_t nrow0 = blk * 16;
+        // the block's output rows, for range-checked stores: rows past N are dropped by the hardware
+        const int64_t rows = N - nrow0 < 16 ? N - nrow0 : 16;
+        const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+            y + nrow0 * C_out * G, (short)0, (int)(rows * yrow_pieces * 16), 0x00020000);
+        // Weight fragments are read from LDS a whole 16-output block ahead of their products when the
+        // block's KS*G fragments fit the register budget (else as the products need them).
+        constexpr bool kWholeBlock = KS * G <= 12;
+        constexpr int PF = kWholeBlock ? KS : 1;
+        uint4 bw[2][PF][G];
+        if constexpr (kWholeBlock) {
+#pragma unroll
+            for (int ks = 0; ks < PF; ++ks)
+#pragma unroll
+                for (int p = 0; p < G; ++p) bw[0][ks][p] = lds[(ks * G + p) * 64 + lane];
+        }
         for (int nb = 0; nb < nb_end; ++nb) {
             const float4 bq = reinterpret_cast<const float4 *>(lbias)[nb * 4 + g];
             f32x4 acc[G];
             acc[0] = f32x4{bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
             for (int p = 1; p < G; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (kWholeBlock) {
+                const int nbn = nb + 1 < nb_end ? nb + 1 : nb;  // last block: harmless re-read
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                uint4 bw[G];
+                for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int p = 0; p < G; ++p) bw[p] = lds[((nb * KS + ks) * G + p) * 64 + lane];
-                spectral_mfma_wx<G>(bw, a[ks], an[ks], acc);
+                    for (int p = 0; p < G; ++p) bw[1][ks][p] = lds[((nbn * KS + ks) * G + p) * 64 + lane];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) spectral_mfma_wx<G>(bw[0][ks], a[ks], an[ks], acc);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int p = 0; p < G; ++p) bw[0][ks][p] = bw[1][ks][p];
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int p = 0; p < G; ++p) bw[0][0][p] = lds[((nb * KS + ks) * G + p) * 64 + lane];
+                    spectral_mfma_wx<G>(bw[0][0], a[ks], an[ks], acc);
+                }
             }
             if (!vec_rows) {
                 store_quad_masked<G>(acc, y, nrow0 + (lane & 15), N, (nb0 + nb) * 16 + 4 * g, C_out);
@@ -343,16 +371,21 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
             }
             if (ub == SG::UO - 1 || nb == nb_end - 1) {
                 // whole 16-byte pieces of the unit's rows, full lines per instruction, non-temporal
-                const int unit_o0 = (nb0 + nb - ub) * 16;                 // first output of the unit
+                const int unit_o0 = (nb0 + nb - ub) * 16;  // first output of the unit
                 const int piece0 = unit_o0 * G / 8;
 #pragma unroll
                 for (int j = 0; j < SG::OINST; ++j) {
                     const int r = j * SG::OROWS + lane / SG::PPR, pc = lane % SG::PPR;
                     const uint4 v = scratch[swz<SG::PPR>(r, pc)];
                     // only the pieces of blocks computed in this unit (a tile's last unit may be
-                    // partial; the rest of its row belongs to the next tile or past C_out)
-                    if (nrow0 + r < N && pc < (ub + 1) * 2 * G && piece0 + pc < yrow_pieces)
-                        st_nt(reinterpret_cast<uint4 *>(y) + (nrow0 + r) * yrow_pieces + piece0 + pc, v);
+                    // partial; the rest of its row belongs to the next tile or past C_out); others
+                    // get an offset past the range, which drops them (no branches)
+                    const int keep = -(int)((pc < (ub + 1) * 2 * G) & (piece0 + pc < yrow_pieces));
+                    const int off = (r * yrow_pieces + piece0 + pc) * 16;
+                    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+                    const u32x4 d = {v.x, v.y, v.z, v.w};
+                    __builtin_amdgcn_raw_buffer_store_b128(d, yrs, (off & keep) | (0x7fffffff & ~keep), 0,
+                                                           2 /* non-temporal */);
                 }
             }
         }
