@@ -84,27 +84,26 @@ def time_eager(torch, launch, K: int, R: int):
 
 
 def cpu_baseline(w, x, W, b, budget_s: float = 12.0):
-    """The fp64 oracle, as it stands, on the host cores over a bounded sample of the workload."""
+    """The fp64 oracle, as it stands, on the host cores over a bounded sample of the workload: whole
+    passes over the workload's tokens until about `budget_s` seconds have run, or (when one pass
+    would take longer) the first tokens that fit the budget, sized by a pilot run."""
     import oracle
 
     threads = oracle.max_threads()
     pilot = min(w.N, 256)
     t0 = time.perf_counter()
     oracle.forward(x[:pilot], W, b)
-    t_pilot = time.perf_counter() - t0
-    per_token = t_pilot / pilot
-    if per_token * w.N <= budget_s:
-        passes = max(1, int(budget_s / max(per_token * w.N, 1e-9)))
-        passes = min(passes, 50)
-        t0 = time.perf_counter()
-        for _ in range(passes):
+    per_token = (time.perf_counter() - t0) / pilot
+    if per_token * w.N <= budget_s / 2:
+        passes, t0 = 0, time.perf_counter()
+        while passes < 1000 and time.perf_counter() - t0 < budget_s:
             oracle.forward(x, W, b)
+            passes += 1
         dt = time.perf_counter() - t0
         tokens = passes * w.N
         sample = f"{passes} pass(es) over all {w.N} tokens of the workload"
     else:
-        n = max(pilot, int(budget_s / per_token))
-        n = min(n, w.N)
+        n = min(w.N, max(pilot, int(budget_s / per_token)))
         t0 = time.perf_counter()
         oracle.forward(x[:n], W, b)
         dt = time.perf_counter() - t0
