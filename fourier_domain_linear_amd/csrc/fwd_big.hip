@@ -5,9 +5,15 @@
 // Transform" (gist.science explainer), "Enfoque Algorítmico" (group DFT -> per-frequency channel
 // products, k = 0..G/2) and "Implementación" (one fused kernel, Fourier fragments on chip).
 //
-// Workgroup tile: BO outputs x BT tokens, all G planes; OW x TW waves, each owning WA x WB blocks of
-// 32 outputs x 32 tokens. The channel (K) loop runs in stages of SC input channels (SC*G*2 bytes per
-// token row: whole 128-byte lines), two stages per loop trip so every register slot is fixed:
+// Persistent workgroups, one per compute unit: workgroup g keeps output tile g % tiles_o (its
+// weights and bias) and walks the token tiles g / tiles_o, + tstep, ... The load pipeline runs on
+// across tile boundaries, and a tile's outputs, staged in LDS, are stored during the next tile's
+// stages instead of in one burst at its end (every compute unit storing at once runs at the HBM
+// write rate while the matrix cores idle).
+//
+// Tile: BO outputs x BT tokens, all G planes; OW x TW waves, each owning WA x WB blocks of 32 outputs
+// x 32 tokens. The channel (K) loop runs in stages of SC input channels (SC*G*2 bytes per token row:
+// whole 128-byte lines), two stages per loop trip so every register slot is fixed:
 //   - x: raw rows are loaded into a two-slot register ring two stages ahead (HBM latency spans
 //     several stages of products), transformed (group DFT, fp32) one stage ahead and written to one
 //     of two LDS buffers as bf16 B operands (32 tokens x 16 channels x 1 plane per 1 KB chunk),
@@ -15,14 +21,17 @@
 //     channel) items, so no transform is repeated;
 //   - weights: each wave owns distinct output rows, so LDS staging would buy no reuse: fragment
 //     chunks (32 outputs x 16 channels x 1 plane per 1 KB, one coalesced load per wave) go straight
-//     into a two-slot register ring one stage ahead (they are L2 hits: every token tile of an output
-//     tile reads the same ones);
+//     into a two-slot register ring one stage ahead (they are L2 hits: the workgroup's output tile
+//     never changes);
 //   - products: weights as the A operand (rows = outputs), x planes as B (columns = tokens); a
 //     complex frequency is four real products (Re = WrXr - WiXi via a sign-flipped Xi operand).
 // All global loads are plain loads, so the compiler's waits count exactly the ones in flight; the
-// per-stage barrier waits for LDS only.
-// Epilogue: the bias sits in the k = 0 accumulator from the start; inverse DFT in fp32; each wave
-// stages its 32 x 32 blocks in LDS (XOR-swizzled) and writes whole lines with non-temporal stores.
+// per-stage barrier waits for LDS only. Vector-memory operations complete in issue order, so each
+// stage issues its weight loads, then its x loads, then its share of stores: a wait for a load never
+// waits for a store issued after it.
+// Epilogue of a tile: inverse DFT in fp32 (the bias entered the k = 0 accumulators at the tile's
+// start), outputs staged per wave in LDS (XOR-swizzled), then written as whole 16-byte pieces with
+// range-checked non-temporal buffer stores.
 #include <stdio.h>
 
 #include <algorithm>
@@ -81,27 +90,25 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-// Scheduling pattern for one region of a stage: a 32x32x16 product keeps the matrix core busy for
-// 32 cycles while the wave goes on issuing independent instructions, so the region's loads and the
-// transform's vector ALU work are spread over its NM products: the region's NR LDS reads first,
-// then after each product one global load (the first NV products) and up to VPM vector ALU
-// instructions.
-template <int NR, int NM, int NV, int VPM>
+// Scheduling pattern for one stage: a 32x32x16 product keeps the matrix core busy for 32 cycles
+// while the wave goes on issuing independent instructions, so the stage's global loads and the
+// transform's vector ALU work are spread over the products (NM of them): the region's NR LDS reads
+// first, then after each product one load (the first NV products) and up to VPM vector ALU
+// instructions; the NS stores last (vector-memory operations complete in issue order, so a store
+// issued ahead of a load would make every wait for that load wait for the store too).
+template <int NR, int NM, int NV, int VPM, int NS = 0>
 __device__ __forceinline__ void interleave_stage() {
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // LDS reads, as one batch
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // the region's LDS reads first, as one batch
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         if (i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
         __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // vector ALU
     }
+    if (NS) __builtin_amdgcn_sched_group_barrier(0x040, NS, 0);  // global stores last
 }
 
-__device__ __forceinline__ void st_nt16(uint4 *p, const uint4 &v) {
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
-}
+constexpr int kStoreAux = 2;  // cache policy of the output stores: non-temporal (measured faster than default)
 
 template <int V>
 struct IC {
@@ -121,37 +128,62 @@ struct BigCfg {
     static constexpr int XST = (BT / 32) * KSS * G * 64;    // uint4 per x-plane buffer (1 KB chunks)
     static constexpr int WF = WA * KSS * G;                 // weight fragments per wave per stage
     static constexpr int VPM = G == 8 ? 10 : G == 2 ? 5 : G == 4 ? 4 : 3;  // transform ALU ops per product
-    static constexpr int PR = 4 * SA * G;                   // 16-byte pieces per staged output row
-    static constexpr int STG = 32 * PR;                     // uint4 of epilogue staging per wave
-    static constexpr int LDS_U4 = 2 * XST > NW * STG ? 2 * XST : NW * STG;
-    static constexpr size_t LDS = (size_t)LDS_U4 * 16 + BO * 4;
+    // output staging: a wave's tile is NU units of 32 tokens x (SA x 32 outputs x G), PR 16-byte
+    // pieces per token row (XOR-swizzled); it leaves in NSTORE whole-wave stores, SPS per stage of
+    // the next tile (the rest, if the tile has too few stages, before that tile's own epilogue)
+    static constexpr int PR = 4 * SA * G;
+    static constexpr int NU = WB * (WA / SA);
+    static constexpr int UST = 32 * PR;                     // uint4 per unit
+    static constexpr int STG = NU * UST;                    // uint4 of staging per wave
+    static constexpr int NSTORE = NU * PR / 2;
+    static constexpr int SPS = G == 8 || G == 1 ? 2 : 3;
+    static constexpr int LDS_U4 = 2 * XST + NW * STG;
+    static constexpr size_t LDS = (size_t)LDS_U4 * 16;
     static_assert(WA % SA == 0, "store unit must divide the wave's output blocks");
     static_assert(ITEMS >= 1 && ITEMS * NT == BT * (SC / NCH), "x items must split evenly over the threads");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int G, int WA, int WB, int OW, int TW>
+// Persistent: workgroup g keeps output tile g % tiles_o (its weights, bias and L2 set) and walks the
+// token tiles g / tiles_o, + tstep, ... (tstep = gridDim.x / tiles_o). The load pipeline runs on
+// across tile boundaries, and a tile's outputs are stored while the next tile computes.
+template <int G, int WA, int WB, int OW, int TW, bool VEC>
 __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ x4,
                                                       const uint4 *__restrict__ wfrag,
                                                       const uint16_t *__restrict__ bias, int bias_shift,
                                                       uint16_t *__restrict__ y, int64_t N, int C_in,
-                                                      int C_out, int n_stages, int KS16, int tiles_t) {
+                                                      int C_out, int n_stages, int KS16, int tiles_t,
+                                                      int tiles_o) {
     using C = BigCfg<G, WA, WB, OW, TW>;
     constexpr int KSS = C::KSS, NCH = C::NCH;
-    __shared__ uint4 lds[C::LDS_U4];  // two x-plane buffers; the epilogue's staging afterwards
-    __shared__ float lbias[C::BO];
+    __shared__ uint4 lds[C::LDS_U4];  // two x-plane buffers, then each wave's output staging
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wo = wave % OW, wt = wave / OW;
-    const int tt = blockIdx.x % tiles_t, ot = blockIdx.x / tiles_t;
-    const int64_t t0 = (int64_t)tt * C::BT;
+    const int ot = blockIdx.x % tiles_o, tt0 = blockIdx.x / tiles_o, tstep = gridDim.x / tiles_o;
+    const int ntl = tt0 < tiles_t ? (tiles_t - 1 - tt0) / tstep + 1 : 0;  // token tiles of this workgroup
+    if (ntl == 0) return;
     const int o0 = ot * C::BO, ob0 = o0 / 32;
+    uint4 *const stg = lds + 2 * C::XST + wave * C::STG;
+    constexpr bool vec_rows = VEC;  // output rows are whole 16-byte pieces: (C_out * G) % 8 == 0
+    const int yrow_pieces = C_out * G / 8;
+    const int yrow_bytes = C_out * G * 2;
+    const int rcol = lane & 31;
 
-    // ---- loaders. Stages past the last one re-load the last stage (valid addresses, unused data),
+    // ---- loaders. A position past the last one re-loads the last (valid addresses, unused data),
     // so the loop body has no branches around loads. ----
-    auto load_x = [&](int stage, uint4 (&dst)[C::ITEMS][C::XU4]) {
-        stage = stage < n_stages ? stage : n_stages - 1;
+    auto load_x = [&](int k, int stage, uint4 (&dst)[C::ITEMS][C::XU4]) {
+        if (stage >= n_stages) {  // uniform: the next tile's first stages
+            stage -= n_stages;
+            ++k;
+        }
+        if (k >= ntl) {
+            k = ntl - 1;
+            stage = n_stages - 1;
+        }
+        const int64_t t0 = (int64_t)(tt0 + k * tstep) * C::BT;
 #pragma unroll
-        for (int k = 0; k < C::ITEMS; ++k) {
-            const int item = tid + k * C::NT;
+        for (int it = 0; it < C::ITEMS; ++it) {
+            const int item = tid + it * C::NT;
             const int tl = item / (C::SC / NCH), cq = item % (C::SC / NCH);
             int64_t n = t0 + tl;
             n = n < N ? n : N - 1;
@@ -159,11 +191,11 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
             i0 = i0 < C_in ? i0 : C_in - NCH;  // padded channels meet zero weight columns
             const uint4 *p = x4 + (n * C_in + i0) * G / 8;
 #pragma unroll
-            for (int q = 0; q < C::XU4; ++q) dst[k][q] = p[q];
+            for (int q = 0; q < C::XU4; ++q) dst[it][q] = p[q];
         }
     };
     auto load_w = [&](int stage, uint4 (&dst)[C::WF]) {
-        stage = stage < n_stages ? stage : n_stages - 1;
+        stage = stage < n_stages ? stage : stage - n_stages;
 #pragma unroll
         for (int a = 0; a < WA; ++a) {
             const uint4 *src = wfrag + (size_t)((ob0 + wo * WA + a) * KS16 + stage * KSS) * G * 64 + lane;
@@ -173,13 +205,13 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     };
     auto dft_store = [&](const uint4 (&src)[C::ITEMS][C::XU4], uint4 *xb) {
 #pragma unroll
-        for (int k = 0; k < C::ITEMS; ++k) {
-            const int item = tid + k * C::NT;
+        for (int it = 0; it < C::ITEMS; ++it) {
+            const int item = tid + it * C::NT;
             const int tl = item / (C::SC / NCH), cq = item % (C::SC / NCH);
             const int c0 = cq * NCH;  // first channel of the item within the stage
             uint4 *dst = xb + ((tl >> 5) * KSS + (c0 >> 4)) * G * 64 + ((c0 >> 3) & 1) * 32 + (tl & 31);
             float pl[G][NCH];
-            dft_ch<G, NCH>(src[k], pl);
+            dft_ch<G, NCH>(src[it], pl);
 #pragma unroll
             for (int p = 0; p < G; ++p) {
                 if constexpr (NCH == 8) {
@@ -193,39 +225,53 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
             }
         }
     };
+    // Store j (0 <= j < NSTORE) of the staged tile: one 16-byte piece per lane, read from the staging
+    // area, then written with a buffer store. Rows past N fall outside the buffer range and are
+    // dropped by the hardware, as are pieces past the row end and every piece when `valid` is false.
+    auto read_staged = [&](int j) {
+        const int u = j / (C::PR / 2), jj = j % (C::PR / 2);
+        const int r = jj * (64 / C::PR) + lane / C::PR, pc = lane % C::PR;
+        return stg[u * C::UST + r * C::PR + (pc ^ (r & 7))];
+    };
+    auto store_staged = [&](int j, const uint4 &v, __amdgpu_buffer_rsrc_t rs, bool valid) {
+        const int u = j / (C::PR / 2), jj = j % (C::PR / 2);
+        const int r = jj * (64 / C::PR) + lane / C::PR, pc = lane % C::PR;
+        const int b = u / (WA / C::SA), a0 = (u % (WA / C::SA)) * C::SA;
+        const int piece = (o0 + (wo * WA + a0) * 32) * G / 8 + pc;
+        const int off = ((wt * WB + b) * 32 + r) * yrow_bytes + piece * 16;
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 d = {v.x, v.y, v.z, v.w};
+        // branch-free: an offset past the range drops the store (bitwise, no short-circuit jumps)
+        const int keep = -(int)(valid & (piece < yrow_pieces));
+        __builtin_amdgcn_raw_buffer_store_b128(d, rs, (off & keep) | (0x7fffffff & ~keep), 0, kStoreAux);
+    };
+    auto tile_rsrc = [&](int k) {
+        const int64_t n0 = (int64_t)(tt0 + k * tstep) * C::BT;
+        const int64_t rows = N - n0 < C::BT ? N - n0 : C::BT;
+        return __builtin_amdgcn_make_buffer_rsrc(y + n0 * (C_out * G), (short)0, (int)(rows * yrow_bytes),
+                                                 0x00020000);
+    };
 
-    // ---- prologue: bias; weights of stage 0 and raw x of stages 0 and 1 requested; x of stage 0
-    // transformed (n_stages is even, so at least 2) ----
+    // Bias: lane l keeps bias[row l % 32] of each of its output blocks (bf16 bits); a tile's k = 0
+    // accumulators start as the product of that column with a row of ones (exact in fp32).
+    uint32_t bcol[WA];
+#pragma unroll
+    for (int a = 0; a < WA; ++a) {
+        const int o = o0 + (wo * WA + a) * 32 + rcol;
+        bcol[a] = (bias && o < C_out) ? bias[o >> bias_shift] : 0u;
+    }
+
+    // ---- prologue: weights of stage 0 and raw x of positions 0 and 1 requested; x(0) transformed ----
     uint4 xr[2][C::ITEMS][C::XU4];
     uint4 wr[2][C::WF];
-    if (tid < C::BO) {
-        const int o = o0 + tid;
-        lbias[tid] = (bias && o < C_out) ? __uint_as_float((uint32_t)bias[o >> bias_shift] << 16) : 0.f;
-    }
     load_w(0, wr[0]);
-    load_x(0, xr[0]);
-    load_x(1, xr[1]);
+    load_x(0, 0, xr[0]);
+    load_x(0, 1, xr[1]);
     dft_store(xr[0], lds);
     lds_barrier();
 
     f32x16 acc[WA][WB][G];
-#pragma unroll
-    for (int a = 0; a < WA; ++a) {
-        f32x16 b0;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) b0[v] = lbias[(wo * WA + a) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)];
-#pragma unroll
-        for (int b = 0; b < WB; ++b) {
-            acc[a][b][0] = b0;
-#pragma unroll
-            for (int p = 1; p < G; ++p) acc[a][b][p] = f32x16{};
-        }
-    }
-
-    // ---- main loop. Stage s: request the weights of s+1 and the raw x of s+2 (each into the
-    // register slot its stage-s predecessor vacated), run the products of stage s, transform the raw
-    // x of s+1 into the other x-plane buffer, barrier. ----
-    // products of (K-step kk, token block b) pairs [lo, hi) of the stage, kk major
+    // products of (K-step kk, token block b) pairs [lo, hi) of a stage, kk major
     auto products = [&](auto lo, auto hi, const uint4 (&w_cur)[C::WF], const uint4 *planes) {
 #pragma unroll
         for (int q = decltype(lo)::value; q < decltype(hi)::value; ++q) {
@@ -244,94 +290,132 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
             }
         }
     };
-    // One stage in two scheduling regions, so the loads leave in a fixed order: the weights of s+1
-    // under the first half of the products, then the raw x of s+2 and the transform of x(s+1) under
-    // the second half. The next stage's products then wait for the weights only, with the raw x
-    // still in flight (vector-memory operations complete in issue order).
-    auto step = [&](int s, uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
+    // One stage (tile k, stage s) in two scheduling regions, so the loads leave in a fixed order:
+    // the weights of s+1 under the first half of the products, then the raw x of position +2 and the
+    // transform of x(+1) under the second half, and last this stage's share of the previous tile's
+    // stores.
+    // The next stage's products then wait for its weights only, with the raw x still in flight
+    // (vector-memory operations complete in issue order).
+    auto step = [&](int k, int s, uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
                     const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF], const uint4 *planes,
-                    uint4 *planes_next) {
+                    uint4 *planes_next, __amdgpu_buffer_rsrc_t rs_prev, bool has_prev) {
         constexpr int P = KSS * WB, H = P / 2;
         load_w(s + 1, w_next);
         products(IC<0>{}, IC<H>{}, w_cur, planes);
         interleave_stage<H * G, H * WA * real_products(G), C::WF, 1>();
         __builtin_amdgcn_sched_barrier(0);
-        load_x(s + 2, x_free);
+        load_x(k, s + 2, x_free);
+        uint4 sv[C::SPS];
+#pragma unroll
+        for (int i = 0; i < C::SPS; ++i) sv[i] = read_staged(min(s * C::SPS + i, C::NSTORE - 1));
         products(IC<H>{}, IC<P>{}, w_cur, planes);
-        dft_store(x_next, planes_next);  // after the last stage: unused planes, harmless
-        interleave_stage<(P - H) * G, (P - H) * WA * real_products(G), C::ITEMS * C::XU4, C::VPM>();
+        dft_store(x_next, planes_next);  // past the last position: unused planes, harmless
+        interleave_stage<(P - H) * G + C::SPS, (P - H) * WA * real_products(G), C::ITEMS * C::XU4, C::VPM>();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < C::SPS; ++i) {
+            const int j = s * C::SPS + i;
+            store_staged(min(j, C::NSTORE - 1), sv[i], rs_prev, has_prev & (j < C::NSTORE));
+        }
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);  // each stage is its own scheduling region
     };
-    for (int s = 0; s < n_stages; s += 2) {  // n_stages is even (the channel padding sees to it)
-        step(s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST);
-        step(s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds);
-    }
 
-    // ---- epilogue: inverse DFT, stage, whole-line non-temporal stores ----
-    const bool vec_rows = (C_out * G) % 8 == 0;
-    const int yrow_pieces = C_out * G / 8;
-    uint4 *stg = lds + wave * C::STG;
-    const int h = lane >> 5, rcol = lane & 31;
+    for (int k = 0; k < ntl; ++k) {
+        // operands built here from one live register per block (constants and the thread id behind
+        // opaque copies, so the compiler does not keep whole tuples live through the loop)
+        int tid_b = threadIdx.x;
+        asm volatile("" : "+v"(tid_b));
+        const uint4 ones = make_uint4((tid_b & 63) < 32 ? 0x3f80u : 0u, 0u, 0u, 0u);  // bf16 1.0 at k = 0
 #pragma unroll
-    for (int b = 0; b < WB; ++b) {
-        const int64_t nblk = t0 + (wt * WB + b) * 32;
+        for (int a = 0; a < WA; ++a) {
+            uint32_t bc = bcol[a];
+            asm volatile("" : "+v"(bc));
 #pragma unroll
-        for (int a0 = 0; a0 < WA; a0 += C::SA) {
-            if (!vec_rows) {
+            for (int b = 0; b < WB; ++b) {
+                acc[a][b][0] = mfma32x32x16(make_uint4(bc, 0u, 0u, 0u), ones, f32x16{});
+#pragma unroll
+                for (int p = 1; p < G; ++p) acc[a][b][p] = f32x16{};
+            }
+        }
+        const bool has_prev = k > 0 && vec_rows;
+        const __amdgpu_buffer_rsrc_t rs_prev = tile_rsrc(k > 0 ? k - 1 : 0);
+        for (int s = 0; s < n_stages; s += 2) {  // n_stages is even (the channel padding sees to it)
+            step(k, s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
+            step(k, s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
+        }
+        // stores of the previous tile that did not fit in this tile's stages
+        if (has_prev)
+            for (int j = n_stages * C::SPS; j < C::NSTORE; ++j) store_staged(j, read_staged(j), rs_prev, true);
+
+        // ---- epilogue of tile k: inverse DFT; stage the outputs (stored during the next tile) ----
+        // lane-derived values are recomputed here (behind an opaque copy) rather than kept live
+        // through the stage loop, where registers are scarce
+        int tid_e = threadIdx.x;
+        asm volatile("" : "+v"(tid_e));
+        const int lane_e = tid_e & 63, wave_e = tid_e >> 6;
+        const int wo_e = wave_e % OW, wt_e = wave_e / OW;
+        const int h_e = lane_e >> 5, rcol_e = lane_e & 31;
+        uint4 *const stg_e = lds + 2 * C::XST + wave_e * C::STG;
+        const int64_t t0 = (int64_t)(tt0 + k * tstep) * C::BT;
+#pragma unroll
+        for (int b = 0; b < WB; ++b) {
+#pragma unroll
+            for (int a0 = 0; a0 < WA; a0 += C::SA) {
+                if constexpr (!vec_rows) {  // rows not a whole number of 16-byte pieces: element stores
+                    const int64_t nblk = t0 + (wt_e * WB + b) * 32;
+#pragma unroll
+                    for (int ai = 0; ai < C::SA; ++ai)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int o = o0 + (wo_e * WA + a0 + ai) * 32 + 8 * (v >> 2) + 4 * h_e + (v & 3);
+                            const int64_t n = nblk + rcol_e;
+                            if (o >= C_out || n >= N) continue;
+                            float Y[G], out[G];
+#pragma unroll
+                            for (int p = 0; p < G; ++p) Y[p] = acc[a0 + ai][b][p][v];
+                            inverse_planes<G>(Y, out);
+#pragma unroll
+                            for (int g = 0; g < G; ++g) y[(n * C_out + o) * G + g] = pack_bf16(out[g]);
+                        }
+                    continue;
+                }
+                uint4 *ust = stg_e + (b * (WA / C::SA) + a0 / C::SA) * C::UST;
 #pragma unroll
                 for (int ai = 0; ai < C::SA; ++ai)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int o = o0 + (wo * WA + a0 + ai) * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                        const int64_t n = nblk + rcol;
-                        if (o >= C_out || n >= N) continue;
-                        float Y[G], out[G];
+                    for (int vq = 0; vq < 4; ++vq) {
+                        float out[4 * G];
 #pragma unroll
-                        for (int p = 0; p < G; ++p) Y[p] = acc[a0 + ai][b][p][v];
-                        inverse_planes<G>(Y, out);
+                        for (int v = 0; v < 4; ++v) {
+                            float Y[G];
 #pragma unroll
-                        for (int g = 0; g < G; ++g) y[(n * C_out + o) * G + g] = pack_bf16(out[g]);
-                    }
-                continue;
-            }
+                            for (int p = 0; p < G; ++p) Y[p] = acc[a0 + ai][b][p][4 * vq + v];
+                            inverse_planes<G>(Y, out + v * G);
+                        }
+                        const int ol = ai * 32 + 8 * vq + 4 * h_e;  // first of the 4 outputs in the unit row
+                        if constexpr (G == 1) {
+                            uint2 w;
+                            w.x = pack_bf16x2(out[0], out[1]);
+                            w.y = pack_bf16x2(out[2], out[3]);
+                            const int piece = ol / 8;  // 8 outputs x 2 B per piece
+                            reinterpret_cast<uint2 *>(ust + rcol_e * C::PR + (piece ^ (rcol_e & 7)))[(ol >> 2) & 1] = w;
+                        } else {
 #pragma unroll
-            for (int ai = 0; ai < C::SA; ++ai)
-#pragma unroll
-                for (int vq = 0; vq < 4; ++vq) {
-                    float out[4 * G];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float Y[G];
-#pragma unroll
-                        for (int p = 0; p < G; ++p) Y[p] = acc[a0 + ai][b][p][4 * vq + v];
-                        inverse_planes<G>(Y, out + v * G);
-                    }
-                    const int ol = ai * 32 + 8 * vq + 4 * h;  // first of the 4 outputs in the unit row
-                    if constexpr (G == 1) {
-                        uint2 w;
-                        w.x = pack_bf16x2(out[0], out[1]);
-                        w.y = pack_bf16x2(out[2], out[3]);
-                        const int piece = ol / 8;  // 8 outputs x 2 B per piece
-                        reinterpret_cast<uint2 *>(stg + rcol * C::PR + (piece ^ (rcol & 7)))[(ol >> 2) & 1] = w;
-                    } else {
-#pragma unroll
-                        for (int k = 0; k < G / 2; ++k) {
-                            const int piece = ol * G / 8 + k;
-                            stg[rcol * C::PR + (piece ^ (rcol & 7))] = pack_bf16x8(out + 8 * k);
+                            for (int kq = 0; kq < G / 2; ++kq) {
+                                const int piece = ol * G / 8 + kq;
+                                ust[rcol_e * C::PR + (piece ^ (rcol_e & 7))] = pack_bf16x8(out + 8 * kq);
+                            }
                         }
                     }
-                }
-            const int piece0 = (o0 + (wo * WA + a0) * 32) * G / 8;
-#pragma unroll
-            for (int j = 0; j < C::PR / 2; ++j) {
-                const int r = j * (64 / C::PR) + lane / C::PR, pc = lane % C::PR;
-                const uint4 v = stg[r * C::PR + (pc ^ (r & 7))];
-                const int64_t n = nblk + r;
-                if (n < N && piece0 + pc < yrow_pieces)
-                    st_nt16(reinterpret_cast<uint4 *>(y) + n * yrow_pieces + piece0 + pc, v);
             }
         }
+    }
+    // the last tile's outputs
+    if constexpr (vec_rows) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(ntl - 1);
+#pragma unroll
+        for (int j = 0; j < C::NSTORE; ++j) store_staged(j, read_staged(j), rs, true);
     }
 }
 
@@ -343,10 +427,21 @@ static hipError_t launch_big(const Plan *p, const void *x, const void *b, void *
     const int64_t tiles_t = (N + C::BT - 1) / C::BT;
     const int tiles_o = p->NB_total / (C::BO / 32);
     const int n_stages = p->KS / C::KSS;
-    if (tiles_t * tiles_o > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_big<G, WA, WB, OW, TW>), dim3((unsigned)(tiles_t * tiles_o)), dim3(C::NT), 0, s,
-                       (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
-                       (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t);
+    // a token tile's output rows are addressed with 32-bit buffer offsets
+    if (tiles_t > 0x7fffffff || (int64_t)C::BT * p->C_out * G * 2 > 0x7fffffff) return hipErrorInvalidValue;
+    // one workgroup per compute unit, a whole number of them per output tile
+    int64_t per_o = std::max(1, p->fwd.num_cus / tiles_o);
+    per_o = std::min<int64_t>(per_o, tiles_t);
+    const int64_t grid = per_o * tiles_o;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if ((p->C_out * G) % 8 == 0)
+        hipLaunchKernelGGL((k_big<G, WA, WB, OW, TW, true>), dim3((unsigned)grid), dim3(C::NT), 0, s,
+                           (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
+                           (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o);
+    else
+        hipLaunchKernelGGL((k_big<G, WA, WB, OW, TW, false>), dim3((unsigned)grid), dim3(C::NT), 0, s,
+                           (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
+                           (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o);
     return hipGetLastError();
 }
 
@@ -382,6 +477,7 @@ bool select_big(int G, int C_in, int C_out, KernelChoice *out) {
         out->tokens_per_block = e.BT;
         out->block_threads = e.NT;
         out->lds_bytes = e.lds;
+        out->num_cus = device_num_cus();
         out->launch = e.launch;
         snprintf(out->name, sizeof(out->name), "bf16 big G=%d BO=%d BT=%d (%s) mfma32x32x16", G, e.BO, e.BT,
                  e.tile);
