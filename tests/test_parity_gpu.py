@@ -80,6 +80,30 @@ def test_workload_full_size_sampled(w, expanded, cuda_device):
            f"{w.name} full N={w.N} sampled {len(idx)} {'expanded' if expanded else 'spectral'}")
 
 
+# Wide outputs make many output tiles, so on a 256-CU device each persistent workgroup of the
+# large-channel kernel walks several token tiles at small N: this exercises the hand-over between
+# tiles (the load pipeline crossing tile boundaries, a tile's outputs stored during the next tile's
+# stages, the last tile's own flush) including a ragged last tile and rows that are not a whole
+# number of 16-byte pieces (C_out * G not a multiple of 8).
+@pytest.mark.parametrize("expanded", [False, True], ids=["spectral", "expanded"])
+@pytest.mark.parametrize("G,C_in,C_out", [(4, 128, 4096), (8, 64, 2048), (4, 128, 4095), (2, 128, 4096),
+                                          (1, 256, 4096)])
+def test_large_channel_multi_tile(G, C_in, C_out, expanded, cuda_device):
+    if expanded and G == 1:
+        pytest.skip("G = 1 has no separate expanded form")
+    N = 3001
+    x, W, b = make_inputs(G, C_in, C_out, N, "bf16", seed=3)
+    h, y = _run(x, W, b, cuda_device, expanded)
+    desc = h.describe()
+    print(f"[kernel] {desc}", flush=True)
+    assert "big" in desc.split("|")[2 if expanded else 1], desc
+    edges = [t * 64 + d for t in range(N // 64 + 1) for d in (0, 63)] + [N - 1]
+    idx = np.unique(np.concatenate([_sample_tokens(N, k=96, seed=5), np.array([e for e in edges if e < N])]))
+    ref = oracle.forward(x[idx], W, b)
+    _check(y[torch.as_tensor(idx, device=y.device)], ref, "bf16",
+           f"G={G} {C_in}->{C_out} N={N} {'expanded' if expanded else 'spectral'} sampled {len(idx)}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("N", [1, 17, 1000])
