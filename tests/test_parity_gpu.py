@@ -85,14 +85,19 @@ def test_workload_full_size_sampled(w, expanded, cuda_device):
 # tiles (the load pipeline crossing tile boundaries, a tile's outputs stored during the next tile's
 # stages, the last tile's own flush) including a ragged last tile and rows that are not a whole
 # number of 16-byte pieces (C_out * G not a multiple of 8).
+@pytest.mark.parametrize("with_bias", [True, False], ids=["bias", "nobias"])
 @pytest.mark.parametrize("expanded", [False, True], ids=["spectral", "expanded"])
 @pytest.mark.parametrize("G,C_in,C_out", [(4, 128, 4096), (8, 64, 2048), (4, 128, 4095), (2, 128, 4096),
                                           (1, 256, 4096)])
-def test_large_channel_multi_tile(G, C_in, C_out, expanded, cuda_device):
+def test_large_channel_multi_tile(G, C_in, C_out, expanded, with_bias, cuda_device):
     if expanded and G == 1:
         pytest.skip("G = 1 has no separate expanded form")
+    if not with_bias and G in (2, 1):
+        pytest.skip("the no-bias case is covered at G = 4 and 8")
     N = 3001
     x, W, b = make_inputs(G, C_in, C_out, N, "bf16", seed=3)
+    if not with_bias:
+        b = None
     h, y = _run(x, W, b, cuda_device, expanded)
     desc = h.describe()
     print(f"[kernel] {desc}", flush=True)
