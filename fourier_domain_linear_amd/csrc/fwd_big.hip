@@ -11,8 +11,8 @@
 // stages instead of in one burst at its end (every compute unit storing at once runs at the HBM
 // write rate while the matrix cores idle).
 //
-// Tile: BO outputs x BT tokens, all G planes; OW x TW waves, each owning WA x WB blocks of 32 outputs
-// x 32 tokens. The channel (K) loop runs in stages of SC input channels (SC*G*2 bytes per token row:
+// Tile: BO outputs x BT tokens, all G planes; OW x TW waves (4 or 8: one or two per SIMD), each owning
+// WA x WB blocks of 32 outputs x 32 tokens. The channel (K) loop runs in stages of SC input channels (SC*G*2 bytes per token row:
 // whole 128-byte lines), two stages per loop trip so every register slot is fixed:
 //   - x: raw rows are loaded into a two-slot register ring two stages ahead (HBM latency spans
 //     several stages of products), transformed (group DFT, fp32) one stage ahead and written to one
@@ -64,7 +64,7 @@ __device__ __forceinline__ void spectral_mfma32(const uint4 (&w)[G], const uint4
     }
 }
 
-// G samples of NCH channels (element j*G+g) -> G planes of NCH bf16 (NCH = 4 or 8).
+// G samples of NCH channels (element j*G+g) -> G planes of NCH bf16 (NCH = 2, 4 or 8).
 template <int G, int NCH>
 __device__ __forceinline__ void dft_ch(const uint4 (&r)[NCH * G / 8], float (&pl)[G][NCH]) {
 #pragma unroll
@@ -121,8 +121,8 @@ struct BigCfg {
     static constexpr int BO = 32 * WA * OW, BT = 32 * WB * TW;
     static constexpr int SC = BigStage<G>::SC, KSS = BigStage<G>::KSS, GRP = BigStage<G>::GRP;
     static constexpr int SA = BigStage<G>::SA;
-    // x work items: (token, NCH channels); NCH = 4 where 8-channel items would leave threads idle
-    static constexpr int NCH = (G >= 2 && BT * GRP < NT) ? 4 : 8;
+    // x work items: (token, NCH channels), as wide as possible while every thread has one
+    static constexpr int NCH = BT * SC / 8 >= NT ? 8 : BT * SC / 4 >= NT ? 4 : 2;
     static constexpr int ITEMS = BT * (SC / NCH) / NT;      // x items per thread per stage
     static constexpr int XU4 = NCH * G / 8;                 // uint4 of raw x per item
     static constexpr int XST = (BT / 32) * KSS * G * 64;    // uint4 per x-plane buffer (1 KB chunks)
@@ -216,6 +216,8 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
             for (int p = 0; p < G; ++p) {
                 if constexpr (NCH == 8) {
                     dst[p * 64] = pack_bf16x8(pl[p]);
+                } else if constexpr (NCH == 2) {
+                    reinterpret_cast<uint32_t *>(dst + p * 64)[(c0 >> 1) & 3] = pack_bf16x2(pl[p][0], pl[p][1]);
                 } else {
                     uint2 w;
                     w.x = pack_bf16x2(pl[p][0], pl[p][1]);
@@ -456,9 +458,12 @@ struct BigEntry {
      BigCfg<G, WA, WB, OW, TW>::NT, BigCfg<G, WA, WB, OW, TW>::LDS, launch_big<G, WA, WB, OW, TW>,         \
      #WA "x" #WB " blocks/wave, " #OW "x" #TW " waves"}
 static const BigEntry kBig[] = {
-    BE(1, 2, 4, 4, 1),
-    BE(2, 2, 4, 4, 1),
-    BE(4, 2, 2, 4, 1),
+    // two waves per SIMD (8 waves, 128 accumulators each) where one wave's 32-output blocks keep
+    // the weight reuse: the waves of a SIMD hide each other's waits. At G = 8 a wave needs all 256
+    // accumulators for two token blocks (fewer would double the L2 traffic per product), so one.
+    BE(1, 2, 4, 8, 1),
+    BE(2, 1, 4, 8, 1),
+    BE(4, 1, 2, 8, 1),
     BE(8, 1, 2, 4, 1),
 };
 #undef BE
