@@ -141,6 +141,7 @@ struct BigCfg {
     static constexpr size_t LDS = (size_t)LDS_U4 * 16;
     static_assert(WA % SA == 0, "store unit must divide the wave's output blocks");
     static_assert(ITEMS >= 1 && ITEMS * NT == BT * (SC / NCH), "x items must split evenly over the threads");
+    static_assert(XU4 >= 1, "an x item must fill at least one 16-byte piece");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
