@@ -136,7 +136,7 @@ struct BigCfg {
     static constexpr int UST = 32 * PR;                     // uint4 per unit
     static constexpr int STG = NU * UST;                    // uint4 of staging per wave
     static constexpr int NSTORE = NU * PR / 2;
-    static constexpr int SPS = G == 8 || G == 1 ? 2 : 3;
+    static constexpr int SPS = NW == 8 ? 1 : 2;  // stores per stage (measured: 8 waves 1, 4 waves 2)
     static constexpr int LDS_U4 = 2 * XST + NW * STG;
     static constexpr size_t LDS = (size_t)LDS_U4 * 16;
     static_assert(WA % SA == 0, "store unit must divide the wave's output blocks");
