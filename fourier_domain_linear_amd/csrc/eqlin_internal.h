@@ -13,8 +13,9 @@ namespace eqlin {
 enum KernelKind {
     KIND_STREAM = 0,    // bf16, small C_in: persistent workgroup per CU, the C_out tile's weights in
                         // LDS, 16-token row blocks streamed through the waves, x straight to registers
-    KIND_TILED = 1,     // bf16, any C: GEMM-style output x token tiles on 32x32x16 matrix cores, x
-                        // planes (transformed once per stage) and weights double-buffered in LDS
+    KIND_BIG = 1,       // bf16, large C: persistent workgroups, each keeping one output tile and
+                        // walking token tiles on 32x32x16 matrix cores; x planes transformed once per
+                        // stage into LDS, weights straight to registers, outputs stored a tile later
     KIND_F32 = 2        // fp32: vector-ALU spectral kernel
 };
 

@@ -474,7 +474,7 @@ bool select_big(int G, int C_in, int C_out, KernelChoice *out) {
     (void)C_out;
     for (const auto &e : kBig) {
         if (e.G != G) continue;
-        out->kind = KIND_TILED;
+        out->kind = KIND_BIG;
         out->frag_kind = 2;
         out->rows_per_block = 32;
         out->kc = 16;
