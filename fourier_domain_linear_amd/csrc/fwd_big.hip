@@ -471,9 +471,10 @@ static const BigEntry kBig[] = {
 
 bool select_big(int G, int C_in, int C_out, KernelChoice *out) {
     (void)C_in;
-    (void)C_out;
     for (const auto &e : kBig) {
         if (e.G != G) continue;
+        // a token tile's output rows are addressed with 32-bit buffer offsets
+        if ((int64_t)e.BT * C_out * G * 2 > 0x7fffffff) return false;
         out->kind = KIND_BIG;
         out->frag_kind = 2;
         out->rows_per_block = 32;

@@ -54,7 +54,8 @@ typedef struct eqlin_plan *eqlin_handle_t;
 typedef enum {
     EQLIN_OK = 0,
     EQLIN_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, G not in {1,2,4,8}, ... */
-    EQLIN_ERR_UNSUPPORTED = 2,   /* valid layer the kernels do not cover (bf16 with C_in % 8 != 0) */
+    EQLIN_ERR_UNSUPPORTED = 2,   /* valid layer the kernels do not cover (bf16 with C_in % 8 != 0;
+                                    C_out * G or C_in * G above 2^20) */
     EQLIN_ERR_OUT_OF_MEMORY = 3, /* device allocation failed */
     EQLIN_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
 } eqlin_status_t;
@@ -75,7 +76,8 @@ typedef enum { EQLIN_F32 = 0, EQLIN_BF16 = 1 } eqlin_dtype_t;
  *
  *   W      device [C_out][C_in][G] of `dtype`; read once, stream-ordered. The caller may free or
  *          overwrite W once `stream` has passed this call.
- *   C_out, C_in >= 1; G in {1, 2, 4, 8}. EQLIN_BF16 needs C_in % 8 == 0 (else UNSUPPORTED).
+ *   C_out, C_in >= 1; G in {1, 2, 4, 8}; C_out * G and C_in * G <= 2^20 (else UNSUPPORTED).
+ *          EQLIN_BF16 needs C_in % 8 == 0 (else UNSUPPORTED).
  *   flags  EQLIN_PREPARE_EXPANDED to also build the unrolled weight for eqlin_forward_expanded.
  *   out    receives the new handle (set to NULL on failure).
  * Allocates device memory (hipMalloc) on the current device; synchronises nothing.
