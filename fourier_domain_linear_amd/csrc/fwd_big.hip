@@ -5,15 +5,16 @@
 // Transform" (gist.science explainer), "Enfoque Algorítmico" (group DFT -> per-frequency channel
 // products, k = 0..G/2) and "Implementación" (one fused kernel, Fourier fragments on chip).
 //
-// Persistent workgroups, one per compute unit: workgroup g keeps output tile g % tiles_o (its
-// weights and bias) and walks the token tiles g / tiles_o, + tstep, ... The load pipeline runs on
-// across tile boundaries, and a tile's outputs, staged in LDS, are stored during the next tile's
-// stages instead of in one burst at its end (every compute unit storing at once runs at the HBM
-// write rate while the matrix cores idle).
+// Persistent workgroups, one per compute unit: each keeps one output tile (its weights and bias) and
+// walks the token tiles tt0, tt0 + tstep, ... (block_tile: XCD-aware, so the workgroups sharing a
+// token tile mostly share an L2). The load pipeline runs on across tile boundaries, and a tile's
+// outputs, staged in LDS, are stored during the next tile's stages instead of in one burst at its
+// end (every compute unit storing at once runs at the HBM write rate while the matrix cores idle).
 //
-// Tile: BO outputs x BT tokens, all G planes; OW x TW waves (4 or 8: one or two per SIMD), each owning
-// WA x WB blocks of 32 outputs x 32 tokens. The channel (K) loop runs in stages of SC input channels (SC*G*2 bytes per token row:
-// whole 128-byte lines), two stages per loop trip so every register slot is fixed:
+// Tile: BO outputs x BT tokens, all G planes; OW x TW waves (4 or 8: one or two per SIMD), each
+// owning WA x WB blocks of 32 outputs x 32 tokens (k_p8, for G = 8, splits the planes instead). The
+// channel (K) loop runs in stages of SC input channels (SC*G*2 bytes per token row: whole 128-byte
+// lines), two stages per loop trip so every register slot is fixed:
 //   - x: raw rows are loaded into a two-slot register ring two stages ahead (HBM latency spans
 //     several stages of products), transformed (group DFT, fp32) one stage ahead and written to one
 //     of two LDS buffers as bf16 B operands (32 tokens x 16 channels x 1 plane per 1 KB chunk),
@@ -115,6 +116,22 @@ struct IC {
     static constexpr int value = V;
 };
 
+// Workgroup -> (output tile, first token tile). Workgroups are dealt to the 8 XCDs (each with its own
+// L2) round-robin: workgroup g runs on XCD g % 8. Workgroups are renumbered so that each XCD holds a
+// contiguous run of the logical order, and the logical order is: groups of xg output tiles, within a
+// group the token streams, within a stream the group's xg output tiles. An XCD then serves each x
+// tile from its L2 to the xg workgroups that share it, while keeping only xg output tiles' weights.
+// (xg divides tiles_o; xg = 1 puts one output tile per XCD when tiles_o = 8.)
+__device__ __forceinline__ void block_tile(int tiles_o, int xg, int &ot, int &tt0, int &tstep) {
+    const int grid = gridDim.x, g = blockIdx.x;
+    const int xcd = g % 8, per = grid / 8, extra = grid % 8;
+    const int L = xcd * per + min(xcd, extra) + g / 8;
+    tstep = grid / tiles_o;  // token streams per output tile
+    const int span = tstep * xg, og = L / span, r = L % span;
+    ot = og * xg + r % xg;
+    tt0 = r / xg;
+}
+
 template <int G, int WA, int WB, int OW, int TW>
 struct BigCfg {
     static constexpr int NW = OW * TW, NT = NW * 64;
@@ -145,8 +162,8 @@ struct BigCfg {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// Persistent: workgroup g keeps output tile g % tiles_o (its weights, bias and L2 set) and walks the
-// token tiles g / tiles_o, + tstep, ... (tstep = gridDim.x / tiles_o). The load pipeline runs on
+// Persistent: each workgroup keeps output tile ot (its weights, bias and L2 set) and walks the token
+// tiles tt0, tt0 + tstep, ... (block_tile; tstep = gridDim.x / tiles_o). The load pipeline runs on
 // across tile boundaries, and a tile's outputs are stored while the next tile computes.
 template <int G, int WA, int WB, int OW, int TW, bool VEC>
 __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ x4,
@@ -154,13 +171,14 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                                                       const uint16_t *__restrict__ bias, int bias_shift,
                                                       uint16_t *__restrict__ y, int64_t N, int C_in,
                                                       int C_out, int n_stages, int KS16, int tiles_t,
-                                                      int tiles_o) {
+                                                      int tiles_o, int xg) {
     using C = BigCfg<G, WA, WB, OW, TW>;
     constexpr int KSS = C::KSS, NCH = C::NCH;
     __shared__ uint4 lds[C::LDS_U4];  // two x-plane buffers, then each wave's output staging
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wo = wave % OW, wt = wave / OW;
-    const int ot = blockIdx.x % tiles_o, tt0 = blockIdx.x / tiles_o, tstep = gridDim.x / tiles_o;
+    int ot, tt0, tstep;
+    block_tile(tiles_o, xg, ot, tt0, tstep);
     const int ntl = tt0 < tiles_t ? (tiles_t - 1 - tt0) / tstep + 1 : 0;  // token tiles of this workgroup
     if (ntl == 0) return;
     const int o0 = ot * C::BO, ob0 = o0 / 32;
@@ -422,6 +440,270 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     }
 }
 
+// Output tiles per XCD group (see block_tile): the largest divisor of tiles_o whose weights fit in
+// kXcdWeightBudget of an XCD's 4 MB L2, leaving the rest to the streaming x tiles.
+constexpr size_t kXcdWeightBudget = 2u << 20;
+static int xcd_group(int tiles_o, size_t weight_bytes_per_tile) {
+    int best = 1;
+    for (int d = 1; d <= tiles_o; ++d)
+        if (tiles_o % d == 0 && d * weight_bytes_per_tile <= kXcdWeightBudget) best = d;
+    return best;
+}
+
+// ------------------------------------------------------------------------------------------------
+// k_p8: the G = 8 forward with two waves per SIMD. At G = 8 one wave needs all 256 accumulator
+// registers to keep two token blocks per weight fragment, so instead of splitting the tile, the two
+// waves of a SIMD split its frequency planes: both own the same 32 outputs and the same two 32-token
+// blocks; role 0 holds planes Re0, Re4, Re1, Im1 (k = 0, 4 and 1: six products per block), role 1
+// Re2, Im2, Re3, Im3 (k = 2 and 3: eight products). Each wave loads only its four weight planes (no
+// weight is read twice) and reads only its four x planes. At a tile's end the pair hands over the
+// four planes of one token block through LDS and each wave finishes one block (inverse DFT over all
+// eight planes, staging). Everything else -- persistence, the load pipeline, the deferred stores --
+// follows k_big.
+struct P8Cfg {
+    static constexpr int G = 8, OW = 4, NW = 8, NT = NW * 64, WB = 2;
+    static constexpr int BO = 32 * OW, BT = 32 * WB;
+    static constexpr int SC = 16, KSS = 1;
+    static constexpr int NCH = 2, ITEMS = BT * (SC / NCH) / NT, XU4 = NCH * G / 8;
+    static constexpr int XST = (BT / 32) * KSS * G * 64;  // uint4 per x-plane buffer
+    static constexpr int HP = G / 2;                     // planes per wave
+    static constexpr int WF = KSS * HP;                  // weight fragments per wave per stage
+    static constexpr int VPM = 10;                       // transform ALU ops per product
+    static constexpr int PR = 4 * G;                     // 16-byte pieces per staged row (32 outputs)
+    static constexpr int STG = 32 * PR;                  // uint4 of staging per wave: one 32 x 32 block
+    static constexpr int NSTORE = PR / 2;
+    static constexpr int SPS = 1;
+    static constexpr int LDS_U4 = 2 * XST + NW * STG;
+    static constexpr size_t LDS = (size_t)LDS_U4 * 16;
+    static_assert(ITEMS == 1 && XU4 == 2, "one 2-channel x item per thread");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(HP * 16 * 64 * 4 <= STG * 16, "a wave's staging holds the four planes it hands over");
+};
+
+__global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, const uint4 *__restrict__ wfrag,
+                                                  const uint16_t *__restrict__ bias, int bias_shift,
+                                                  uint16_t *__restrict__ y, int64_t N, int C_in, int C_out,
+                                                  int n_stages, int KS16, int tiles_t, int tiles_o, int xg) {
+    using C = P8Cfg;
+    constexpr int G = 8, KSS = C::KSS, NCH = C::NCH, WB = C::WB, HP = C::HP;
+    __shared__ uint4 lds[C::LDS_U4];  // two x-plane buffers, then each wave's staging / hand-over area
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wo = wave & 3;  // waves w and w + 4 share a SIMD, the output block and the token blocks
+    int ot, tt0, tstep;
+    block_tile(tiles_o, xg, ot, tt0, tstep);
+    const int ntl = tt0 < tiles_t ? (tiles_t - 1 - tt0) / tstep + 1 : 0;
+    if (ntl == 0) return;
+    const int o0 = ot * C::BO, ob0 = o0 / 32;
+    uint4 *const stg = lds + 2 * C::XST + wave * C::STG;
+    const int yrow_pieces = C_out * G / 8;
+    const int yrow_bytes = C_out * G * 2;
+    const int rcol = lane & 31;
+
+    auto load_x = [&](int k, int stage, uint4 (&dst)[C::ITEMS][C::XU4]) {
+        if (stage >= n_stages) {
+            stage -= n_stages;
+            ++k;
+        }
+        if (k >= ntl) {
+            k = ntl - 1;
+            stage = n_stages - 1;
+        }
+        const int64_t t0 = (int64_t)(tt0 + k * tstep) * C::BT;
+        const int tl = tid / (C::SC / NCH), cq = tid % (C::SC / NCH);
+        int64_t n = t0 + tl;
+        n = n < N ? n : N - 1;
+        int i0 = stage * C::SC + cq * NCH;
+        i0 = i0 < C_in ? i0 : C_in - NCH;  // padded channels meet zero weight columns
+        const uint4 *p = x4 + (n * C_in + i0) * G / 8;
+#pragma unroll
+        for (int q = 0; q < C::XU4; ++q) dst[0][q] = p[q];
+    };
+    auto load_w = [&](int stage, int role, uint4 (&dst)[C::WF]) {
+        stage = stage < n_stages ? stage : stage - n_stages;
+        const uint4 *src = wfrag + (size_t)((ob0 + wo) * KS16 + stage * KSS) * G * 64 + role * HP * 64 + lane;
+#pragma unroll
+        for (int r = 0; r < HP; ++r) dst[r] = src[r * 64];
+    };
+    auto dft_store = [&](const uint4 (&src)[C::ITEMS][C::XU4], uint4 *xb) {
+        const int tl = tid / (C::SC / NCH), cq = tid % (C::SC / NCH);
+        const int c0 = cq * NCH;
+        uint4 *dst = xb + ((tl >> 5) * KSS + (c0 >> 4)) * G * 64 + ((c0 >> 3) & 1) * 32 + (tl & 31);
+        float pl[G][NCH];
+        dft_ch<G, NCH>(src[0], pl);
+#pragma unroll
+        for (int p = 0; p < G; ++p)
+            reinterpret_cast<uint32_t *>(dst + p * 64)[(c0 >> 1) & 3] = pack_bf16x2(pl[p][0], pl[p][1]);
+    };
+    // a wave's staged block: role r finishes token block r
+    auto read_staged = [&](int j) {
+        const int r = j * (64 / C::PR) + lane / C::PR, pc = lane % C::PR;
+        return stg[r * C::PR + (pc ^ (r & 7))];
+    };
+    auto store_staged = [&](int j, int role, const uint4 &v, __amdgpu_buffer_rsrc_t rs, bool valid) {
+        const int r = j * (64 / C::PR) + lane / C::PR, pc = lane % C::PR;
+        const int piece = (o0 + wo * 32) * G / 8 + pc;
+        const int off = (role * 32 + r) * yrow_bytes + piece * 16;
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 d = {v.x, v.y, v.z, v.w};
+        const int keep = -(int)(valid & (piece < yrow_pieces));
+        __builtin_amdgcn_raw_buffer_store_b128(d, rs, (off & keep) | (0x7fffffff & ~keep), 0, kStoreAux);
+    };
+    auto tile_rsrc = [&](int k) {
+        const int64_t n0 = (int64_t)(tt0 + k * tstep) * C::BT;
+        const int64_t rows = N - n0 < C::BT ? N - n0 : C::BT;
+        return __builtin_amdgcn_make_buffer_rsrc(y + n0 * (C_out * G), (short)0, (int)(rows * yrow_bytes),
+                                                 0x00020000);
+    };
+
+    const int o_b = o0 + wo * 32 + rcol;
+    const uint32_t bcol = (bias && o_b < C_out) ? bias[o_b >> bias_shift] : 0u;
+
+    uint4 xr[2][C::ITEMS][C::XU4];
+    uint4 wr[2][C::WF];
+    load_w(0, wave >> 2, wr[0]);
+    load_x(0, 0, xr[0]);
+    load_x(0, 1, xr[1]);
+    dft_store(xr[0], lds);
+    lds_barrier();
+
+    // the whole tile loop, once per role (wave-uniform), so each copy's stages are branch-free
+    auto run = [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        constexpr int NMB = R == 0 ? 6 : 8;  // products per token block per K-step
+        f32x16 acc[WB][HP];
+        auto products = [&](int b, const uint4 (&w_cur)[C::WF], const uint4 *planes) {
+            uint4 xf[HP], xn[HP];
+#pragma unroll
+            for (int r = 0; r < HP; ++r) xf[r] = planes[((b * KSS) * G + R * HP + r) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < HP; ++r) {
+                const int pg = R * HP + r;  // global plane index: negated copies of Im planes
+                xn[r] = (pg >= 3 && (pg & 1)) ? neg_bf16x8(xf[r]) : xf[r];
+            }
+            if constexpr (R == 0) {
+                acc[b][0] = mfma32x32x16(w_cur[0], xf[0], acc[b][0]);
+                acc[b][1] = mfma32x32x16(w_cur[1], xf[1], acc[b][1]);
+                acc[b][2] = mfma32x32x16(w_cur[2], xf[2], acc[b][2]);
+                acc[b][2] = mfma32x32x16(w_cur[3], xn[3], acc[b][2]);
+                acc[b][3] = mfma32x32x16(w_cur[3], xf[2], acc[b][3]);
+                acc[b][3] = mfma32x32x16(w_cur[2], xf[3], acc[b][3]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < HP; c += 2) {
+                    acc[b][c] = mfma32x32x16(w_cur[c], xf[c], acc[b][c]);
+                    acc[b][c] = mfma32x32x16(w_cur[c + 1], xn[c + 1], acc[b][c]);
+                    acc[b][c + 1] = mfma32x32x16(w_cur[c + 1], xf[c], acc[b][c + 1]);
+                    acc[b][c + 1] = mfma32x32x16(w_cur[c], xf[c + 1], acc[b][c + 1]);
+                }
+            }
+        };
+        auto step = [&](int k, int s, uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
+                        const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF], const uint4 *planes,
+                        uint4 *planes_next, __amdgpu_buffer_rsrc_t rs_prev, bool has_prev) {
+            load_w(s + 1, R, w_next);
+            products(0, w_cur, planes);
+            interleave_stage<HP, NMB, C::WF, 1>();
+            __builtin_amdgcn_sched_barrier(0);
+            load_x(k, s + 2, x_free);
+            const int j = s * C::SPS;
+            const uint4 sv = read_staged(min(j, C::NSTORE - 1));
+            products(1, w_cur, planes);
+            dft_store(x_next, planes_next);  // past the last position: unused planes, harmless
+            interleave_stage<HP + 1, NMB, C::ITEMS * C::XU4, C::VPM>();
+            __builtin_amdgcn_sched_barrier(0);
+            store_staged(min(j, C::NSTORE - 1), R, sv, rs_prev, has_prev & (j < C::NSTORE));
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        for (int k = 0; k < ntl; ++k) {
+            int tid_b = threadIdx.x;
+            asm volatile("" : "+v"(tid_b));
+#pragma unroll
+            for (int b = 0; b < WB; ++b)
+#pragma unroll
+                for (int q = 0; q < HP; ++q) acc[b][q] = f32x16{};
+            if constexpr (R == 0) {  // the bias enters plane k = 0: one product of the bias column with ones
+                const uint4 ones = make_uint4((tid_b & 63) < 32 ? 0x3f80u : 0u, 0u, 0u, 0u);
+                uint32_t bc = bcol;
+                asm volatile("" : "+v"(bc));
+#pragma unroll
+                for (int b = 0; b < WB; ++b) acc[b][0] = mfma32x32x16(make_uint4(bc, 0u, 0u, 0u), ones, f32x16{});
+            }
+            const bool has_prev = k > 0;
+            const __amdgpu_buffer_rsrc_t rs_prev = tile_rsrc(k > 0 ? k - 1 : 0);
+            for (int s = 0; s < n_stages; s += 2) {  // n_stages is even (the channel padding sees to it)
+                step(k, s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
+                step(k, s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
+            }
+            if (has_prev)
+                for (int j = n_stages * C::SPS; j < C::NSTORE; ++j) store_staged(j, R, read_staged(j), rs_prev, true);
+
+            // ---- epilogue: hand the partner the planes of the block it finishes, take ours ----
+            int tid_e = threadIdx.x;
+            asm volatile("" : "+v"(tid_e));
+            const int lane_e = tid_e & 63, wave_e = tid_e >> 6;
+            float *const mine = reinterpret_cast<float *>(lds + 2 * C::XST + wave_e * C::STG);
+            const float *const theirs = reinterpret_cast<const float *>(lds + 2 * C::XST + (wave_e ^ 4) * C::STG);
+#pragma unroll
+            for (int q = 0; q < HP; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mine[(q * 16 + v) * 64 + lane_e] = acc[1 - R][q][v];
+            lds_barrier();
+            float recv[HP][16];
+#pragma unroll
+            for (int q = 0; q < HP; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) recv[q][v] = theirs[(q * 16 + v) * 64 + lane_e];
+            lds_barrier();
+            // inverse DFT of token block R over all eight planes, staged for the next tile's stages
+            const int h_e = lane_e >> 5, rcol_e = lane_e & 31;
+            auto plane = [&](int p, int v) { return (p / HP == R) ? acc[R][p % HP][v] : recv[p % HP][v]; };
+#pragma unroll
+            for (int vq = 0; vq < 4; ++vq) {
+                float out[4 * G];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float Y[G];
+#pragma unroll
+                    for (int p = 0; p < G; ++p) Y[p] = plane(p, 4 * vq + v);
+                    inverse_planes<G>(Y, out + v * G);
+                }
+                const int ol = 8 * vq + 4 * h_e;  // first of the 4 outputs in the staged row
+#pragma unroll
+                for (int kq = 0; kq < G / 2; ++kq) {
+                    const int piece = ol * G / 8 + kq;
+                    reinterpret_cast<uint4 *>(mine)[rcol_e * C::PR + (piece ^ (rcol_e & 7))] = pack_bf16x8(out + 8 * kq);
+                }
+            }
+        }
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(ntl - 1);
+#pragma unroll
+        for (int j = 0; j < C::NSTORE; ++j) store_staged(j, R, read_staged(j), rs, true);
+    };
+    if (wave < 4)
+        run(IC<0>{});
+    else
+        run(IC<1>{});
+}
+
+static hipError_t launch_p8(const Plan *p, const void *x, const void *b, void *y, int64_t N, hipStream_t s) {
+    using C = P8Cfg;
+    const int64_t tiles_t = (N + C::BT - 1) / C::BT;
+    const int tiles_o = p->NB_total / (C::BO / 32);
+    const int n_stages = p->KS / C::KSS;
+    if (tiles_t > 0x7fffffff || (int64_t)C::BT * p->C_out * C::G * 2 > 0x7fffffff) return hipErrorInvalidValue;
+    int64_t per_o = std::max(1, p->fwd.num_cus / tiles_o);
+    per_o = std::min<int64_t>(per_o, tiles_t);
+    const int64_t grid = per_o * tiles_o;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_p8, dim3((unsigned)grid), dim3(C::NT), 0, s, (const uint4 *)x,
+                       (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in,
+                       p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o,
+                       xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * C::G * 2));
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------------------------
 
 template <int G, int WA, int WB, int OW, int TW>
@@ -437,14 +719,15 @@ static hipError_t launch_big(const Plan *p, const void *x, const void *b, void *
     per_o = std::min<int64_t>(per_o, tiles_t);
     const int64_t grid = per_o * tiles_o;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    const int xg = xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * G * 2);
     if ((p->C_out * G) % 8 == 0)
         hipLaunchKernelGGL((k_big<G, WA, WB, OW, TW, true>), dim3((unsigned)grid), dim3(C::NT), 0, s,
                            (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
-                           (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o);
+                           (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o, xg);
     else
         hipLaunchKernelGGL((k_big<G, WA, WB, OW, TW, false>), dim3((unsigned)grid), dim3(C::NT), 0, s,
                            (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
-                           (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o);
+                           (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o, xg);
     return hipGetLastError();
 }
 
@@ -465,7 +748,7 @@ static const BigEntry kBig[] = {
     BE(1, 2, 4, 8, 1),
     BE(2, 1, 4, 8, 1),
     BE(4, 1, 2, 8, 1),
-    BE(8, 1, 2, 4, 1),
+    {8, P8Cfg::BO, P8Cfg::BT, P8Cfg::KSS, P8Cfg::NT, P8Cfg::LDS, launch_p8, "planes split over 2 waves/SIMD, 4x2 waves"},
 };
 #undef BE
 
