@@ -57,14 +57,15 @@ EQLIN_HD void forward_planes(const float *v, float *P) {
         static_assert(G == 8, "G must be 1, 2, 4 or 8");
         const float a0 = v[0] + v[4], a1 = v[1] + v[5], a2 = v[2] + v[6], a3 = v[3] + v[7];
         const float d0 = v[0] - v[4], d1 = v[1] - v[5], d2 = v[2] - v[6], d3 = v[3] - v[7];
-        const float e0 = a0 + a2, e1 = a1 + a3, f0 = a0 - a2, f1 = a1 - a3;
+        const float e0 = a0 + a2, e1 = a1 + a3, f0 = a0 - a2;
         const float t1 = d1 - d3, t2 = d1 + d3;
+        // the signs sit on the operands (exactly equal to negating the results; saves an instruction)
         P[0] = e0 + e1;                      // X0
         P[1] = e0 - e1;                      // X4
         P[2] = d0 + kSqrtHalf * t1;          // Re X1
-        P[3] = -(d2 + kSqrtHalf * t2);       // Im X1
+        P[3] = -kSqrtHalf * t2 - d2;         // Im X1
         P[4] = f0;                           // Re X2
-        P[5] = -f1;                          // Im X2
+        P[5] = a3 - a1;                      // Im X2
         P[6] = d0 - kSqrtHalf * t1;          // Re X3
         P[7] = d2 - kSqrtHalf * t2;          // Im X3
     }

@@ -499,33 +499,51 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
     const int yrow_bytes = C_out * G * 2;
     const int rcol = lane & 31;
 
-    auto load_x = [&](int k, int stage, uint4 (&dst)[C::ITEMS][C::XU4]) {
-        if (stage >= n_stages) {
-            stage -= n_stages;
-            ++k;
-        }
-        if (k >= ntl) {
-            k = ntl - 1;
-            stage = n_stages - 1;
-        }
-        const int64_t t0 = (int64_t)(tt0 + k * tstep) * C::BT;
-        const int tl = tid / (C::SC / NCH), cq = tid % (C::SC / NCH);
-        int64_t n = t0 + tl;
-        n = n < N ? n : N - 1;
-        int i0 = stage * C::SC + cq * NCH;
-        i0 = i0 < C_in ? i0 : C_in - NCH;  // padded channels meet zero weight columns
-        const uint4 *p = x4 + (n * C_in + i0) * G / 8;
-#pragma unroll
-        for (int q = 0; q < C::XU4; ++q) dst[0][q] = p[q];
+    // Loads are buffer loads: the per-stage part of every address is a scalar offset, so the stage loop
+    // spends no vector ALU on addresses. x: one resource per token tile (rows past N lie outside its
+    // range and read as zeros); this thread's (token, channel pair) offset is the same in every tile.
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const int tl = tid / (C::SC / NCH), cq = tid % (C::SC / NCH);
+    const int x_row = C_in * G * 2;                                  // bytes per token row
+    const int x_vo = tl * x_row + cq * NCH * G * 2;                  // stage 0 offset in the tile
+    const int x_vo_last = tl * x_row + (C_in - NCH) * G * 2;         // the row's last channel pair
+    auto x_rsrc = [&](int k) {  // k >= ntl (past the last tile): an empty range, loads read zeros
+        const int64_t n0 = (int64_t)(tt0 + k * tstep) * C::BT;
+        int64_t rows = N - n0 < C::BT ? N - n0 : C::BT;
+        rows = k < ntl ? rows : 0;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(x4 + (k < ntl ? n0 : 0) * C_in * G / 8), (short)0,
+                                                 (int)(rows * x_row), 0x00020000);
     };
-    auto load_w = [&](int stage, int role, uint4 (&dst)[C::WF]) {
-        stage = stage < n_stages ? stage : stage - n_stages;
-        const uint4 *src = wfrag + (size_t)((ob0 + wo) * KS16 + stage * KSS) * G * 64 + role * HP * 64 + lane;
+    // stage of the current tile (resource rs_c), or past its end: the next tile's (rs_n)
+    auto load_x = [&](__amdgpu_buffer_rsrc_t rs_c, __amdgpu_buffer_rsrc_t rs_n, int stage,
+                      uint4 (&dst)[C::ITEMS][C::XU4]) {
+        const bool next = stage >= n_stages;  // uniform
+        const __amdgpu_buffer_rsrc_t rs = next ? rs_n : rs_c;
+        stage = next ? stage - n_stages : stage;
+        // channels past C_in (the stage count is padded) re-read the row's last pair: finite values
+        // that meet zero weight columns
+        const int soff = stage * C::SC * G * 2;
+        const int vo = (stage * C::SC + cq * NCH < C_in) ? x_vo : x_vo_last - soff;
 #pragma unroll
-        for (int r = 0; r < HP; ++r) dst[r] = src[r * 64];
+        for (int q = 0; q < C::XU4; ++q) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, vo + 16 * q, soff, 0);
+            dst[0][q] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
+    // weights: one resource per wave (its output block and role's planes), stage as a scalar offset
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(wfrag + (size_t)((ob0 + (wave_u & 3)) * KS16) * G * 64 + (wave_u >> 2) * HP * 64), (short)0,
+        KS16 * G * 1024 - (wave_u >> 2) * HP * 1024, 0x00020000);
+    auto load_w = [&](int stage, uint4 (&dst)[C::WF]) {
+        stage = stage < n_stages ? stage : stage - n_stages;
+#pragma unroll
+        for (int r = 0; r < HP; ++r) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(w_rs, lane * 16 + r * 1024, stage * G * 1024, 0);
+            dst[r] = make_uint4(v.x, v.y, v.z, v.w);
+        }
     };
     auto dft_store = [&](const uint4 (&src)[C::ITEMS][C::XU4], uint4 *xb) {
-        const int tl = tid / (C::SC / NCH), cq = tid % (C::SC / NCH);
         const int c0 = cq * NCH;
         uint4 *dst = xb + ((tl >> 5) * KSS + (c0 >> 4)) * G * 64 + ((c0 >> 3) & 1) * 32 + (tl & 31);
         float pl[G][NCH];
@@ -560,9 +578,12 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
 
     uint4 xr[2][C::ITEMS][C::XU4];
     uint4 wr[2][C::WF];
-    load_w(0, wave >> 2, wr[0]);
-    load_x(0, 0, xr[0]);
-    load_x(0, 1, xr[1]);
+    load_w(0, wr[0]);
+    {
+        const __amdgpu_buffer_rsrc_t rs0 = x_rsrc(0);
+        load_x(rs0, rs0, 0, xr[0]);
+        load_x(rs0, rs0, 1, xr[1]);
+    }
     dft_store(xr[0], lds);
     lds_barrier();
 
@@ -571,43 +592,48 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
         constexpr int R = decltype(rc)::value;
         constexpr int NMB = R == 0 ? 6 : 8;  // products per token block per K-step
         f32x16 acc[WB][HP];
-        auto products = [&](int b, const uint4 (&w_cur)[C::WF], const uint4 *planes) {
-            uint4 xf[HP], xn[HP];
+        // Re += Wr Xr + (-Wi) Xi and Im += Wi Xr + Wr Xi: the sign goes on the weight fragment (wn, one
+        // negated copy per stage and Im plane), which serves both token blocks
+        // (first: the tile's first stage, whose products start the accumulators from zero; role 0's
+        // k = 0 plane starts from the bias instead)
+        auto products = [&](auto first, int b, const uint4 (&w)[C::WF], const uint4 (&wn)[2], const uint4 *planes) {
+            constexpr bool F = decltype(first)::value;
+            uint4 xf[HP];
 #pragma unroll
             for (int r = 0; r < HP; ++r) xf[r] = planes[((b * KSS) * G + R * HP + r) * 64 + lane];
-#pragma unroll
-            for (int r = 0; r < HP; ++r) {
-                const int pg = R * HP + r;  // global plane index: negated copies of Im planes
-                xn[r] = (pg >= 3 && (pg & 1)) ? neg_bf16x8(xf[r]) : xf[r];
-            }
+            auto acc0 = [&](int q) { return F ? f32x16{} : acc[b][q]; };
             if constexpr (R == 0) {
-                acc[b][0] = mfma32x32x16(w_cur[0], xf[0], acc[b][0]);
-                acc[b][1] = mfma32x32x16(w_cur[1], xf[1], acc[b][1]);
-                acc[b][2] = mfma32x32x16(w_cur[2], xf[2], acc[b][2]);
-                acc[b][2] = mfma32x32x16(w_cur[3], xn[3], acc[b][2]);
-                acc[b][3] = mfma32x32x16(w_cur[3], xf[2], acc[b][3]);
-                acc[b][3] = mfma32x32x16(w_cur[2], xf[3], acc[b][3]);
+                acc[b][0] = mfma32x32x16(w[0], xf[0], acc[b][0]);
+                acc[b][1] = mfma32x32x16(w[1], xf[1], acc0(1));
+                acc[b][2] = mfma32x32x16(w[2], xf[2], acc0(2));
+                acc[b][2] = mfma32x32x16(wn[1], xf[3], acc[b][2]);
+                acc[b][3] = mfma32x32x16(w[3], xf[2], acc0(3));
+                acc[b][3] = mfma32x32x16(w[2], xf[3], acc[b][3]);
             } else {
 #pragma unroll
                 for (int c = 0; c < HP; c += 2) {
-                    acc[b][c] = mfma32x32x16(w_cur[c], xf[c], acc[b][c]);
-                    acc[b][c] = mfma32x32x16(w_cur[c + 1], xn[c + 1], acc[b][c]);
-                    acc[b][c + 1] = mfma32x32x16(w_cur[c + 1], xf[c], acc[b][c + 1]);
-                    acc[b][c + 1] = mfma32x32x16(w_cur[c], xf[c + 1], acc[b][c + 1]);
+                    acc[b][c] = mfma32x32x16(w[c], xf[c], acc0(c));
+                    acc[b][c] = mfma32x32x16(wn[c / 2], xf[c + 1], acc[b][c]);
+                    acc[b][c + 1] = mfma32x32x16(w[c + 1], xf[c], acc0(c + 1));
+                    acc[b][c + 1] = mfma32x32x16(w[c], xf[c + 1], acc[b][c + 1]);
                 }
             }
         };
-        auto step = [&](int k, int s, uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
+        auto step = [&](auto first, __amdgpu_buffer_rsrc_t xrs_c, __amdgpu_buffer_rsrc_t xrs_n, int s,
+                        uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
                         const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF], const uint4 *planes,
                         uint4 *planes_next, __amdgpu_buffer_rsrc_t rs_prev, bool has_prev) {
-            load_w(s + 1, R, w_next);
-            products(0, w_cur, planes);
+            load_w(s + 1, w_next);
+            uint4 wn[2];  // role 0: -W(Im1) in slot 1; role 1: -W(Im2), -W(Im3)
+            wn[0] = neg_bf16x8(w_cur[1]);
+            wn[1] = neg_bf16x8(w_cur[3]);
+            products(first, 0, w_cur, wn, planes);
             interleave_stage<HP, NMB, C::WF, 1>();
             __builtin_amdgcn_sched_barrier(0);
-            load_x(k, s + 2, x_free);
+            load_x(xrs_c, xrs_n, s + 2, x_free);
             const int j = s * C::SPS;
             const uint4 sv = read_staged(min(j, C::NSTORE - 1));
-            products(1, w_cur, planes);
+            products(first, 1, w_cur, wn, planes);
             dft_store(x_next, planes_next);  // past the last position: unused planes, harmless
             interleave_stage<HP + 1, NMB, C::ITEMS * C::XU4, C::VPM>();
             __builtin_amdgcn_sched_barrier(0);
@@ -619,10 +645,6 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
         for (int k = 0; k < ntl; ++k) {
             int tid_b = threadIdx.x;
             asm volatile("" : "+v"(tid_b));
-#pragma unroll
-            for (int b = 0; b < WB; ++b)
-#pragma unroll
-                for (int q = 0; q < HP; ++q) acc[b][q] = f32x16{};
             if constexpr (R == 0) {  // the bias enters plane k = 0: one product of the bias column with ones
                 const uint4 ones = make_uint4((tid_b & 63) < 32 ? 0x3f80u : 0u, 0u, 0u, 0u);
                 uint32_t bc = bcol;
@@ -632,9 +654,14 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
             }
             const bool has_prev = k > 0;
             const __amdgpu_buffer_rsrc_t rs_prev = tile_rsrc(k > 0 ? k - 1 : 0);
-            for (int s = 0; s < n_stages; s += 2) {  // n_stages is even (the channel padding sees to it)
-                step(k, s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
-                step(k, s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
+            const __amdgpu_buffer_rsrc_t xrs_c = x_rsrc(k), xrs_n = x_rsrc(k + 1);
+            // n_stages is even (the channel padding sees to it); the first pair is peeled so the first
+            // products can start the accumulators without clearing them
+            step(IC<1>{}, xrs_c, xrs_n, 0, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
+            step(IC<0>{}, xrs_c, xrs_n, 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
+            for (int s = 2; s < n_stages; s += 2) {
+                step(IC<0>{}, xrs_c, xrs_n, s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
+                step(IC<0>{}, xrs_c, xrs_n, s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
             }
             if (has_prev)
                 for (int j = n_stages * C::SPS; j < C::NSTORE; ++j) store_staged(j, R, read_staged(j), rs_prev, true);
