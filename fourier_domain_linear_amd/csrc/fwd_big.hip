@@ -50,17 +50,21 @@ struct BigStage {
     static constexpr int SA = G == 1 ? 2 : 1;        // 32-output blocks per epilogue store unit
 };
 
-template <int G>
-__device__ __forceinline__ void spectral_mfma32(const uint4 (&w)[G], const uint4 (&a)[G],
-                                                const uint4 (&an)[G], f32x16 (&acc)[G]) {
+// The products of one K-step for all planes: Re += Wr Xr + (-Wi) Xi, Im += Wi Xr + Wr Xi (wn holds the
+// negated Im weight fragments, indexed like w). F: the accumulators of planes 1.. start from zero
+// (plane 0 always accumulates: it starts from the bias).
+template <int G, bool F>
+__device__ __forceinline__ void spectral_mfma32(const uint4 (&w)[G], const uint4 (&wn)[G], const uint4 (&a)[G],
+                                                f32x16 (&acc)[G]) {
+    auto c = [&](int p) { return F ? f32x16{} : acc[p]; };
     acc[0] = mfma32x32x16(w[0], a[0], acc[0]);
-    if constexpr (G >= 2) acc[1] = mfma32x32x16(w[1], a[1], acc[1]);
+    if constexpr (G >= 2) acc[1] = mfma32x32x16(w[1], a[1], c(1));
 #pragma unroll
     for (int k = 1; k < G / 2; ++k) {
         const int r = 2 * k, i = 2 * k + 1;
-        acc[r] = mfma32x32x16(w[r], a[r], acc[r]);
-        acc[r] = mfma32x32x16(w[i], an[i], acc[r]);
-        acc[i] = mfma32x32x16(w[i], a[r], acc[i]);
+        acc[r] = mfma32x32x16(w[r], a[r], c(r));
+        acc[r] = mfma32x32x16(wn[i], a[i], acc[r]);
+        acc[i] = mfma32x32x16(w[i], a[r], c(i));
         acc[i] = mfma32x32x16(w[r], a[i], acc[i]);
     }
 }
@@ -188,39 +192,56 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     const int yrow_bytes = C_out * G * 2;
     const int rcol = lane & 31;
 
-    // ---- loaders. A position past the last one re-loads the last (valid addresses, unused data),
-    // so the loop body has no branches around loads. ----
-    auto load_x = [&](int k, int stage, uint4 (&dst)[C::ITEMS][C::XU4]) {
-        if (stage >= n_stages) {  // uniform: the next tile's first stages
-            stage -= n_stages;
-            ++k;
-        }
-        if (k >= ntl) {
-            k = ntl - 1;
-            stage = n_stages - 1;
-        }
-        const int64_t t0 = (int64_t)(tt0 + k * tstep) * C::BT;
-#pragma unroll
-        for (int it = 0; it < C::ITEMS; ++it) {
-            const int item = tid + it * C::NT;
-            const int tl = item / (C::SC / NCH), cq = item % (C::SC / NCH);
-            int64_t n = t0 + tl;
-            n = n < N ? n : N - 1;
-            int i0 = stage * C::SC + cq * NCH;
-            i0 = i0 < C_in ? i0 : C_in - NCH;  // padded channels meet zero weight columns
-            const uint4 *p = x4 + (n * C_in + i0) * G / 8;
-#pragma unroll
-            for (int q = 0; q < C::XU4; ++q) dst[it][q] = p[q];
-        }
+    // ---- loaders: buffer loads whose per-stage offset is a scalar, so the stage loop spends no
+    // vector ALU on addresses. x: one resource per token tile (rows past N read as zeros; past the
+    // last tile, an empty range); a thread's (token, channel) offsets are the same in every tile.
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    // (item it of a thread is token tl + it * NT / (SC / NCH), same channels: a scalar row offset)
+    static_assert(C::NT % (C::SC / NCH) == 0, "items of a thread differ by whole token rows");
+    const int x_row = C_in * G * 2;  // bytes per token row
+    const int x_tl = tid / (C::SC / NCH), x_c0 = (tid % (C::SC / NCH)) * NCH;
+    const int x_vo = x_tl * x_row + x_c0 * G * 2;
+    const int x_vo_last = x_tl * x_row + (C_in - NCH) * G * 2;  // the row's last channels
+    auto x_rsrc = [&](int k) {
+        const int64_t n0 = (int64_t)(tt0 + k * tstep) * C::BT;
+        int64_t rows = N - n0 < C::BT ? N - n0 : C::BT;
+        rows = k < ntl ? rows : 0;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(x4 + (k < ntl ? n0 : 0) * C_in * G / 8), (short)0,
+                                                 (int)(rows * x_row), 0x00020000);
     };
+    // stage of the current tile (resource rs_c), or past its end: the next tile's (rs_n)
+    auto load_x = [&](__amdgpu_buffer_rsrc_t rs_c, __amdgpu_buffer_rsrc_t rs_n, int stage,
+                      uint4 (&dst)[C::ITEMS][C::XU4]) {
+        const bool next = stage >= n_stages;  // uniform
+        const __amdgpu_buffer_rsrc_t rs = next ? rs_n : rs_c;
+        stage = next ? stage - n_stages : stage;
+        const int soff = stage * C::SC * G * 2;
+        // channels past C_in (the stage count is padded) re-read the row's last channels: finite
+        // values that meet zero weight columns
+        const int vo = (stage * C::SC + x_c0 < C_in) ? x_vo : x_vo_last - soff;
+#pragma unroll
+        for (int it = 0; it < C::ITEMS; ++it)
+#pragma unroll
+            for (int q = 0; q < C::XU4; ++q) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, vo + 16 * q, soff + it * (C::NT / (C::SC / NCH)) * x_row, 0);
+                dst[it][q] = make_uint4(v.x, v.y, v.z, v.w);
+            }
+    };
+    // weights: one resource per wave (its WA output blocks), block and stage as a scalar offset
+    const int wo_u = __builtin_amdgcn_readfirstlane(wave) % OW;
+    const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(wfrag + (size_t)((ob0 + wo_u * WA) * KS16) * G * 64), (short)0, WA * KS16 * G * 1024, 0x00020000);
     auto load_w = [&](int stage, uint4 (&dst)[C::WF]) {
         stage = stage < n_stages ? stage : stage - n_stages;
 #pragma unroll
-        for (int a = 0; a < WA; ++a) {
-            const uint4 *src = wfrag + (size_t)((ob0 + wo * WA + a) * KS16 + stage * KSS) * G * 64 + lane;
+        for (int a = 0; a < WA; ++a)
 #pragma unroll
-            for (int r = 0; r < KSS * G; ++r) dst[a * KSS * G + r] = src[r * 64];
-        }
+            for (int r = 0; r < KSS * G; ++r) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(w_rs, lane * 16 + r * 1024,
+                                                                      (a * KS16 + stage * KSS) * G * 1024, 0);
+                dst[a * KSS * G + r] = make_uint4(v.x, v.y, v.z, v.w);
+            }
     };
     auto dft_store = [&](const uint4 (&src)[C::ITEMS][C::XU4], uint4 *xb) {
 #pragma unroll
@@ -286,28 +307,37 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     uint4 xr[2][C::ITEMS][C::XU4];
     uint4 wr[2][C::WF];
     load_w(0, wr[0]);
-    load_x(0, 0, xr[0]);
-    load_x(0, 1, xr[1]);
+    {
+        const __amdgpu_buffer_rsrc_t rs0 = x_rsrc(0);
+        load_x(rs0, rs0, 0, xr[0]);
+        load_x(rs0, rs0, 1, xr[1]);
+    }
     dft_store(xr[0], lds);
     lds_barrier();
 
     f32x16 acc[WA][WB][G];
     // products of (K-step kk, token block b) pairs [lo, hi) of a stage, kk major
-    auto products = [&](auto lo, auto hi, const uint4 (&w_cur)[C::WF], const uint4 *planes) {
+    // first: the tile's first stage (its first K-step starts the accumulators)
+    auto products = [&](auto first, auto lo, auto hi, const uint4 (&w_cur)[C::WF], const uint4 (&w_neg)[C::WF],
+                        const uint4 *planes) {
 #pragma unroll
         for (int q = decltype(lo)::value; q < decltype(hi)::value; ++q) {
             const int kk = q / WB, b = q % WB;
-            uint4 xf[G], xn[G];
+            uint4 xf[G];
 #pragma unroll
             for (int p = 0; p < G; ++p) xf[p] = planes[(((wt * WB + b) * KSS + kk) * G + p) * 64 + lane];
 #pragma unroll
-            for (int p = 0; p < G; ++p) xn[p] = (p >= 3 && (p & 1)) ? neg_bf16x8(xf[p]) : xf[p];
-#pragma unroll
             for (int a = 0; a < WA; ++a) {
-                uint4 wf[G];
+                uint4 wf[G], wn[G];
 #pragma unroll
-                for (int p = 0; p < G; ++p) wf[p] = w_cur[(a * KSS + kk) * G + p];
-                spectral_mfma32<G>(wf, xf, xn, acc[a][b]);
+                for (int p = 0; p < G; ++p) {
+                    wf[p] = w_cur[(a * KSS + kk) * G + p];
+                    wn[p] = w_neg[(a * KSS + kk) * G + p];
+                }
+                if (decltype(first)::value && kk == 0)
+                    spectral_mfma32<G, true>(wf, wn, xf, acc[a][b]);
+                else
+                    spectral_mfma32<G, false>(wf, wn, xf, acc[a][b]);
             }
         }
     };
@@ -317,19 +347,25 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     // stores.
     // The next stage's products then wait for its weights only, with the raw x still in flight
     // (vector-memory operations complete in issue order).
-    auto step = [&](int k, int s, uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
+    auto step = [&](auto first, __amdgpu_buffer_rsrc_t xrs_c, __amdgpu_buffer_rsrc_t xrs_n, int s,
+                    uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
                     const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF], const uint4 *planes,
                     uint4 *planes_next, __amdgpu_buffer_rsrc_t rs_prev, bool has_prev) {
         constexpr int P = KSS * WB, H = P / 2;
         load_w(s + 1, w_next);
-        products(IC<0>{}, IC<H>{}, w_cur, planes);
+        // the Im weight fragments negated once per stage (each serves WB token blocks); only the
+        // slots the products read are used, the rest is dead code
+        uint4 w_neg[C::WF];
+#pragma unroll
+        for (int r = 0; r < C::WF; ++r) w_neg[r] = (r % G >= 3 && (r % G) % 2 == 1) ? neg_bf16x8(w_cur[r]) : w_cur[r];
+        products(first, IC<0>{}, IC<H>{}, w_cur, w_neg, planes);
         interleave_stage<H * G, H * WA * real_products(G), C::WF, 1>();
         __builtin_amdgcn_sched_barrier(0);
-        load_x(k, s + 2, x_free);
+        load_x(xrs_c, xrs_n, s + 2, x_free);
         uint4 sv[C::SPS];
 #pragma unroll
         for (int i = 0; i < C::SPS; ++i) sv[i] = read_staged(min(s * C::SPS + i, C::NSTORE - 1));
-        products(IC<H>{}, IC<P>{}, w_cur, planes);
+        products(first, IC<H>{}, IC<P>{}, w_cur, w_neg, planes);
         dft_store(x_next, planes_next);  // past the last position: unused planes, harmless
         interleave_stage<(P - H) * G + C::SPS, (P - H) * WA * real_products(G), C::ITEMS * C::XU4, C::VPM>();
         __builtin_amdgcn_sched_barrier(0);
@@ -353,17 +389,23 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
             uint32_t bc = bcol[a];
             asm volatile("" : "+v"(bc));
 #pragma unroll
-            for (int b = 0; b < WB; ++b) {
-                acc[a][b][0] = mfma32x32x16(make_uint4(bc, 0u, 0u, 0u), ones, f32x16{});
-#pragma unroll
-                for (int p = 1; p < G; ++p) acc[a][b][p] = f32x16{};
-            }
+            for (int b = 0; b < WB; ++b) acc[a][b][0] = mfma32x32x16(make_uint4(bc, 0u, 0u, 0u), ones, f32x16{});
         }
         const bool has_prev = k > 0 && vec_rows;
         const __amdgpu_buffer_rsrc_t rs_prev = tile_rsrc(k > 0 ? k - 1 : 0);
-        for (int s = 0; s < n_stages; s += 2) {  // n_stages is even (the channel padding sees to it)
-            step(k, s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
-            step(k, s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
+        const __amdgpu_buffer_rsrc_t xrs_c = x_rsrc(k), xrs_n = x_rsrc(k + 1);
+        // n_stages is even (the channel padding sees to it); for G >= 2 the first pair is peeled so
+        // the first products can start the accumulators of planes 1.. without clearing them (G = 1
+        // has only the bias plane)
+        int s0 = 0;
+        if constexpr (G >= 2) {
+            step(IC<1>{}, xrs_c, xrs_n, 0, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
+            step(IC<0>{}, xrs_c, xrs_n, 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
+            s0 = 2;
+        }
+        for (int s = s0; s < n_stages; s += 2) {
+            step(IC<0>{}, xrs_c, xrs_n, s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
+            step(IC<0>{}, xrs_c, xrs_n, s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
         }
         // stores of the previous tile that did not fit in this tile's stages
         if (has_prev)
