@@ -84,11 +84,12 @@ def test_workload_full_size_sampled(w, expanded, cuda_device):
 # large-channel kernel walks several token tiles at small N: this exercises the hand-over between
 # tiles (the load pipeline crossing tile boundaries, a tile's outputs stored during the next tile's
 # stages, the last tile's own flush) including a ragged last tile and rows that are not a whole
-# number of 16-byte pieces (C_out * G not a multiple of 8).
+# number of 16-byte pieces (C_out * G not a multiple of 8). C_in = 200 pads the channel stages: the
+# last stage's loads past C_in re-read real channels, which meet zero weight columns.
 @pytest.mark.parametrize("with_bias", [True, False], ids=["bias", "nobias"])
 @pytest.mark.parametrize("expanded", [False, True], ids=["spectral", "expanded"])
 @pytest.mark.parametrize("G,C_in,C_out", [(4, 128, 4096), (8, 64, 2048), (4, 128, 4095), (2, 128, 4096),
-                                          (1, 256, 4096)])
+                                          (1, 256, 4096), (8, 200, 1024), (4, 200, 2048)])
 def test_large_channel_multi_tile(G, C_in, C_out, expanded, with_bias, cuda_device):
     if expanded and G == 1:
         pytest.skip("G = 1 has no separate expanded form")
