@@ -317,28 +317,28 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
 
     f32x16 acc[WA][WB][G];
     // products of (K-step kk, token block b) pairs [lo, hi) of a stage, kk major
-    // first: the tile's first stage (its first K-step starts the accumulators)
-    auto products = [&](auto first, auto lo, auto hi, const uint4 (&w_cur)[C::WF], const uint4 (&w_neg)[C::WF],
-                        const uint4 *planes) {
+    // the x planes of (K-step kk, token block b) pair q = kk * WB + b of a stage
+    auto read_planes = [&](int q, const uint4 *planes, uint4 (&xf)[G]) {
+        const int kk = q / WB, b = q % WB;
 #pragma unroll
-        for (int q = decltype(lo)::value; q < decltype(hi)::value; ++q) {
-            const int kk = q / WB, b = q % WB;
-            uint4 xf[G];
+        for (int p = 0; p < G; ++p) xf[p] = planes[(((wt * WB + b) * KSS + kk) * G + p) * 64 + lane];
+    };
+    // the products of pair q; first: the tile's first stage (its first K-step starts the accumulators)
+    auto products = [&](auto first, int q, const uint4 (&xf)[G], const uint4 (&w_cur)[C::WF],
+                        const uint4 (&w_neg)[C::WF]) {
+        const int kk = q / WB, b = q % WB;
 #pragma unroll
-            for (int p = 0; p < G; ++p) xf[p] = planes[(((wt * WB + b) * KSS + kk) * G + p) * 64 + lane];
+        for (int a = 0; a < WA; ++a) {
+            uint4 wf[G], wn[G];
 #pragma unroll
-            for (int a = 0; a < WA; ++a) {
-                uint4 wf[G], wn[G];
-#pragma unroll
-                for (int p = 0; p < G; ++p) {
-                    wf[p] = w_cur[(a * KSS + kk) * G + p];
-                    wn[p] = w_neg[(a * KSS + kk) * G + p];
-                }
-                if (decltype(first)::value && kk == 0)
-                    spectral_mfma32<G, true>(wf, wn, xf, acc[a][b]);
-                else
-                    spectral_mfma32<G, false>(wf, wn, xf, acc[a][b]);
+            for (int p = 0; p < G; ++p) {
+                wf[p] = w_cur[(a * KSS + kk) * G + p];
+                wn[p] = w_neg[(a * KSS + kk) * G + p];
             }
+            if (decltype(first)::value && kk == 0)
+                spectral_mfma32<G, true>(wf, wn, xf, acc[a][b]);
+            else
+                spectral_mfma32<G, false>(wf, wn, xf, acc[a][b]);
         }
     };
     // One stage (tile k, stage s) in two scheduling regions, so the loads leave in a fixed order:
@@ -352,22 +352,37 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                     const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF], const uint4 *planes,
                     uint4 *planes_next, __amdgpu_buffer_rsrc_t rs_prev, bool has_prev) {
         constexpr int P = KSS * WB, H = P / 2;
+        // the second half's planes are read with the first half's when they fit in 4 registers of 16
+        // bytes, so its products do not wait for LDS after the first half's
+        constexpr bool PRE = (P - H) * G <= 4;
         load_w(s + 1, w_next);
         // the Im weight fragments negated once per stage (each serves WB token blocks); only the
         // slots the products read are used, the rest is dead code
         uint4 w_neg[C::WF];
 #pragma unroll
         for (int r = 0; r < C::WF; ++r) w_neg[r] = (r % G >= 3 && (r % G) % 2 == 1) ? neg_bf16x8(w_cur[r]) : w_cur[r];
-        products(first, IC<0>{}, IC<H>{}, w_cur, w_neg, planes);
-        interleave_stage<H * G, H * WA * real_products(G), C::WF, 1>();
+        uint4 xa[H][G], xb[P - H][G];
+#pragma unroll
+        for (int q = 0; q < H; ++q) read_planes(q, planes, xa[q]);
+        if constexpr (PRE)
+#pragma unroll
+            for (int q = H; q < P; ++q) read_planes(q, planes, xb[q - H]);
+#pragma unroll
+        for (int q = 0; q < H; ++q) products(first, q, xa[q], w_cur, w_neg);
+        interleave_stage<(PRE ? P : H) * G, H * WA * real_products(G), C::WF, 1>();
         __builtin_amdgcn_sched_barrier(0);
         load_x(xrs_c, xrs_n, s + 2, x_free);
         uint4 sv[C::SPS];
 #pragma unroll
         for (int i = 0; i < C::SPS; ++i) sv[i] = read_staged(min(s * C::SPS + i, C::NSTORE - 1));
-        products(first, IC<H>{}, IC<P>{}, w_cur, w_neg, planes);
+        if constexpr (!PRE)
+#pragma unroll
+            for (int q = H; q < P; ++q) read_planes(q, planes, xb[q - H]);
+#pragma unroll
+        for (int q = H; q < P; ++q) products(first, q, xb[q - H], w_cur, w_neg);
         dft_store(x_next, planes_next);  // past the last position: unused planes, harmless
-        interleave_stage<(P - H) * G + C::SPS, (P - H) * WA * real_products(G), C::ITEMS * C::XU4, C::VPM>();
+        interleave_stage<(PRE ? 0 : (P - H) * G) + C::SPS, (P - H) * WA * real_products(G), C::ITEMS * C::XU4,
+                         C::VPM>();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < C::SPS; ++i) {
