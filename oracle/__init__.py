@@ -15,10 +15,16 @@ Fourier Transform" (explainer page, gist.science/es/paper/2607.21271):
 * ``expand`` -- the unrolled matrix E itself (same section).
 * ``dft_weights`` -- section "Enfoque Algorítmico": the DFT of W along the group axis, kept for the
   non-redundant half k = 0..G/2 (conjugate symmetry of a real signal's spectrum).
+* ``backward_data``, ``backward_weights`` -- the layer's gradients (section "Implementación": the
+  operator has forward and backward kernels), by the chain rule through the unrolled product:
+  dx = E^T dy; dE = sum over tokens of dy x^T, folded back onto W along the circulant diagonals
+  (dW[o, i, d] = sum_h dE[o*G+h, i*G+(h-d) mod G]); db[o] = sum over tokens and h of dy.
 
-All three are pinned in ``tests/test_oracle.py`` against things other than themselves (an
-independent Kronecker construction of the block-circulant matrix, numpy's FFT convolution theorem,
-closed forms for delta / constant / alternating inputs, equivariance, the G=1 plain linear layer).
+All are pinned in ``tests/test_oracle.py`` against things other than themselves (an independent
+Kronecker construction of the block-circulant matrix, numpy's FFT convolution theorem, closed forms
+for delta / constant / alternating inputs, equivariance, the G=1 plain linear layer; for the
+gradients: the adjoint identities <dy, y(x)> = <dx, x> and <dy, y(W)> = <dW, W> against the forward,
+central finite differences of a scalar loss, and the G=1 case where dW is the plain dy^T x).
 """
 from __future__ import annotations
 
@@ -63,6 +69,10 @@ def _load():
     lib.eqlin_oracle_expand.restype = ctypes.c_int
     lib.eqlin_oracle_dft_weights.argtypes = [dp, i64, i64, i64, dp, dp]
     lib.eqlin_oracle_dft_weights.restype = ctypes.c_int
+    lib.eqlin_oracle_backward_data.argtypes = [dp, dp, dp, i64, i64, i64, i64, ctypes.c_int]
+    lib.eqlin_oracle_backward_data.restype = ctypes.c_int
+    lib.eqlin_oracle_backward_weights.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int]
+    lib.eqlin_oracle_backward_weights.restype = ctypes.c_int
     lib.eqlin_oracle_max_threads.argtypes = []
     lib.eqlin_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -136,3 +146,42 @@ def dft_weights(W) -> np.ndarray:
     if rc != 0:
         raise RuntimeError(f"eqlin_oracle_dft_weights failed with code {rc}")
     return re + 1j * im
+
+
+def backward_data(dy, W, threads: int = 0) -> np.ndarray:
+    """dx[n, i, g] = sum_{o, h} W[o, i, (h-g) mod G] * dy[n, o, h] (the transpose of the unrolled
+    product), in fp64. dy: [N, C_out, G]; W: [C_out, C_in, G]."""
+    lib = _load()
+    W = _f64(W)
+    dy = _f64(dy)
+    C_out, C_in, G = W.shape
+    if dy.ndim != 3 or dy.shape[1:] != (C_out, G):
+        raise ValueError(f"dy shape {dy.shape} does not match W shape {W.shape}")
+    N = dy.shape[0]
+    dx = np.empty((N, C_in, G), dtype=np.float64)
+    rc = lib.eqlin_oracle_backward_data(_ptr(dy) if N else None, _ptr(W), _ptr(dx) if N else None,
+                                        N, C_out, C_in, G, int(threads))
+    if rc != 0:
+        raise RuntimeError(f"eqlin_oracle_backward_data failed with code {rc}")
+    return dx
+
+
+def backward_weights(x, dy, threads: int = 0):
+    """(dW, db): dW[o, i, d] = sum_n sum_h dy[n, o, h] * x[n, i, (h-d) mod G] (through the unrolled
+    matrix: dE = dy^T x folded along the circulant diagonals), db[o] = sum_{n, h} dy[n, o, h]; fp64.
+    x: [N, C_in, G]; dy: [N, C_out, G]. dW[o, i, :] depends on x[:, i, :] and dy[:, o, :] only, so a
+    channel subset of dW is this function of the matching channel slices."""
+    lib = _load()
+    x = _f64(x)
+    dy = _f64(dy)
+    if x.ndim != 3 or dy.ndim != 3 or x.shape[0] != dy.shape[0] or x.shape[2] != dy.shape[2]:
+        raise ValueError(f"x shape {x.shape} and dy shape {dy.shape} do not match")
+    N, C_in, G = x.shape
+    C_out = dy.shape[1]
+    dW = np.empty((C_out, C_in, G), dtype=np.float64)
+    db = np.empty((C_out,), dtype=np.float64)
+    rc = lib.eqlin_oracle_backward_weights(_ptr(x) if N else None, _ptr(dy) if N else None, _ptr(dW),
+                                           _ptr(db), N, C_out, C_in, G, int(threads))
+    if rc != 0:
+        raise RuntimeError(f"eqlin_oracle_backward_weights failed with code {rc}")
+    return dW, db

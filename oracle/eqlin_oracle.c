@@ -23,8 +23,17 @@
  * the group axis, kept to check the library's spectral weights: section "Enfoque Algorítmico"
  * (transform to the frequency domain; only the non-redundant half of a real signal's spectrum).
  *
+ * The gradients of the same layer (the pages' operator has a backward pass: section
+ * "Implementación", forward and backward kernels; "Resultados Experimentales", backward speedups)
+ * follow from the unrolled product by the chain rule and nothing else: with y = E x + b,
+ *   dx = E^T dy,
+ *   dE = dy^T x summed over tokens, and since E[o*G+h][i*G+g] = W[o][i][(h-g) mod G] each W entry
+ *   collects the dE entries it was copied to: dW[o][i][d] = sum over h of dE[o*G+h][i*G+(h-d) mod G],
+ *   db[o] = sum over tokens and h of dy[n][o*G+h].
+ *
  * Layouts (all row-major, fp64): x[N][C_in][G], W[C_out][C_in][G], b[C_out] (or NULL),
- * y[N][C_out][G], E[C_out*G][C_in*G]; spectral re/im[C_out][C_in][G/2+1].
+ * y[N][C_out][G], E[C_out*G][C_in*G]; spectral re/im[C_out][C_in][G/2+1]; dy like y, dx like x,
+ * dW like W, db like b.
  * Return value: 0 on success, -1 on a bad argument, -2 when memory runs out.
  */
 #include <math.h>
@@ -107,4 +116,78 @@ int eqlin_oracle_dft_weights(const double *W, int64_t C_out, int64_t C_in, int64
                 im[(o * C_in + i) * K + k] = si;
             }
     return 0;
+}
+
+/* dx[n][c] = sum_r E[r][c] * dy[n][r], r = o*G+h, c = i*G+g, r ascending (the transpose of the
+ * unrolled product; the bias does not depend on x). */
+int eqlin_oracle_backward_data(const double *dy, const double *W, double *dx, int64_t N, int64_t C_out,
+                               int64_t C_in, int64_t G, int nthreads) {
+    if (N < 0 || C_out <= 0 || C_in <= 0 || G <= 0 || !W) return -1;
+    if (N == 0) return 0;
+    if (!dy || !dx) return -1;
+    const int64_t rows = C_out * G, cols = C_in * G;
+    double *E = (double *)malloc((size_t)(rows * cols) * sizeof(double));
+    if (!E) return -2;
+    eqlin_oracle_expand(W, C_out, C_in, G, E);
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const double *dyn = dy + n * rows;
+        double *dxn = dx + n * cols;
+        for (int64_t c = 0; c < cols; ++c) {
+            double acc = 0.0;
+            for (int64_t r = 0; r < rows; ++r) acc += E[r * cols + c] * dyn[r];
+            dxn[c] = acc;
+        }
+    }
+    free(E);
+    return 0;
+}
+
+/* dE[r][c] = sum_n dy[n][r] * x[n][c] (n ascending); dW[o][i][d] = sum_h dE[o*G+h][i*G+(h-d) mod G]
+ * (h ascending); db[o] = sum_n sum_h dy[n][o*G+h] (n, then h ascending). db may be NULL. */
+int eqlin_oracle_backward_weights(const double *x, const double *dy, double *dW, double *db, int64_t N,
+                                  int64_t C_out, int64_t C_in, int64_t G, int nthreads) {
+    if (N < 0 || C_out <= 0 || C_in <= 0 || G <= 0 || !dW) return -1;
+    if (N > 0 && (!x || !dy)) return -1;
+    const int64_t rows = C_out * G, cols = C_in * G;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static) reduction(| : failed)
+    for (int64_t o = 0; o < C_out; ++o) {
+        /* the G rows of dE that belong to output channel o */
+        double *dE = (double *)malloc((size_t)(G * cols) * sizeof(double));
+        if (!dE) {
+            failed = 1;
+            continue;
+        }
+        for (int64_t k = 0; k < G * cols; ++k) dE[k] = 0.0;
+        double bsum = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double *xn = x + n * cols;
+            for (int64_t h = 0; h < G; ++h) {
+                const double d = dy[n * rows + o * G + h];
+                bsum += d;
+                double *row = dE + h * cols;
+                for (int64_t c = 0; c < cols; ++c) row[c] += d * xn[c];
+            }
+        }
+        for (int64_t i = 0; i < C_in; ++i)
+            for (int64_t d = 0; d < G; ++d) {
+                double acc = 0.0;
+                for (int64_t h = 0; h < G; ++h) acc += dE[h * cols + i * G + ((h - d) % G + G) % G];
+                dW[(o * C_in + i) * G + d] = acc;
+            }
+        if (db) db[o] = bsum;
+        free(dE);
+    }
+    return failed ? -2 : 0;
 }

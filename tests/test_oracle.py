@@ -185,3 +185,94 @@ def test_empty_batch():
 def test_bad_shapes_raise():
     with pytest.raises(ValueError):
         oracle.forward(np.zeros((2, 3, 4)), np.zeros((3, 2, 4)))
+
+
+# ---- the gradients (section "Implementación": the operator has forward and backward kernels) ----
+
+# B-1: adjoint identities against the forward. The layer is bilinear in (x, W) plus b, so for any dy
+# <dy, y(x, W, 0)> = <dx, x> = <dW, W> and <dy, y(0, 0, b)> = <db, b>. A transposed W, a wrong
+# fold direction (h+d instead of h-d) or a dropped group sample breaks one of them.
+@pytest.mark.parametrize("G", GROUPS)
+def test_backward_adjoint_identities(G):
+    N, C_in, C_out = 9, 5, 6
+    x, W, b, dy = _rand((N, C_in, G), 40), _rand((C_out, C_in, G), 41), _rand((C_out,), 42), _rand((N, C_out, G), 43)
+    lhs = np.sum(dy * oracle.forward(x, W))
+    dx = oracle.backward_data(dy, W)
+    dW, db = oracle.backward_weights(x, dy)
+    assert abs(np.sum(dx * x) - lhs) <= 1e-12 * max(1.0, abs(lhs))
+    assert abs(np.sum(dW * W) - lhs) <= 1e-12 * max(1.0, abs(lhs))
+    lb = np.sum(dy * oracle.forward(x, np.zeros_like(W), b))
+    assert abs(np.sum(db * b) - lb) <= 1e-12 * max(1.0, abs(lb))
+
+
+# B-2: central finite differences of L = <dy, y(x, W, b)>. L is linear in each argument, so the
+# central difference is exact up to rounding; checked entry by entry on a sample.
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_backward_finite_differences(G):
+    N, C_in, C_out = 4, 3, 5
+    x, W, b, dy = _rand((N, C_in, G), 44), _rand((C_out, C_in, G), 45), _rand((C_out,), 46), _rand((N, C_out, G), 47)
+    L = lambda x_, W_, b_: float(np.sum(dy * oracle.forward(x_, W_, b_)))
+    dx = oracle.backward_data(dy, W)
+    dW, db = oracle.backward_weights(x, dy)
+    rng = np.random.default_rng(48)
+    eps = 0.5
+    for _ in range(6):
+        n, i, g = rng.integers(N), rng.integers(C_in), rng.integers(G)
+        e = np.zeros_like(x)
+        e[n, i, g] = eps
+        assert abs((L(x + e, W, b) - L(x - e, W, b)) / (2 * eps) - dx[n, i, g]) <= 1e-10
+        o, i, d = rng.integers(C_out), rng.integers(C_in), rng.integers(G)
+        e = np.zeros_like(W)
+        e[o, i, d] = eps
+        assert abs((L(x, W + e, b) - L(x, W - e, b)) / (2 * eps) - dW[o, i, d]) <= 1e-10
+        o = rng.integers(C_out)
+        e = np.zeros_like(b)
+        e[o] = eps
+        assert abs((L(x, W, b + e) - L(x, W, b - e)) / (2 * eps) - db[o]) <= 1e-10
+
+
+# B-3: G = 1 is a plain linear layer: dx = dy W, dW = dy^T x, db = column sums of dy.
+def test_backward_g1_is_plain_linear():
+    x, W, dy = _rand((8, 5, 1), 49), _rand((4, 5, 1), 50), _rand((8, 4, 1), 51)
+    np.testing.assert_allclose(oracle.backward_data(dy, W)[:, :, 0], dy[:, :, 0] @ W[:, :, 0], atol=1e-12)
+    dW, db = oracle.backward_weights(x, dy)
+    np.testing.assert_allclose(dW[:, :, 0], dy[:, :, 0].T @ x[:, :, 0], atol=1e-12)
+    np.testing.assert_allclose(db, dy[:, :, 0].sum(axis=0), atol=1e-12)
+
+
+# B-4: dx through the independently built block-circulant matrix: dx_flat = dy_flat E.
+@pytest.mark.parametrize("G", GROUPS)
+def test_backward_data_is_transpose_product(G):
+    W, dy = _rand((4, 3, G), 52), _rand((6, 4, G), 53)
+    ref = (dy.reshape(6, -1) @ _kron_block_circulant(W)).reshape(6, 3, G)
+    assert _rel(oracle.backward_data(dy, W), ref) <= 1e-13
+
+
+# B-5: dW by the correlation theorem with numpy's FFT along the group axis: the DFT of
+# c[d] = sum_h dy[h] x[h-d] is DY_k conj(X_k); summed over tokens, then inverted.
+@pytest.mark.parametrize("G", GROUPS)
+def test_backward_weights_correlation_theorem(G):
+    x, dy = _rand((7, 3, G), 54), _rand((7, 5, G), 55)
+    C = np.einsum("nok,nik->oik", np.fft.fft(dy, axis=2), np.conj(np.fft.fft(x, axis=2)))
+    ref = np.fft.ifft(C, axis=2).real
+    dW, db = oracle.backward_weights(x, dy)
+    assert _rel(dW, ref) <= 1e-12
+    np.testing.assert_allclose(db, dy.sum(axis=(0, 2)), atol=1e-12)
+
+
+# B-6: a channel subset of dW is the same function of the matching channel slices (the parity tests
+# at full token counts rely on this to check sampled channels).
+def test_backward_weights_channel_subset():
+    x, dy = _rand((6, 7, 4), 56), _rand((6, 5, 4), 57)
+    dW, db = oracle.backward_weights(x, dy)
+    osub, isub = [0, 3, 4], [1, 2, 6]
+    dWs, dbs = oracle.backward_weights(x[:, isub], dy[:, osub])
+    np.testing.assert_allclose(dWs, dW[np.ix_(osub, isub)], rtol=0, atol=0)
+    np.testing.assert_allclose(dbs, db[osub], rtol=0, atol=0)
+
+
+def test_backward_empty_batch():
+    W = _rand((3, 2, 4), 58)
+    assert oracle.backward_data(np.zeros((0, 3, 4)), W).shape == (0, 2, 4)
+    dW, db = oracle.backward_weights(np.zeros((0, 2, 4)), np.zeros((0, 3, 4)))
+    assert np.all(dW == 0) and np.all(db == 0)
