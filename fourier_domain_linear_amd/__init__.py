@@ -8,6 +8,8 @@ is missing, every call raises.
     h = eq.prepare_weights(W)                 # W: cuda tensor [C_out, C_in, G], bf16 or fp32
     y = eq.forward(h, x, b)                   # x: [N, C_in, G]; b: [C_out] or None
     y2 = eq.forward_expanded(h, x, b)         # needs prepare_weights(W, expanded=True)
+    dx = eq.backward_data(h, dy)              # needs prepare_weights(W, backward=True)
+    dW, db = eq.backward_weights(h, x, dy)    # float32 gradients of W and b
 
 Method: "Flash EQ-Linear: Accelerating Equivariant Linear Layers via Group-wise Discrete Fourier
 Transform" (explainer page, gist.science/es/paper/2607.21271).
@@ -30,10 +32,12 @@ EQLIN_ERR_HIP = 4
 EQLIN_F32 = 0
 EQLIN_BF16 = 1
 EQLIN_PREPARE_EXPANDED = 1
+EQLIN_PREPARE_BACKWARD = 2
 
 # Every symbol include/eqlin.h declares.
 EXPORTED = (
-    "eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_destroy",
+    "eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_backward_data",
+    "eqlin_backward_weights_workspace", "eqlin_backward_weights", "eqlin_destroy",
     "eqlin_export_spectral_weights", "eqlin_export_expanded_weight", "eqlin_describe",
     "eqlin_status_string", "eqlin_last_error", "eqlin_version",
 )
@@ -61,6 +65,10 @@ def load_library() -> ctypes.CDLL:
     lib.eqlin_prepare_weights.argtypes = [vp, i32, i32, i32, i32, u32, vp, ctypes.POINTER(vp)]
     lib.eqlin_forward.argtypes = [vp, vp, vp, vp, i64, vp]
     lib.eqlin_forward_expanded.argtypes = [vp, vp, vp, vp, i64, vp]
+    lib.eqlin_backward_data.argtypes = [vp, vp, vp, i64, vp]
+    lib.eqlin_backward_weights_workspace.argtypes = [vp, i64]
+    lib.eqlin_backward_weights_workspace.restype = ctypes.c_size_t
+    lib.eqlin_backward_weights.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
     lib.eqlin_destroy.argtypes = [vp]
     lib.eqlin_export_spectral_weights.argtypes = [vp, vp, vp]
     lib.eqlin_export_expanded_weight.argtypes = [vp, vp, vp]
@@ -109,10 +117,11 @@ def _need_cuda(t: torch.Tensor, name: str):
 class Handle:
     """Owns an eqlin_handle_t; destroyed with the object (or explicitly via destroy())."""
 
-    def __init__(self, ptr: int, C_out: int, C_in: int, G: int, dtype: torch.dtype, device, expanded: bool):
+    def __init__(self, ptr: int, C_out: int, C_in: int, G: int, dtype: torch.dtype, device, expanded: bool,
+                 backward: bool = False):
         self.ptr = ptr
         self.C_out, self.C_in, self.G = C_out, C_in, G
-        self.dtype, self.device, self.expanded = dtype, device, expanded
+        self.dtype, self.device, self.expanded, self.backward = dtype, device, expanded, backward
 
     def destroy(self):
         if self.ptr:
@@ -129,20 +138,21 @@ class Handle:
         return describe(self)
 
 
-def prepare_weights(W: torch.Tensor, expanded: bool = False) -> Handle:
-    """eqlin_prepare_weights: W [C_out, C_in, G] (cuda, bf16 or fp32) -> Handle."""
+def prepare_weights(W: torch.Tensor, expanded: bool = False, backward: bool = False) -> Handle:
+    """eqlin_prepare_weights: W [C_out, C_in, G] (cuda, bf16 or fp32) -> Handle. ``expanded`` builds the
+    unrolled comparator, ``backward`` the weights of backward_data."""
     lib = load_library()
     _need_cuda(W, "W")
     if W.dim() != 3:
         raise ValueError(f"W must be [C_out, C_in, G], got {tuple(W.shape)}")
     C_out, C_in, G = W.shape
     out = ctypes.c_void_p()
-    flags = EQLIN_PREPARE_EXPANDED if expanded else 0
+    flags = (EQLIN_PREPARE_EXPANDED if expanded else 0) | (EQLIN_PREPARE_BACKWARD if backward else 0)
     with torch.cuda.device(W.device):
         st = lib.eqlin_prepare_weights(ctypes.c_void_p(W.data_ptr()), C_out, C_in, G, _dtype_code(W.dtype),
                                        flags, _stream(W), ctypes.byref(out))
     _check(st, "eqlin_prepare_weights")
-    return Handle(out.value, C_out, C_in, G, W.dtype, W.device, expanded)
+    return Handle(out.value, C_out, C_in, G, W.dtype, W.device, expanded, backward)
 
 
 def _forward(fn, what: str, h: Handle, x: torch.Tensor, b: torch.Tensor | None, y: torch.Tensor | None):
@@ -181,6 +191,59 @@ def forward_expanded(h: Handle, x: torch.Tensor, b: torch.Tensor | None = None, 
     if not h.expanded:
         raise ValueError("handle was prepared without expanded=True")
     return _forward(load_library().eqlin_forward_expanded, "eqlin_forward_expanded", h, x, b, y)
+
+
+def backward_data(h: Handle, dy: torch.Tensor, dx: torch.Tensor | None = None) -> torch.Tensor:
+    """eqlin_backward_data: dx[n, i, g] = sum_{o, h} W[o, i, (h-g) mod G] dy[n, o, h]."""
+    if not h.backward:
+        raise ValueError("handle was prepared without backward=True")
+    _need_cuda(dy, "dy")
+    if dy.dtype != h.dtype or dy.dim() != 3 or dy.shape[1] != h.C_out or dy.shape[2] != h.G:
+        raise ValueError(f"dy must be [N, {h.C_out}, {h.G}] of {h.dtype}, got {tuple(dy.shape)} {dy.dtype}")
+    N = dy.shape[0]
+    if dx is None:
+        dx = torch.empty((N, h.C_in, h.G), dtype=dy.dtype, device=dy.device)
+    else:
+        _need_cuda(dx, "dx")
+        if dx.dtype != h.dtype or tuple(dx.shape) != (N, h.C_in, h.G):
+            raise ValueError(f"dx must be [{N}, {h.C_in}, {h.G}] of {h.dtype}")
+    with torch.cuda.device(dy.device):
+        st = load_library().eqlin_backward_data(ctypes.c_void_p(h.ptr), ctypes.c_void_p(dy.data_ptr()),
+                                                ctypes.c_void_p(dx.data_ptr()), N, _stream(dy))
+    _check(st, "eqlin_backward_data")
+    return dx
+
+
+def backward_weights_workspace(h: Handle, N: int) -> int:
+    """Bytes of device scratch eqlin_backward_weights needs for N tokens."""
+    return int(load_library().eqlin_backward_weights_workspace(ctypes.c_void_p(h.ptr), int(N)))
+
+
+def backward_weights(h: Handle, x: torch.Tensor, dy: torch.Tensor, with_bias: bool = True,
+                     workspace: torch.Tensor | None = None):
+    """eqlin_backward_weights -> (dW float32 [C_out, C_in, G], db float32 [C_out] or None):
+    dW[o, i, d] = sum_{n, h} dy[n, o, h] x[n, i, (h-d) mod G], db[o] = sum_{n, h} dy[n, o, h]."""
+    _need_cuda(x, "x")
+    _need_cuda(dy, "dy")
+    if x.dtype != h.dtype or dy.dtype != h.dtype:
+        raise TypeError(f"x and dy must be {h.dtype}")
+    if x.dim() != 3 or x.shape[1:] != (h.C_in, h.G) or dy.dim() != 3 or dy.shape[1:] != (h.C_out, h.G) \
+            or x.shape[0] != dy.shape[0]:
+        raise ValueError(f"x must be [N, {h.C_in}, {h.G}] and dy [N, {h.C_out}, {h.G}]")
+    N = x.shape[0]
+    dW = torch.empty((h.C_out, h.C_in, h.G), dtype=torch.float32, device=x.device)
+    db = torch.empty((h.C_out,), dtype=torch.float32, device=x.device) if with_bias else None
+    need = backward_weights_workspace(h, N)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    wsp = ctypes.c_void_p(workspace.data_ptr()) if need else None
+    with torch.cuda.device(x.device):
+        st = load_library().eqlin_backward_weights(
+            ctypes.c_void_p(h.ptr), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(dy.data_ptr()),
+            ctypes.c_void_p(dW.data_ptr()), ctypes.c_void_p(db.data_ptr()) if db is not None else None, N, wsp,
+            need, _stream(x))
+    _check(st, "eqlin_backward_weights")
+    return dW, db
 
 
 def export_spectral_weights(h: Handle) -> torch.Tensor:

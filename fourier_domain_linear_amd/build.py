@@ -28,7 +28,7 @@ CXXFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
-SOURCES = ["eqlin_api.cpp", "prepare.hip", "fwd_bf16.hip", "fwd_big.hip", "fwd_f32.hip"]
+SOURCES = ["eqlin_api.cpp", "prepare.hip", "fwd_bf16.hip", "fwd_big.hip", "fwd_f32.hip", "bwd.hip"]
 
 
 def _compile(src: str) -> str:

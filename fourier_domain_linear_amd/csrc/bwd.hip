@@ -1,0 +1,453 @@
+// bwd.hip -- the gradients of the EQ-Linear layer: dW (and db) from x and dy.
+//
+// Method: "Flash EQ-Linear: Accelerating Equivariant Linear Layers via Group-wise Discrete Fourier
+// Transform" (gist.science explainer), "Implementación" (the operator has forward and backward
+// kernels) and "Enfoque Algorítmico" (group DFT -> independent per-frequency channel products). The
+// data gradient dx is a forward pass of the layer whose weight is W transposed over (o, i) and
+// reversed along the group axis (built at prepare; eqlin_api.cpp). This file computes the weight
+// gradient
+//
+//     dW[o, i, d] = sum_n sum_h dy[n, o, h] * x[n, i, (h - d) mod G],   db[o] = sum_{n, h} dy[n, o, h],
+//
+// a circular cross-correlation along the group axis summed over tokens. With the same DFT as the
+// forward (X_k = sum_g x_g e^{-2 pi i g k / G}) it becomes one channel product per frequency,
+//
+//     C_k[o, i] = sum_n DY_k[n, o] * conj(X_k[n, i]),   k = 0..G/2,
+//
+// and dW[o, i, :] is the inverse DFT of C (Hermitian symmetry fills k > G/2): the forward's inverse
+// transform with its 1/G and 2/G plane scalings. In real planes, a complex frequency is four real
+// products: Re C = DYr Xr + DYi Xi, Im C = DYi Xr - DYr Xi.
+//
+// bf16, G = 4 or 8 (matrix cores), three passes over a caller-provided workspace:
+//   1. k_bw_planes: x and dy -> DFT planes (fp32, rounded once to bf16) in 32x32x16 fragment order
+//      with tokens along K: chunk (channel block cb of 32, token step kt of 16, plane p) is 1 KB, lane
+//      l holds channel cb*32 + l%32, tokens kt*16 + 8*(l/32) .. +7. Each token's transform is done
+//      once (in the product pass every x tile meets many dy tiles). Tokens past N are zeros. The dy
+//      pass also sums plane 0 (= sum over h, in fp32) over its 64 tokens: db partials.
+//   2. k_bw_gemm: C_k over a split of the tokens for one output tile (128 outputs x 32*WB inputs),
+//      written as fp32 partial planes. Two waves per SIMD split the planes (role 0: planes 0..G/2-1,
+//      role 1: the rest) and share the tile; the dy fragments go straight to registers (each wave its
+//      own), the x fragments through LDS (shared by all waves).
+//   3. k_bw_reduce: sum of the splits, inverse DFT (scaled) -> dW fp32; db from its partials.
+// Other cases (fp32, G = 1 or 2): k_bw_direct, the definition above in fp32 with LDS token tiles.
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "eqlin_internal.h"
+
+namespace eqlin {
+
+// ------------------------------------------------------------------------------------------------
+// Pass 1: group DFT of a [N][C][G] bf16 tensor into K-major fragments.
+constexpr int kBwTok = 64;         // tokens per pass-1 workgroup (4 token steps of 16)
+constexpr int kBwRow = kBwTok + 8;  // LDS row of one (plane, channel): padded against bank conflicts
+
+template <int G>
+__global__ __launch_bounds__(256) void k_bw_planes(const uint16_t *__restrict__ src, int64_t N, int C, int KT,
+                                                   uint4 *__restrict__ frag, float *__restrict__ db_part) {
+    __shared__ __attribute__((aligned(16))) uint16_t sp[G][32][kBwRow];
+    __shared__ float red[32][kBwTok + 1];
+    const int t = threadIdx.x;
+    const int tl = t >> 2, cg = t & 3;            // token within the tile, 8-channel group
+    const int64_t n = (int64_t)blockIdx.x * kBwTok + tl;
+    const int cb = blockIdx.y, c0 = cb * 32 + cg * 8;
+    // 8 channels x G samples of one token (C % 8 == 0: a group is wholly inside or outside)
+    uint4 r[G];
+    const bool live = n < N && c0 < C;
+    const uint4 *p = reinterpret_cast<const uint4 *>(src + (live ? (n * C + c0) * G : 0));
+#pragma unroll
+    for (int q = 0; q < G; ++q) r[q] = live ? p[q] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float v[G], P[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] = bf16_at(r[(j * G + g) >> 3], (j * G + g) & 7);
+        forward_planes<G>(v, P);
+#pragma unroll
+        for (int pl = 0; pl < G; ++pl) sp[pl][cg * 8 + j][tl] = pack_bf16(P[pl]);
+        red[cg * 8 + j][tl] = P[0];  // plane 0 is the sum over the group samples
+    }
+    __syncthreads();
+    if (db_part && t < 32) {
+        float s = 0.f;
+        for (int k = 0; k < kBwTok; ++k) s += red[t][k];
+        db_part[(int64_t)blockIdx.x * gridDim.y * 32 + cb * 32 + t] = s;
+    }
+    // 4 token steps x G planes, one 1 KB chunk each; a thread writes one 16-byte piece per round
+#pragma unroll
+    for (int rd = 0; rd < G; ++rd) {
+        const int q = rd * 4 + (t >> 6), lane = t & 63;
+        const int ktl = q & 3, pl = q >> 2;
+        const int c = lane & 31, tok = ktl * 16 + 8 * (lane >> 5);
+        const uint4 v = *reinterpret_cast<const uint4 *>(&sp[pl][c][tok]);
+        const int kt = blockIdx.x * (kBwTok / 16) + ktl;
+        frag[((int64_t)(cb * KT + kt) * G + pl) * 64 + lane] = v;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Pass 2: per-frequency products over a token split.
+template <int V>
+struct IC2 {
+    static constexpr int value = V;
+};
+
+template <int G>
+struct BwCfg {
+    static constexpr int NW = 8, NT = NW * 64;
+    static constexpr int HP = G / 2;              // planes per role
+    static constexpr int WB = G == 8 ? 2 : 4;     // 32-input blocks per wave (accumulators: WB * HP * 16)
+    static constexpr int BO = 128, BI = 32 * WB;  // output tile: 4 o-blocks (one per SIMD) x WB i-blocks
+    static constexpr int XCH = WB * G;            // x chunks per token step (1 KB each)
+    static constexpr int XU = XCH * 64 / NT;      // 16-byte pieces per thread per token step
+    static constexpr int LDS_U4 = 2 * XCH * 64;
+    static_assert(XU * NT == XCH * 64, "x chunks split evenly over the threads");
+};
+
+// LDS-only workgroup barrier: outstanding global loads stay in flight across it.
+__device__ __forceinline__ void bw_lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <int G>
+__global__ __launch_bounds__(512) void k_bw_gemm(const uint4 *__restrict__ xf, const uint4 *__restrict__ dyf,
+                                                 float *__restrict__ part, int KT, int tiles_i, int splits,
+                                                 int C_in_pad, int C_out_pad) {
+    using C = BwCfg<G>;
+    constexpr int HP = C::HP, WB = C::WB;
+    __shared__ uint4 lds[C::LDS_U4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wo = wave_u & 3, role = wave_u >> 2;
+    const int split = blockIdx.x % splits, tile = blockIdx.x / splits;
+    const int ti = tile % tiles_i, to = tile / tiles_i;
+    const int ob = to * 4 + wo;  // this wave's 32-output block
+    const int ib0 = ti * WB;     // the tile's first 32-input block
+    const int kt0 = (int)((int64_t)KT * split / splits), kt1 = (int)((int64_t)KT * (split + 1) / splits);
+    const int nk = kt1 - kt0;
+    const int nst = (nk + 1) & ~1;  // even: the loop runs stages in pairs (the extra one reads zeros)
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    // a position past the split's range reads zeros: its offset lies outside every resource's range
+    constexpr int kDead = 0x7fffffff;
+
+    // dy fragments of this wave: (ob, kt, plane role * HP + r), straight to registers
+    const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(dyf + ((int64_t)ob * KT + kt0) * G * 64 + role * HP * 64), (short)0,
+        nk * G * 1024 - role * HP * 1024, 0x00020000);
+    auto load_a = [&](int s, uint4 (&dst)[HP]) {
+        const bool live = s < nk;
+#pragma unroll
+        for (int r = 0; r < HP; ++r) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(a_rs, live ? lane * 16 + r * 1024 : kDead,
+                                                                  live ? s * G * 1024 : 0, 0);
+            dst[r] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
+    // x fragments of the tile (WB blocks x G planes per token step): the thread's XU pieces, which
+    // belong to block e / (G * 64); one resource per piece slot
+    __amdgpu_buffer_rsrc_t b_rs[C::XU];
+#pragma unroll
+    for (int u = 0; u < C::XU; ++u) {
+        const int blk = (tid + u * C::NT) / (G * 64);
+        b_rs[u] = __builtin_amdgcn_make_buffer_rsrc((void *)(xf + ((int64_t)(ib0 + blk) * KT + kt0) * G * 64),
+                                                    (short)0, nk * G * 1024, 0x00020000);
+    }
+    auto load_b = [&](int s, uint4 (&dst)[C::XU]) {
+        const bool live = s < nk;
+#pragma unroll
+        for (int u = 0; u < C::XU; ++u) {
+            const int rem = (tid + u * C::NT) % (G * 64);  // (plane, lane) within the block
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b_rs[u], live ? rem * 16 : kDead,
+                                                                  live ? s * G * 1024 : 0, 0);
+            dst[u] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
+    auto store_b = [&](const uint4 (&src)[C::XU], uint4 *buf) {
+#pragma unroll
+        for (int u = 0; u < C::XU; ++u) buf[tid + u * C::NT] = src[u];  // [block][plane][lane]
+    };
+
+    // the whole loop once per role (wave-uniform), so the products are branch-free; both roles run
+    // the same barriers
+    auto run = [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        f32x16 acc[WB][HP];
+#pragma unroll
+        for (int b = 0; b < WB; ++b)
+#pragma unroll
+            for (int q = 0; q < HP; ++q) acc[b][q] = f32x16{};
+        // one token step: Re C += Ar Br + Ai Bi, Im C += Ai Br + (-Ar) Bi; role 0's planes 0 and 1
+        // are the real frequencies 0 and G/2
+        auto products = [&](const uint4 (&a)[HP], const uint4 *buf) {
+            uint4 an[HP];
+#pragma unroll
+            for (int r = 0; r < HP; ++r) an[r] = neg_bf16x8(a[r]);
+#pragma unroll
+            for (int b = 0; b < WB; ++b) {
+                uint4 bf[HP];
+#pragma unroll
+                for (int r = 0; r < HP; ++r) bf[r] = buf[(b * G + R * HP + r) * 64 + lane];
+#pragma unroll
+                for (int c = 0; c < HP; c += 2) {
+                    if constexpr (R == 0) {
+                        if (c == 0) {
+                            acc[b][0] = mfma32x32x16(a[0], bf[0], acc[b][0]);
+                            acc[b][1] = mfma32x32x16(a[1], bf[1], acc[b][1]);
+                            continue;
+                        }
+                    }
+                    acc[b][c] = mfma32x32x16(a[c], bf[c], acc[b][c]);
+                    acc[b][c] = mfma32x32x16(a[c + 1], bf[c + 1], acc[b][c]);
+                    acc[b][c + 1] = mfma32x32x16(a[c + 1], bf[c], acc[b][c + 1]);
+                    acc[b][c + 1] = mfma32x32x16(an[c], bf[c + 1], acc[b][c + 1]);
+                }
+            }
+        };
+
+        uint4 ar[2][HP], br[2][C::XU];
+        load_a(0, ar[0]);
+        load_b(0, br[0]);
+        load_b(1, br[1]);
+        store_b(br[0], lds);
+        bw_lds_barrier();
+        for (int s = 0; s < nst; s += 2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int st = s + h;
+                const uint4 *cur = lds + h * C::XCH * 64;
+                uint4 *nxt = lds + (1 - h) * C::XCH * 64;
+                load_a(st + 1, ar[1 - h]);
+                load_b(st + 2, br[h]);  // past the range: zeros, unused
+                products(ar[h], cur);
+                store_b(br[1 - h], nxt);  // the next step's x (past the range: zeros, unused)
+                bw_lds_barrier();
+            }
+        }
+
+        // fp32 partial planes part[split][plane][o][i]; D lane l: input column l % 32, outputs
+        // 8 (v / 4) + 4 (l / 32) + v % 4 of the wave's block
+        const int64_t plane_sz = (int64_t)C_out_pad * C_in_pad;
+        float *pb = part + (int64_t)split * G * plane_sz;
+#pragma unroll
+        for (int b = 0; b < WB; ++b)
+#pragma unroll
+            for (int q = 0; q < HP; ++q) {
+                const int pl = R * HP + q;
+                const int i = (ib0 + b) * 32 + (lane & 31);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int o = ob * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    pb[pl * plane_sz + (int64_t)o * C_in_pad + i] = acc[b][q][v];
+                }
+            }
+    };
+    if (role == 0)
+        run(IC2<0>{});
+    else
+        run(IC2<1>{});
+}
+
+// ------------------------------------------------------------------------------------------------
+// Pass 3: splits summed, inverse DFT with the plane scalings -> dW; db from its partials.
+template <int G>
+__global__ __launch_bounds__(256) void k_bw_reduce(const float *__restrict__ part, int splits, int C_out, int C_in,
+                                                   int C_out_pad, int C_in_pad, float *__restrict__ dW,
+                                                   const float *__restrict__ db_part, int n_tiles,
+                                                   float *__restrict__ db) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t plane_sz = (int64_t)C_out_pad * C_in_pad;
+    if (t < (int64_t)C_out * C_in) {
+        const int o = (int)(t / C_in), i = (int)(t % C_in);
+        float Y[G], out[G];
+#pragma unroll
+        for (int p = 0; p < G; ++p) {
+            float s = 0.f;
+            for (int k = 0; k < splits; ++k) s += part[((int64_t)k * G + p) * plane_sz + (int64_t)o * C_in_pad + i];
+            Y[p] = s * plane_scale(G, p);
+        }
+        inverse_planes<G>(Y, out);
+#pragma unroll
+        for (int d = 0; d < G; ++d) dW[t * G + d] = out[d];
+    }
+    if (db && t < C_out) {
+        float s = 0.f;
+        for (int k = 0; k < n_tiles; ++k) s += db_part[(int64_t)k * C_out_pad + t];
+        db[t] = s;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Direct kernel (fp32 or bf16 inputs, any G): the definition in fp32. Workgroup: 16 x 16 (o, i)
+// pairs, 256 threads (one pair each, all G shifts d); token tiles of 32 through LDS.
+template <typename T, int G>
+__global__ __launch_bounds__(256) void k_bw_direct(const T *__restrict__ x, const T *__restrict__ dy, int64_t N,
+                                                   int C_in, int C_out, float *__restrict__ dW) {
+    constexpr int TK = 32;
+    __shared__ float xs[TK][16][G + 1];
+    __shared__ float ds[TK][16][G + 1];
+    const int t = threadIdx.x, ol = t >> 4, il = t & 15;
+    const int o0 = blockIdx.y * 16, i0 = blockIdx.x * 16;
+    auto ld = [](const T *p, int64_t k) -> float {
+        if constexpr (sizeof(T) == 2)
+            return __uint_as_float((uint32_t)p[k] << 16);
+        else
+            return p[k];
+    };
+    float acc[G];
+#pragma unroll
+    for (int d = 0; d < G; ++d) acc[d] = 0.f;
+    for (int64_t n0 = 0; n0 < N; n0 += TK) {
+        for (int e = t; e < TK * 16 * G; e += 256) {
+            const int k = e / (16 * G), c = (e / G) % 16, g = e % G;
+            const int64_t n = n0 + k;
+            const int i = i0 + c, o = o0 + c;
+            xs[k][c][g] = (n < N && i < C_in) ? ld(x, (n * C_in + i) * G + g) : 0.f;
+            ds[k][c][g] = (n < N && o < C_out) ? ld(dy, (n * C_out + o) * G + g) : 0.f;
+        }
+        __syncthreads();
+        for (int k = 0; k < TK; ++k)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float dv = ds[k][ol][h];
+#pragma unroll
+                for (int d = 0; d < G; ++d) acc[d] += dv * xs[k][il][(h - d + G) % G];
+            }
+        __syncthreads();
+    }
+    const int o = o0 + ol, i = i0 + il;
+    if (o < C_out && i < C_in)
+#pragma unroll
+        for (int d = 0; d < G; ++d) dW[((int64_t)o * C_in + i) * G + d] = acc[d];
+}
+
+// db[o] = sum_{n, h} dy[n, o, h] (fp32): 64 outputs per workgroup, 4 token phases reduced in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void k_bw_bias(const T *__restrict__ dy, int64_t N, int C_out, int G,
+                                                 float *__restrict__ db) {
+    __shared__ float red[4][64];
+    const int t = threadIdx.x, ol = t & 63, ph = t >> 6;
+    const int o = blockIdx.x * 64 + ol;
+    float s = 0.f;
+    if (o < C_out)
+        for (int64_t n = ph; n < N; n += 4)
+            for (int h = 0; h < G; ++h) {
+                const int64_t k = (n * C_out + o) * G + h;
+                if constexpr (sizeof(T) == 2)
+                    s += __uint_as_float((uint32_t)dy[k] << 16);
+                else
+                    s += dy[k];
+            }
+    red[ph][ol] = s;
+    __syncthreads();
+    if (ph == 0 && o < C_out) db[o] = ((red[0][ol] + red[1][ol]) + red[2][ol]) + red[3][ol];
+}
+
+// ------------------------------------------------------------------------------------------------
+// Host side: workspace layout and launch.
+namespace {
+
+bool mfma_path(const Plan *p) { return p->dtype == EQLIN_BF16 && (p->G == 4 || p->G == 8); }
+
+struct BwLayout {
+    int KT = 0, CB_in = 0, CB_out = 0, tiles_i = 0, tiles_o = 0, splits = 0, ptiles = 0;
+    int C_in_pad = 0, C_out_pad = 0;
+    size_t off_x = 0, off_dy = 0, off_part = 0, off_db = 0, total = 0;
+};
+
+template <int G>
+BwLayout bw_layout(const Plan *p, int64_t N) {
+    using C = BwCfg<G>;
+    BwLayout L;
+    const int64_t n_pad = (N + kBwTok - 1) / kBwTok * kBwTok;
+    L.KT = (int)(n_pad / 16);
+    L.ptiles = (int)(n_pad / kBwTok);
+    L.tiles_i = (p->C_in + C::BI - 1) / C::BI;
+    L.tiles_o = (p->C_out + C::BO - 1) / C::BO;
+    L.C_in_pad = L.tiles_i * C::BI;
+    L.C_out_pad = L.tiles_o * C::BO;
+    L.CB_in = L.C_in_pad / 32;
+    L.CB_out = L.C_out_pad / 32;
+    const int tiles = L.tiles_i * L.tiles_o;
+    const int cus = device_num_cus();
+    L.splits = std::max(1, std::min(cus / std::max(1, tiles), L.KT / 8));
+    auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+    L.off_x = 0;
+    L.off_dy = al(L.off_x + (size_t)L.CB_in * L.KT * G * 1024);
+    L.off_part = al(L.off_dy + (size_t)L.CB_out * L.KT * G * 1024);
+    L.off_db = al(L.off_part + (size_t)L.splits * G * L.C_out_pad * L.C_in_pad * 4);
+    L.total = al(L.off_db + (size_t)L.ptiles * L.C_out_pad * 4);
+    return L;
+}
+
+BwLayout layout_for(const Plan *p, int64_t N) {
+    if (p->G == 8) return bw_layout<8>(p, N);
+    return bw_layout<4>(p, N);
+}
+
+template <int G>
+hipError_t launch_mfma(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N, void *ws,
+                       hipStream_t s) {
+    const BwLayout L = bw_layout<G>(p, N);
+    char *w = static_cast<char *>(ws);
+    uint4 *xf = reinterpret_cast<uint4 *>(w + L.off_x), *dyf = reinterpret_cast<uint4 *>(w + L.off_dy);
+    float *part = reinterpret_cast<float *>(w + L.off_part), *dbp = reinterpret_cast<float *>(w + L.off_db);
+    if ((int64_t)L.ptiles > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_bw_planes<G>, dim3(L.ptiles, L.CB_in), dim3(256), 0, s, (const uint16_t *)x, N, p->C_in,
+                       L.KT, xf, (float *)nullptr);
+    hipLaunchKernelGGL(k_bw_planes<G>, dim3(L.ptiles, L.CB_out), dim3(256), 0, s, (const uint16_t *)dy, N, p->C_out,
+                       L.KT, dyf, dbp);
+    const int grid = L.tiles_i * L.tiles_o * L.splits;
+    hipLaunchKernelGGL(k_bw_gemm<G>, dim3(grid), dim3(512), 0, s, (const uint4 *)xf, (const uint4 *)dyf, part,
+                       L.KT, L.tiles_i, L.splits, L.C_in_pad, L.C_out_pad);
+    const int64_t pairs = std::max<int64_t>((int64_t)p->C_out * p->C_in, p->C_out);
+    hipLaunchKernelGGL(k_bw_reduce<G>, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, (const float *)part,
+                       L.splits, p->C_out, p->C_in, L.C_out_pad, L.C_in_pad, dW, (const float *)dbp, L.ptiles, db);
+    return hipGetLastError();
+}
+
+template <typename T, int G>
+hipError_t launch_direct(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N,
+                         hipStream_t s) {
+    hipLaunchKernelGGL((k_bw_direct<T, G>), dim3((p->C_in + 15) / 16, (p->C_out + 15) / 16), dim3(256), 0, s,
+                       (const T *)x, (const T *)dy, N, p->C_in, p->C_out, dW);
+    if (db)
+        hipLaunchKernelGGL(k_bw_bias<T>, dim3((p->C_out + 63) / 64), dim3(256), 0, s, (const T *)dy, N, p->C_out,
+                           G, db);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_direct_g(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N,
+                           hipStream_t s) {
+    switch (p->G) {
+        case 1: return launch_direct<T, 1>(p, x, dy, dW, db, N, s);
+        case 2: return launch_direct<T, 2>(p, x, dy, dW, db, N, s);
+        case 4: return launch_direct<T, 4>(p, x, dy, dW, db, N, s);
+        case 8: return launch_direct<T, 8>(p, x, dy, dW, db, N, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+size_t bw_workspace_bytes(const Plan *p, int64_t N) {
+    if (!mfma_path(p) || N <= 0) return 0;
+    return layout_for(p, N).total;
+}
+
+hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N,
+                                   void *ws, hipStream_t s) {
+    if (mfma_path(p)) return p->G == 8 ? launch_mfma<8>(p, x, dy, dW, db, N, ws, s)
+                                       : launch_mfma<4>(p, x, dy, dW, db, N, ws, s);
+    if (p->dtype == EQLIN_BF16) return launch_direct_g<uint16_t>(p, x, dy, dW, db, N, s);
+    return launch_direct_g<float>(p, x, dy, dW, db, N, s);
+}
+
+const char *bw_kernel_name(const Plan *p) {
+    return mfma_path(p) ? "bf16 dft planes + plane-split mfma32x32x16 split-K + reduce" : "direct fp32 valu";
+}
+
+}  // namespace eqlin

@@ -38,8 +38,10 @@ int ilog2(int g) {
 void free_plan(Plan *p) {
     if (!p) return;
     if (p->expanded) free_plan(p->expanded);
+    if (p->backward) free_plan(p->backward);
     if (p->planes) (void)hipFree(p->planes);
     if (p->wexp) (void)hipFree(p->wexp);
+    if (p->wt) (void)hipFree(p->wt);
     delete static_cast<eqlin_plan *>(p);
 }
 
@@ -117,12 +119,15 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
     if (C_out < 1 || C_in < 1) return fail(EQLIN_ERR_INVALID_ARG, "C_out = %d, C_in = %d must be >= 1", C_out, C_in);
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(EQLIN_ERR_INVALID_ARG, "G = %d not in {1, 2, 4, 8}", G);
     if (dtype != EQLIN_F32 && dtype != EQLIN_BF16) return fail(EQLIN_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
-    if (flags & ~EQLIN_PREPARE_EXPANDED) return fail(EQLIN_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    if (flags & ~(EQLIN_PREPARE_EXPANDED | EQLIN_PREPARE_BACKWARD))
+        return fail(EQLIN_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     if ((int64_t)C_out * G > (1 << 20) || (int64_t)C_in * G > (1 << 20))
         return fail(EQLIN_ERR_UNSUPPORTED, "channel counts beyond 2^20 unrolled columns");
     if (!aligned(W, 16)) return fail(EQLIN_ERR_INVALID_ARG, "W must be 16-byte aligned");
     if (dtype == EQLIN_BF16 && C_in % 8 != 0)
         return fail(EQLIN_ERR_UNSUPPORTED, "bf16 path needs C_in %% 8 == 0 (C_in = %d)", C_in);
+    if ((flags & EQLIN_PREPARE_BACKWARD) && dtype == EQLIN_BF16 && C_out % 8 != 0)
+        return fail(EQLIN_ERR_UNSUPPORTED, "bf16 backward needs C_out %% 8 == 0 (C_out = %d)", C_out);
 
     hipStream_t s = (hipStream_t)stream;
     Plan *p = new (std::nothrow) eqlin_plan();
@@ -174,6 +179,37 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
             return st;
         }
     }
+    if (flags & EQLIN_PREPARE_BACKWARD) {
+        const size_t eb = dtype == EQLIN_BF16 ? 2 : 4;
+        const size_t bytes = (size_t)C_out * C_in * G * eb;
+        e = hipMalloc(&p->wt, bytes);
+        if (e != hipSuccess) {
+            p->wt = nullptr;
+            free_plan(p);
+            return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for the backward weight", bytes);
+        }
+        e = eqlin::launch_transpose_reverse(W, (int)eb, G, C_out, C_in, p->wt, s);
+        if (e != hipSuccess) {
+            free_plan(p);
+            return hip_fail(e, "backward weight");
+        }
+        Plan *q = new (std::nothrow) eqlin_plan();
+        if (!q) {
+            free_plan(p);
+            return fail(EQLIN_ERR_OUT_OF_MEMORY, "host allocation");
+        }
+        q->C_out = C_in;
+        q->C_in = C_out;
+        q->G = G;
+        q->dtype = dtype;
+        q->device = p->device;
+        p->backward = q;
+        st = build_spectral(q, p->wt, s);
+        if (st != EQLIN_OK) {
+            free_plan(p);
+            return st;
+        }
+    }
     *out = static_cast<eqlin_handle_t>(static_cast<eqlin_plan *>(p));
     return EQLIN_OK;
 }
@@ -204,6 +240,44 @@ eqlin_status_t eqlin_forward_expanded(eqlin_handle_t h, const void *x, const voi
     eqlin_status_t st = check_forward_args(h, x, b, y, N, h->C_in, h->C_out, h->G);
     if (st != EQLIN_OK || N == 0) return st;
     return run_forward(h->expanded, x, b, y, N, stream, "eqlin_forward_expanded launch");
+}
+
+eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, int64_t N, eqlin_stream_t stream) {
+    g_err[0] = 0;
+    if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
+    if (!h->backward) return fail(EQLIN_ERR_INVALID_ARG, "handle was prepared without EQLIN_PREPARE_BACKWARD");
+    eqlin_status_t st = check_forward_args(h, dy, nullptr, dx, N, h->C_out, h->C_in, h->G);
+    if (st != EQLIN_OK || N == 0) return st;
+    return run_forward(h->backward, dy, nullptr, dx, N, stream, "eqlin_backward_data launch");
+}
+
+size_t eqlin_backward_weights_workspace(eqlin_handle_t h, int64_t N) {
+    if (!h || N <= 0) return 0;
+    return eqlin::bw_workspace_bytes(h, N);
+}
+
+eqlin_status_t eqlin_backward_weights(eqlin_handle_t h, const void *x, const void *dy, float *dW, float *db,
+                                      int64_t N, void *workspace, size_t workspace_bytes, eqlin_stream_t stream) {
+    g_err[0] = 0;
+    if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
+    if (!dW) return fail(EQLIN_ERR_INVALID_ARG, "null dW");
+    if (!aligned(dW, 4) || (db && !aligned(db, 4))) return fail(EQLIN_ERR_INVALID_ARG, "dW and db must be 4-byte aligned");
+    // x plays the forward's x, dy the forward's y (shapes, alignment, overlap, device)
+    eqlin_status_t st = check_forward_args(h, x, nullptr, dy, N, h->C_in, h->C_out, h->G);
+    if (st != EQLIN_OK) return st;
+    const size_t need = eqlin::bw_workspace_bytes(h, N);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(EQLIN_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    if (need > 0 && !aligned(workspace, 256)) return fail(EQLIN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    (void)hipGetLastError();
+    hipError_t e;
+    if (N == 0) {  // no tokens: zero gradients
+        e = hipMemsetAsync(dW, 0, (size_t)h->C_out * h->C_in * h->G * sizeof(float), (hipStream_t)stream);
+        if (e == hipSuccess && db) e = hipMemsetAsync(db, 0, (size_t)h->C_out * sizeof(float), (hipStream_t)stream);
+        return e == hipSuccess ? EQLIN_OK : hip_fail(e, "eqlin_backward_weights clear");
+    }
+    e = eqlin::launch_backward_weights(h, x, dy, dW, db, N, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? EQLIN_OK : hip_fail(e, "eqlin_backward_weights launch");
 }
 
 eqlin_status_t eqlin_destroy(eqlin_handle_t h) {
@@ -237,9 +311,11 @@ eqlin_status_t eqlin_export_expanded_weight(eqlin_handle_t h, void *out, eqlin_s
 
 int eqlin_describe(eqlin_handle_t h, char *buf, size_t len) {
     if (!h) return snprintf(buf, len, "(null handle)");
-    return snprintf(buf, len, "G=%d C_in=%d C_out=%d %s | forward: %s | expanded: %s", h->G, h->C_in,
-                    h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : "f32", h->fwd.name,
-                    h->expanded ? h->expanded->fwd.name : "(not prepared)");
+    return snprintf(buf, len,
+                    "G=%d C_in=%d C_out=%d %s | forward: %s | expanded: %s | backward data: %s | backward weights: %s",
+                    h->G, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : "f32", h->fwd.name,
+                    h->expanded ? h->expanded->fwd.name : "(not prepared)",
+                    h->backward ? h->backward->fwd.name : "(not prepared)", eqlin::bw_kernel_name(h));
 }
 
 const char *eqlin_status_string(eqlin_status_t s) {

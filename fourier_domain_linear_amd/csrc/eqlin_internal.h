@@ -58,6 +58,11 @@ struct Plan {
     // unrolled weight (flags & EQLIN_PREPARE_EXPANDED): a G = 1 plan over E, plus E itself
     Plan *expanded = nullptr;
     void *wexp = nullptr;  // [C_out*G][C_in*G] of dtype
+
+    // data gradient (flags & EQLIN_PREPARE_BACKWARD): a plan over Wt[i][o][d] = W[o][i][-d mod G]
+    // (C_in and C_out swapped), whose forward is dx; plus Wt itself
+    Plan *backward = nullptr;
+    void *wt = nullptr;  // [C_in][C_out][G] of dtype
 };
 
 // ---- fwd_bf16.hip ----
@@ -68,6 +73,14 @@ bool select_big(int G, int C_in, int C_out, KernelChoice *out);
 // ---- fwd_f32.hip ----
 bool select_f32(int G, int C_in, int C_out, KernelChoice *out);
 
+// ---- bwd.hip ----
+// Workspace bytes eqlin_backward_weights needs for N tokens (0: none).
+size_t bw_workspace_bytes(const Plan *p, int64_t N);
+// dW [C_out][C_in][G] fp32 and db [C_out] fp32 (or null) from x and dy of the plan's dtype.
+hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N,
+                                   void *ws, hipStream_t s);
+const char *bw_kernel_name(const Plan *p);
+
 // ---- prepare.hip ----
 // W [C_out][C_in][G] (bf16 bits or fp32) -> fragment-ordered bf16 spectral planes.
 hipError_t launch_prep_frag(const void *W, bool w_is_bf16, int G, int C_out, int C_in, int KS,
@@ -75,6 +88,9 @@ hipError_t launch_prep_frag(const void *W, bool w_is_bf16, int G, int C_out, int
 // W fp32 -> planes [G][C_out][C_in] fp32.
 hipError_t launch_prep_plain_f32(const float *W, int G, int C_out, int C_in, float *planes,
                                  hipStream_t s);
+// W -> Wt[C_in][C_out][G], Wt[i][o][d] = W[o][i][(G - d) mod G] (same element size, 2 or 4 bytes).
+hipError_t launch_transpose_reverse(const void *W, int elem_bytes, int G, int C_out, int C_in, void *Wt,
+                                   hipStream_t s);
 // W -> E[C_out*G][C_in*G] (same element size, 2 or 4 bytes).
 hipError_t launch_expand(const void *W, int elem_bytes, int G, int C_out, int C_in, void *E,
                          hipStream_t s);

@@ -111,6 +111,19 @@ __global__ void k_expand(const T *__restrict__ W, int G, int C_out, int C_in, T 
     E[t] = W[((int64_t)o * C_in + i) * G + d];
 }
 
+// Wt[i][o][d] = W[o][i][(G - d) mod G]: the weight of the layer whose forward is this layer's data
+// gradient (dx[n, i, g] = sum_{o, h} W[o, i, (h - g) mod G] dy[n, o, h] = sum_{o, h} Wt[i, o, (g - h) mod G]
+// dy[n, o, h]). Pure index permutation: exact in any element type.
+template <typename T>
+__global__ void k_transpose_reverse(const T *__restrict__ W, int G, int C_out, int C_in, T *__restrict__ Wt) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)C_out * C_in * G) return;
+    const int d = (int)(t % G);
+    const int64_t io = t / G;
+    const int o = (int)(io % C_out), i = (int)(io / C_out);
+    Wt[t] = W[((int64_t)o * C_in + i) * G + (G - d) % G];
+}
+
 static inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
 
 #define DISPATCH_G(G, CALL)                     \
@@ -152,6 +165,18 @@ hipError_t launch_export_plain_f32(const float *planes, int G, int C_out, int C_
     const int64_t n = (int64_t)C_out * C_in;
     DISPATCH_G(G, hipLaunchKernelGGL(k_export_plain_f32<GG>, dim3(blocks_for(n, 256)), dim3(256), 0,
                                      s, planes, C_out, C_in, out));
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_reverse(const void *W, int elem_bytes, int G, int C_out, int C_in, void *Wt,
+                                   hipStream_t s) {
+    const int64_t n = (int64_t)C_out * C_in * G;
+    if (elem_bytes == 2)
+        hipLaunchKernelGGL(k_transpose_reverse<uint16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
+                           (const uint16_t *)W, G, C_out, C_in, (uint16_t *)Wt);
+    else
+        hipLaunchKernelGGL(k_transpose_reverse<float>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
+                           (const float *)W, G, C_out, C_in, (float *)Wt);
     return hipGetLastError();
 }
 

@@ -67,6 +67,16 @@ def make_inputs(G: int, C_in: int, C_out: int, N: int, dtype: str = "bf16", seed
     return x, W, b
 
 
+def make_grad(G: int, C_out: int, N: int, dtype: str = "bf16", seed: int = 0):
+    """An upstream gradient dy[N, C_out, G] ~ N(0, 1) (CPU tensor in the workload dtype) for the
+    backward passes; seeded like make_inputs but from its own stream (seed + 7919)."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    gen = torch.Generator().manual_seed(int(seed) + 7919)
+    dy = torch.randn((N, C_out, G), generator=gen, dtype=torch.float32)
+    return dy.to(torch.bfloat16) if dtype == "bf16" else dy
+
+
 def workload_inputs(w: Workload, seed: int = 0, N: int | None = None):
     """Inputs of workload ``w`` (optionally with a different token count N)."""
     return make_inputs(w.G, w.C_in, w.C_out, w.N if N is None else N, w.dtype, seed)

@@ -64,6 +64,7 @@ typedef enum { EQLIN_F32 = 0, EQLIN_BF16 = 1 } eqlin_dtype_t;
 
 /* flags for eqlin_prepare_weights */
 #define EQLIN_PREPARE_EXPANDED 1u /* also build the unrolled weight for eqlin_forward_expanded */
+#define EQLIN_PREPARE_BACKWARD 2u /* also build the data-gradient weights for eqlin_backward_data */
 
 /*
  * eqlin_prepare_weights -- W -> spectral weights, once per weight set.
@@ -78,7 +79,9 @@ typedef enum { EQLIN_F32 = 0, EQLIN_BF16 = 1 } eqlin_dtype_t;
  *          overwrite W once `stream` has passed this call.
  *   C_out, C_in >= 1; G in {1, 2, 4, 8}; C_out * G and C_in * G <= 2^20 (else UNSUPPORTED).
  *          EQLIN_BF16 needs C_in % 8 == 0 (else UNSUPPORTED).
- *   flags  EQLIN_PREPARE_EXPANDED to also build the unrolled weight for eqlin_forward_expanded.
+ *   flags  EQLIN_PREPARE_EXPANDED to also build the unrolled weight for eqlin_forward_expanded;
+ *          EQLIN_PREPARE_BACKWARD to also build the weights of eqlin_backward_data (EQLIN_BF16 then
+ *          also needs C_out % 8 == 0, else UNSUPPORTED).
  *   out    receives the new handle (set to NULL on failure).
  * Allocates device memory (hipMalloc) on the current device; synchronises nothing.
  */
@@ -108,6 +111,43 @@ eqlin_status_t eqlin_forward(eqlin_handle_t h, const void *x, const void *b, voi
  */
 eqlin_status_t eqlin_forward_expanded(eqlin_handle_t h, const void *x, const void *b, void *y,
                                       int64_t N, eqlin_stream_t stream);
+
+/*
+ * eqlin_backward_data -- the data gradient of the layer ("Implementación": the operator has forward
+ * and backward passes; "Resultados Experimentales": backward speedups):
+ *
+ *     dx[n, i, g] = sum_{o < C_out} sum_{h < G} W[o, i, (h - g) mod G] * dy[n, o, h]
+ *
+ * i.e. the transpose of the unrolled product. It is itself an EQ-Linear layer -- with the weight
+ * Wt[i, o, d] = W[o, i, (-d) mod G] (C_in and C_out swapped, group axis reversed; the DFT of Wt is
+ * the conjugate of the DFT of W) and no bias -- and runs on the forward kernels.
+ *   dy     device [N][C_out][G] of the handle's dtype; dx device [N][C_in][G] (same type).
+ *   N      >= 0; N == 0 enqueues nothing.
+ * Needs a handle prepared with EQLIN_PREPARE_BACKWARD (else EQLIN_ERR_INVALID_ARG). Same alignment,
+ * overlap, device and stream rules as eqlin_forward; allocates nothing.
+ */
+eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, int64_t N, eqlin_stream_t stream);
+
+/*
+ * eqlin_backward_weights -- the weight and bias gradients (same passages):
+ *
+ *     dW[o, i, d] = sum_n sum_{h < G} dy[n, o, h] * x[n, i, (h - d) mod G],   db[o] = sum_{n, h} dy[n, o, h]
+ *
+ * computed per frequency as C_k = sum_n DY_k conj(X_k) (the same group DFT as the forward) followed
+ * by the inverse DFT. bf16 with G = 4 or 8: x and dy are transformed into bf16 planes, multiplied on
+ * the matrix cores with fp32 accumulation over token splits, and the splits summed in fp32; other
+ * cases (fp32, G = 1 or 2) evaluate the definition in fp32 on the vector ALU.
+ *   x      device [N][C_in][G], dy device [N][C_out][G], both of the handle's dtype.
+ *   dW     device float [C_out][C_in][G] (overwritten); db device float [C_out] or NULL (overwritten).
+ *   workspace, workspace_bytes: device scratch of at least eqlin_backward_weights_workspace(h, N)
+ *          bytes, 256-byte aligned (may be NULL when that is 0); owned by the caller, not kept.
+ *   N      >= 0; N == 0 writes zeros.
+ * Any handle (no prepare flag needed). Asynchronous on `stream`; allocates nothing. Calls sharing a
+ * workspace must not overlap.
+ */
+size_t eqlin_backward_weights_workspace(eqlin_handle_t h, int64_t N);
+eqlin_status_t eqlin_backward_weights(eqlin_handle_t h, const void *x, const void *dy, float *dW, float *db,
+                                      int64_t N, void *workspace, size_t workspace_bytes, eqlin_stream_t stream);
 
 /* Frees the handle's device memory (hipFree, which synchronises the device). NULL is a no-op. */
 eqlin_status_t eqlin_destroy(eqlin_handle_t h);

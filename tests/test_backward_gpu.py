@@ -1,0 +1,130 @@
+"""GPU parity of the backward passes (eqlin_backward_data, eqlin_backward_weights) through the C ABI
+against the fp64 oracle's gradients (oracle.backward_data / oracle.backward_weights) on the same
+seeded bf16-rounded inputs.
+
+Bars. The forward's bars are stated for outputs of unit scale; the gradients are not (dx has rms
+sqrt(C_out / C_in) here, dW grows like sqrt(N)), so the max-abs bar is taken relative to the
+reference's rms: bf16 -- relative Frobenius error <= 1e-2 AND max abs error <= 3e-2 * rms(ref);
+fp32 -- relative Frobenius error <= 1e-5. (For the forward's unit-scale outputs this is the forward's
+own bar.)
+
+Sizes: small ragged shapes the oracle finishes in seconds (several tiles, partial token steps,
+padded channels), and every workload's channel shape at its full token count: dx on a sample of
+tokens (dx[n] depends only on dy[n]), dW on a sample of output and input channels at all tokens
+(dW[o, i] depends only on dy[:, o] and x[:, i]).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fourier_domain_linear_amd as eq
+import oracle
+from fourier_domain_linear_amd.workloads import WORKLOADS, make_grad, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+REL_BF16, MAX_BF16, REL_F32 = 1e-2, 3e-2, 1e-5
+
+
+def _check(got: torch.Tensor, ref: np.ndarray, dtype: str, label: str):
+    g = got.detach().to("cpu", torch.float64).numpy()
+    assert np.all(np.isfinite(g)), label
+    diff = g - ref
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(diff) / max(nref, 1e-300)
+    rms = nref / np.sqrt(max(ref.size, 1))
+    mx = float(np.max(np.abs(diff))) if diff.size else 0.0
+    print(f"[parity] {label}: rel_frob={rel:.3e} max_abs={mx:.3e} rms_ref={rms:.3e}", flush=True)
+    if dtype == "bf16":
+        assert rel <= REL_BF16 and mx <= MAX_BF16 * max(rms, 1e-30), (label, rel, mx, rms)
+    else:
+        assert rel <= REL_F32, (label, rel)
+
+
+def _handle(W, dev):
+    return eq.prepare_weights(W.to(dev), backward=True)
+
+
+SHAPES = [(4, 32, 48, 1000, "bf16"), (8, 64, 64, 517, "bf16"), (4, 96, 96, 777, "bf16"),
+          (4, 192, 768, 300, "bf16"), (8, 256, 1024, 130, "bf16"), (8, 136, 200, 203, "bf16"),
+          (4, 40, 24, 70, "bf16"), (2, 64, 32, 333, "bf16"), (1, 48, 40, 100, "bf16"),
+          (4, 16, 16, 64, "f32"), (8, 24, 40, 150, "f32")]
+
+
+@pytest.mark.parametrize("G,C_in,C_out,N,dtype", SHAPES,
+                         ids=[f"p{g}_{ci}x{co}_n{n}_{d}" for g, ci, co, n, d in SHAPES])
+def test_backward_small(G, C_in, C_out, N, dtype, cuda_device):
+    x, W, _ = make_inputs(G, C_in, C_out, N, dtype, seed=11)
+    dy = make_grad(G, C_out, N, dtype, seed=11)
+    h = _handle(W, cuda_device)
+    dx = eq.backward_data(h, dy.to(cuda_device))
+    dW, db = eq.backward_weights(h, x.to(cuda_device), dy.to(cuda_device))
+    torch.cuda.synchronize()
+    print(f"[kernel] {h.describe()}", flush=True)
+    _check(dx, oracle.backward_data(dy, W), dtype, f"dx G={G} {C_in}x{C_out} N={N} {dtype}")
+    rW, rb = oracle.backward_weights(x, dy)
+    _check(dW, rW, dtype, f"dW G={G} {C_in}x{C_out} N={N} {dtype}")
+    _check(db, rb, dtype, f"db G={G} {C_in}x{C_out} N={N} {dtype}")
+
+
+@pytest.mark.parametrize("w", WORKLOADS, ids=[w.name for w in WORKLOADS])
+def test_backward_full_size_sampled(w, cuda_device):
+    x, W, _ = make_inputs(w.G, w.C_in, w.C_out, w.N, w.dtype, seed=0)
+    dy = make_grad(w.G, w.C_out, w.N, w.dtype, seed=0)
+    h = _handle(W, cuda_device)
+    xd, dyd = x.to(cuda_device), dy.to(cuda_device)
+    dx = eq.backward_data(h, dyd)
+    dW, db = eq.backward_weights(h, xd, dyd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    tok = np.unique(np.concatenate([[0, w.N - 1, w.N // 2], rng.choice(w.N, size=min(96, w.N), replace=False)]))
+    _check(dx[torch.as_tensor(tok, device=dx.device)], oracle.backward_data(dy[tok], W), w.dtype,
+           f"{w.name} dx sampled {len(tok)} tokens")
+    osub = np.unique(np.concatenate([[0, w.C_out - 1], rng.choice(w.C_out, size=min(12, w.C_out), replace=False)]))
+    isub = np.unique(np.concatenate([[0, w.C_in - 1], rng.choice(w.C_in, size=min(12, w.C_in), replace=False)]))
+    rW, rb = oracle.backward_weights(x[:, isub], dy[:, osub])
+    got = dW[torch.as_tensor(osub, device=dW.device)][:, torch.as_tensor(isub, device=dW.device)]
+    _check(got, rW, w.dtype, f"{w.name} dW sampled {len(osub)}x{len(isub)} channels, all {w.N} tokens")
+    _check(db[torch.as_tensor(osub, device=db.device)], rb, w.dtype, f"{w.name} db sampled")
+
+
+def test_backward_weights_empty_and_tiny(cuda_device):
+    x, W, _ = make_inputs(8, 32, 64, 1, "bf16", seed=5)
+    h = _handle(W, cuda_device)
+    dW, db = eq.backward_weights(h, x[:0].to(cuda_device), make_grad(8, 64, 0).to(cuda_device))
+    assert torch.count_nonzero(dW).item() == 0 and torch.count_nonzero(db).item() == 0
+    dy = make_grad(8, 64, 1, seed=5)
+    dW, db = eq.backward_weights(h, x.to(cuda_device), dy.to(cuda_device))
+    rW, rb = oracle.backward_weights(x, dy)
+    _check(dW, rW, "bf16", "dW N=1")
+    _check(db, rb, "bf16", "db N=1")
+    assert eq.backward_data(h, dy[:0].to(cuda_device)).shape == (0, 32, 8)
+
+
+def test_backward_without_bias_and_reused_workspace(cuda_device):
+    x, W, _ = make_inputs(4, 64, 128, 2000, "bf16", seed=9)
+    dy = make_grad(4, 128, 2000, seed=9)
+    h = _handle(W, cuda_device)
+    need = eq.backward_weights_workspace(h, 2000)
+    ws = torch.empty((need,), dtype=torch.uint8, device=cuda_device)
+    ws.fill_(0xff)  # garbage in the workspace must not leak into the result
+    dW1, db1 = eq.backward_weights(h, x.to(cuda_device), dy.to(cuda_device), with_bias=False, workspace=ws)
+    assert db1 is None
+    dW2, _ = eq.backward_weights(h, x[:700].to(cuda_device), dy[:700].to(cuda_device), workspace=ws)
+    torch.cuda.synchronize()
+    _check(dW1, oracle.backward_weights(x, dy)[0], "bf16", "dW N=2000 caller workspace")
+    _check(dW2, oracle.backward_weights(x[:700], dy[:700])[0], "bf16", "dW N=700 same workspace")
+
+
+def test_backward_data_needs_flag(cuda_device):
+    _, W, _ = make_inputs(4, 32, 32, 1, "bf16")
+    h = eq.prepare_weights(W.to(cuda_device))
+    with pytest.raises(ValueError):
+        eq.backward_data(h, make_grad(4, 32, 4).to(cuda_device))
+
+
+def test_backward_bf16_needs_c_out_multiple_of_8(cuda_device):
+    _, W, _ = make_inputs(4, 32, 12, 1, "bf16")
+    with pytest.raises(eq.EqlinError) as ei:
+        eq.prepare_weights(W.to(cuda_device), backward=True)
+    assert ei.value.status == eq.EQLIN_ERR_UNSUPPORTED
