@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-expanded", action="store_true")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time eqlin_backward_data and eqlin_backward_weights (reported under 'backward')")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (the counter calibration for traffic)")
     args = ap.parse_args()
@@ -146,7 +148,7 @@ def main():
 
     import fourier_domain_linear_amd as eq
     from fourier_domain_linear_amd import roofline as rl
-    from fourier_domain_linear_amd.workloads import BENCH_WORKLOAD, BY_NAME, workload_inputs
+    from fourier_domain_linear_amd.workloads import BENCH_WORKLOAD, BY_NAME, make_grad, workload_inputs
 
     w = BY_NAME[args.workload] if args.workload else BENCH_WORKLOAD
     if not torch.cuda.is_available():
@@ -164,7 +166,7 @@ def main():
     xs = [xd0] + [xd0.clone() for _ in range(R - 1)]
     ys = [torch.empty((w.N, w.C_out, w.G), dtype=w.torch_dtype, device=dev) for _ in range(R)]
     bd = b.to(dev)
-    h = eq.prepare_weights(W.to(dev), expanded=not args.no_expanded)
+    h = eq.prepare_weights(W.to(dev), expanded=not args.no_expanded, backward=args.backward)
     torch.cuda.synchronize()
     log(f"[bench] {h.describe()}  rotating buffer sets: {R} ({R * set_bytes / 2**20:.0f} MiB)")
 
@@ -213,6 +215,44 @@ def main():
             "hbm_frac": round(Bd / te / 1e9 / rl.PEAK_HBM_GBS, 4), "effective_tflops": round(Fd / te / 1e12, 2)}
         extra["speedup_vs_expanded"] = round(ms_e / ms, 3)
         log(f"[bench] expanded: {ms_e * 1e3:.2f} us/step  speedup {ms_e / ms:.2f}x")
+    if args.backward:
+        # the gradients of the same layer: dx on the forward kernels (transposed, group-reversed W),
+        # dW and db by the frequency-domain products over tokens; dy is a seeded upstream gradient
+        dy0 = make_grad(w.G, w.C_out, w.N, w.dtype, seed=0).to(dev)
+        dys = [dy0] + [dy0.clone() for _ in range(R - 1)]
+        dxs = [torch.empty_like(xd0) for _ in range(R)]
+        ws = torch.empty((max(1, eq.backward_weights_workspace(h, w.N)),), dtype=torch.uint8, device=dev)
+        dW = torch.empty((w.C_out, w.C_in, w.G), dtype=torch.float32, device=dev)
+        db = torch.empty((w.C_out,), dtype=torch.float32, device=dev)
+        lib = eq.load_library()
+        import ctypes
+
+        def bwd_data(i):
+            eq.backward_data(h, dys[i], dxs[i])
+
+        def bwd_weights(i):
+            st = lib.eqlin_backward_weights(ctypes.c_void_p(h.ptr), ctypes.c_void_p(xs[i].data_ptr()),
+                                            ctypes.c_void_p(dys[i].data_ptr()), ctypes.c_void_p(dW.data_ptr()),
+                                            ctypes.c_void_p(db.data_ptr()), w.N, ctypes.c_void_p(ws.data_ptr()),
+                                            ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"eqlin_backward_weights: {eq.status_string(st)}")
+
+        res = {}
+        for name, fn, Bk in (("data", bwd_data, B),
+                             ("weights", bwd_weights,
+                              w.N * (w.C_in + w.C_out) * w.G * eb + w.C_out * w.C_in * w.G * 4 + w.C_out * 4)):
+            for i in range(Wm):
+                fn(i % R)
+            torch.cuda.synchronize()
+            ms_b = timer(torch, fn, K, R)
+            tb = ms_b / 1e3
+            res[name] = {"ms_per_step": round(ms_b, 6), "tokens_per_s": w.N / tb,
+                         "useful_tflops": round(F / tb / 1e12, 2), "mfma_frac": round(F / tb / 1e12 / peak_c, 4),
+                         "algorithmic_bytes": Bk, "hbm_frac": round(Bk / tb / 1e9 / rl.PEAK_HBM_GBS, 4)}
+            log(f"[bench] backward {name}: {ms_b * 1e3:.2f} us/step")
+        res["kernels"] = h.describe().split("|")[3:]
+        extra["backward"] = res
     extra["effective_tflops"] = round(rl.dense_flops(w.N, w.C_in, w.C_out, w.G) / t / 1e12, 2)
     extra["useful_tflops"] = round(F / t / 1e12, 2)
 

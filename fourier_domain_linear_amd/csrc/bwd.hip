@@ -28,11 +28,13 @@
 //      written as fp32 partial planes. Two waves per SIMD split the planes (role 0: planes 0..G/2-1,
 //      role 1: the rest) and share the tile; the dy fragments go straight to registers (each wave its
 //      own), the x fragments through LDS (shared by all waves).
-//   3. k_bw_reduce: sum of the splits, inverse DFT (scaled) -> dW fp32; db from its partials.
+//   3. k_bw_reduce: sum of the splits, inverse DFT (scaled) -> dW fp32; k_bw_dbsum: db from its
+//      partials.
 // Other cases (fp32, G = 1 or 2): k_bw_direct, the definition above in fp32 with LDS token tiles.
 #include <stdio.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "device_common.h"
 #include "eqlin_internal.h"
@@ -251,31 +253,55 @@ __global__ __launch_bounds__(512) void k_bw_gemm(const uint4 *__restrict__ xf, c
 }
 
 // ------------------------------------------------------------------------------------------------
-// Pass 3: splits summed, inverse DFT with the plane scalings -> dW; db from its partials.
+// Pass 3: splits summed, inverse DFT with the plane scalings -> dW. A workgroup covers 32 consecutive
+// inputs i of one output o (whole 128-byte lines of every partial plane): thread (sub, i) sums the
+// splits sub, sub + 8, ... of each plane; the 8 shares are added in a fixed order in LDS, then 32
+// threads run the inverse transforms.
 template <int G>
 __global__ __launch_bounds__(256) void k_bw_reduce(const float *__restrict__ part, int splits, int C_out, int C_in,
-                                                   int C_out_pad, int C_in_pad, float *__restrict__ dW,
-                                                   const float *__restrict__ db_part, int n_tiles,
-                                                   float *__restrict__ db) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                                                   int C_out_pad, int C_in_pad, float *__restrict__ dW) {
+    __shared__ float red[G][8][33];
+    const int t = threadIdx.x, il = t & 31, sub = t >> 5;
+    const int ib = C_in_pad / 32;
+    const int o = blockIdx.x / ib, i = (blockIdx.x % ib) * 32 + il;
     const int64_t plane_sz = (int64_t)C_out_pad * C_in_pad;
-    if (t < (int64_t)C_out * C_in) {
-        const int o = (int)(t / C_in), i = (int)(t % C_in);
+    const float *src = part + (int64_t)o * C_in_pad + i;
+#pragma unroll
+    for (int p = 0; p < G; ++p) {
+        float s = 0.f;
+        for (int k = sub; k < splits; k += 8) s += src[((int64_t)k * G + p) * plane_sz];
+        red[p][sub][il] = s;
+    }
+    __syncthreads();
+    if (t < 32 && o < C_out && i < C_in) {
         float Y[G], out[G];
 #pragma unroll
         for (int p = 0; p < G; ++p) {
-            float s = 0.f;
-            for (int k = 0; k < splits; ++k) s += part[((int64_t)k * G + p) * plane_sz + (int64_t)o * C_in_pad + i];
-            Y[p] = s * plane_scale(G, p);
+            const float a = (red[p][0][il] + red[p][1][il]) + (red[p][2][il] + red[p][3][il]);
+            const float b = (red[p][4][il] + red[p][5][il]) + (red[p][6][il] + red[p][7][il]);
+            Y[p] = (a + b) * plane_scale(G, p);
         }
         inverse_planes<G>(Y, out);
 #pragma unroll
-        for (int d = 0; d < G; ++d) dW[t * G + d] = out[d];
+        for (int d = 0; d < G; ++d) dW[((int64_t)o * C_in + i) * G + d] = out[d];
     }
-    if (db && t < C_out) {
-        float s = 0.f;
-        for (int k = 0; k < n_tiles; ++k) s += db_part[(int64_t)k * C_out_pad + t];
-        db[t] = s;
+}
+
+// db[o] from the per-token-tile partials: 64 threads per output, each a strided share, LDS sum.
+__global__ __launch_bounds__(256) void k_bw_dbsum(const float *__restrict__ db_part, int n_tiles, int C_out,
+                                                  int C_out_pad, float *__restrict__ db) {
+    __shared__ float red[4][65];
+    const int t = threadIdx.x, ol = t >> 6, sub = t & 63;
+    const int o = blockIdx.x * 4 + ol;
+    float s = 0.f;
+    if (o < C_out)
+        for (int k = sub; k < n_tiles; k += 64) s += db_part[(int64_t)k * C_out_pad + o];
+    red[ol][sub] = s;
+    __syncthreads();
+    if (sub == 0 && o < C_out) {
+        float acc = 0.f;
+        for (int k = 0; k < 64; ++k) acc += red[ol][k];
+        db[o] = acc;
     }
 }
 
@@ -372,7 +398,13 @@ BwLayout bw_layout(const Plan *p, int64_t N) {
     L.CB_out = L.C_out_pad / 32;
     const int tiles = L.tiles_i * L.tiles_o;
     const int cus = device_num_cus();
-    L.splits = std::max(1, std::min(cus / std::max(1, tiles), L.KT / 8));
+    // token splits: enough workgroups to stream the fragments (cus / tiles), at least 8 token steps
+    // each, and no more than balances a split's fragment reads (KT / S steps at a CU's ~90 GB/s)
+    // against the partial planes all splits write and the reduction reads back (S x the tile's
+    // output at ~3 TB/s for the chip): S ~ sqrt(KT * step bytes * 33 / tile bytes) (estimates)
+    const double step_bytes = (double)(C::BO + C::BI) * 16 * G * 2, out_bytes = (double)C::BO * C::BI * G * 4;
+    const int s_bal = std::max(1, (int)std::sqrt((double)L.KT * step_bytes * 33.0 / out_bytes));
+    L.splits = std::max(1, std::min({cus / std::max(1, tiles), L.KT / 8, s_bal}));
     auto al = [](size_t v) { return (v + 255) / 256 * 256; };
     L.off_x = 0;
     L.off_dy = al(L.off_x + (size_t)L.CB_in * L.KT * G * 1024);
@@ -402,9 +434,13 @@ hipError_t launch_mfma(const Plan *p, const void *x, const void *dy, float *dW, 
     const int grid = L.tiles_i * L.tiles_o * L.splits;
     hipLaunchKernelGGL(k_bw_gemm<G>, dim3(grid), dim3(512), 0, s, (const uint4 *)xf, (const uint4 *)dyf, part,
                        L.KT, L.tiles_i, L.splits, L.C_in_pad, L.C_out_pad);
-    const int64_t pairs = std::max<int64_t>((int64_t)p->C_out * p->C_in, p->C_out);
-    hipLaunchKernelGGL(k_bw_reduce<G>, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, (const float *)part,
-                       L.splits, p->C_out, p->C_in, L.C_out_pad, L.C_in_pad, dW, (const float *)dbp, L.ptiles, db);
+    const int64_t rgrid = (int64_t)p->C_out * (L.C_in_pad / 32);
+    if (rgrid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_bw_reduce<G>, dim3((unsigned)rgrid), dim3(256), 0, s, (const float *)part, L.splits,
+                       p->C_out, p->C_in, L.C_out_pad, L.C_in_pad, dW);
+    if (db)
+        hipLaunchKernelGGL(k_bw_dbsum, dim3((p->C_out + 3) / 4), dim3(256), 0, s, (const float *)dbp, L.ptiles,
+                           p->C_out, L.C_out_pad, db);
     return hipGetLastError();
 }
 
