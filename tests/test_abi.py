@@ -58,6 +58,9 @@ def test_prepare_argument_errors(lib):
     assert _prepare(lib, fake, 4, 8, 4, flags=0x10)[0] == eq.EQLIN_ERR_INVALID_ARG
     assert _prepare(lib, ctypes.c_void_p(0x10008), 4, 8, 4)[0] == eq.EQLIN_ERR_INVALID_ARG  # misaligned
     assert _prepare(lib, fake, 4, 12, 4, dtype=1)[0] == eq.EQLIN_ERR_UNSUPPORTED  # bf16, C_in % 8
+    # the backward weights need C_out % 8 == 0 in bf16 (C_out is their C_in)
+    assert _prepare(lib, fake, 12, 8, 4, dtype=1, flags=eq.EQLIN_PREPARE_BACKWARD)[0] == eq.EQLIN_ERR_UNSUPPORTED
+    assert "C_out" in lib.eqlin_last_error().decode()
     assert "C_in" in lib.eqlin_last_error().decode()
     assert _prepare(lib, fake, (1 << 18) + 1, 8, 4)[0] == eq.EQLIN_ERR_UNSUPPORTED  # C_out * G > 2^20
     assert _prepare(lib, fake, 8, (1 << 17) + 8, 8)[0] == eq.EQLIN_ERR_UNSUPPORTED  # C_in * G > 2^20
@@ -71,3 +74,9 @@ def test_forward_null_handle(lib):
     assert lib.eqlin_export_spectral_weights(None, None, None) == eq.EQLIN_ERR_INVALID_ARG
     n = lib.eqlin_describe(None, None, 0)
     assert n > 0
+
+
+def test_backward_null_handle(lib):
+    assert lib.eqlin_backward_data(None, None, None, 10, None) == eq.EQLIN_ERR_INVALID_ARG
+    assert lib.eqlin_backward_weights(None, None, None, None, None, 10, None, 0, None) == eq.EQLIN_ERR_INVALID_ARG
+    assert lib.eqlin_backward_weights_workspace(None, 10) == 0
