@@ -19,12 +19,20 @@ Fourier Transform" (explainer page, gist.science/es/paper/2607.21271):
   operator has forward and backward kernels), by the chain rule through the unrolled product:
   dx = E^T dy; dE = sum over tokens of dy x^T, folded back onto W along the circulant diagonals
   (dW[o, i, d] = sum_h dE[o*G+h, i*G+(h-d) mod G]); db[o] = sum over tokens and h of dy.
+* ``gelu``, ``mlp_block`` -- the transformer MLP block the layer is built into ("Resultados
+  Experimentales", network level: EQ-ViT / EQ-Swin), as EQ-Linear(C -> 4C), GELU, EQ-Linear(4C -> C).
+  The activation is the GELU the ViT-on-mobile page names ("El Efecto GELU"), in its exact form
+  x * Phi(x), Phi the standard normal CDF written with the error function (scipy's erf). Acting on
+  each value alone, it commutes with the cyclic shift of the group axis, so the block stays
+  equivariant.
 
 All are pinned in ``tests/test_oracle.py`` against things other than themselves (an independent
 Kronecker construction of the block-circulant matrix, numpy's FFT convolution theorem, closed forms
 for delta / constant / alternating inputs, equivariance, the G=1 plain linear layer; for the
 gradients: the adjoint identities <dy, y(x)> = <dx, x> and <dy, y(W)> = <dW, W> against the forward,
-central finite differences of a scalar loss, and the G=1 case where dW is the plain dy^T x).
+central finite differences of a scalar loss, and the G=1 case where dW is the plain dy^T x; for the
+block: the normal CDF's table values and its quadrature, GELU(x) - GELU(-x) = x, the G=1 plain MLP,
+equivariance, and the saturated cases where GELU is the identity or zero).
 """
 from __future__ import annotations
 
@@ -185,3 +193,20 @@ def backward_weights(x, dy, threads: int = 0):
     if rc != 0:
         raise RuntimeError(f"eqlin_oracle_backward_weights failed with code {rc}")
     return dW, db
+
+
+def gelu(v) -> np.ndarray:
+    """GELU(v) = v * Phi(v) = v/2 * (1 + erf(v / sqrt(2))), elementwise in fp64 (exact form, not the
+    tanh approximation)."""
+    from scipy.special import erf
+
+    v = _f64(v)
+    return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+
+
+def mlp_block(x, W1, b1, W2, b2, threads: int = 0) -> np.ndarray:
+    """y = EQ-Linear_2(GELU(EQ-Linear_1(x))): W1 [C_h, C, G], b1 [C_h], W2 [C, C_h, G], b2 [C]
+    (either bias may be None); x [N, C, G] -> y [N, C_out2, G], fp64 throughout (the hidden
+    activation is not rounded)."""
+    hidden = gelu(forward(x, W1, b1, threads))
+    return forward(hidden, W2, b2, threads)

@@ -276,3 +276,76 @@ def test_backward_empty_batch():
     assert oracle.backward_data(np.zeros((0, 3, 4)), W).shape == (0, 2, 4)
     dW, db = oracle.backward_weights(np.zeros((0, 2, 4)), np.zeros((0, 3, 4)))
     assert np.all(dW == 0) and np.all(db == 0)
+
+
+# ---- the MLP block (EQ-Linear(C -> 4C), GELU, EQ-Linear(4C -> C); "Resultados Experimentales",
+# network level) and its activation (the ViT-on-mobile page, "El Efecto GELU"). ----
+
+def _phi_quadrature(v):
+    """Standard normal CDF by composite Simpson quadrature of the density from 0 to v (independent of
+    erf): Phi(v) = 1/2 + int_0^v exp(-t^2/2) / sqrt(2 pi) dt."""
+    v = np.asarray(v, dtype=np.float64)
+    m = 4000  # even number of panels
+    t = np.linspace(0.0, 1.0, m + 1)
+    w = np.ones(m + 1)
+    w[1:-1:2], w[2:-1:2] = 4.0, 2.0
+    pts = v[..., None] * t
+    dens = np.exp(-0.5 * pts * pts) / np.sqrt(2.0 * np.pi)
+    return 0.5 + v * (dens @ w) / (3.0 * m)
+
+
+def test_gelu_table_values():
+    # Phi(1), Phi(2), Phi(-1) from a standard normal table (15+ digits); GELU(v) = v Phi(v).
+    g = oracle.gelu(np.array([0.0, 1.0, -1.0, 2.0]))
+    np.testing.assert_allclose(g, [0.0, 0.8413447460685429, -0.15865525393145707, 2 * 0.9772498680518208],
+                               rtol=1e-15, atol=0)
+
+
+def test_gelu_matches_quadrature_cdf():
+    v = np.linspace(-6.0, 6.0, 241)
+    np.testing.assert_allclose(oracle.gelu(v), v * _phi_quadrature(v), rtol=0, atol=1e-13)
+
+
+def test_gelu_odd_part_and_limits():
+    # Phi(v) + Phi(-v) = 1, so GELU(v) - GELU(-v) = v; GELU -> v for v >> 0 and -> 0 for v << 0.
+    v = _rand((1000,), 40) * 3
+    np.testing.assert_allclose(oracle.gelu(v) - oracle.gelu(-v), v, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(oracle.gelu(np.array([40.0, -40.0])), [40.0, -0.0])
+    # slope 1/2 at 0 (Phi(0) = 1/2)
+    assert abs(oracle.gelu(np.array([1e-8]))[0] / 1e-8 - 0.5) < 1e-8
+
+
+def test_mlp_block_g1_is_plain_mlp():
+    # G = 1: x W1^T + b1, GELU (quadrature CDF), then W2^T + b2, all by numpy's matmul.
+    N, C, H = 7, 5, 12
+    x, W1, b1 = _rand((N, C, 1), 41), _rand((H, C, 1), 42), _rand((H,), 43)
+    W2, b2 = _rand((C, H, 1), 44), _rand((C,), 45)
+    pre = x[:, :, 0] @ W1[:, :, 0].T + b1
+    ref = (pre * _phi_quadrature(pre)) @ W2[:, :, 0].T + b2
+    assert _rel(oracle.mlp_block(x, W1, b1, W2, b2)[:, :, 0], ref) <= 1e-12
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_mlp_block_equivariance(G):
+    x, W1, b1 = _rand((4, 3, G), 46), _rand((12, 3, G), 47), _rand((12,), 48)
+    W2, b2 = _rand((3, 12, G), 49), _rand((3,), 50)
+    y = oracle.mlp_block(x, W1, b1, W2, b2)
+    for s in range(1, G):
+        assert _rel(oracle.mlp_block(np.roll(x, s, axis=2), W1, b1, W2, b2), np.roll(y, s, axis=2)) <= 1e-12
+
+
+@pytest.mark.parametrize("G", [4, 8])
+def test_mlp_block_saturated_cases(G):
+    # A hidden bias of +60 puts every pre-activation where Phi is 1 in fp64, so the block is the
+    # product of the two unrolled matrices (order and biases pinned); -60 zeroes the hidden layer,
+    # leaving b2 broadcast over the group axis.
+    N, C, H = 5, 3, 12
+    x, W1 = _rand((N, C, G), 51) * 0.1, _rand((H, C, G), 52) * 0.1
+    W2, b2 = _rand((C, H, G), 53), _rand((C,), 54)
+    b1 = np.full(H, 60.0)
+    E1, E2 = _kron_block_circulant(W1), _kron_block_circulant(W2)
+    hid = x.reshape(N, C * G) @ E1.T + np.repeat(b1, G)
+    ref = (hid @ E2.T + np.repeat(b2, G)).reshape(N, C, G)
+    assert _rel(oracle.mlp_block(x, W1, b1, W2, b2), ref) <= 1e-13
+    y0 = oracle.mlp_block(x, W1, -b1, W2, b2)
+    np.testing.assert_allclose(y0, np.broadcast_to(b2[None, :, None], (N, C, G)), rtol=0, atol=1e-12)
