@@ -113,6 +113,56 @@ def cpu_baseline(w, x, W, b, budget_s: float = 12.0):
             "seconds": round(dt, 3)}
 
 
+def bench_block(torch, eq, rl, timer, dev, K: int, Wm: int, with_expanded: bool):
+    """Time the MLP block (layer 1 with GELU in its epilogue, then layer 2; two launches per step) on
+    its seeded inputs, its two layers alone, and the same block on the unrolled weights."""
+    from fourier_domain_linear_amd.workloads import BLOCK_WORKLOAD as bw, make_block_inputs
+
+    G, C, H, N, eb = bw.G, bw.C_in, bw.C_out, bw.N, bw.elem_bytes
+    log(f"[bench] block {bw.name}: G={G} C={C} hidden={H} N={N} {bw.dtype}")
+    x, W1, b1, W2, b2 = make_block_inputs(G, C, H, N, bw.dtype, seed=0)
+    set_bytes = N * (C + H + C) * G * eb
+    R = max(3, math.ceil((1 << 30) / set_bytes))
+    x0 = x.to(dev)
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    hs = [torch.empty((N, H, G), dtype=bw.torch_dtype, device=dev) for _ in range(R)]
+    ys = [torch.empty((N, C, G), dtype=bw.torch_dtype, device=dev) for _ in range(R)]
+    h1 = eq.prepare_weights(W1.to(dev), expanded=with_expanded)
+    h2 = eq.prepare_weights(W2.to(dev), expanded=with_expanded)
+    b1d, b2d = b1.to(dev), b2.to(dev)
+    torch.cuda.synchronize()
+    steps = {
+        "block": lambda i: eq.mlp_block(h1, b1d, h2, b2d, xs[i], hs[i], ys[i]),
+        "layer1_gelu": lambda i: eq.forward(h1, xs[i], b1d, hs[i], act="gelu"),
+        "layer1_plain": lambda i: eq.forward(h1, xs[i], b1d, hs[i]),
+        "layer2": lambda i: eq.forward(h2, hs[i], b2d, ys[i]),
+    }
+    if with_expanded:
+        steps["expanded_block"] = lambda i: eq.mlp_block(h1, b1d, h2, b2d, xs[i], hs[i], ys[i], expanded=True)
+    ms = {}
+    for name, fn in steps.items():
+        for i in range(Wm):
+            fn(i % R)
+        torch.cuda.synchronize()
+        ms[name] = timer(torch, fn, K, R)
+        log(f"[bench] block {name}: {ms[name] * 1e3:.2f} us/step")
+    F = rl.spectral_flops(N, C, H, G) + rl.spectral_flops(N, H, C, G)
+    Fd = rl.dense_flops(N, C, H, G) + rl.dense_flops(N, H, C, G)
+    t = ms["block"] / 1e3
+    res = {"workload": bw.name, "ms_per_step": round(ms["block"], 6), "tokens_per_s": N / t,
+           "useful_tflops": round(F / t / 1e12, 2), "effective_tflops": round(Fd / t / 1e12, 2),
+           "mfma_frac": round(F / t / 1e12 / rl.PEAK_BF16_TFLOPS, 4),
+           "layers_ms": {k: round(v, 6) for k, v in ms.items() if k != "block" and k != "expanded_block"},
+           "gelu_epilogue_us": round((ms["layer1_gelu"] - ms["layer1_plain"]) * 1e3, 2),
+           "kernels": [h1.describe(), h2.describe()]}
+    if with_expanded:
+        te = ms["expanded_block"] / 1e3
+        res["expanded_block"] = {"ms_per_step": round(ms["expanded_block"], 6), "tokens_per_s": N / te,
+                                 "effective_tflops": round(Fd / te / 1e12, 2)}
+        res["speedup_vs_expanded"] = round(ms["expanded_block"] / ms["block"], 3)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +175,9 @@ def main():
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--backward", action="store_true",
                     help="also time eqlin_backward_data and eqlin_backward_weights (reported under 'backward')")
+    ap.add_argument("--block", action="store_true",
+                    help="also time the transformer MLP block EQ-Linear(C->4C), GELU, EQ-Linear(4C->C) at the "
+                         "p4 192-channel shape, spectral and expanded (reported under 'block')")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (the counter calibration for traffic)")
     args = ap.parse_args()
@@ -253,6 +306,8 @@ def main():
             log(f"[bench] backward {name}: {ms_b * 1e3:.2f} us/step")
         res["kernels"] = h.describe().split("|")[3:]
         extra["backward"] = res
+    if args.block:
+        extra["block"] = bench_block(torch, eq, rl, timer, dev, K, Wm, not args.no_expanded)
     extra["effective_tflops"] = round(rl.dense_flops(w.N, w.C_in, w.C_out, w.G) / t / 1e12, 2)
     extra["useful_tflops"] = round(F / t / 1e12, 2)
 

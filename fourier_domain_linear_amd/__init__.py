@@ -10,6 +10,8 @@ is missing, every call raises.
     y2 = eq.forward_expanded(h, x, b)         # needs prepare_weights(W, expanded=True)
     dx = eq.backward_data(h, dy)              # needs prepare_weights(W, backward=True)
     dW, db = eq.backward_weights(h, x, dy)    # float32 gradients of W and b
+    z = eq.forward(h, x, b, act="gelu")       # GELU(y), applied in the kernel's epilogue
+    y = eq.mlp_block(h1, b1, h2, b2, x)       # EQ-Linear(C -> 4C), GELU, EQ-Linear(4C -> C)
 
 Method: "Flash EQ-Linear: Accelerating Equivariant Linear Layers via Group-wise Discrete Fourier
 Transform" (explainer page, gist.science/es/paper/2607.21271).
@@ -33,10 +35,14 @@ EQLIN_F32 = 0
 EQLIN_BF16 = 1
 EQLIN_PREPARE_EXPANDED = 1
 EQLIN_PREPARE_BACKWARD = 2
+EQLIN_ACT_NONE = 0
+EQLIN_ACT_GELU = 1
+_ACTS = {None: EQLIN_ACT_NONE, "none": EQLIN_ACT_NONE, "gelu": EQLIN_ACT_GELU}
 
 # Every symbol include/eqlin.h declares.
 EXPORTED = (
-    "eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_backward_data",
+    "eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_forward_act",
+    "eqlin_forward_expanded_act", "eqlin_backward_data",
     "eqlin_backward_weights_workspace", "eqlin_backward_weights", "eqlin_destroy",
     "eqlin_export_spectral_weights", "eqlin_export_expanded_weight", "eqlin_describe",
     "eqlin_status_string", "eqlin_last_error", "eqlin_version",
@@ -65,6 +71,8 @@ def load_library() -> ctypes.CDLL:
     lib.eqlin_prepare_weights.argtypes = [vp, i32, i32, i32, i32, u32, vp, ctypes.POINTER(vp)]
     lib.eqlin_forward.argtypes = [vp, vp, vp, vp, i64, vp]
     lib.eqlin_forward_expanded.argtypes = [vp, vp, vp, vp, i64, vp]
+    lib.eqlin_forward_act.argtypes = [vp, vp, vp, vp, i64, i32, vp]
+    lib.eqlin_forward_expanded_act.argtypes = [vp, vp, vp, vp, i64, i32, vp]
     lib.eqlin_backward_data.argtypes = [vp, vp, vp, i64, vp]
     lib.eqlin_backward_weights_workspace.argtypes = [vp, i64]
     lib.eqlin_backward_weights_workspace.restype = ctypes.c_size_t
@@ -155,7 +163,14 @@ def prepare_weights(W: torch.Tensor, expanded: bool = False, backward: bool = Fa
     return Handle(out.value, C_out, C_in, G, W.dtype, W.device, expanded, backward)
 
 
-def _forward(fn, what: str, h: Handle, x: torch.Tensor, b: torch.Tensor | None, y: torch.Tensor | None):
+def _act_code(act) -> int:
+    if act not in _ACTS:
+        raise ValueError(f"act must be one of {sorted(k for k in _ACTS if k)} or None, got {act!r}")
+    return _ACTS[act]
+
+
+def _forward(fn, what: str, h: Handle, x: torch.Tensor, b: torch.Tensor | None, y: torch.Tensor | None,
+             act: int | None = None):
     _need_cuda(x, "x")
     if x.dtype != h.dtype:
         raise TypeError(f"x dtype {x.dtype} != handle dtype {h.dtype}")
@@ -174,23 +189,45 @@ def _forward(fn, what: str, h: Handle, x: torch.Tensor, b: torch.Tensor | None, 
         if b.dtype != h.dtype or tuple(b.shape) != (h.C_out,):
             raise ValueError(f"b must be [{h.C_out}] of {h.dtype}")
         bp = ctypes.c_void_p(b.data_ptr())
+    args = (ctypes.c_void_p(h.ptr), ctypes.c_void_p(x.data_ptr()), bp, ctypes.c_void_p(y.data_ptr()), N)
     with torch.cuda.device(x.device):
-        st = fn(ctypes.c_void_p(h.ptr), ctypes.c_void_p(x.data_ptr()), bp, ctypes.c_void_p(y.data_ptr()), N,
-                _stream(x))
+        st = fn(*args, _stream(x)) if act is None else fn(*args, act, _stream(x))
     _check(st, what)
     return y
 
 
-def forward(h: Handle, x: torch.Tensor, b: torch.Tensor | None = None, y: torch.Tensor | None = None):
-    """eqlin_forward: y[n, o, h] = b[o] + sum_{i,g} W[o, i, (h-g) mod G] x[n, i, g] (spectral kernel)."""
-    return _forward(load_library().eqlin_forward, "eqlin_forward", h, x, b, y)
+def forward(h: Handle, x: torch.Tensor, b: torch.Tensor | None = None, y: torch.Tensor | None = None,
+            act: str | None = None):
+    """eqlin_forward: y[n, o, h] = b[o] + sum_{i,g} W[o, i, (h-g) mod G] x[n, i, g] (spectral kernel).
+    act="gelu" calls eqlin_forward_act instead, which applies GELU to y in the kernel's epilogue."""
+    lib = load_library()
+    if _act_code(act) == EQLIN_ACT_NONE:
+        return _forward(lib.eqlin_forward, "eqlin_forward", h, x, b, y)
+    return _forward(lib.eqlin_forward_act, "eqlin_forward_act", h, x, b, y, _act_code(act))
 
 
-def forward_expanded(h: Handle, x: torch.Tensor, b: torch.Tensor | None = None, y: torch.Tensor | None = None):
-    """eqlin_forward_expanded: the same layer as one dense product with the unrolled weight."""
+def forward_expanded(h: Handle, x: torch.Tensor, b: torch.Tensor | None = None, y: torch.Tensor | None = None,
+                     act: str | None = None):
+    """eqlin_forward_expanded: the same layer as one dense product with the unrolled weight (with
+    act="gelu": eqlin_forward_expanded_act)."""
     if not h.expanded:
         raise ValueError("handle was prepared without expanded=True")
-    return _forward(load_library().eqlin_forward_expanded, "eqlin_forward_expanded", h, x, b, y)
+    lib = load_library()
+    if _act_code(act) == EQLIN_ACT_NONE:
+        return _forward(lib.eqlin_forward_expanded, "eqlin_forward_expanded", h, x, b, y)
+    return _forward(lib.eqlin_forward_expanded_act, "eqlin_forward_expanded_act", h, x, b, y, _act_code(act))
+
+
+def mlp_block(h1: Handle, b1: torch.Tensor | None, h2: Handle, b2: torch.Tensor | None, x: torch.Tensor,
+              hidden: torch.Tensor | None = None, y: torch.Tensor | None = None, expanded: bool = False):
+    """The transformer MLP block as two library calls on the current stream: hidden = GELU(layer 1 (x))
+    with GELU in layer 1's epilogue, then y = layer 2 (hidden). h1: [C_h, C, G] weights, h2: [C, C_h, G].
+    expanded=True runs both layers as dense products with the unrolled weights (the comparator)."""
+    if h1.C_out != h2.C_in or h1.G != h2.G or h1.dtype != h2.dtype:
+        raise ValueError("layer 2 must take layer 1's outputs (C_in, G and dtype)")
+    fwd = forward_expanded if expanded else forward
+    hidden = fwd(h1, x, b1, hidden, act="gelu")
+    return fwd(h2, hidden, b2, y)
 
 
 def backward_data(h: Handle, dy: torch.Tensor, dx: torch.Tensor | None = None) -> torch.Tensor:

@@ -214,32 +214,46 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
     return EQLIN_OK;
 }
 
-static eqlin_status_t run_forward(const Plan *h, const void *x, const void *b, void *y, int64_t N,
+static eqlin_status_t run_forward(const Plan *h, const void *x, const void *b, void *y, int64_t N, int act,
                                   eqlin_stream_t stream, const char *what) {
     (void)hipGetLastError();  // drop a stale error left by someone else's call on this thread
-    hipError_t e = h->fwd.launch(h, x, b, y, N, (hipStream_t)stream);
+    hipError_t e = h->fwd.launch(h, x, b, y, N, act, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, what);
     return EQLIN_OK;
 }
 
-eqlin_status_t eqlin_forward(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N,
-                             eqlin_stream_t stream) {
+static bool valid_act(int act) { return act == EQLIN_ACT_NONE || act == EQLIN_ACT_GELU; }
+
+eqlin_status_t eqlin_forward_act(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N, int act,
+                                 eqlin_stream_t stream) {
     g_err[0] = 0;
     if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
+    if (!valid_act(act)) return fail(EQLIN_ERR_INVALID_ARG, "unknown activation %d", act);
     eqlin_status_t st = check_forward_args(h, x, b, y, N, h->C_in, h->C_out, h->G);
     if (st != EQLIN_OK || N == 0) return st;
-    return run_forward(h, x, b, y, N, stream, "eqlin_forward launch");
+    return run_forward(h, x, b, y, N, act, stream, "eqlin_forward launch");
 }
 
-eqlin_status_t eqlin_forward_expanded(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N,
-                                      eqlin_stream_t stream) {
+eqlin_status_t eqlin_forward(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N,
+                             eqlin_stream_t stream) {
+    return eqlin_forward_act(h, x, b, y, N, EQLIN_ACT_NONE, stream);
+}
+
+eqlin_status_t eqlin_forward_expanded_act(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N,
+                                          int act, eqlin_stream_t stream) {
     g_err[0] = 0;
     if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
     if (!h->expanded)
         return fail(EQLIN_ERR_INVALID_ARG, "handle was prepared without EQLIN_PREPARE_EXPANDED");
+    if (!valid_act(act)) return fail(EQLIN_ERR_INVALID_ARG, "unknown activation %d", act);
     eqlin_status_t st = check_forward_args(h, x, b, y, N, h->C_in, h->C_out, h->G);
     if (st != EQLIN_OK || N == 0) return st;
-    return run_forward(h->expanded, x, b, y, N, stream, "eqlin_forward_expanded launch");
+    return run_forward(h->expanded, x, b, y, N, act, stream, "eqlin_forward_expanded launch");
+}
+
+eqlin_status_t eqlin_forward_expanded(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N,
+                                      eqlin_stream_t stream) {
+    return eqlin_forward_expanded_act(h, x, b, y, N, EQLIN_ACT_NONE, stream);
 }
 
 eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, int64_t N, eqlin_stream_t stream) {
@@ -248,7 +262,7 @@ eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, i
     if (!h->backward) return fail(EQLIN_ERR_INVALID_ARG, "handle was prepared without EQLIN_PREPARE_BACKWARD");
     eqlin_status_t st = check_forward_args(h, dy, nullptr, dx, N, h->C_out, h->C_in, h->G);
     if (st != EQLIN_OK || N == 0) return st;
-    return run_forward(h->backward, dy, nullptr, dx, N, stream, "eqlin_backward_data launch");
+    return run_forward(h->backward, dy, nullptr, dx, N, EQLIN_ACT_NONE, stream, "eqlin_backward_data launch");
 }
 
 size_t eqlin_backward_weights_workspace(eqlin_handle_t h, int64_t N) {

@@ -21,7 +21,8 @@ enum KernelKind {
 
 struct Plan;
 
-typedef hipError_t (*LaunchFn)(const Plan *p, const void *x, const void *b, void *y, int64_t N,
+// act: an eqlin_act_t applied to every output value in the epilogue
+typedef hipError_t (*LaunchFn)(const Plan *p, const void *x, const void *b, void *y, int64_t N, int act,
                                hipStream_t s);
 
 // Kernel choice for one plan. The weight layout (padding of C_in and C_out) depends on it.

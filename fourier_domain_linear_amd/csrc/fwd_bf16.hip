@@ -33,6 +33,7 @@
 
 #include <algorithm>
 
+#include "act.h"
 #include "device_common.h"
 #include "eqlin_internal.h"
 
@@ -103,31 +104,8 @@ __device__ __forceinline__ void spectral_mfma_wx(const uint4 (&w)[G], const uint
     }
 }
 
-// Inverse DFT of the 4 consecutive outputs v = 0..3 a lane holds (bias already in plane 0), then
-// one contiguous store of 4*G bf16 at dst (16-byte aligned when G >= 2).
-template <int G>
-__device__ __forceinline__ void store_quad(const f32x4 (&acc)[G], uint16_t *__restrict__ dst) {
-    float out[4 * G];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        float Y[G];
-#pragma unroll
-        for (int p = 0; p < G; ++p) Y[p] = acc[p][v];
-        inverse_planes<G>(Y, out + v * G);
-    }
-    if constexpr (G == 1) {
-        uint2 w;
-        w.x = pack_bf16x2(out[0], out[1]);
-        w.y = pack_bf16x2(out[2], out[3]);
-        *reinterpret_cast<uint2 *>(dst) = w;
-    } else {
-#pragma unroll
-        for (int q = 0; q < G / 2; ++q) reinterpret_cast<uint4 *>(dst)[q] = pack_bf16x8(out + 8 * q);
-    }
-}
-
 // Element-wise tail store for a partial output block or the last token rows: output o0 + v of token n.
-template <int G>
+template <int G, bool GELU>
 __device__ __forceinline__ void store_quad_masked(const f32x4 (&acc)[G], uint16_t *__restrict__ y,
                                                   int64_t n, int64_t N, int o0, int C_out) {
     if (n >= N) return;
@@ -138,6 +116,7 @@ __device__ __forceinline__ void store_quad_masked(const f32x4 (&acc)[G], uint16_
 #pragma unroll
         for (int p = 0; p < G; ++p) Y[p] = acc[p][v];
         inverse_planes<G>(Y, out);
+        apply_act<GELU>(out);
         uint16_t *dst = y + (n * C_out + o0 + v) * G;
 #pragma unroll
         for (int h = 0; h < G; ++h) dst[h] = pack_bf16(out[h]);
@@ -217,7 +196,7 @@ __device__ __forceinline__ void load_x_raw(const uint4 *__restrict__ x4, int64_t
         }
 }
 
-template <int G, int KS>
+template <int G, int KS, bool GELU>
 __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__restrict__ x4,
                                                               const uint4 *__restrict__ wfrag,
                                                               const uint16_t *__restrict__ bias,
@@ -344,20 +323,17 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
                 }
             }
             if (!vec_rows) {
-                store_quad_masked<G>(acc, y, nrow0 + (lane & 15), N, (nb0 + nb) * 16 + 4 * g, C_out);
+                store_quad_masked<G, GELU>(acc, y, nrow0 + (lane & 15), N, (nb0 + nb) * 16 + 4 * g, C_out);
                 continue;
             }
-            // inverse DFT -> this lane's 4 outputs x G (8G bytes) -> staging row lane%16
-            float out[4 * G];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float Y[G];
-#pragma unroll
-                for (int p = 0; p < G; ++p) Y[p] = acc[p][v];
-                inverse_planes<G>(Y, out + v * G);
-            }
+            // inverse DFT (+ activation) -> this lane's 4 outputs x G (8G bytes) -> staging row lane%16,
+            // one 16-byte piece (8 / G outputs) at a time to keep few values live
             const int ub = nb % SG::UO;  // block within the store unit
             if constexpr (G == 1) {
+                float out[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) out[v] = acc[0][v];
+                apply_act<GELU>(out);
                 uint2 w;
                 w.x = pack_bf16x2(out[0], out[1]);
                 w.y = pack_bf16x2(out[2], out[3]);
@@ -365,9 +341,20 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
                 const int piece = ub * 2 + (g >> 1);
                 reinterpret_cast<uint2 *>(scratch + swz<SG::PPR>(lane & 15, piece))[g & 1] = w;
             } else {
+                constexpr int VP = 8 / G;  // outputs per piece
 #pragma unroll
-                for (int k = 0; k < G / 2; ++k)
-                    scratch[swz<SG::PPR>(lane & 15, ub * 2 * G + g * (G / 2) + k)] = pack_bf16x8(out + 8 * k);
+                for (int k = 0; k < G / 2; ++k) {
+                    float out[8];
+#pragma unroll
+                    for (int vv = 0; vv < VP; ++vv) {
+                        float Y[G];
+#pragma unroll
+                        for (int p = 0; p < G; ++p) Y[p] = acc[p][k * VP + vv];
+                        inverse_planes<G>(Y, out + vv * G);
+                    }
+                    apply_act<GELU>(out);
+                    scratch[swz<SG::PPR>(lane & 15, ub * 2 * G + g * (G / 2) + k)] = pack_bf16x8(out);
+                }
             }
             if (ub == SG::UO - 1 || nb == nb_end - 1) {
                 // whole 16-byte pieces of the unit's rows, full lines per instruction, non-temporal
@@ -419,7 +406,7 @@ int device_num_cus() {
 }
 
 template <int G, int KS>
-static hipError_t launch_stream(const Plan *p, const void *x, const void *b, void *y, int64_t N,
+static hipError_t launch_stream(const Plan *p, const void *x, const void *b, void *y, int64_t N, int act,
                                 hipStream_t s) {
     const size_t lds = p->fwd.lds_bytes;
     const int64_t blocks = (N + 15) / 16;
@@ -427,15 +414,20 @@ static hipError_t launch_stream(const Plan *p, const void *x, const void *b, voi
     // one workgroup per CU in total (over all C_out tiles), at least one row block each
     int64_t wg = std::max<int64_t>(1, p->fwd.num_cus / tiles);
     wg = std::min<int64_t>(wg, blocks);
-    hipLaunchKernelGGL((k_stream<G, KS>), dim3((unsigned)wg, (unsigned)tiles), dim3(kStreamWaves * 64), lds, s,
-                       (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
-                       (uint16_t *)y, N, p->C_in, p->C_out, p->fwd.nb_tile);
+    const dim3 grid((unsigned)wg, (unsigned)tiles), block(kStreamWaves * 64);
+    if (act == EQLIN_ACT_GELU)
+        hipLaunchKernelGGL((k_stream<G, KS, true>), grid, block, lds, s, (const uint4 *)x, (const uint4 *)p->planes,
+                           (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, p->fwd.nb_tile);
+    else
+        hipLaunchKernelGGL((k_stream<G, KS, false>), grid, block, lds, s, (const uint4 *)x, (const uint4 *)p->planes,
+                           (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, p->fwd.nb_tile);
     return hipGetLastError();
 }
 
 template <int G, int KS>
 static hipError_t init_stream(size_t lds) {
-    return set_lds_limit((const void *)k_stream<G, KS>, lds);
+    const hipError_t e = set_lds_limit((const void *)k_stream<G, KS, false>, lds);
+    return e != hipSuccess ? e : set_lds_limit((const void *)k_stream<G, KS, true>, lds);
 }
 
 struct StreamEntry {

@@ -37,6 +37,7 @@
 
 #include <algorithm>
 
+#include "act.h"
 #include "device_common.h"
 #include "eqlin_internal.h"
 
@@ -169,7 +170,7 @@ struct BigCfg {
 // Persistent: each workgroup keeps output tile ot (its weights, bias and L2 set) and walks the token
 // tiles tt0, tt0 + tstep, ... (block_tile; tstep = gridDim.x / tiles_o). The load pipeline runs on
 // across tile boundaries, and a tile's outputs are stored while the next tile computes.
-template <int G, int WA, int WB, int OW, int TW, bool VEC>
+template <int G, int WA, int WB, int OW, int TW, bool VEC, bool GELU>
 __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ x4,
                                                       const uint4 *__restrict__ wfrag,
                                                       const uint16_t *__restrict__ bias, int bias_shift,
@@ -453,6 +454,7 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
 #pragma unroll
                             for (int p = 0; p < G; ++p) Y[p] = acc[a0 + ai][b][p][v];
                             inverse_planes<G>(Y, out);
+                            apply_act<GELU>(out);
 #pragma unroll
                             for (int g = 0; g < G; ++g) y[(n * C_out + o) * G + g] = pack_bf16(out[g]);
                         }
@@ -471,6 +473,7 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                             for (int p = 0; p < G; ++p) Y[p] = acc[a0 + ai][b][p][4 * vq + v];
                             inverse_planes<G>(Y, out + v * G);
                         }
+                        apply_act<GELU>(out);
                         const int ol = ai * 32 + 8 * vq + 4 * h_e;  // first of the 4 outputs in the unit row
                         if constexpr (G == 1) {
                             uint2 w;
@@ -537,6 +540,7 @@ struct P8Cfg {
     static_assert(HP * 16 * 64 * 4 <= STG * 16, "a wave's staging holds the four planes it hands over");
 };
 
+template <bool GELU>
 __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, const uint4 *__restrict__ wfrag,
                                                   const uint16_t *__restrict__ bias, int bias_shift,
                                                   uint16_t *__restrict__ y, int64_t N, int C_in, int C_out,
@@ -753,6 +757,7 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
                     for (int p = 0; p < G; ++p) Y[p] = plane(p, 4 * vq + v);
                     inverse_planes<G>(Y, out + v * G);
                 }
+                apply_act<GELU>(out);
                 const int ol = 8 * vq + 4 * h_e;  // first of the 4 outputs in the staged row
 #pragma unroll
                 for (int kq = 0; kq < G / 2; ++kq) {
@@ -771,7 +776,8 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
         run(IC<1>{});
 }
 
-static hipError_t launch_p8(const Plan *p, const void *x, const void *b, void *y, int64_t N, hipStream_t s) {
+static hipError_t launch_p8(const Plan *p, const void *x, const void *b, void *y, int64_t N, int act,
+                            hipStream_t s) {
     using C = P8Cfg;
     const int64_t tiles_t = (N + C::BT - 1) / C::BT;
     const int tiles_o = p->NB_total / (C::BO / 32);
@@ -781,17 +787,19 @@ static hipError_t launch_p8(const Plan *p, const void *x, const void *b, void *y
     per_o = std::min<int64_t>(per_o, tiles_t);
     const int64_t grid = per_o * tiles_o;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_p8, dim3((unsigned)grid), dim3(C::NT), 0, s, (const uint4 *)x,
-                       (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in,
-                       p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o,
-                       xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * C::G * 2));
+    const int xg = xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * C::G * 2);
+    auto kern = act == EQLIN_ACT_GELU ? k_p8<true> : k_p8<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), 0, s, (const uint4 *)x, (const uint4 *)p->planes,
+                       (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS,
+                       (int)tiles_t, tiles_o, xg);
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------------
 
 template <int G, int WA, int WB, int OW, int TW>
-static hipError_t launch_big(const Plan *p, const void *x, const void *b, void *y, int64_t N, hipStream_t s) {
+static hipError_t launch_big(const Plan *p, const void *x, const void *b, void *y, int64_t N, int act,
+                             hipStream_t s) {
     using C = BigCfg<G, WA, WB, OW, TW>;
     const int64_t tiles_t = (N + C::BT - 1) / C::BT;
     const int tiles_o = p->NB_total / (C::BO / 32);
@@ -804,14 +812,12 @@ static hipError_t launch_big(const Plan *p, const void *x, const void *b, void *
     const int64_t grid = per_o * tiles_o;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     const int xg = xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * G * 2);
-    if ((p->C_out * G) % 8 == 0)
-        hipLaunchKernelGGL((k_big<G, WA, WB, OW, TW, true>), dim3((unsigned)grid), dim3(C::NT), 0, s,
-                           (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
-                           (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o, xg);
-    else
-        hipLaunchKernelGGL((k_big<G, WA, WB, OW, TW, false>), dim3((unsigned)grid), dim3(C::NT), 0, s,
-                           (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b, p->bias_shift,
-                           (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS, (int)tiles_t, tiles_o, xg);
+    const bool vec = (p->C_out * G) % 8 == 0, gelu = act == EQLIN_ACT_GELU;
+    auto kern = vec ? (gelu ? k_big<G, WA, WB, OW, TW, true, true> : k_big<G, WA, WB, OW, TW, true, false>)
+                    : (gelu ? k_big<G, WA, WB, OW, TW, false, true> : k_big<G, WA, WB, OW, TW, false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), 0, s, (const uint4 *)x, (const uint4 *)p->planes,
+                       (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS,
+                       (int)tiles_t, tiles_o, xg);
     return hipGetLastError();
 }
 

@@ -9,6 +9,7 @@
 // o0 + t%8 + 8j. K steps of 16 channels through LDS (rows padded to 17 floats: no bank conflicts).
 #include <stdio.h>
 
+#include "act.h"
 #include "device_common.h"
 #include "eqlin_internal.h"
 
@@ -16,7 +17,7 @@ namespace eqlin {
 
 constexpr int F_TM = 32, F_TN = 64, F_KC = 16, F_PAD = F_KC + 1;
 
-template <int G>
+template <int G, bool GELU>
 __global__ __launch_bounds__(256) void k_fwd_f32(const float *__restrict__ x,
                                                  const float *__restrict__ planes,
                                                  const float *__restrict__ bias, int bias_shift,
@@ -94,17 +95,20 @@ __global__ __launch_bounds__(256) void k_fwd_f32(const float *__restrict__ x,
         float out[G];
         inverse_planes<G>(acc[j], out);
 #pragma unroll
-        for (int h = 0; h < G; ++h) y[(n * C_out + o) * G + h] = out[h] + bo;
+        for (int h = 0; h < G; ++h) out[h] += bo;
+        apply_act<GELU>(out);
+#pragma unroll
+        for (int h = 0; h < G; ++h) y[(n * C_out + o) * G + h] = out[h];
     }
 }
 
 template <int G>
-static hipError_t launch_f32(const Plan *p, const void *x, const void *b, void *y, int64_t N,
+static hipError_t launch_f32(const Plan *p, const void *x, const void *b, void *y, int64_t N, int act,
                              hipStream_t s) {
     const dim3 grid((unsigned)((N + F_TM - 1) / F_TM), (unsigned)((p->C_out + F_TN - 1) / F_TN));
-    hipLaunchKernelGGL(k_fwd_f32<G>, grid, dim3(256), 0, s, (const float *)x,
-                       (const float *)p->planes, (const float *)b, p->bias_shift, (float *)y, N,
-                       p->C_in, p->C_out);
+    auto kern = act == EQLIN_ACT_GELU ? k_fwd_f32<G, true> : k_fwd_f32<G, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const float *)x, (const float *)p->planes,
+                       (const float *)b, p->bias_shift, (float *)y, N, p->C_in, p->C_out);
     return hipGetLastError();
 }
 

@@ -80,3 +80,18 @@ def make_grad(G: int, C_out: int, N: int, dtype: str = "bf16", seed: int = 0):
 def workload_inputs(w: Workload, seed: int = 0, N: int | None = None):
     """Inputs of workload ``w`` (optionally with a different token count N)."""
     return make_inputs(w.G, w.C_in, w.C_out, w.N if N is None else N, w.dtype, seed)
+
+
+# The MLP block of a transformer stage (EQ-Linear(C -> 4C), GELU, EQ-Linear(4C -> C); the networks of
+# "A Nivel de Red") at the p4 MLP-expansion shape: its first layer is the p4_c192x768 workload.
+BLOCK_WORKLOAD = Workload("p4_mlp_c192x768x192_n12544_bf16", G=4, C_in=192, C_out=768, N=16 * 28 * 28,
+                          dtype="bf16")
+
+
+def make_block_inputs(G: int, C: int, C_h: int, N: int, dtype: str = "bf16", seed: int = 0):
+    """CPU tensors (x[N, C, G], W1[C_h, C, G], b1[C_h], W2[C, C_h, G], b2[C]) for the MLP block:
+    x, W1, b1 are make_inputs(G, C, C_h, N, dtype, seed); W2, b2 come from
+    make_inputs(G, C_h, C, 0, dtype, seed + 104729) (so W2 ~ N(0, 1/(C_h*G)), b2 ~ N(0, 0.01))."""
+    x, W1, b1 = make_inputs(G, C, C_h, N, dtype, seed)
+    _, W2, b2 = make_inputs(G, C_h, C, 0, dtype, seed + 104729)
+    return x, W1, b1, W2, b2

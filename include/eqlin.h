@@ -62,6 +62,13 @@ typedef enum {
 
 typedef enum { EQLIN_F32 = 0, EQLIN_BF16 = 1 } eqlin_dtype_t;
 
+/* Element-wise activation applied to the layer's output (after the bias, before the store's single
+ * rounding). EQLIN_ACT_GELU is GELU in its exact form, y * Phi(y) = y/2 (1 + erf(y / sqrt 2)): the
+ * activation between the two EQ-Linear layers of a transformer MLP block (EQ-ViT / EQ-Swin,
+ * "Resultados Experimentales", network level; GELU as the ViT-on-mobile page names it, "El Efecto
+ * GELU"). Acting on each value alone, it keeps the layer equivariant. */
+typedef enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 } eqlin_act_t;
+
 /* flags for eqlin_prepare_weights */
 #define EQLIN_PREPARE_EXPANDED 1u /* also build the unrolled weight for eqlin_forward_expanded */
 #define EQLIN_PREPARE_BACKWARD 2u /* also build the data-gradient weights for eqlin_backward_data */
@@ -111,6 +118,18 @@ eqlin_status_t eqlin_forward(eqlin_handle_t h, const void *x, const void *b, voi
  */
 eqlin_status_t eqlin_forward_expanded(eqlin_handle_t h, const void *x, const void *b, void *y,
                                       int64_t N, eqlin_stream_t stream);
+
+/*
+ * eqlin_forward_act, eqlin_forward_expanded_act -- eqlin_forward and eqlin_forward_expanded with
+ * `act` applied to every output value in the kernel's epilogue (no extra pass over y):
+ *     y[n, o, h] = act(b[o] + sum_{i, g} W[o, i, (h - g) mod G] * x[n, i, g]).
+ * act is an eqlin_act_t (else EQLIN_ERR_INVALID_ARG); EQLIN_ACT_NONE is eqlin_forward itself. Same
+ * arguments, rules and handle requirements as the entry points they extend.
+ */
+eqlin_status_t eqlin_forward_act(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N, int act,
+                                 eqlin_stream_t stream);
+eqlin_status_t eqlin_forward_expanded_act(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N,
+                                          int act, eqlin_stream_t stream);
 
 /*
  * eqlin_backward_data -- the data gradient of the layer ("Implementación": the operator has forward

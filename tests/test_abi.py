@@ -70,6 +70,9 @@ def test_prepare_argument_errors(lib):
 def test_forward_null_handle(lib):
     assert lib.eqlin_forward(None, None, None, None, 10, None) == eq.EQLIN_ERR_INVALID_ARG
     assert lib.eqlin_forward_expanded(None, None, None, None, 10, None) == eq.EQLIN_ERR_INVALID_ARG
+    assert lib.eqlin_forward_act(None, None, None, None, 10, eq.EQLIN_ACT_GELU, None) == eq.EQLIN_ERR_INVALID_ARG
+    assert lib.eqlin_forward_expanded_act(None, None, None, None, 10, eq.EQLIN_ACT_GELU, None) == \
+        eq.EQLIN_ERR_INVALID_ARG
     assert lib.eqlin_destroy(None) == eq.EQLIN_OK
     assert lib.eqlin_export_spectral_weights(None, None, None) == eq.EQLIN_ERR_INVALID_ARG
     n = lib.eqlin_describe(None, None, 0)
