@@ -63,6 +63,28 @@ def test_forward_gelu(dtype, G, C_in, C_out, N, expanded, cuda_device):
            f"gelu {dtype} G={G} {C_in}->{C_out} N={N} {'expanded' if expanded else 'spectral'} [{h.describe()}]")
 
 
+@pytest.mark.parametrize("dtype,G", [("f32", 4), ("bf16", 4), ("bf16", 8)])
+def test_forward_gelu_wide_range(dtype, G, cuda_device):
+    # outputs spread over about +-100: the far tails (GELU -> 0 for v << 0, -> v for v >> 0) and the
+    # transition, all against the oracle's erf
+    x, W, b = make_inputs(G, 64, 64, 200, dtype, seed=9)
+    x = (x.float() * 25).to(x.dtype)
+    h = eq.prepare_weights(W.to(cuda_device))
+    y = eq.forward(h, x.to(cuda_device), b.to(cuda_device), act="gelu")
+    torch.cuda.synchronize()
+    pre = oracle.forward(x, W, b)
+    assert pre.max() > 40 and pre.min() < -40
+    ref = oracle.gelu(pre)
+    if dtype == "bf16":  # the bar's max-abs term is for unit-scale outputs: scale it with the output
+        yv = y.to("cpu", torch.float64).numpy()
+        rel = np.linalg.norm(yv - ref) / np.linalg.norm(ref)
+        assert rel <= REL_BF16 and np.max(np.abs(yv - ref)) <= MAX_BF16 * np.abs(pre).max() / 3, rel
+        neg = pre < -10  # deep negative tail: exactly representable tiny values, no sign flips
+        assert np.all(np.abs(yv[neg]) <= 1e-6)
+    else:
+        _check(y, ref, dtype, f"gelu wide range {dtype} G={G}")
+
+
 def test_forward_gelu_no_bias_and_plain_unchanged(cuda_device):
     # act = none through eqlin_forward_act is eqlin_forward, bit for bit (the same kernel); GELU with
     # no bias against the oracle.
