@@ -25,6 +25,8 @@ Fourier Transform" (explainer page, gist.science/es/paper/2607.21271):
   x * Phi(x), Phi the standard normal CDF written with the error function (scipy's erf). Acting on
   each value alone, it commutes with the cyclic shift of the group axis, so the block stays
   equivariant.
+* ``dihedral`` (submodule) -- the same layer over the dihedral group D4 (reflections added to the
+  p4 rotations), the generalisation the pages name as future work; see its docstring.
 
 All are pinned in ``tests/test_oracle.py`` against things other than themselves (an independent
 Kronecker construction of the block-circulant matrix, numpy's FFT convolution theorem, closed forms
@@ -41,6 +43,8 @@ import os
 import subprocess
 
 import numpy as np
+
+from . import dihedral  # noqa: F401  (oracle.dihedral)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "eqlin_oracle.c")
