@@ -35,6 +35,8 @@ EQLIN_F32 = 0
 EQLIN_BF16 = 1
 EQLIN_PREPARE_EXPANDED = 1
 EQLIN_PREPARE_BACKWARD = 2
+EQLIN_PREPARE_D4 = 4
+GROUPS = ("cyclic", "d4")
 EQLIN_ACT_NONE = 0
 EQLIN_ACT_GELU = 1
 _ACTS = {None: EQLIN_ACT_NONE, "none": EQLIN_ACT_NONE, "gelu": EQLIN_ACT_GELU}
@@ -126,9 +128,9 @@ class Handle:
     """Owns an eqlin_handle_t; destroyed with the object (or explicitly via destroy())."""
 
     def __init__(self, ptr: int, C_out: int, C_in: int, G: int, dtype: torch.dtype, device, expanded: bool,
-                 backward: bool = False):
+                 backward: bool = False, group: str = "cyclic"):
         self.ptr = ptr
-        self.C_out, self.C_in, self.G = C_out, C_in, G
+        self.C_out, self.C_in, self.G, self.group = C_out, C_in, G, group
         self.dtype, self.device, self.expanded, self.backward = dtype, device, expanded, backward
 
     def destroy(self):
@@ -146,21 +148,25 @@ class Handle:
         return describe(self)
 
 
-def prepare_weights(W: torch.Tensor, expanded: bool = False, backward: bool = False) -> Handle:
+def prepare_weights(W: torch.Tensor, expanded: bool = False, backward: bool = False, group: str = "cyclic") -> Handle:
     """eqlin_prepare_weights: W [C_out, C_in, G] (cuda, bf16 or fp32) -> Handle. ``expanded`` builds the
-    unrolled comparator, ``backward`` the weights of backward_data."""
+    unrolled comparator, ``backward`` the weights of backward_data. ``group``: "cyclic" (G = 1, 2, 4, 8)
+    or "d4", the dihedral group of the square (G = 8, element a + 4b = r^a s^b; EQLIN_PREPARE_D4)."""
+    if group not in GROUPS:
+        raise ValueError(f"group must be one of {GROUPS}, got {group!r}")
     lib = load_library()
     _need_cuda(W, "W")
     if W.dim() != 3:
         raise ValueError(f"W must be [C_out, C_in, G], got {tuple(W.shape)}")
     C_out, C_in, G = W.shape
     out = ctypes.c_void_p()
-    flags = (EQLIN_PREPARE_EXPANDED if expanded else 0) | (EQLIN_PREPARE_BACKWARD if backward else 0)
+    flags = (EQLIN_PREPARE_EXPANDED if expanded else 0) | (EQLIN_PREPARE_BACKWARD if backward else 0) | \
+        (EQLIN_PREPARE_D4 if group == "d4" else 0)
     with torch.cuda.device(W.device):
         st = lib.eqlin_prepare_weights(ctypes.c_void_p(W.data_ptr()), C_out, C_in, G, _dtype_code(W.dtype),
                                        flags, _stream(W), ctypes.byref(out))
     _check(st, "eqlin_prepare_weights")
-    return Handle(out.value, C_out, C_in, G, W.dtype, W.device, expanded, backward)
+    return Handle(out.value, C_out, C_in, G, W.dtype, W.device, expanded, backward, group)
 
 
 def _act_code(act) -> int:
@@ -223,7 +229,7 @@ def mlp_block(h1: Handle, b1: torch.Tensor | None, h2: Handle, b2: torch.Tensor 
     """The transformer MLP block as two library calls on the current stream: hidden = GELU(layer 1 (x))
     with GELU in layer 1's epilogue, then y = layer 2 (hidden). h1: [C_h, C, G] weights, h2: [C, C_h, G].
     expanded=True runs both layers as dense products with the unrolled weights (the comparator)."""
-    if h1.C_out != h2.C_in or h1.G != h2.G or h1.dtype != h2.dtype:
+    if h1.C_out != h2.C_in or h1.G != h2.G or h1.dtype != h2.dtype or h1.group != h2.group:
         raise ValueError("layer 2 must take layer 1's outputs (C_in, G and dtype)")
     fwd = forward_expanded if expanded else forward
     hidden = fwd(h1, x, b1, hidden, act="gelu")

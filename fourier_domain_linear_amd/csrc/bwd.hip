@@ -30,7 +30,9 @@
 //      own), the x fragments through LDS (shared by all waves).
 //   3. k_bw_reduce: sum of the splits, inverse DFT (scaled) -> dW fp32; k_bw_dbsum: db from its
 //      partials.
-// Other cases (fp32, G = 1 or 2): k_bw_direct, the definition above in fp32 with LDS token tiles.
+// Other cases (fp32, G = 1 or 2, the dihedral group D4): k_bw_direct, the definition above in fp32
+// with LDS token tiles. For D4 (element a + 4b = r^a s^b) the definition reads
+// dW[o, i, d] = sum_n sum_h dy[n, o, h] x[n, i, h d^-1] (the g with g^-1 h = d).
 #include <stdio.h>
 
 #include <algorithm>
@@ -308,7 +310,21 @@ __global__ __launch_bounds__(256) void k_bw_dbsum(const float *__restrict__ db_p
 // ------------------------------------------------------------------------------------------------
 // Direct kernel (fp32 or bf16 inputs, any G): the definition in fp32. Workgroup: 16 x 16 (o, i)
 // pairs, 256 threads (one pair each, all G shifts d); token tiles of 32 through LDS.
-template <typename T, int G>
+// Index of h d^-1: (h - d) mod G, or in D4, with h = r^c s^e and d = r^a s^b: d^-1 = r^a' s^b (a' = -a
+// for a rotation, a for a reflection) and the product rule r^c s^e r^a' s^b = r^(c + (-1)^e a') s^(e + b).
+template <int G, bool D4>
+__host__ __device__ constexpr int h_dinv(int h, int d) {
+    if constexpr (!D4) {
+        return (h - d + G) % G;
+    } else {
+        const int a = d & 3, b = d >> 2;
+        const int ai = b ? a : (4 - a) & 3;  // d^-1 = r^ai s^b
+        const int c = h & 3, e = h >> 2;
+        return ((e ? c - ai : c + ai) & 3) + 4 * ((e + b) & 1);
+    }
+}
+
+template <typename T, int G, bool D4>
 __global__ __launch_bounds__(256) void k_bw_direct(const T *__restrict__ x, const T *__restrict__ dy, int64_t N,
                                                    int C_in, int C_out, float *__restrict__ dW) {
     constexpr int TK = 32;
@@ -339,7 +355,7 @@ __global__ __launch_bounds__(256) void k_bw_direct(const T *__restrict__ x, cons
             for (int h = 0; h < G; ++h) {
                 const float dv = ds[k][ol][h];
 #pragma unroll
-                for (int d = 0; d < G; ++d) acc[d] += dv * xs[k][il][(h - d + G) % G];
+                for (int d = 0; d < G; ++d) acc[d] += dv * xs[k][il][h_dinv<G, D4>(h, d)];
             }
         __syncthreads();
     }
@@ -375,7 +391,7 @@ __global__ __launch_bounds__(256) void k_bw_bias(const T *__restrict__ dy, int64
 // Host side: workspace layout and launch.
 namespace {
 
-bool mfma_path(const Plan *p) { return p->dtype == EQLIN_BF16 && (p->G == 4 || p->G == 8); }
+bool mfma_path(const Plan *p) { return p->dtype == EQLIN_BF16 && (p->G == 4 || p->G == 8) && !p->d4; }
 
 struct BwLayout {
     int KT = 0, CB_in = 0, CB_out = 0, tiles_i = 0, tiles_o = 0, splits = 0, ptiles = 0;
@@ -444,10 +460,10 @@ hipError_t launch_mfma(const Plan *p, const void *x, const void *dy, float *dW, 
     return hipGetLastError();
 }
 
-template <typename T, int G>
+template <typename T, int G, bool D4 = false>
 hipError_t launch_direct(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N,
                          hipStream_t s) {
-    hipLaunchKernelGGL((k_bw_direct<T, G>), dim3((p->C_in + 15) / 16, (p->C_out + 15) / 16), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_bw_direct<T, G, D4>), dim3((p->C_in + 15) / 16, (p->C_out + 15) / 16), dim3(256), 0, s,
                        (const T *)x, (const T *)dy, N, p->C_in, p->C_out, dW);
     if (db)
         hipLaunchKernelGGL(k_bw_bias<T>, dim3((p->C_out + 63) / 64), dim3(256), 0, s, (const T *)dy, N, p->C_out,
@@ -462,7 +478,8 @@ hipError_t launch_direct_g(const Plan *p, const void *x, const void *dy, float *
         case 1: return launch_direct<T, 1>(p, x, dy, dW, db, N, s);
         case 2: return launch_direct<T, 2>(p, x, dy, dW, db, N, s);
         case 4: return launch_direct<T, 4>(p, x, dy, dW, db, N, s);
-        case 8: return launch_direct<T, 8>(p, x, dy, dW, db, N, s);
+        case 8: return p->d4 ? launch_direct<T, 8, true>(p, x, dy, dW, db, N, s)
+                             : launch_direct<T, 8, false>(p, x, dy, dW, db, N, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -103,4 +103,68 @@ EQLIN_HD void inverse_planes(const float *Y, float *y) {
     }
 }
 
+// ---- The dihedral group D4 (p4's rotations plus reflections; order 8) ----
+//
+// The Flash EQ-Linear page names reflection groups as the method's next generalisation
+// ("Limitaciones y Trabajo Futuro"). The layer is the group convolution y(h) = sum_g W(g^-1 h) x(g).
+// Element e = a + 4b is r^a s^b (rotation by 90a degrees after the mirror s when b = 1; s r = r^-1 s).
+// Its Fourier transform F(rho) = sum_g f(g) rho(g) runs over the irreducible representations: four
+// characters (1, (-1)^b, (-1)^a, (-1)^(a+b)) and the 2-D one rho(r^a s^b) = R^a S^b with R the
+// 90-degree rotation [[0, -1], [1, 0]] and S = diag(1, -1). The layer becomes, per irrep and channel
+// pair, Y(rho) = X(rho) W(rho): four real products for the characters and a 2 x 2 matrix product
+// (eight real products) for rho -- twelve in all, against 64 for the unrolled 8 x 8 block.
+//
+// Plane order: P0..P3 the characters' values, P4..P7 the entries (0,0), (0,1), (1,0), (1,1) of F(rho).
+// All coefficients are 0 or +-1. Inverse (Schur orthogonality):
+//   f(g) = (1/8) sum_k chi_k(g) F_k + (2/8) sum_{jk} rho(g)_jk F(rho)_jk,
+// with the 1/8 and 2/8 folded into the stored weight planes (plane_scale_d4), as for the cyclic case.
+EQLIN_HD float plane_scale_d4(int p) { return p < 4 ? 0.125f : 0.25f; }
+
+EQLIN_HD void forward_planes_d4(const float *v, float *P) {
+    // rotations v0..v3 and reflections v4..v7, each split into even/odd rotation parts
+    const float A = v[0] + v[2], B = v[1] + v[3], C = v[0] - v[2], D = v[1] - v[3];
+    const float A2 = v[4] + v[6], B2 = v[5] + v[7], C2 = v[4] - v[6], D2 = v[5] - v[7];
+    const float s0 = A + B, s1 = A2 + B2, t0 = A - B, t1 = A2 - B2;
+    P[0] = s0 + s1;  // trivial
+    P[1] = s0 - s1;  // (-1)^b
+    P[2] = t0 + t1;  // (-1)^a
+    P[3] = t0 - t1;  // (-1)^(a+b)
+    P[4] = C + C2;   // rho_00 = v0 - v2 + v4 - v6
+    P[5] = D2 - D;   // rho_01 = -v1 + v3 + v5 - v7
+    P[6] = D + D2;   // rho_10 = v1 - v3 + v5 - v7
+    P[7] = C - C2;   // rho_11 = v0 - v2 - v4 + v6
+}
+
+EQLIN_HD void inverse_planes_d4(const float *Y, float *y) {
+    const float p = Y[0] + Y[1], m = Y[0] - Y[1], q = Y[2] + Y[3], n = Y[2] - Y[3];
+    const float e0 = p + q, e1 = p - q, e2 = m + n, e3 = m - n;  // characters at (b, a mod 2)
+    const float m0 = Y[4] + Y[7], m1 = Y[6] - Y[5];               // trace terms, rotations
+    const float n0 = Y[4] - Y[7], n1 = Y[5] + Y[6];               // trace terms, reflections
+    y[0] = e0 + m0; y[2] = e0 - m0;
+    y[1] = e1 + m1; y[3] = e1 - m1;
+    y[4] = e2 + n0; y[6] = e2 - n0;
+    y[5] = e3 + n1; y[7] = e3 - n1;
+}
+
+// The group's own transform for kernels templated on (G, D4); D4 requires G = 8.
+template <int G, bool D4>
+EQLIN_HD void group_forward(const float *v, float *P) {
+    if constexpr (D4) {
+        static_assert(G == 8, "D4 has order 8");
+        forward_planes_d4(v, P);
+    } else {
+        forward_planes<G>(v, P);
+    }
+}
+template <int G, bool D4>
+EQLIN_HD void group_inverse(const float *Y, float *y) {
+    if constexpr (D4) {
+        static_assert(G == 8, "D4 has order 8");
+        inverse_planes_d4(Y, y);
+    } else {
+        inverse_planes<G>(Y, y);
+    }
+}
+EQLIN_HD float group_plane_scale(int G, bool d4, int p) { return d4 ? plane_scale_d4(p) : plane_scale(G, p); }
+
 }  // namespace eqlin

@@ -49,7 +49,7 @@ void free_plan(Plan *p) {
 eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
     hipError_t e;
     if (p->dtype == EQLIN_BF16) {
-        if (!eqlin::select_bf16(p->G, p->C_in, p->C_out, &p->fwd))
+        if (!eqlin::select_bf16(p->G, p->d4, p->C_in, p->C_out, &p->fwd))
             return fail(EQLIN_ERR_UNSUPPORTED, "no bf16 kernel for G=%d C_in=%d C_out=%d", p->G, p->C_in,
                         p->C_out);
         const int ks = (p->C_in + p->fwd.kc - 1) / p->fwd.kc;
@@ -63,10 +63,11 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
             return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for spectral weights: %s", p->planes_bytes,
                         hipGetErrorString(e));
         }
-        e = eqlin::launch_prep_frag(W, true, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->fwd.frag_kind, p->planes, s);
+        e = eqlin::launch_prep_frag(W, true, p->d4, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->fwd.frag_kind,
+                                    p->planes, s);
         if (e != hipSuccess) return hip_fail(e, "spectral weight preparation");
     } else {
-        if (!eqlin::select_f32(p->G, p->C_in, p->C_out, &p->fwd))
+        if (!eqlin::select_f32(p->G, p->d4, p->C_in, p->C_out, &p->fwd))
             return fail(EQLIN_ERR_UNSUPPORTED, "no f32 kernel for G=%d", p->G);
         p->planes_bytes = (size_t)p->G * p->C_out * p->C_in * sizeof(float);
         e = hipMalloc(&p->planes, p->planes_bytes);
@@ -75,7 +76,7 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
             return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for spectral weights: %s", p->planes_bytes,
                         hipGetErrorString(e));
         }
-        e = eqlin::launch_prep_plain_f32((const float *)W, p->G, p->C_out, p->C_in, (float *)p->planes, s);
+        e = eqlin::launch_prep_plain_f32((const float *)W, p->d4, p->G, p->C_out, p->C_in, (float *)p->planes, s);
         if (e != hipSuccess) return hip_fail(e, "spectral weight preparation");
     }
     return EQLIN_OK;
@@ -119,8 +120,10 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
     if (C_out < 1 || C_in < 1) return fail(EQLIN_ERR_INVALID_ARG, "C_out = %d, C_in = %d must be >= 1", C_out, C_in);
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(EQLIN_ERR_INVALID_ARG, "G = %d not in {1, 2, 4, 8}", G);
     if (dtype != EQLIN_F32 && dtype != EQLIN_BF16) return fail(EQLIN_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
-    if (flags & ~(EQLIN_PREPARE_EXPANDED | EQLIN_PREPARE_BACKWARD))
+    if (flags & ~(EQLIN_PREPARE_EXPANDED | EQLIN_PREPARE_BACKWARD | EQLIN_PREPARE_D4))
         return fail(EQLIN_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    const bool d4 = (flags & EQLIN_PREPARE_D4) != 0;
+    if (d4 && G != 8) return fail(EQLIN_ERR_INVALID_ARG, "EQLIN_PREPARE_D4 needs G = 8 (got G = %d)", G);
     if ((int64_t)C_out * G > (1 << 20) || (int64_t)C_in * G > (1 << 20))
         return fail(EQLIN_ERR_UNSUPPORTED, "channel counts beyond 2^20 unrolled columns");
     if (!aligned(W, 16)) return fail(EQLIN_ERR_INVALID_ARG, "W must be 16-byte aligned");
@@ -135,6 +138,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
     p->C_out = C_out;
     p->C_in = C_in;
     p->G = G;
+    p->d4 = d4;
     p->dtype = dtype;
     p->flags = flags;
     hipError_t e = hipGetDevice(&p->device);
@@ -156,7 +160,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
             free_plan(p);
             return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for the unrolled weight", ebytes);
         }
-        e = eqlin::launch_expand(W, (int)eb, G, C_out, C_in, p->wexp, s);
+        e = eqlin::launch_expand(W, (int)eb, d4, G, C_out, C_in, p->wexp, s);
         if (e != hipSuccess) {
             free_plan(p);
             return hip_fail(e, "unrolled weight");
@@ -188,7 +192,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
             free_plan(p);
             return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for the backward weight", bytes);
         }
-        e = eqlin::launch_transpose_reverse(W, (int)eb, G, C_out, C_in, p->wt, s);
+        e = eqlin::launch_transpose_reverse(W, (int)eb, d4, G, C_out, C_in, p->wt, s);
         if (e != hipSuccess) {
             free_plan(p);
             return hip_fail(e, "backward weight");
@@ -201,6 +205,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
         q->C_out = C_in;
         q->C_in = C_out;
         q->G = G;
+        q->d4 = d4;
         q->dtype = dtype;
         q->device = p->device;
         p->backward = q;
@@ -305,10 +310,10 @@ eqlin_status_t eqlin_export_spectral_weights(eqlin_handle_t h, float *out, eqlin
     if (!h || !out) return fail(EQLIN_ERR_INVALID_ARG, "null handle or out");
     hipError_t e;
     if (h->dtype == EQLIN_BF16)
-        e = eqlin::launch_export_frag(h->planes, h->G, h->C_out, h->C_in, h->KS, h->NB_total, h->fwd.frag_kind,
-                                      out, (hipStream_t)stream);
+        e = eqlin::launch_export_frag(h->planes, h->d4, h->G, h->C_out, h->C_in, h->KS, h->NB_total,
+                                      h->fwd.frag_kind, out, (hipStream_t)stream);
     else
-        e = eqlin::launch_export_plain_f32((const float *)h->planes, h->G, h->C_out, h->C_in, out,
+        e = eqlin::launch_export_plain_f32((const float *)h->planes, h->d4, h->G, h->C_out, h->C_in, out,
                                            (hipStream_t)stream);
     return e == hipSuccess ? EQLIN_OK : hip_fail(e, "export of spectral weights");
 }
@@ -326,8 +331,8 @@ eqlin_status_t eqlin_export_expanded_weight(eqlin_handle_t h, void *out, eqlin_s
 int eqlin_describe(eqlin_handle_t h, char *buf, size_t len) {
     if (!h) return snprintf(buf, len, "(null handle)");
     return snprintf(buf, len,
-                    "G=%d C_in=%d C_out=%d %s | forward: %s | expanded: %s | backward data: %s | backward weights: %s",
-                    h->G, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : "f32", h->fwd.name,
+                    "%s%d C_in=%d C_out=%d %s | forward: %s | expanded: %s | backward data: %s | backward weights: %s",
+                    h->d4 ? "D" : "G=", h->d4 ? 4 : h->G, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : "f32", h->fwd.name,
                     h->expanded ? h->expanded->fwd.name : "(not prepared)",
                     h->backward ? h->backward->fwd.name : "(not prepared)", eqlin::bw_kernel_name(h));
 }

@@ -44,6 +44,7 @@ struct KernelChoice {
 
 struct Plan {
     int C_out = 0, C_in = 0, G = 0;
+    bool d4 = false;   // the group is the dihedral D4 (G = 8), not the cyclic group of order G
     eqlin_dtype_t dtype = EQLIN_BF16;
     unsigned flags = 0;
     int device = 0;
@@ -67,12 +68,12 @@ struct Plan {
 };
 
 // ---- fwd_bf16.hip ----
-bool select_bf16(int G, int C_in, int C_out, KernelChoice *out);
+bool select_bf16(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 int device_num_cus();  // compute units of the current device (queried once)
 // ---- fwd_big.hip ----
-bool select_big(int G, int C_in, int C_out, KernelChoice *out);
+bool select_big(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 // ---- fwd_f32.hip ----
-bool select_f32(int G, int C_in, int C_out, KernelChoice *out);
+bool select_f32(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 
 // ---- bwd.hip ----
 // Workspace bytes eqlin_backward_weights needs for N tokens (0: none).
@@ -84,21 +85,21 @@ const char *bw_kernel_name(const Plan *p);
 
 // ---- prepare.hip ----
 // W [C_out][C_in][G] (bf16 bits or fp32) -> fragment-ordered bf16 spectral planes.
-hipError_t launch_prep_frag(const void *W, bool w_is_bf16, int G, int C_out, int C_in, int KS,
+hipError_t launch_prep_frag(const void *W, bool w_is_bf16, bool d4, int G, int C_out, int C_in, int KS,
                             int NB_total, int frag_kind, void *frag, hipStream_t s);
 // W fp32 -> planes [G][C_out][C_in] fp32.
-hipError_t launch_prep_plain_f32(const float *W, int G, int C_out, int C_in, float *planes,
+hipError_t launch_prep_plain_f32(const float *W, bool d4, int G, int C_out, int C_in, float *planes,
                                  hipStream_t s);
 // W -> Wt[C_in][C_out][G], Wt[i][o][d] = W[o][i][(G - d) mod G] (same element size, 2 or 4 bytes).
-hipError_t launch_transpose_reverse(const void *W, int elem_bytes, int G, int C_out, int C_in, void *Wt,
+hipError_t launch_transpose_reverse(const void *W, int elem_bytes, bool d4, int G, int C_out, int C_in, void *Wt,
                                    hipStream_t s);
 // W -> E[C_out*G][C_in*G] (same element size, 2 or 4 bytes).
-hipError_t launch_expand(const void *W, int elem_bytes, int G, int C_out, int C_in, void *E,
+hipError_t launch_expand(const void *W, int elem_bytes, bool d4, int G, int C_out, int C_in, void *E,
                          hipStream_t s);
 // stored spectral weights -> canonical fp32 [G][C_out][C_in] with the scaling undone.
-hipError_t launch_export_frag(const void *frag, int G, int C_out, int C_in, int KS, int NB_total,
+hipError_t launch_export_frag(const void *frag, bool d4, int G, int C_out, int C_in, int KS, int NB_total,
                               int frag_kind, float *out, hipStream_t s);
-hipError_t launch_export_plain_f32(const float *planes, int G, int C_out, int C_in, float *out,
+hipError_t launch_export_plain_f32(const float *planes, bool d4, int G, int C_out, int C_in, float *out,
                                    hipStream_t s);
 
 }  // namespace eqlin

@@ -48,8 +48,9 @@ __device__ __forceinline__ void chunk_to_lds(const uint4 *src_lane, uint4 *dst_w
     __builtin_amdgcn_global_load_lds((gbl_void *)src_lane, (lds_void *)dst_wave, 16, 0, 0);
 }
 
-// G samples of 8 channels (channel-major, sample-minor: element j*G+g) -> G planes of 8 bf16.
-template <int G>
+// G samples of 8 channels (channel-major, sample-minor: element j*G+g) -> G planes of 8 bf16 (the
+// cyclic group's DFT, or D4's Fourier transform when D4).
+template <int G, bool D4>
 __device__ __forceinline__ void dft_to_frags(const uint4 (&r)[G], uint4 (&a)[G]) {
     float pl[G][8];
 #pragma unroll
@@ -57,7 +58,7 @@ __device__ __forceinline__ void dft_to_frags(const uint4 (&r)[G], uint4 (&a)[G])
         float v[G], P[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) v[g] = bf16_at(r[(j * G + g) >> 3], (j * G + g) & 7);
-        forward_planes<G>(v, P);
+        group_forward<G, D4>(v, P);
 #pragma unroll
         for (int p = 0; p < G; ++p) pl[p][j] = P[p];
     }
@@ -88,10 +89,23 @@ __device__ __forceinline__ void load_x_clamped(const uint4 *__restrict__ x4, int
 }
 
 // The 2G-2 real products with the weights as the A operand (rows = outputs) and the x planes as
-// the B operand (columns = tokens): D lane l holds outputs 4*(l/16)+v of token l%16.
-template <int G>
+// the B operand (columns = tokens): D lane l holds outputs 4*(l/16)+v of token l%16. D4: the four
+// characters' products, then Y(rho) = X(rho) W(rho) entry by entry, Y_ab += W_cb X_ac over c = 0, 1
+// (twelve products; no negated operand).
+template <int G, bool D4>
 __device__ __forceinline__ void spectral_mfma_wx(const uint4 (&w)[G], const uint4 (&a)[G],
                                                  const uint4 (&an)[G], f32x4 (&acc)[G]) {
+    if constexpr (D4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = mfma16x16x32(w[k], a[k], acc[k]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ra = e >> 1, cb = e & 1;
+            acc[4 + e] = mfma16x16x32(w[4 + cb], a[4 + 2 * ra], acc[4 + e]);
+            acc[4 + e] = mfma16x16x32(w[6 + cb], a[5 + 2 * ra], acc[4 + e]);
+        }
+        return;
+    }
     acc[0] = mfma16x16x32(w[0], a[0], acc[0]);
     if constexpr (G >= 2) acc[1] = mfma16x16x32(w[1], a[1], acc[1]);
 #pragma unroll
@@ -105,7 +119,7 @@ __device__ __forceinline__ void spectral_mfma_wx(const uint4 (&w)[G], const uint
 }
 
 // Element-wise tail store for a partial output block or the last token rows: output o0 + v of token n.
-template <int G, bool GELU>
+template <int G, bool GELU, bool D4>
 __device__ __forceinline__ void store_quad_masked(const f32x4 (&acc)[G], uint16_t *__restrict__ y,
                                                   int64_t n, int64_t N, int o0, int C_out) {
     if (n >= N) return;
@@ -115,7 +129,7 @@ __device__ __forceinline__ void store_quad_masked(const f32x4 (&acc)[G], uint16_
         float Y[G], out[G];
 #pragma unroll
         for (int p = 0; p < G; ++p) Y[p] = acc[p][v];
-        inverse_planes<G>(Y, out);
+        group_inverse<G, D4>(Y, out);
         apply_act<GELU>(out);
         uint16_t *dst = y + (n * C_out + o0 + v) * G;
 #pragma unroll
@@ -196,7 +210,7 @@ __device__ __forceinline__ void load_x_raw(const uint4 *__restrict__ x4, int64_t
         }
 }
 
-template <int G, int KS, bool GELU>
+template <int G, int KS, bool GELU, bool D4>
 __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__restrict__ x4,
                                                               const uint4 *__restrict__ wfrag,
                                                               const uint16_t *__restrict__ bias,
@@ -273,8 +287,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
                 uint4 r[G];
 #pragma unroll
                 for (int q = 0; q < G; ++q) r[q] = scratch[swz<SG::PX>(lane & 15, ku * 4 * G + 4 * q + g)];
-                dft_to_frags<G>(r, a[u * SG::U + ku]);
-                negate_imag<G>(a[u * SG::U + ku], an[u * SG::U + ku]);
+                dft_to_frags<G, D4>(r, a[u * SG::U + ku]);
+                if constexpr (!D4) negate_imag<G>(a[u * SG::U + ku], an[u * SG::U + ku]);
             }
         }
         const int64_t nxt = blk + NW;
@@ -309,7 +323,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
 #pragma unroll
                     for (int p = 0; p < G; ++p) bw[1][ks][p] = lds[((nbn * KS + ks) * G + p) * 64 + lane];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) spectral_mfma_wx<G>(bw[0][ks], a[ks], an[ks], acc);
+                for (int ks = 0; ks < KS; ++ks) spectral_mfma_wx<G, D4>(bw[0][ks], a[ks], an[ks], acc);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -319,11 +333,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
                 for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                     for (int p = 0; p < G; ++p) bw[0][0][p] = lds[((nb * KS + ks) * G + p) * 64 + lane];
-                    spectral_mfma_wx<G>(bw[0][0], a[ks], an[ks], acc);
+                    spectral_mfma_wx<G, D4>(bw[0][0], a[ks], an[ks], acc);
                 }
             }
             if (!vec_rows) {
-                store_quad_masked<G, GELU>(acc, y, nrow0 + (lane & 15), N, (nb0 + nb) * 16 + 4 * g, C_out);
+                store_quad_masked<G, GELU, D4>(acc, y, nrow0 + (lane & 15), N, (nb0 + nb) * 16 + 4 * g, C_out);
                 continue;
             }
             // inverse DFT (+ activation) -> this lane's 4 outputs x G (8G bytes) -> staging row lane%16,
@@ -350,7 +364,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
                         float Y[G];
 #pragma unroll
                         for (int p = 0; p < G; ++p) Y[p] = acc[p][k * VP + vv];
-                        inverse_planes<G>(Y, out + vv * G);
+                        group_inverse<G, D4>(Y, out + vv * G);
                     }
                     apply_act<GELU>(out);
                     scratch[swz<SG::PPR>(lane & 15, ub * 2 * G + g * (G / 2) + k)] = pack_bf16x8(out);
@@ -405,7 +419,7 @@ int device_num_cus() {
     return g_num_cus;
 }
 
-template <int G, int KS>
+template <int G, int KS, bool D4>
 static hipError_t launch_stream(const Plan *p, const void *x, const void *b, void *y, int64_t N, int act,
                                 hipStream_t s) {
     const size_t lds = p->fwd.lds_bytes;
@@ -416,33 +430,37 @@ static hipError_t launch_stream(const Plan *p, const void *x, const void *b, voi
     wg = std::min<int64_t>(wg, blocks);
     const dim3 grid((unsigned)wg, (unsigned)tiles), block(kStreamWaves * 64);
     if (act == EQLIN_ACT_GELU)
-        hipLaunchKernelGGL((k_stream<G, KS, true>), grid, block, lds, s, (const uint4 *)x, (const uint4 *)p->planes,
+        hipLaunchKernelGGL((k_stream<G, KS, true, D4>), grid, block, lds, s, (const uint4 *)x, (const uint4 *)p->planes,
                            (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, p->fwd.nb_tile);
     else
-        hipLaunchKernelGGL((k_stream<G, KS, false>), grid, block, lds, s, (const uint4 *)x, (const uint4 *)p->planes,
+        hipLaunchKernelGGL((k_stream<G, KS, false, D4>), grid, block, lds, s, (const uint4 *)x, (const uint4 *)p->planes,
                            (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, p->fwd.nb_tile);
     return hipGetLastError();
 }
 
-template <int G, int KS>
+template <int G, int KS, bool D4>
 static hipError_t init_stream(size_t lds) {
-    const hipError_t e = set_lds_limit((const void *)k_stream<G, KS, false>, lds);
-    return e != hipSuccess ? e : set_lds_limit((const void *)k_stream<G, KS, true>, lds);
+    const hipError_t e = set_lds_limit((const void *)k_stream<G, KS, false, D4>, lds);
+    return e != hipSuccess ? e : set_lds_limit((const void *)k_stream<G, KS, true, D4>, lds);
 }
 
 struct StreamEntry {
     int G, KS;
+    bool d4;
     LaunchFn launch;
     hipError_t (*init)(size_t);
 };
-#define SE(G, KS) {G, KS, launch_stream<G, KS>, init_stream<G, KS>}
+#define SE(G, KS) {G, KS, false, launch_stream<G, KS, false>, init_stream<G, KS, false>}
+#define SD(KS) {8, KS, true, launch_stream<8, KS, true>, init_stream<8, KS, true>}
 static const StreamEntry kStream[] = {
     SE(1, 2), SE(1, 4), SE(1, 6), SE(1, 8), SE(1, 10), SE(1, 12), SE(1, 14), SE(1, 16),
     SE(2, 1), SE(2, 2), SE(2, 3), SE(2, 4), SE(2, 6), SE(2, 8),
     SE(4, 1), SE(4, 2), SE(4, 3), SE(4, 4),
     SE(8, 1), SE(8, 2),
+    SD(1), SD(2),  // the dihedral group D4 (order 8)
 };
 #undef SE
+#undef SD
 static constexpr size_t kStreamLdsMax = 160 * 1024;
 static constexpr int kStreamMaxTiles = 4;
 
@@ -455,13 +473,13 @@ static size_t stream_scratch(int G) {
     }
 }
 
-bool select_bf16(int G, int C_in, int C_out, KernelChoice *out) {
+bool select_bf16(int G, bool d4, int C_in, int C_out, KernelChoice *out) {
     const int KS = (C_in + 31) / 32;
     const int nb_needed = (C_out + 15) / 16;
     // Stream kernel when x of a row block fits in registers (an instantiated KS) and the C_out tiles
     // whose weights fit LDS number at most kStreamMaxTiles (x is re-read and re-transformed per tile).
     for (const auto &e : kStream) {
-        if (e.G != G || e.KS != KS) continue;
+        if (e.G != G || e.KS != KS || e.d4 != d4) continue;
         const size_t fixed = (size_t)kStreamWaves * stream_scratch(G);
         const size_t per_nb = (size_t)KS * G * 1024 + 16 * sizeof(float);
         const int nb_fit = (int)((kStreamLdsMax - fixed) / per_nb);
@@ -482,11 +500,11 @@ bool select_bf16(int G, int C_in, int C_out, KernelChoice *out) {
         out->ks_mult = 1;
         out->launch = e.launch;
         (void)e.init(out->lds_bytes);
-        snprintf(out->name, sizeof(out->name), "bf16 stream G=%d KS=%d nb_tile=%d tiles=%d waves=%d", G, KS,
-                 nb_tile, tiles, kStreamWaves);
+        snprintf(out->name, sizeof(out->name), "bf16 stream %s%d KS=%d nb_tile=%d tiles=%d waves=%d",
+                 d4 ? "D" : "G=", d4 ? 4 : G, KS, nb_tile, tiles, kStreamWaves);
         return true;
     }
-    return select_big(G, C_in, C_out, out);
+    return select_big(G, d4, C_in, C_out, out);
 }
 
 }  // namespace eqlin

@@ -70,8 +70,9 @@ __device__ __forceinline__ void spectral_mfma32(const uint4 (&w)[G], const uint4
     }
 }
 
-// G samples of NCH channels (element j*G+g) -> G planes of NCH bf16 (NCH = 2, 4 or 8).
-template <int G, int NCH>
+// G samples of NCH channels (element j*G+g) -> G planes of NCH bf16 (NCH = 2, 4 or 8); D4: the
+// dihedral group's Fourier transform instead of the cyclic DFT.
+template <int G, int NCH, bool D4 = false>
 __device__ __forceinline__ void dft_ch(const uint4 (&r)[NCH * G / 8], float (&pl)[G][NCH]) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
@@ -83,7 +84,7 @@ __device__ __forceinline__ void dft_ch(const uint4 (&r)[NCH * G / 8], float (&pl
             const uint32_t wd = (e >> 1) == 0 ? q.x : (e >> 1) == 1 ? q.y : (e >> 1) == 2 ? q.z : q.w;
             v[g] = (e & 1) ? __uint_as_float(wd & 0xffff0000u) : __uint_as_float(wd << 16);
         }
-        forward_planes<G>(v, P);
+        group_forward<G, D4>(v, P);
 #pragma unroll
         for (int p = 0; p < G; ++p) pl[p][j] = P[p];
     }
@@ -540,7 +541,7 @@ struct P8Cfg {
     static_assert(HP * 16 * 64 * 4 <= STG * 16, "a wave's staging holds the four planes it hands over");
 };
 
-template <bool GELU>
+template <bool GELU, bool D4>
 __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, const uint4 *__restrict__ wfrag,
                                                   const uint16_t *__restrict__ bias, int bias_shift,
                                                   uint16_t *__restrict__ y, int64_t N, int C_in, int C_out,
@@ -608,7 +609,7 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
         const int c0 = cq * NCH;
         uint4 *dst = xb + ((tl >> 5) * KSS + (c0 >> 4)) * G * 64 + ((c0 >> 3) & 1) * 32 + (tl & 31);
         float pl[G][NCH];
-        dft_ch<G, NCH>(src[0], pl);
+        dft_ch<G, NCH, D4>(src[0], pl);
 #pragma unroll
         for (int p = 0; p < G; ++p)
             reinterpret_cast<uint32_t *>(dst + p * 64)[(c0 >> 1) & 3] = pack_bf16x2(pl[p][0], pl[p][1]);
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
     // the whole tile loop, once per role (wave-uniform), so each copy's stages are branch-free
     auto run = [&](auto rc) {
         constexpr int R = decltype(rc)::value;
-        constexpr int NMB = R == 0 ? 6 : 8;  // products per token block per K-step
+        constexpr int NMB = D4 ? (R == 0 ? 4 : 8) : (R == 0 ? 6 : 8);  // products per token block per K-step
         f32x16 acc[WB][HP];
         // Re += Wr Xr + (-Wi) Xi and Im += Wi Xr + Wr Xi: the sign goes on the weight fragment (wn, one
         // negated copy per stage and Im plane), which serves both token blocks
@@ -663,7 +664,22 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
 #pragma unroll
             for (int r = 0; r < HP; ++r) xf[r] = planes[((b * KSS) * G + R * HP + r) * 64 + lane];
             auto acc0 = [&](int q) { return F ? f32x16{} : acc[b][q]; };
-            if constexpr (R == 0) {
+            if constexpr (D4) {
+                // D4, role 0: the four characters, one product each; role 1: the 2 x 2 irrep,
+                // Y_ab += W_0b X_a0 + W_1b X_a1 (local planes 0..3 = entries 00, 01, 10, 11)
+                if constexpr (R == 0) {
+                    acc[b][0] = mfma32x32x16(w[0], xf[0], acc[b][0]);
+#pragma unroll
+                    for (int q = 1; q < 4; ++q) acc[b][q] = mfma32x32x16(w[q], xf[q], acc0(q));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int ra = e >> 1, cb = e & 1;
+                        acc[b][e] = mfma32x32x16(w[cb], xf[2 * ra], acc0(e));
+                        acc[b][e] = mfma32x32x16(w[2 + cb], xf[2 * ra + 1], acc[b][e]);
+                    }
+                }
+            } else if constexpr (R == 0) {
                 acc[b][0] = mfma32x32x16(w[0], xf[0], acc[b][0]);
                 acc[b][1] = mfma32x32x16(w[1], xf[1], acc0(1));
                 acc[b][2] = mfma32x32x16(w[2], xf[2], acc0(2));
@@ -755,7 +771,7 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
                     float Y[G];
 #pragma unroll
                     for (int p = 0; p < G; ++p) Y[p] = plane(p, 4 * vq + v);
-                    inverse_planes<G>(Y, out + v * G);
+                    group_inverse<G, D4>(Y, out + v * G);
                 }
                 apply_act<GELU>(out);
                 const int ol = 8 * vq + 4 * h_e;  // first of the 4 outputs in the staged row
@@ -788,7 +804,8 @@ static hipError_t launch_p8(const Plan *p, const void *x, const void *b, void *y
     const int64_t grid = per_o * tiles_o;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     const int xg = xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * C::G * 2);
-    auto kern = act == EQLIN_ACT_GELU ? k_p8<true> : k_p8<false>;
+    auto kern = p->d4 ? (act == EQLIN_ACT_GELU ? k_p8<true, true> : k_p8<false, true>)
+                      : (act == EQLIN_ACT_GELU ? k_p8<true, false> : k_p8<false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), 0, s, (const uint4 *)x, (const uint4 *)p->planes,
                        (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS,
                        (int)tiles_t, tiles_o, xg);
@@ -842,10 +859,10 @@ static const BigEntry kBig[] = {
 };
 #undef BE
 
-bool select_big(int G, int C_in, int C_out, KernelChoice *out) {
+bool select_big(int G, bool d4, int C_in, int C_out, KernelChoice *out) {
     (void)C_in;
     for (const auto &e : kBig) {
-        if (e.G != G) continue;
+        if (e.G != G || (d4 && G != 8)) continue;  // D4 runs on the plane-split G = 8 kernel
         // a token tile's output rows are addressed with 32-bit buffer offsets
         if ((int64_t)e.BT * C_out * G * 2 > 0x7fffffff) return false;
         out->kind = KIND_BIG;
@@ -859,8 +876,8 @@ bool select_big(int G, int C_in, int C_out, KernelChoice *out) {
         out->lds_bytes = e.lds;
         out->num_cus = device_num_cus();
         out->launch = e.launch;
-        snprintf(out->name, sizeof(out->name), "bf16 big G=%d BO=%d BT=%d (%s) mfma32x32x16", G, e.BO, e.BT,
-                 e.tile);
+        snprintf(out->name, sizeof(out->name), "bf16 big %s%d BO=%d BT=%d (%s) mfma32x32x16", d4 ? "D" : "G=",
+                 d4 ? 4 : G, e.BO, e.BT, e.tile);
         return true;
     }
     return false;

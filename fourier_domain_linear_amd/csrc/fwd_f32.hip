@@ -17,7 +17,7 @@ namespace eqlin {
 
 constexpr int F_TM = 32, F_TN = 64, F_KC = 16, F_PAD = F_KC + 1;
 
-template <int G, bool GELU>
+template <int G, bool GELU, bool D4>
 __global__ __launch_bounds__(256) void k_fwd_f32(const float *__restrict__ x,
                                                  const float *__restrict__ planes,
                                                  const float *__restrict__ bias, int bias_shift,
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(const float *__restrict__ x,
             const bool live = n < N && i < C_in;
 #pragma unroll
             for (int g = 0; g < G; ++g) v[g] = live ? x[(n * C_in + i) * G + g] : 0.f;
-            forward_planes<G>(v, P);
+            group_forward<G, D4>(v, P);
 #pragma unroll
             for (int p = 0; p < G; ++p) Xs[p][m][c] = P[p];
         }
@@ -70,6 +70,18 @@ __global__ __launch_bounds__(256) void k_fwd_f32(const float *__restrict__ x,
                 float wv[G];
 #pragma unroll
                 for (int p = 0; p < G; ++p) wv[p] = Ws[p][ol][c];
+                if constexpr (D4) {
+                    // characters: one product each; 2 x 2 irrep: Y_ab += X_a0 W_0b + X_a1 W_1b
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(xv[q], wv[q], acc[j][q]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int ra = e >> 1, cb = e & 1;
+                        acc[j][4 + e] = fmaf(xv[4 + 2 * ra], wv[4 + cb], acc[j][4 + e]);
+                        acc[j][4 + e] = fmaf(xv[5 + 2 * ra], wv[6 + cb], acc[j][4 + e]);
+                    }
+                    continue;
+                }
                 acc[j][0] = fmaf(xv[0], wv[0], acc[j][0]);
                 if constexpr (G >= 2) acc[j][1] = fmaf(xv[1], wv[1], acc[j][1]);
 #pragma unroll
@@ -93,7 +105,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(const float *__restrict__ x,
         if (o >= C_out) continue;
         const float bo = bias ? bias[o >> bias_shift] : 0.f;
         float out[G];
-        inverse_planes<G>(acc[j], out);
+        group_inverse<G, D4>(acc[j], out);
 #pragma unroll
         for (int h = 0; h < G; ++h) out[h] += bo;
         apply_act<GELU>(out);
@@ -102,34 +114,35 @@ __global__ __launch_bounds__(256) void k_fwd_f32(const float *__restrict__ x,
     }
 }
 
-template <int G>
+template <int G, bool D4>
 static hipError_t launch_f32(const Plan *p, const void *x, const void *b, void *y, int64_t N, int act,
                              hipStream_t s) {
     const dim3 grid((unsigned)((N + F_TM - 1) / F_TM), (unsigned)((p->C_out + F_TN - 1) / F_TN));
-    auto kern = act == EQLIN_ACT_GELU ? k_fwd_f32<G, true> : k_fwd_f32<G, false>;
+    auto kern = act == EQLIN_ACT_GELU ? k_fwd_f32<G, true, D4> : k_fwd_f32<G, false, D4>;
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const float *)x, (const float *)p->planes,
                        (const float *)b, p->bias_shift, (float *)y, N, p->C_in, p->C_out);
     return hipGetLastError();
 }
 
-bool select_f32(int G, int C_in, int C_out, KernelChoice *out) {
+bool select_f32(int G, bool d4, int C_in, int C_out, KernelChoice *out) {
     (void)C_in;
     (void)C_out;
     LaunchFn fn = nullptr;
     switch (G) {
-        case 1: fn = launch_f32<1>; break;
-        case 2: fn = launch_f32<2>; break;
-        case 4: fn = launch_f32<4>; break;
-        case 8: fn = launch_f32<8>; break;
+        case 1: fn = launch_f32<1, false>; break;
+        case 2: fn = launch_f32<2, false>; break;
+        case 4: fn = launch_f32<4, false>; break;
+        case 8: fn = d4 ? launch_f32<8, true> : launch_f32<8, false>; break;
         default: return false;
     }
+    if (d4 && G != 8) return false;
     out->kind = KIND_F32;
     out->nb_tile = F_TN / 16;
     out->tokens_per_block = F_TM;
     out->block_threads = 256;
     out->lds_bytes = (size_t)G * (F_TM + F_TN) * F_PAD * sizeof(float);
     out->launch = fn;
-    snprintf(out->name, sizeof(out->name), "f32 valu G=%d tile=%dx%d", G, F_TM, F_TN);
+    snprintf(out->name, sizeof(out->name), "f32 valu %s%d tile=%dx%d", d4 ? "D" : "G=", d4 ? 4 : G, F_TM, F_TN);
     return true;
 }
 

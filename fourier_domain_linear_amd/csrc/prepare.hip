@@ -9,6 +9,10 @@
 //
 // Unrolled weight ("Declaración del Problema": the naive layer replicates and cyclically shifts the
 // shared weights into a dense matrix): E[o*G+h][i*G+g] = W[o][i][(h-g) mod G].
+//
+// Every kernel here also serves the dihedral group D4 (d4 = true, G = 8; element a + 4b = r^a s^b):
+// its Fourier transform (dft.h) with the 1/8 and 2/8 scalings, and the group product g^-1 h in place
+// of h - g.
 #include "device_common.h"
 #include "eqlin_internal.h"
 
@@ -17,6 +21,32 @@ namespace eqlin {
 __device__ __forceinline__ float load_w(const void *W, bool is_bf16, size_t idx) {
     return is_bf16 ? __uint_as_float((uint32_t)((const uint16_t *)W)[idx] << 16)
                    : ((const float *)W)[idx];
+}
+
+// The group's forward transform and plane scale, cyclic or D4 (D4 only exists at G = 8).
+template <int G>
+__device__ __forceinline__ void weight_planes(bool d4, const float *v, float *P) {
+    if constexpr (G == 8) {
+        if (d4) {
+            forward_planes_d4(v, P);
+            return;
+        }
+    }
+    forward_planes<G>(v, P);
+}
+
+// Index of g^-1 h: the cyclic (h - g) mod G, or D4's product (r^a s^b)^-1 r^c s^d, which is
+// r^(c - a) s^d when b = 0 and r^(a - c) s^(1 + d) when b = 1 (s r = r^-1 s).
+__device__ __forceinline__ int ginv_h(bool d4, int G, int g, int h) {
+    if (!d4) return (h - g + G) % G;
+    const int a = g & 3, b = g >> 2, c = h & 3, d = h >> 2;
+    return b == 0 ? ((c - a) & 3) + 4 * d : ((a - c) & 3) + 4 * (d ^ 1);
+}
+
+// Index of v^-1: -v mod G, or for D4 r^-a for a rotation and v itself for a reflection.
+__device__ __forceinline__ int ginv(bool d4, int G, int v) {
+    if (!d4) return (G - v) % G;
+    return v >= 4 ? v : (4 - v) & 3;
 }
 
 // Fragment position of What_p[o][i] in the chunked layouts the forward kernels read. Every chunk is
@@ -48,7 +78,7 @@ __device__ __forceinline__ size_t frag_index(int G, int KS, int kind, int o, int
 
 // One thread per (o, i) of the padded domain [NB_total * rows] x [KS * kc]; padding gets zeros.
 template <int G>
-__global__ void k_prep_frag(const void *__restrict__ W, bool w_is_bf16, int C_out, int C_in, int KS,
+__global__ void k_prep_frag(const void *__restrict__ W, bool w_is_bf16, bool d4, int C_out, int C_in, int KS,
                             int NB_total, int kind, uint16_t *__restrict__ frag) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int ipad = KS * (kind == 2 ? 16 : 32), rows = kind == 2 ? 32 : 16;
@@ -58,13 +88,13 @@ __global__ void k_prep_frag(const void *__restrict__ W, bool w_is_bf16, int C_ou
     const bool live = o < C_out && i < C_in;
 #pragma unroll
     for (int d = 0; d < G; ++d) v[d] = live ? load_w(W, w_is_bf16, ((size_t)o * C_in + i) * G + d) : 0.f;
-    forward_planes<G>(v, P);
+    weight_planes<G>(d4, v, P);
 #pragma unroll
-    for (int p = 0; p < G; ++p) frag[frag_index(G, KS, kind, o, i, p)] = pack_bf16(P[p] * plane_scale(G, p));
+    for (int p = 0; p < G; ++p) frag[frag_index(G, KS, kind, o, i, p)] = pack_bf16(P[p] * group_plane_scale(G, d4, p));
 }
 
 template <int G>
-__global__ void k_export_frag(const uint16_t *__restrict__ frag, int C_out, int C_in, int KS, int kind,
+__global__ void k_export_frag(const uint16_t *__restrict__ frag, bool d4, int C_out, int C_in, int KS, int kind,
                               float *__restrict__ out) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= (int64_t)C_out * C_in) return;
@@ -72,56 +102,55 @@ __global__ void k_export_frag(const uint16_t *__restrict__ frag, int C_out, int 
 #pragma unroll
     for (int p = 0; p < G; ++p) {
         const float s = __uint_as_float((uint32_t)frag[frag_index(G, KS, kind, o, i, p)] << 16);
-        out[((size_t)p * C_out + o) * C_in + i] = s / plane_scale(G, p);
+        out[((size_t)p * C_out + o) * C_in + i] = s / group_plane_scale(G, d4, p);
     }
 }
 
 template <int G>
-__global__ void k_prep_plain_f32(const float *__restrict__ W, int C_out, int C_in,
+__global__ void k_prep_plain_f32(const float *__restrict__ W, bool d4, int C_out, int C_in,
                                  float *__restrict__ planes) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= (int64_t)C_out * C_in) return;
     float v[G], P[G];
 #pragma unroll
     for (int d = 0; d < G; ++d) v[d] = W[t * G + d];
-    forward_planes<G>(v, P);
+    weight_planes<G>(d4, v, P);
 #pragma unroll
-    for (int p = 0; p < G; ++p) planes[(size_t)p * C_out * C_in + t] = P[p] * plane_scale(G, p);
+    for (int p = 0; p < G; ++p) planes[(size_t)p * C_out * C_in + t] = P[p] * group_plane_scale(G, d4, p);
 }
 
 template <int G>
-__global__ void k_export_plain_f32(const float *__restrict__ planes, int C_out, int C_in,
+__global__ void k_export_plain_f32(const float *__restrict__ planes, bool d4, int C_out, int C_in,
                                    float *__restrict__ out) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= (int64_t)C_out * C_in) return;
 #pragma unroll
     for (int p = 0; p < G; ++p)
-        out[(size_t)p * C_out * C_in + t] = planes[(size_t)p * C_out * C_in + t] / plane_scale(G, p);
+        out[(size_t)p * C_out * C_in + t] = planes[(size_t)p * C_out * C_in + t] / group_plane_scale(G, d4, p);
 }
 
-// E[o*G+h][i*G+g] = W[o][i][(h-g) mod G]; one thread per element of E.
+// E[o*G+h][i*G+g] = W[o][i][g^-1 h] ((h-g) mod G for the cyclic group); one thread per element of E.
 template <typename T>
-__global__ void k_expand(const T *__restrict__ W, int G, int C_out, int C_in, T *__restrict__ E) {
+__global__ void k_expand(const T *__restrict__ W, bool d4, int G, int C_out, int C_in, T *__restrict__ E) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t cols = (int64_t)C_in * G;
     if (t >= (int64_t)C_out * G * cols) return;
     const int64_t r = t / cols, c = t % cols;
     const int o = (int)(r / G), h = (int)(r % G), i = (int)(c / G), g = (int)(c % G);
-    const int d = (h - g + G) % G;
-    E[t] = W[((int64_t)o * C_in + i) * G + d];
+    E[t] = W[((int64_t)o * C_in + i) * G + ginv_h(d4, G, g, h)];
 }
 
-// Wt[i][o][d] = W[o][i][(G - d) mod G]: the weight of the layer whose forward is this layer's data
-// gradient (dx[n, i, g] = sum_{o, h} W[o, i, (h - g) mod G] dy[n, o, h] = sum_{o, h} Wt[i, o, (g - h) mod G]
-// dy[n, o, h]). Pure index permutation: exact in any element type.
+// Wt[i][o][d] = W[o][i][d^-1] ((G - d) mod G for the cyclic group): the weight of the layer whose
+// forward is this layer's data gradient (dx[n, i, g] = sum_{o, h} W[o, i, g^-1 h] dy[n, o, h]
+// = sum_{o, h} Wt[i, o, h^-1 g] dy[n, o, h]). Pure index permutation: exact in any element type.
 template <typename T>
-__global__ void k_transpose_reverse(const T *__restrict__ W, int G, int C_out, int C_in, T *__restrict__ Wt) {
+__global__ void k_transpose_reverse(const T *__restrict__ W, bool d4, int G, int C_out, int C_in, T *__restrict__ Wt) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= (int64_t)C_out * C_in * G) return;
     const int d = (int)(t % G);
     const int64_t io = t / G;
     const int o = (int)(io % C_out), i = (int)(io / C_out);
-    Wt[t] = W[((int64_t)o * C_in + i) * G + (G - d) % G];
+    Wt[t] = W[((int64_t)o * C_in + i) * G + ginv(d4, G, d)];
 }
 
 static inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
@@ -135,60 +164,60 @@ static inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n
         default: return hipErrorInvalidValue;   \
     }
 
-hipError_t launch_prep_frag(const void *W, bool w_is_bf16, int G, int C_out, int C_in, int KS,
+hipError_t launch_prep_frag(const void *W, bool w_is_bf16, bool d4, int G, int C_out, int C_in, int KS,
                             int NB_total, int kind, void *frag, hipStream_t s) {
     const int64_t n = (int64_t)NB_total * KS * 512;
     DISPATCH_G(G, hipLaunchKernelGGL(k_prep_frag<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s, W,
-                                     w_is_bf16, C_out, C_in, KS, NB_total, kind, (uint16_t *)frag));
+                                     w_is_bf16, d4, C_out, C_in, KS, NB_total, kind, (uint16_t *)frag));
     return hipGetLastError();
 }
 
-hipError_t launch_export_frag(const void *frag, int G, int C_out, int C_in, int KS, int NB_total,
+hipError_t launch_export_frag(const void *frag, bool d4, int G, int C_out, int C_in, int KS, int NB_total,
                               int kind, float *out, hipStream_t s) {
     (void)NB_total;
     const int64_t n = (int64_t)C_out * C_in;
     DISPATCH_G(G, hipLaunchKernelGGL(k_export_frag<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
-                                     (const uint16_t *)frag, C_out, C_in, KS, kind, out));
+                                     (const uint16_t *)frag, d4, C_out, C_in, KS, kind, out));
     return hipGetLastError();
 }
 
-hipError_t launch_prep_plain_f32(const float *W, int G, int C_out, int C_in, float *planes,
+hipError_t launch_prep_plain_f32(const float *W, bool d4, int G, int C_out, int C_in, float *planes,
                                  hipStream_t s) {
     const int64_t n = (int64_t)C_out * C_in;
     DISPATCH_G(G, hipLaunchKernelGGL(k_prep_plain_f32<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
-                                     W, C_out, C_in, planes));
+                                     W, d4, C_out, C_in, planes));
     return hipGetLastError();
 }
 
-hipError_t launch_export_plain_f32(const float *planes, int G, int C_out, int C_in, float *out,
+hipError_t launch_export_plain_f32(const float *planes, bool d4, int G, int C_out, int C_in, float *out,
                                    hipStream_t s) {
     const int64_t n = (int64_t)C_out * C_in;
     DISPATCH_G(G, hipLaunchKernelGGL(k_export_plain_f32<GG>, dim3(blocks_for(n, 256)), dim3(256), 0,
-                                     s, planes, C_out, C_in, out));
+                                     s, planes, d4, C_out, C_in, out));
     return hipGetLastError();
 }
 
-hipError_t launch_transpose_reverse(const void *W, int elem_bytes, int G, int C_out, int C_in, void *Wt,
+hipError_t launch_transpose_reverse(const void *W, int elem_bytes, bool d4, int G, int C_out, int C_in, void *Wt,
                                    hipStream_t s) {
     const int64_t n = (int64_t)C_out * C_in * G;
     if (elem_bytes == 2)
         hipLaunchKernelGGL(k_transpose_reverse<uint16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
-                           (const uint16_t *)W, G, C_out, C_in, (uint16_t *)Wt);
+                           (const uint16_t *)W, d4, G, C_out, C_in, (uint16_t *)Wt);
     else
         hipLaunchKernelGGL(k_transpose_reverse<float>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
-                           (const float *)W, G, C_out, C_in, (float *)Wt);
+                           (const float *)W, d4, G, C_out, C_in, (float *)Wt);
     return hipGetLastError();
 }
 
-hipError_t launch_expand(const void *W, int elem_bytes, int G, int C_out, int C_in, void *E,
+hipError_t launch_expand(const void *W, int elem_bytes, bool d4, int G, int C_out, int C_in, void *E,
                          hipStream_t s) {
     const int64_t n = (int64_t)C_out * G * C_in * G;
     if (elem_bytes == 2)
         hipLaunchKernelGGL(k_expand<uint16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
-                           (const uint16_t *)W, G, C_out, C_in, (uint16_t *)E);
+                           (const uint16_t *)W, d4, G, C_out, C_in, (uint16_t *)E);
     else
         hipLaunchKernelGGL(k_expand<float>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
-                           (const float *)W, G, C_out, C_in, (float *)E);
+                           (const float *)W, d4, G, C_out, C_in, (float *)E);
     return hipGetLastError();
 }
 

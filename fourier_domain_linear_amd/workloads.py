@@ -95,3 +95,11 @@ def make_block_inputs(G: int, C: int, C_h: int, N: int, dtype: str = "bf16", see
     x, W1, b1 = make_inputs(G, C, C_h, N, dtype, seed)
     _, W2, b2 = make_inputs(G, C_h, C, 0, dtype, seed + 104729)
     return x, W1, b1, W2, b2
+
+
+# The dihedral group D4 (rotations and reflections of the square, order 8) at the two p8 shapes: the
+# same tensor sizes as the p8 workloads, a different group.
+D4_WORKLOADS = [
+    Workload("d4_c64_n25088_bf16", G=8, C_in=64, C_out=64, N=32 * 28 * 28, dtype="bf16"),
+    Workload("d4_c256x1024_n12544_bf16", G=8, C_in=256, C_out=1024, N=64 * 14 * 14, dtype="bf16"),
+]

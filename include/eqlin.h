@@ -72,6 +72,22 @@ typedef enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 } eqlin_act_t;
 /* flags for eqlin_prepare_weights */
 #define EQLIN_PREPARE_EXPANDED 1u /* also build the unrolled weight for eqlin_forward_expanded */
 #define EQLIN_PREPARE_BACKWARD 2u /* also build the data-gradient weights for eqlin_backward_data */
+#define EQLIN_PREPARE_D4 4u       /* the group is the dihedral group D4 (needs G = 8), see below */
+
+/*
+ * The dihedral group D4 (EQLIN_PREPARE_D4). The p4 rotations plus the mirror images: the reflection
+ * groups the Flash EQ-Linear page names as the method's next generalisation ("Limitaciones y Trabajo
+ * Futuro"; reflection symmetry also in the EQ-VMamba page's section 5.2). The group axis has 8
+ * entries, element e = a + 4b being r^a s^b (rotation by 90a degrees after the mirror s when b = 1;
+ * s r = r^-1 s), and the layer is the group convolution
+ *
+ *     y[n, o, h] = b[o] + sum_{i, g} W[o, i, g^-1 h] * x[n, i, g]
+ *
+ * (the cyclic layer is the case g^-1 h = h - g mod G). The kernels use D4's Fourier transform over its
+ * irreducible representations (four characters and one 2-D representation): per channel pair four
+ * real products and one 2 x 2 matrix product, twelve real products against 64 for the unrolled block.
+ * Every entry point takes a D4 handle; the backward weights then run on the vector ALU (fp32).
+ */
 
 /*
  * eqlin_prepare_weights -- W -> spectral weights, once per weight set.
@@ -88,7 +104,8 @@ typedef enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 } eqlin_act_t;
  *          EQLIN_BF16 needs C_in % 8 == 0 (else UNSUPPORTED).
  *   flags  EQLIN_PREPARE_EXPANDED to also build the unrolled weight for eqlin_forward_expanded;
  *          EQLIN_PREPARE_BACKWARD to also build the weights of eqlin_backward_data (EQLIN_BF16 then
- *          also needs C_out % 8 == 0, else UNSUPPORTED).
+ *          also needs C_out % 8 == 0, else UNSUPPORTED); EQLIN_PREPARE_D4 for the dihedral group
+ *          (G must be 8, else INVALID_ARG; W's group axis in the element order above).
  *   out    receives the new handle (set to NULL on failure).
  * Allocates device memory (hipMalloc) on the current device; synchronises nothing.
  */
@@ -175,7 +192,10 @@ eqlin_status_t eqlin_destroy(eqlin_handle_t h);
  * eqlin_export_spectral_weights -- copy the stored spectral weights out, for checking.
  * out: device float [G][C_out][C_in], plane order: k = 0 (real); k = G/2 (real, when G >= 2);
  * then Re and Im of each k = 1..G/2-1 in turn. Values are What itself (the forward's internal
- * 1/G and 2/G scalings are undone exactly), as stored: bf16-rounded for an EQLIN_BF16 handle.
+ * 1/G and 2/G scalings are undone exactly), as stored: bf16-rounded for an EQLIN_BF16 handle. A D4
+ * handle's planes are sum_g W[., ., g] chi_k(g) for its four characters chi_k = 1, (-1)^b, (-1)^a,
+ * (-1)^(a+b), then the entries (0,0), (0,1), (1,0), (1,1) of sum_g W[., ., g] rho(g), rho(r^a s^b) =
+ * R^a S^b with R = [[0, -1], [1, 0]] and S = diag(1, -1).
  */
 eqlin_status_t eqlin_export_spectral_weights(eqlin_handle_t h, float *out, eqlin_stream_t stream);
 

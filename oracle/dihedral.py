@@ -30,6 +30,15 @@ import numpy as np
 ORDER = 8
 
 
+def _f64(a) -> np.ndarray:
+    """numpy array or CPU torch tensor (bf16 included) -> float64 numpy array."""
+    if hasattr(a, "detach"):
+        import torch
+
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
 def element(e: int):
     """(a, b) of element index e = a + 4 b (r^a s^b)."""
     return e % 4, e // 4
@@ -54,7 +63,7 @@ def inv(g: int) -> int:
 
 def expand(W) -> np.ndarray:
     """The unrolled weight E[o*8 + h, i*8 + g] = W[o, i, g^-1 h] (fp64)."""
-    W = np.asarray(W, dtype=np.float64)
+    W = _f64(W)
     C_out, C_in, G = W.shape
     if G != ORDER:
         raise ValueError(f"D4 weights need a group axis of 8, got {G}")
@@ -66,15 +75,15 @@ def expand(W) -> np.ndarray:
 def forward(x, W, b=None) -> np.ndarray:
     """y[n, o, h] = b[o] + sum_{i, g} W[o, i, g^-1 h] x[n, i, g] in fp64, as the dense product with
     the unrolled weight (numpy's matmul)."""
-    x = np.asarray(x, dtype=np.float64)
-    W = np.asarray(W, dtype=np.float64)
+    x = _f64(x)
+    W = _f64(W)
     C_out, C_in, G = W.shape
     if x.ndim != 3 or x.shape[1:] != (C_in, G):
         raise ValueError(f"x shape {x.shape} does not match W shape {W.shape}")
     N = x.shape[0]
     y = x.reshape(N, C_in * G) @ expand(W).T
     if b is not None:
-        y = y + np.repeat(np.asarray(b, dtype=np.float64), G)[None, :]
+        y = y + np.repeat(_f64(b), G)[None, :]
     return y.reshape(N, C_out, G)
 
 
@@ -97,10 +106,34 @@ def chi(k: int, g: int) -> float:
 def fourier(f) -> np.ndarray:
     """Fourier transform along the last axis (length 8): [..., 8] with the four characters' values
     first, then the 2-D irrep's F(rho) entries (0,0), (0,1), (1,0), (1,1)."""
-    f = np.asarray(f, dtype=np.float64)
+    f = _f64(f)
     T = np.zeros((8, ORDER))
     for g in range(ORDER):
         for k in range(4):
             T[k, g] = chi(k, g)
         T[4:, g] = rho(g).reshape(4)
     return f @ T.T
+
+
+def backward_data(dy, W) -> np.ndarray:
+    """dx[n, i, g] = sum_{o, h} W[o, i, g^-1 h] dy[n, o, h]: the transpose of the unrolled product."""
+    dy = _f64(dy)
+    W = _f64(W)
+    C_out, C_in, G = W.shape
+    N = dy.shape[0]
+    return (dy.reshape(N, C_out * G) @ expand(W)).reshape(N, C_in, G)
+
+
+def backward_weights(x, dy):
+    """(dW, db): dE = sum over tokens of dy x^T, folded back onto W (dW[o, i, d] is the sum of dE over
+    the (h, g) with g^-1 h = d), db[o] = sum_{n, h} dy[n, o, h]; fp64."""
+    x = _f64(x)
+    dy = _f64(dy)
+    N, C_in, G = x.shape
+    C_out = dy.shape[1]
+    dE = (dy.reshape(N, C_out * G).T @ x.reshape(N, C_in * G)).reshape(C_out, G, C_in, G)  # [o, h, i, g]
+    dW = np.zeros((C_out, C_in, G))
+    for h in range(G):
+        for g in range(G):
+            dW[:, :, mul(inv(g), h)] += dE[:, h, :, g]
+    return dW, dy.sum(axis=(0, 2))

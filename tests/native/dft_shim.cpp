@@ -22,4 +22,7 @@ int dft_inverse(int G, const float *Y, float *y) {
     return -1;
 }
 float dft_plane_scale(int G, int p) { return eqlin::plane_scale(G, p); }
+void d4_forward(const float *v, float *P) { eqlin::forward_planes_d4(v, P); }
+void d4_inverse(const float *Y, float *y) { eqlin::inverse_planes_d4(Y, y); }
+float d4_plane_scale(int p) { return eqlin::plane_scale_d4(p); }
 }

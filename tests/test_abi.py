@@ -62,6 +62,8 @@ def test_prepare_argument_errors(lib):
     # the backward weights need C_out % 8 == 0 in bf16 (C_out is their C_in)
     assert _prepare(lib, fake, 12, 8, 4, dtype=1, flags=eq.EQLIN_PREPARE_BACKWARD)[0] == eq.EQLIN_ERR_UNSUPPORTED
     assert "C_out" in lib.eqlin_last_error().decode()
+    assert _prepare(lib, fake, 4, 8, 4, flags=eq.EQLIN_PREPARE_D4)[0] == eq.EQLIN_ERR_INVALID_ARG  # D4 needs G = 8
+    assert "D4" in lib.eqlin_last_error().decode()
     assert _prepare(lib, fake, (1 << 18) + 1, 8, 4)[0] == eq.EQLIN_ERR_UNSUPPORTED  # C_out * G > 2^20
     assert _prepare(lib, fake, 8, (1 << 17) + 8, 8)[0] == eq.EQLIN_ERR_UNSUPPORTED  # C_in * G > 2^20
     assert "2^20" in lib.eqlin_last_error().decode()

@@ -25,6 +25,10 @@ def shim(tmp_path_factory):
     lib.dft_inverse.argtypes = [ctypes.c_int, fp, fp]
     lib.dft_plane_scale.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.dft_plane_scale.restype = ctypes.c_float
+    lib.d4_forward.argtypes = [fp, fp]
+    lib.d4_inverse.argtypes = [fp, fp]
+    lib.d4_plane_scale.argtypes = [ctypes.c_int]
+    lib.d4_plane_scale.restype = ctypes.c_float
     return lib
 
 
@@ -94,3 +98,48 @@ def test_p4_needs_no_multiplies(shim):
         P = _call(shim.dft_forward, 4, e)
         assert set(np.unique(P)).issubset({-1.0, 0.0, 1.0})
     assert [shim.dft_plane_scale(4, p) for p in range(4)] == [0.25, 0.25, 0.5, 0.5]
+
+
+# ---- D4 (rotations + reflections): the kernels' butterflies against the oracle's irreps ----
+
+def _d4(fn, v):
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(8, dtype=np.float32)
+    fp = ctypes.POINTER(ctypes.c_float)
+    fn(v.ctypes.data_as(fp), out.ctypes.data_as(fp))
+    return out
+
+
+def test_d4_forward_matches_irreps(shim):
+    from oracle import dihedral
+
+    rng = np.random.default_rng(31)
+    for _ in range(50):
+        v = rng.standard_normal(8).astype(np.float32)
+        np.testing.assert_allclose(_d4(shim.d4_forward, v), dihedral.fourier(v.astype(np.float64)),
+                                   rtol=0, atol=2e-6)
+    # coefficients 0 / +-1 only
+    for e in range(8):
+        u = np.zeros(8, dtype=np.float32)
+        u[e] = 1
+        assert set(np.unique(_d4(shim.d4_forward, u))).issubset({-1.0, 0.0, 1.0})
+
+
+def test_d4_inverse_and_group_convolution(shim):
+    # x, w -> planes; Y = X W per irrep (characters: products; rho: 2 x 2 product X @ W) with the
+    # scales; inverse -> the group convolution y(h) = sum_g w(g^-1 h) x(g) written with the oracle's
+    # group product
+    from oracle import dihedral as d4
+
+    rng = np.random.default_rng(32)
+    scale = np.array([shim.d4_plane_scale(p) for p in range(8)])
+    assert list(scale) == [0.125] * 4 + [0.25] * 4
+    for _ in range(30):
+        x, w = rng.standard_normal(8), rng.standard_normal(8)
+        X = _d4(shim.d4_forward, x).astype(np.float64)
+        Wp = _d4(shim.d4_forward, w).astype(np.float64) * scale
+        Y = np.empty(8)
+        Y[:4] = X[:4] * Wp[:4]
+        Y[4:] = (X[4:].reshape(2, 2) @ Wp[4:].reshape(2, 2)).reshape(4)
+        ref = np.array([sum(w[d4.mul(d4.inv(g), h)] * x[g] for g in range(8)) for h in range(8)])
+        np.testing.assert_allclose(_d4(shim.d4_inverse, Y), ref, rtol=0, atol=2e-5)

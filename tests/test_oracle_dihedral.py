@@ -133,3 +133,31 @@ def test_empty_and_bad_shapes():
     assert d4.forward(np.zeros((0, 3, 8)), _rand((2, 3, 8), 14)).shape == (0, 2, 8)
     with pytest.raises(ValueError):
         d4.forward(np.zeros((1, 3, 4)), _rand((2, 3, 4), 15))
+
+
+def test_backward_adjoint_identities():
+    # <dy, y(x)> = <dx, x> (x -> y is linear without bias) and <dy, y(W)> = <dW, W>, against forward
+    x, W, dy = _rand((5, 3, 8), 16), _rand((4, 3, 8), 17), _rand((5, 4, 8), 18)
+    y = d4.forward(x, W)
+    dx = d4.backward_data(dy, W)
+    dW, db = d4.backward_weights(x, dy)
+    assert abs(np.sum(dy * y) - np.sum(dx * x)) <= 1e-10 * np.abs(dy * y).sum()
+    assert abs(np.sum(dy * y) - np.sum(dW * W)) <= 1e-10 * np.abs(dy * y).sum()
+    np.testing.assert_allclose(db, dy.sum(axis=(0, 2)), rtol=1e-14)
+
+
+def test_backward_finite_differences():
+    # L = sum(c * y(x, W, b)); central differences along random directions
+    x, W, b, c = _rand((3, 2, 8), 19), _rand((3, 2, 8), 20), _rand((3,), 21), _rand((3, 3, 8), 22)
+    L = lambda xx, WW, bb: np.sum(c * d4.forward(xx, WW, bb))
+    dx = d4.backward_data(c, W)
+    dW, db = d4.backward_weights(x, c)
+    eps = 1e-6
+    for (arg, grad, k) in ((x, dx, 0), (W, dW, 1), (b, db, 2)):
+        u = _rand(arg.shape, 23 + k)
+        args_p = [x, W, b]
+        args_m = [x, W, b]
+        args_p[k] = arg + eps * u
+        args_m[k] = arg - eps * u
+        fd = (L(*args_p) - L(*args_m)) / (2 * eps)
+        assert abs(fd - np.sum(grad * u)) <= 1e-6 * max(1.0, abs(fd))
