@@ -90,14 +90,15 @@ def cpu_baseline(w, x, W, b, budget_s: float = 12.0):
     import oracle
 
     threads = oracle.max_threads()
+    fwd = oracle.dihedral.forward if w.group == "d4" else oracle.forward  # D4: numpy's matmul (its BLAS threads)
     pilot = min(w.N, 256)
     t0 = time.perf_counter()
-    oracle.forward(x[:pilot], W, b)
+    fwd(x[:pilot], W, b)
     per_token = (time.perf_counter() - t0) / pilot
     if per_token * w.N <= budget_s / 2:
         passes, t0 = 0, time.perf_counter()
         while passes < 1000 and time.perf_counter() - t0 < budget_s:
-            oracle.forward(x, W, b)
+            fwd(x, W, b)
             passes += 1
         dt = time.perf_counter() - t0
         tokens = passes * w.N
@@ -105,7 +106,7 @@ def cpu_baseline(w, x, W, b, budget_s: float = 12.0):
     else:
         n = min(w.N, max(pilot, int(budget_s / per_token)))
         t0 = time.perf_counter()
-        oracle.forward(x[:n], W, b)
+        fwd(x[:n], W, b)
         dt = time.perf_counter() - t0
         tokens = n
         sample = f"first {n} of {w.N} tokens of the workload"
@@ -219,7 +220,7 @@ def main():
     xs = [xd0] + [xd0.clone() for _ in range(R - 1)]
     ys = [torch.empty((w.N, w.C_out, w.G), dtype=w.torch_dtype, device=dev) for _ in range(R)]
     bd = b.to(dev)
-    h = eq.prepare_weights(W.to(dev), expanded=not args.no_expanded, backward=args.backward)
+    h = eq.prepare_weights(W.to(dev), expanded=not args.no_expanded, backward=args.backward, group=w.group)
     torch.cuda.synchronize()
     log(f"[bench] {h.describe()}  rotating buffer sets: {R} ({R * set_bytes / 2**20:.0f} MiB)")
 
@@ -237,7 +238,7 @@ def main():
     ms = timer(torch, spectral, K, R)
     log(f"[bench] spectral: {ms * 1e3:.2f} us/step")
 
-    F = rl.spectral_flops(w.N, w.C_in, w.C_out, w.G)
+    F = rl.spectral_flops(w.N, w.C_in, w.C_out, w.G, w.group)
     B = rl.spectral_bytes(w.N, w.C_in, w.C_out, w.G, eb)
     peak_c = rl.PEAK_BF16_TFLOPS if w.dtype == "bf16" else rl.PEAK_FP32_TFLOPS
     _, bound = rl.roof_time_s(F, B, peak_c)
@@ -315,7 +316,7 @@ def main():
         "metric": METRIC, "value": w.N / t, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
         "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded Gaussian x, W, b; see fourier_domain_linear_amd/workloads.py)",
-        "config": {"workload": w.name, "G": w.G, "C_in": w.C_in, "C_out": w.C_out, "tokens": w.N,
+        "config": {"workload": w.name, "group": w.group, "G": w.G, "C_in": w.C_in, "C_out": w.C_out, "tokens": w.N,
                    "timing": ("eager launches" if args.no_graph else "one HIP graph of K launches")
                    + f", {R} rotating buffer sets"},
         "roofline": roof,

@@ -13,6 +13,10 @@ via Group-wise Discrete Fourier Transform", gist.science/es/paper/2607.21271):
 In general k = 0 and k = G/2 are real (one real product each) and the G/2 - 1 frequencies between
 them are complex (four real products each), so the spectral path does 2G - 2 real C_out x C_in
 products per token (G = 1: one). Transform adds are O(N*(C_in + C_out)*G) and are not counted.
+
+The dihedral group D4 (order 8; the reflection groups of "Limitaciones y Trabajo Futuro"): four
+characters (one real product each) and one 2-D irreducible representation (a 2 x 2 matrix product:
+eight real products), twelve per token.
 """
 from __future__ import annotations
 
@@ -22,15 +26,19 @@ PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector / MFMA
 
 
-def real_products(G: int) -> int:
+def real_products(G: int, group: str = "cyclic") -> int:
     """Real C_out x C_in matrix products per token on the spectral path."""
+    if group == "d4":
+        if G != 8:
+            raise ValueError("D4 has order 8")
+        return 12
     if G < 1 or (G & (G - 1)):
         raise ValueError("G must be a power of two")
     return 1 if G == 1 else 2 * G - 2
 
 
-def spectral_flops(N: int, C_in: int, C_out: int, G: int) -> int:
-    return 2 * N * C_in * C_out * real_products(G)
+def spectral_flops(N: int, C_in: int, C_out: int, G: int, group: str = "cyclic") -> int:
+    return 2 * N * C_in * C_out * real_products(G, group)
 
 
 def dense_flops(N: int, C_in: int, C_out: int, G: int) -> int:

@@ -31,6 +31,7 @@ class Workload:
     C_out: int
     N: int
     dtype: str  # "f32" or "bf16"
+    group: str = "cyclic"  # or "d4" (G = 8)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -100,6 +101,7 @@ def make_block_inputs(G: int, C: int, C_h: int, N: int, dtype: str = "bf16", see
 # The dihedral group D4 (rotations and reflections of the square, order 8) at the two p8 shapes: the
 # same tensor sizes as the p8 workloads, a different group.
 D4_WORKLOADS = [
-    Workload("d4_c64_n25088_bf16", G=8, C_in=64, C_out=64, N=32 * 28 * 28, dtype="bf16"),
-    Workload("d4_c256x1024_n12544_bf16", G=8, C_in=256, C_out=1024, N=64 * 14 * 14, dtype="bf16"),
+    Workload("d4_c64_n25088_bf16", G=8, C_in=64, C_out=64, N=32 * 28 * 28, dtype="bf16", group="d4"),
+    Workload("d4_c256x1024_n12544_bf16", G=8, C_in=256, C_out=1024, N=64 * 14 * 14, dtype="bf16", group="d4"),
 ]
+BY_NAME.update({w.name: w for w in D4_WORKLOADS})
