@@ -240,7 +240,8 @@ def main():
 
     F = rl.spectral_flops(w.N, w.C_in, w.C_out, w.G, w.group)
     B = rl.spectral_bytes(w.N, w.C_in, w.C_out, w.G, eb)
-    peak_c = rl.PEAK_BF16_TFLOPS if w.dtype == "bf16" else rl.PEAK_FP32_TFLOPS
+    # fp16 matrix cores have the bf16 dense peak on this chip (2.5 PFLOP/s)
+    peak_c = rl.PEAK_BF16_TFLOPS if w.dtype in ("bf16", "f16") else rl.PEAK_FP32_TFLOPS
     _, bound = rl.roof_time_s(F, B, peak_c)
     t = ms / 1e3
     if bound == "hbm":

@@ -33,6 +33,7 @@ EQLIN_ERR_OUT_OF_MEMORY = 3
 EQLIN_ERR_HIP = 4
 EQLIN_F32 = 0
 EQLIN_BF16 = 1
+EQLIN_F16 = 2
 EQLIN_PREPARE_EXPANDED = 1
 EQLIN_PREPARE_BACKWARD = 2
 EQLIN_PREPARE_D4 = 4
@@ -112,9 +113,11 @@ def _stream(t: torch.Tensor):
 def _dtype_code(dt: torch.dtype) -> int:
     if dt == torch.bfloat16:
         return EQLIN_BF16
+    if dt == torch.float16:
+        return EQLIN_F16
     if dt == torch.float32:
         return EQLIN_F32
-    raise TypeError(f"unsupported dtype {dt} (bfloat16 or float32)")
+    raise TypeError(f"unsupported dtype {dt} (bfloat16, float16 or float32)")
 
 
 def _need_cuda(t: torch.Tensor, name: str):

@@ -30,7 +30,7 @@
 //      own), the x fragments through LDS (shared by all waves).
 //   3. k_bw_reduce: sum of the splits, inverse DFT (scaled) -> dW fp32; k_bw_dbsum: db from its
 //      partials.
-// Other cases (fp32, G = 1 or 2, the dihedral group D4): k_bw_direct, the definition above in fp32
+// Other cases (fp32, fp16, G = 1 or 2, the dihedral group D4): k_bw_direct, the definition above in fp32
 // with LDS token tiles. For D4 (element a + 4b = r^a s^b) the definition reads
 // dW[o, i, d] = sum_n sum_h dy[n, o, h] x[n, i, h d^-1] (the g with g^-1 h = d).
 #include <stdio.h>
@@ -324,20 +324,24 @@ __host__ __device__ constexpr int h_dinv(int h, int d) {
     }
 }
 
+// One element of a layer tensor as fp32: T is float, or the 16-bit tag BF16 / F16.
+template <typename T>
+__device__ __forceinline__ float load_elem(const void *p, int64_t k) {
+    if constexpr (__is_same(T, float))
+        return static_cast<const float *>(p)[k];
+    else
+        return elem_to_float<T>(static_cast<const uint16_t *>(p)[k]);
+}
+
 template <typename T, int G, bool D4>
-__global__ __launch_bounds__(256) void k_bw_direct(const T *__restrict__ x, const T *__restrict__ dy, int64_t N,
+__global__ __launch_bounds__(256) void k_bw_direct(const void *__restrict__ x, const void *__restrict__ dy, int64_t N,
                                                    int C_in, int C_out, float *__restrict__ dW) {
     constexpr int TK = 32;
     __shared__ float xs[TK][16][G + 1];
     __shared__ float ds[TK][16][G + 1];
     const int t = threadIdx.x, ol = t >> 4, il = t & 15;
     const int o0 = blockIdx.y * 16, i0 = blockIdx.x * 16;
-    auto ld = [](const T *p, int64_t k) -> float {
-        if constexpr (sizeof(T) == 2)
-            return __uint_as_float((uint32_t)p[k] << 16);
-        else
-            return p[k];
-    };
+    auto ld = [](const void *p, int64_t k) -> float { return load_elem<T>(p, k); };
     float acc[G];
 #pragma unroll
     for (int d = 0; d < G; ++d) acc[d] = 0.f;
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(256) void k_bw_direct(const T *__restrict__ x, cons
 
 // db[o] = sum_{n, h} dy[n, o, h] (fp32): 64 outputs per workgroup, 4 token phases reduced in LDS.
 template <typename T>
-__global__ __launch_bounds__(256) void k_bw_bias(const T *__restrict__ dy, int64_t N, int C_out, int G,
+__global__ __launch_bounds__(256) void k_bw_bias(const void *__restrict__ dy, int64_t N, int C_out, int G,
                                                  float *__restrict__ db) {
     __shared__ float red[4][64];
     const int t = threadIdx.x, ol = t & 63, ph = t >> 6;
@@ -376,11 +380,7 @@ __global__ __launch_bounds__(256) void k_bw_bias(const T *__restrict__ dy, int64
     if (o < C_out)
         for (int64_t n = ph; n < N; n += 4)
             for (int h = 0; h < G; ++h) {
-                const int64_t k = (n * C_out + o) * G + h;
-                if constexpr (sizeof(T) == 2)
-                    s += __uint_as_float((uint32_t)dy[k] << 16);
-                else
-                    s += dy[k];
+                s += load_elem<T>(dy, (n * C_out + o) * G + h);
             }
     red[ph][ol] = s;
     __syncthreads();
@@ -464,10 +464,8 @@ template <typename T, int G, bool D4 = false>
 hipError_t launch_direct(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N,
                          hipStream_t s) {
     hipLaunchKernelGGL((k_bw_direct<T, G, D4>), dim3((p->C_in + 15) / 16, (p->C_out + 15) / 16), dim3(256), 0, s,
-                       (const T *)x, (const T *)dy, N, p->C_in, p->C_out, dW);
-    if (db)
-        hipLaunchKernelGGL(k_bw_bias<T>, dim3((p->C_out + 63) / 64), dim3(256), 0, s, (const T *)dy, N, p->C_out,
-                           G, db);
+                       x, dy, N, p->C_in, p->C_out, dW);
+    if (db) hipLaunchKernelGGL(k_bw_bias<T>, dim3((p->C_out + 63) / 64), dim3(256), 0, s, dy, N, p->C_out, G, db);
     return hipGetLastError();
 }
 
@@ -495,7 +493,8 @@ hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy,
                                    void *ws, hipStream_t s) {
     if (mfma_path(p)) return p->G == 8 ? launch_mfma<8>(p, x, dy, dW, db, N, ws, s)
                                        : launch_mfma<4>(p, x, dy, dW, db, N, ws, s);
-    if (p->dtype == EQLIN_BF16) return launch_direct_g<uint16_t>(p, x, dy, dW, db, N, s);
+    if (p->dtype == EQLIN_BF16) return launch_direct_g<BF16>(p, x, dy, dW, db, N, s);
+    if (p->dtype == EQLIN_F16) return launch_direct_g<F16>(p, x, dy, dW, db, N, s);
     return launch_direct_g<float>(p, x, dy, dW, db, N, s);
 }
 

@@ -1,5 +1,5 @@
-// device_common.h -- small gfx950 helpers shared by the library's kernels: bf16 packing and the
-// bf16 matrix-core instruction used by the spectral and expanded kernels.
+// device_common.h -- small gfx950 helpers shared by the library's kernels: bf16 / fp16 packing and the
+// half-precision matrix-core instructions used by the spectral and expanded kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,6 +62,79 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const uint4 &a, const uint4 &b, f
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+
+// ---- Element types. The half-precision paths run in bf16 (the default) or IEEE fp16 (the page's FP16
+// kernels, "Implementación"); kernels take one of these tags and use the helpers below, which for
+// BF16 are exactly the bf16 functions above. ----
+struct BF16 {
+    static constexpr uint32_t kOne = 0x3f80u;  // 1.0
+};
+struct F16 {
+    static constexpr uint32_t kOne = 0x3c00u;  // 1.0
+};
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <class E>
+__device__ __forceinline__ float elem_lo(uint32_t w) {
+    if constexpr (__is_same(E, F16)) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    else return bf16_lo(w);
+}
+template <class E>
+__device__ __forceinline__ float elem_hi(uint32_t w) {
+    if constexpr (__is_same(E, F16)) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    else return bf16_hi(w);
+}
+template <class E>
+__device__ __forceinline__ float elem_at(const uint4 &v, int e) {
+    const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return (e & 1) ? elem_hi<E>(w) : elem_lo<E>(w);
+}
+template <class E>
+__device__ __forceinline__ float elem_to_float(uint16_t bits) { return elem_lo<E>(bits); }
+// 8 fp32 -> 8 elements, round to nearest even
+template <class E>
+__device__ __forceinline__ uint4 pack8(const float *f) {
+    if constexpr (__is_same(E, F16)) {
+        f32x8 v = {f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]};
+        return __builtin_bit_cast(uint4, __builtin_convertvector(v, f16x8));
+    } else {
+        return pack_bf16x8(f);
+    }
+}
+template <class E>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (__is_same(E, F16)) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        f32x2 v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    } else {
+        return pack_bf16x2(a, b);
+    }
+}
+template <class E>
+__device__ __forceinline__ uint16_t pack1(float a) {
+    if constexpr (__is_same(E, F16)) return __builtin_bit_cast(uint16_t, (_Float16)a);
+    else return pack_bf16(a);
+}
+// the matrix-core products of mfma16x16x32 / mfma32x32x16 in the element type (same layouts)
+template <class E>
+__device__ __forceinline__ f32x4 mma16(const uint4 &a, const uint4 &b, f32x4 c) {
+    if constexpr (__is_same(E, F16))
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return mfma16x16x32(a, b, c);
+}
+template <class E>
+__device__ __forceinline__ f32x16 mma32(const uint4 &a, const uint4 &b, f32x16 c) {
+    if constexpr (__is_same(E, F16))
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return mfma32x32x16(a, b, c);
+}
+// neg_bf16x8 flips the sign bit of each 16-bit lane: the same for fp16.
 
 // Number of real matrix products per frequency-plane set (k = 0 and G/2 real, the rest complex).
 __host__ __device__ constexpr int real_products(int G) { return G == 1 ? 1 : 2 * G - 2; }

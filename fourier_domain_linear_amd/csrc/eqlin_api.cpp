@@ -48,10 +48,11 @@ void free_plan(Plan *p) {
 // Fill p->planes from a weight W[C_out][C_in][G] of p->dtype (W may be the unrolled E, G = 1).
 eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
     hipError_t e;
-    if (p->dtype == EQLIN_BF16) {
+    if (p->dtype != EQLIN_F32) {  // bf16 or fp16: the matrix-core kernels
         if (!eqlin::select_bf16(p->G, p->d4, p->C_in, p->C_out, &p->fwd))
-            return fail(EQLIN_ERR_UNSUPPORTED, "no bf16 kernel for G=%d C_in=%d C_out=%d", p->G, p->C_in,
+            return fail(EQLIN_ERR_UNSUPPORTED, "no half-precision kernel for G=%d C_in=%d C_out=%d", p->G, p->C_in,
                         p->C_out);
+        if (p->dtype == EQLIN_F16 && strncmp(p->fwd.name, "bf16", 4) == 0) memcpy(p->fwd.name, "f16 ", 4);
         const int ks = (p->C_in + p->fwd.kc - 1) / p->fwd.kc;
         p->KS = (ks + p->fwd.ks_mult - 1) / p->fwd.ks_mult * p->fwd.ks_mult;
         const int nb = (p->C_out + p->fwd.rows_per_block - 1) / p->fwd.rows_per_block;
@@ -63,7 +64,7 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
             return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for spectral weights: %s", p->planes_bytes,
                         hipGetErrorString(e));
         }
-        e = eqlin::launch_prep_frag(W, true, p->d4, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->fwd.frag_kind,
+        e = eqlin::launch_prep_frag(W, true, p->dtype == EQLIN_F16, p->d4, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->fwd.frag_kind,
                                     p->planes, s);
         if (e != hipSuccess) return hip_fail(e, "spectral weight preparation");
     } else {
@@ -89,7 +90,7 @@ eqlin_status_t check_forward_args(const Plan *h, const void *x, const void *b, c
     if (N == 0) return EQLIN_OK;
     if (!x || !y) return fail(EQLIN_ERR_INVALID_ARG, "null x or y");
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(EQLIN_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
-    const size_t eb = h->dtype == EQLIN_BF16 ? 2 : 4;
+    const size_t eb = h->dtype == EQLIN_F32 ? 4 : 2;
     if (b && !aligned(b, eb)) return fail(EQLIN_ERR_INVALID_ARG, "b misaligned");
     const int64_t lim = INT64_C(1) << 60;
     if (N > lim / ((int64_t)C_in * G) || N > lim / ((int64_t)C_out * G))
@@ -119,7 +120,8 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
     if (!W) return fail(EQLIN_ERR_INVALID_ARG, "null W");
     if (C_out < 1 || C_in < 1) return fail(EQLIN_ERR_INVALID_ARG, "C_out = %d, C_in = %d must be >= 1", C_out, C_in);
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(EQLIN_ERR_INVALID_ARG, "G = %d not in {1, 2, 4, 8}", G);
-    if (dtype != EQLIN_F32 && dtype != EQLIN_BF16) return fail(EQLIN_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+    if (dtype != EQLIN_F32 && dtype != EQLIN_BF16 && dtype != EQLIN_F16)
+        return fail(EQLIN_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
     if (flags & ~(EQLIN_PREPARE_EXPANDED | EQLIN_PREPARE_BACKWARD | EQLIN_PREPARE_D4))
         return fail(EQLIN_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     const bool d4 = (flags & EQLIN_PREPARE_D4) != 0;
@@ -127,10 +129,10 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
     if ((int64_t)C_out * G > (1 << 20) || (int64_t)C_in * G > (1 << 20))
         return fail(EQLIN_ERR_UNSUPPORTED, "channel counts beyond 2^20 unrolled columns");
     if (!aligned(W, 16)) return fail(EQLIN_ERR_INVALID_ARG, "W must be 16-byte aligned");
-    if (dtype == EQLIN_BF16 && C_in % 8 != 0)
-        return fail(EQLIN_ERR_UNSUPPORTED, "bf16 path needs C_in %% 8 == 0 (C_in = %d)", C_in);
-    if ((flags & EQLIN_PREPARE_BACKWARD) && dtype == EQLIN_BF16 && C_out % 8 != 0)
-        return fail(EQLIN_ERR_UNSUPPORTED, "bf16 backward needs C_out %% 8 == 0 (C_out = %d)", C_out);
+    if (dtype != EQLIN_F32 && C_in % 8 != 0)
+        return fail(EQLIN_ERR_UNSUPPORTED, "bf16/f16 path needs C_in %% 8 == 0 (C_in = %d)", C_in);
+    if ((flags & EQLIN_PREPARE_BACKWARD) && dtype != EQLIN_F32 && C_out % 8 != 0)
+        return fail(EQLIN_ERR_UNSUPPORTED, "bf16/f16 backward needs C_out %% 8 == 0 (C_out = %d)", C_out);
 
     hipStream_t s = (hipStream_t)stream;
     Plan *p = new (std::nothrow) eqlin_plan();
@@ -152,7 +154,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
         return st;
     }
     if (flags & EQLIN_PREPARE_EXPANDED) {
-        const size_t eb = dtype == EQLIN_BF16 ? 2 : 4;
+        const size_t eb = dtype == EQLIN_F32 ? 4 : 2;
         const size_t ebytes = (size_t)C_out * G * C_in * G * eb;
         e = hipMalloc(&p->wexp, ebytes);
         if (e != hipSuccess) {
@@ -184,7 +186,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
         }
     }
     if (flags & EQLIN_PREPARE_BACKWARD) {
-        const size_t eb = dtype == EQLIN_BF16 ? 2 : 4;
+        const size_t eb = dtype == EQLIN_F32 ? 4 : 2;
         const size_t bytes = (size_t)C_out * C_in * G * eb;
         e = hipMalloc(&p->wt, bytes);
         if (e != hipSuccess) {
@@ -309,8 +311,8 @@ eqlin_status_t eqlin_export_spectral_weights(eqlin_handle_t h, float *out, eqlin
     g_err[0] = 0;
     if (!h || !out) return fail(EQLIN_ERR_INVALID_ARG, "null handle or out");
     hipError_t e;
-    if (h->dtype == EQLIN_BF16)
-        e = eqlin::launch_export_frag(h->planes, h->d4, h->G, h->C_out, h->C_in, h->KS, h->NB_total,
+    if (h->dtype != EQLIN_F32)
+        e = eqlin::launch_export_frag(h->planes, h->dtype == EQLIN_F16, h->d4, h->G, h->C_out, h->C_in, h->KS, h->NB_total,
                                       h->fwd.frag_kind, out, (hipStream_t)stream);
     else
         e = eqlin::launch_export_plain_f32((const float *)h->planes, h->d4, h->G, h->C_out, h->C_in, out,
@@ -322,7 +324,7 @@ eqlin_status_t eqlin_export_expanded_weight(eqlin_handle_t h, void *out, eqlin_s
     g_err[0] = 0;
     if (!h || !out) return fail(EQLIN_ERR_INVALID_ARG, "null handle or out");
     if (!h->wexp) return fail(EQLIN_ERR_INVALID_ARG, "handle was prepared without EQLIN_PREPARE_EXPANDED");
-    const size_t eb = h->dtype == EQLIN_BF16 ? 2 : 4;
+    const size_t eb = h->dtype == EQLIN_F32 ? 4 : 2;
     const size_t bytes = (size_t)h->C_out * h->G * h->C_in * h->G * eb;
     hipError_t e = hipMemcpyAsync(out, h->wexp, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
     return e == hipSuccess ? EQLIN_OK : hip_fail(e, "export of the unrolled weight");
@@ -332,7 +334,7 @@ int eqlin_describe(eqlin_handle_t h, char *buf, size_t len) {
     if (!h) return snprintf(buf, len, "(null handle)");
     return snprintf(buf, len,
                     "%s%d C_in=%d C_out=%d %s | forward: %s | expanded: %s | backward data: %s | backward weights: %s",
-                    h->d4 ? "D" : "G=", h->d4 ? 4 : h->G, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : "f32", h->fwd.name,
+                    h->d4 ? "D" : "G=", h->d4 ? 4 : h->G, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : h->dtype == EQLIN_F16 ? "f16" : "f32", h->fwd.name,
                     h->expanded ? h->expanded->fwd.name : "(not prepared)",
                     h->backward ? h->backward->fwd.name : "(not prepared)", eqlin::bw_kernel_name(h));
 }

@@ -84,8 +84,9 @@ hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy,
 const char *bw_kernel_name(const Plan *p);
 
 // ---- prepare.hip ----
-// W [C_out][C_in][G] (bf16 bits or fp32) -> fragment-ordered bf16 spectral planes.
-hipError_t launch_prep_frag(const void *W, bool w_is_bf16, bool d4, int G, int C_out, int C_in, int KS,
+// W [C_out][C_in][G] (16-bit elements of the half type when w_is_half, else fp32) -> fragment-ordered
+// spectral planes in the half type (fp16 when f16, else bf16).
+hipError_t launch_prep_frag(const void *W, bool w_is_half, bool f16, bool d4, int G, int C_out, int C_in, int KS,
                             int NB_total, int frag_kind, void *frag, hipStream_t s);
 // W fp32 -> planes [G][C_out][C_in] fp32.
 hipError_t launch_prep_plain_f32(const float *W, bool d4, int G, int C_out, int C_in, float *planes,
@@ -97,7 +98,7 @@ hipError_t launch_transpose_reverse(const void *W, int elem_bytes, bool d4, int 
 hipError_t launch_expand(const void *W, int elem_bytes, bool d4, int G, int C_out, int C_in, void *E,
                          hipStream_t s);
 // stored spectral weights -> canonical fp32 [G][C_out][C_in] with the scaling undone.
-hipError_t launch_export_frag(const void *frag, bool d4, int G, int C_out, int C_in, int KS, int NB_total,
+hipError_t launch_export_frag(const void *frag, bool f16, bool d4, int G, int C_out, int C_in, int KS, int NB_total,
                               int frag_kind, float *out, hipStream_t s);
 hipError_t launch_export_plain_f32(const float *planes, bool d4, int G, int C_out, int C_in, float *out,
                                    hipStream_t s);

@@ -50,20 +50,20 @@ __device__ __forceinline__ void chunk_to_lds(const uint4 *src_lane, uint4 *dst_w
 
 // G samples of 8 channels (channel-major, sample-minor: element j*G+g) -> G planes of 8 bf16 (the
 // cyclic group's DFT, or D4's Fourier transform when D4).
-template <int G, bool D4>
+template <int G, bool D4, class E>
 __device__ __forceinline__ void dft_to_frags(const uint4 (&r)[G], uint4 (&a)[G]) {
     float pl[G][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         float v[G], P[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) v[g] = bf16_at(r[(j * G + g) >> 3], (j * G + g) & 7);
+        for (int g = 0; g < G; ++g) v[g] = elem_at<E>(r[(j * G + g) >> 3], (j * G + g) & 7);
         group_forward<G, D4>(v, P);
 #pragma unroll
         for (int p = 0; p < G; ++p) pl[p][j] = P[p];
     }
 #pragma unroll
-    for (int p = 0; p < G; ++p) a[p] = pack_bf16x8(pl[p]);
+    for (int p = 0; p < G; ++p) a[p] = pack8<E>(pl[p]);
 }
 
 // Negated copies of the imaginary planes (p odd, p >= 3) for the Re = XrWr - XiWi products.
@@ -92,34 +92,34 @@ __device__ __forceinline__ void load_x_clamped(const uint4 *__restrict__ x4, int
 // the B operand (columns = tokens): D lane l holds outputs 4*(l/16)+v of token l%16. D4: the four
 // characters' products, then Y(rho) = X(rho) W(rho) entry by entry, Y_ab += W_cb X_ac over c = 0, 1
 // (twelve products; no negated operand).
-template <int G, bool D4>
+template <int G, bool D4, class E>
 __device__ __forceinline__ void spectral_mfma_wx(const uint4 (&w)[G], const uint4 (&a)[G],
                                                  const uint4 (&an)[G], f32x4 (&acc)[G]) {
     if constexpr (D4) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[k] = mfma16x16x32(w[k], a[k], acc[k]);
+        for (int k = 0; k < 4; ++k) acc[k] = mma16<E>(w[k], a[k], acc[k]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int ra = e >> 1, cb = e & 1;
-            acc[4 + e] = mfma16x16x32(w[4 + cb], a[4 + 2 * ra], acc[4 + e]);
-            acc[4 + e] = mfma16x16x32(w[6 + cb], a[5 + 2 * ra], acc[4 + e]);
+            acc[4 + e] = mma16<E>(w[4 + cb], a[4 + 2 * ra], acc[4 + e]);
+            acc[4 + e] = mma16<E>(w[6 + cb], a[5 + 2 * ra], acc[4 + e]);
         }
         return;
     }
-    acc[0] = mfma16x16x32(w[0], a[0], acc[0]);
-    if constexpr (G >= 2) acc[1] = mfma16x16x32(w[1], a[1], acc[1]);
+    acc[0] = mma16<E>(w[0], a[0], acc[0]);
+    if constexpr (G >= 2) acc[1] = mma16<E>(w[1], a[1], acc[1]);
 #pragma unroll
     for (int k = 1; k < G / 2; ++k) {
         const int r = 2 * k, i = 2 * k + 1;
-        acc[r] = mfma16x16x32(w[r], a[r], acc[r]);
-        acc[r] = mfma16x16x32(w[i], an[i], acc[r]);
-        acc[i] = mfma16x16x32(w[i], a[r], acc[i]);
-        acc[i] = mfma16x16x32(w[r], a[i], acc[i]);
+        acc[r] = mma16<E>(w[r], a[r], acc[r]);
+        acc[r] = mma16<E>(w[i], an[i], acc[r]);
+        acc[i] = mma16<E>(w[i], a[r], acc[i]);
+        acc[i] = mma16<E>(w[r], a[i], acc[i]);
     }
 }
 
 // Element-wise tail store for a partial output block or the last token rows: output o0 + v of token n.
-template <int G, bool GELU, bool D4>
+template <int G, bool GELU, bool D4, class E>
 __device__ __forceinline__ void store_quad_masked(const f32x4 (&acc)[G], uint16_t *__restrict__ y,
                                                   int64_t n, int64_t N, int o0, int C_out) {
     if (n >= N) return;
@@ -133,7 +133,7 @@ __device__ __forceinline__ void store_quad_masked(const f32x4 (&acc)[G], uint16_
         apply_act<GELU>(out);
         uint16_t *dst = y + (n * C_out + o0 + v) * G;
 #pragma unroll
-        for (int h = 0; h < G; ++h) dst[h] = pack_bf16(out[h]);
+        for (int h = 0; h < G; ++h) dst[h] = pack1<E>(out[h]);
     }
 }
 
@@ -210,7 +210,7 @@ __device__ __forceinline__ void load_x_raw(const uint4 *__restrict__ x4, int64_t
         }
 }
 
-template <int G, int KS, bool GELU, bool D4>
+template <int G, int KS, bool GELU, bool D4, class E>
 __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__restrict__ x4,
                                                               const uint4 *__restrict__ wfrag,
                                                               const uint16_t *__restrict__ bias,
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
 #pragma unroll
     for (int k = 0; k < kStreamBiasPerThread; ++k) {
         const int t = threadIdx.x + k * NW * 64;
-        if (t < n_bias) lbias[t] = (bias && nb0 * 16 + t < C_out) ? __uint_as_float(braw[k] << 16) : 0.f;
+        if (t < n_bias) lbias[t] = (bias && nb0 * 16 + t < C_out) ? elem_to_float<E>((uint16_t)braw[k]) : 0.f;
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
     asm volatile("s_barrier" ::: "memory");
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
                 uint4 r[G];
 #pragma unroll
                 for (int q = 0; q < G; ++q) r[q] = scratch[swz<SG::PX>(lane & 15, ku * 4 * G + 4 * q + g)];
-                dft_to_frags<G, D4>(r, a[u * SG::U + ku]);
+                dft_to_frags<G, D4, E>(r, a[u * SG::U + ku]);
                 if constexpr (!D4) negate_imag<G>(a[u * SG::U + ku], an[u * SG::U + ku]);
             }
         }
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
 #pragma unroll
                     for (int p = 0; p < G; ++p) bw[1][ks][p] = lds[((nbn * KS + ks) * G + p) * 64 + lane];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) spectral_mfma_wx<G, D4>(bw[0][ks], a[ks], an[ks], acc);
+                for (int ks = 0; ks < KS; ++ks) spectral_mfma_wx<G, D4, E>(bw[0][ks], a[ks], an[ks], acc);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -333,11 +333,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
                 for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                     for (int p = 0; p < G; ++p) bw[0][0][p] = lds[((nb * KS + ks) * G + p) * 64 + lane];
-                    spectral_mfma_wx<G, D4>(bw[0][0], a[ks], an[ks], acc);
+                    spectral_mfma_wx<G, D4, E>(bw[0][0], a[ks], an[ks], acc);
                 }
             }
             if (!vec_rows) {
-                store_quad_masked<G, GELU, D4>(acc, y, nrow0 + (lane & 15), N, (nb0 + nb) * 16 + 4 * g, C_out);
+                store_quad_masked<G, GELU, D4, E>(acc, y, nrow0 + (lane & 15), N, (nb0 + nb) * 16 + 4 * g, C_out);
                 continue;
             }
             // inverse DFT (+ activation) -> this lane's 4 outputs x G (8G bytes) -> staging row lane%16,
@@ -349,8 +349,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
                 for (int v = 0; v < 4; ++v) out[v] = acc[0][v];
                 apply_act<GELU>(out);
                 uint2 w;
-                w.x = pack_bf16x2(out[0], out[1]);
-                w.y = pack_bf16x2(out[2], out[3]);
+                w.x = pack2<E>(out[0], out[1]);
+                w.y = pack2<E>(out[2], out[3]);
                 // 8 bytes at byte (ub*32 + g*8) of the row's 128-byte unit segment
                 const int piece = ub * 2 + (g >> 1);
                 reinterpret_cast<uint2 *>(scratch + swz<SG::PPR>(lane & 15, piece))[g & 1] = w;
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
                         group_inverse<G, D4>(Y, out + vv * G);
                     }
                     apply_act<GELU>(out);
-                    scratch[swz<SG::PPR>(lane & 15, ub * 2 * G + g * (G / 2) + k)] = pack_bf16x8(out);
+                    scratch[swz<SG::PPR>(lane & 15, ub * 2 * G + g * (G / 2) + k)] = pack8<E>(out);
                 }
             }
             if (ub == SG::UO - 1 || nb == nb_end - 1) {
@@ -429,19 +429,23 @@ static hipError_t launch_stream(const Plan *p, const void *x, const void *b, voi
     int64_t wg = std::max<int64_t>(1, p->fwd.num_cus / tiles);
     wg = std::min<int64_t>(wg, blocks);
     const dim3 grid((unsigned)wg, (unsigned)tiles), block(kStreamWaves * 64);
-    if (act == EQLIN_ACT_GELU)
-        hipLaunchKernelGGL((k_stream<G, KS, true, D4>), grid, block, lds, s, (const uint4 *)x, (const uint4 *)p->planes,
-                           (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, p->fwd.nb_tile);
-    else
-        hipLaunchKernelGGL((k_stream<G, KS, false, D4>), grid, block, lds, s, (const uint4 *)x, (const uint4 *)p->planes,
-                           (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, p->fwd.nb_tile);
+    const bool gelu = act == EQLIN_ACT_GELU;
+    auto kern = p->dtype == EQLIN_F16 ? (gelu ? k_stream<G, KS, true, D4, F16> : k_stream<G, KS, false, D4, F16>)
+                                      : (gelu ? k_stream<G, KS, true, D4, BF16> : k_stream<G, KS, false, D4, BF16>);
+    hipLaunchKernelGGL(kern, grid, block, lds, s, (const uint4 *)x, (const uint4 *)p->planes, (const uint16_t *)b,
+                       p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, p->fwd.nb_tile);
     return hipGetLastError();
 }
 
 template <int G, int KS, bool D4>
 static hipError_t init_stream(size_t lds) {
-    const hipError_t e = set_lds_limit((const void *)k_stream<G, KS, false, D4>, lds);
-    return e != hipSuccess ? e : set_lds_limit((const void *)k_stream<G, KS, true, D4>, lds);
+    const void *fns[] = {(const void *)k_stream<G, KS, false, D4, BF16>, (const void *)k_stream<G, KS, true, D4, BF16>,
+                         (const void *)k_stream<G, KS, false, D4, F16>, (const void *)k_stream<G, KS, true, D4, F16>};
+    for (const void *f : fns) {
+        const hipError_t e = set_lds_limit(f, lds);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 struct StreamEntry {

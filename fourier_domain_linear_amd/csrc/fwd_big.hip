@@ -54,25 +54,25 @@ struct BigStage {
 // The products of one K-step for all planes: Re += Wr Xr + (-Wi) Xi, Im += Wi Xr + Wr Xi (wn holds the
 // negated Im weight fragments, indexed like w). F: the accumulators of planes 1.. start from zero
 // (plane 0 always accumulates: it starts from the bias).
-template <int G, bool F>
+template <int G, bool F, class E>
 __device__ __forceinline__ void spectral_mfma32(const uint4 (&w)[G], const uint4 (&wn)[G], const uint4 (&a)[G],
                                                 f32x16 (&acc)[G]) {
     auto c = [&](int p) { return F ? f32x16{} : acc[p]; };
-    acc[0] = mfma32x32x16(w[0], a[0], acc[0]);
-    if constexpr (G >= 2) acc[1] = mfma32x32x16(w[1], a[1], c(1));
+    acc[0] = mma32<E>(w[0], a[0], acc[0]);
+    if constexpr (G >= 2) acc[1] = mma32<E>(w[1], a[1], c(1));
 #pragma unroll
     for (int k = 1; k < G / 2; ++k) {
         const int r = 2 * k, i = 2 * k + 1;
-        acc[r] = mfma32x32x16(w[r], a[r], c(r));
-        acc[r] = mfma32x32x16(wn[i], a[i], acc[r]);
-        acc[i] = mfma32x32x16(w[i], a[r], c(i));
-        acc[i] = mfma32x32x16(w[r], a[i], acc[i]);
+        acc[r] = mma32<E>(w[r], a[r], c(r));
+        acc[r] = mma32<E>(wn[i], a[i], acc[r]);
+        acc[i] = mma32<E>(w[i], a[r], c(i));
+        acc[i] = mma32<E>(w[r], a[i], acc[i]);
     }
 }
 
 // G samples of NCH channels (element j*G+g) -> G planes of NCH bf16 (NCH = 2, 4 or 8); D4: the
 // dihedral group's Fourier transform instead of the cyclic DFT.
-template <int G, int NCH, bool D4 = false>
+template <int G, int NCH, bool D4, class E>
 __device__ __forceinline__ void dft_ch(const uint4 (&r)[NCH * G / 8], float (&pl)[G][NCH]) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
@@ -82,7 +82,7 @@ __device__ __forceinline__ void dft_ch(const uint4 (&r)[NCH * G / 8], float (&pl
             const uint4 &q = r[(j * G + g) >> 3];
             const int e = (j * G + g) & 7;
             const uint32_t wd = (e >> 1) == 0 ? q.x : (e >> 1) == 1 ? q.y : (e >> 1) == 2 ? q.z : q.w;
-            v[g] = (e & 1) ? __uint_as_float(wd & 0xffff0000u) : __uint_as_float(wd << 16);
+            v[g] = (e & 1) ? elem_hi<E>(wd) : elem_lo<E>(wd);
         }
         group_forward<G, D4>(v, P);
 #pragma unroll
@@ -171,7 +171,7 @@ struct BigCfg {
 // Persistent: each workgroup keeps output tile ot (its weights, bias and L2 set) and walks the token
 // tiles tt0, tt0 + tstep, ... (block_tile; tstep = gridDim.x / tiles_o). The load pipeline runs on
 // across tile boundaries, and a tile's outputs are stored while the next tile computes.
-template <int G, int WA, int WB, int OW, int TW, bool VEC, bool GELU>
+template <int G, int WA, int WB, int OW, int TW, bool VEC, bool GELU, class E>
 __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ x4,
                                                       const uint4 *__restrict__ wfrag,
                                                       const uint16_t *__restrict__ bias, int bias_shift,
@@ -253,17 +253,17 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
             const int c0 = cq * NCH;  // first channel of the item within the stage
             uint4 *dst = xb + ((tl >> 5) * KSS + (c0 >> 4)) * G * 64 + ((c0 >> 3) & 1) * 32 + (tl & 31);
             float pl[G][NCH];
-            dft_ch<G, NCH>(src[it], pl);
+            dft_ch<G, NCH, false, E>(src[it], pl);
 #pragma unroll
             for (int p = 0; p < G; ++p) {
                 if constexpr (NCH == 8) {
-                    dst[p * 64] = pack_bf16x8(pl[p]);
+                    dst[p * 64] = pack8<E>(pl[p]);
                 } else if constexpr (NCH == 2) {
-                    reinterpret_cast<uint32_t *>(dst + p * 64)[(c0 >> 1) & 3] = pack_bf16x2(pl[p][0], pl[p][1]);
+                    reinterpret_cast<uint32_t *>(dst + p * 64)[(c0 >> 1) & 3] = pack2<E>(pl[p][0], pl[p][1]);
                 } else {
                     uint2 w;
-                    w.x = pack_bf16x2(pl[p][0], pl[p][1]);
-                    w.y = pack_bf16x2(pl[p][2], pl[p][3]);
+                    w.x = pack2<E>(pl[p][0], pl[p][1]);
+                    w.y = pack2<E>(pl[p][2], pl[p][3]);
                     reinterpret_cast<uint2 *>(dst + p * 64)[(c0 >> 2) & 1] = w;
                 }
             }
@@ -338,9 +338,9 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                 wn[p] = w_neg[(a * KSS + kk) * G + p];
             }
             if (decltype(first)::value && kk == 0)
-                spectral_mfma32<G, true>(wf, wn, xf, acc[a][b]);
+                spectral_mfma32<G, true, E>(wf, wn, xf, acc[a][b]);
             else
-                spectral_mfma32<G, false>(wf, wn, xf, acc[a][b]);
+                spectral_mfma32<G, false, E>(wf, wn, xf, acc[a][b]);
         }
     };
     // One stage (tile k, stage s) in two scheduling regions, so the loads leave in a fixed order:
@@ -400,13 +400,13 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
         // opaque copies, so the compiler does not keep whole tuples live through the loop)
         int tid_b = threadIdx.x;
         asm volatile("" : "+v"(tid_b));
-        const uint4 ones = make_uint4((tid_b & 63) < 32 ? 0x3f80u : 0u, 0u, 0u, 0u);  // bf16 1.0 at k = 0
+        const uint4 ones = make_uint4((tid_b & 63) < 32 ? E::kOne : 0u, 0u, 0u, 0u);  // 1.0 at k = 0
 #pragma unroll
         for (int a = 0; a < WA; ++a) {
             uint32_t bc = bcol[a];
             asm volatile("" : "+v"(bc));
 #pragma unroll
-            for (int b = 0; b < WB; ++b) acc[a][b][0] = mfma32x32x16(make_uint4(bc, 0u, 0u, 0u), ones, f32x16{});
+            for (int b = 0; b < WB; ++b) acc[a][b][0] = mma32<E>(make_uint4(bc, 0u, 0u, 0u), ones, f32x16{});
         }
         const bool has_prev = k > 0 && vec_rows;
         const __amdgpu_buffer_rsrc_t rs_prev = tile_rsrc(k > 0 ? k - 1 : 0);
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                             inverse_planes<G>(Y, out);
                             apply_act<GELU>(out);
 #pragma unroll
-                            for (int g = 0; g < G; ++g) y[(n * C_out + o) * G + g] = pack_bf16(out[g]);
+                            for (int g = 0; g < G; ++g) y[(n * C_out + o) * G + g] = pack1<E>(out[g]);
                         }
                     continue;
                 }
@@ -478,15 +478,15 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                         const int ol = ai * 32 + 8 * vq + 4 * h_e;  // first of the 4 outputs in the unit row
                         if constexpr (G == 1) {
                             uint2 w;
-                            w.x = pack_bf16x2(out[0], out[1]);
-                            w.y = pack_bf16x2(out[2], out[3]);
+                            w.x = pack2<E>(out[0], out[1]);
+                            w.y = pack2<E>(out[2], out[3]);
                             const int piece = ol / 8;  // 8 outputs x 2 B per piece
                             reinterpret_cast<uint2 *>(ust + rcol_e * C::PR + (piece ^ (rcol_e & 7)))[(ol >> 2) & 1] = w;
                         } else {
 #pragma unroll
                             for (int kq = 0; kq < G / 2; ++kq) {
                                 const int piece = ol * G / 8 + kq;
-                                ust[rcol_e * C::PR + (piece ^ (rcol_e & 7))] = pack_bf16x8(out + 8 * kq);
+                                ust[rcol_e * C::PR + (piece ^ (rcol_e & 7))] = pack8<E>(out + 8 * kq);
                             }
                         }
                     }
@@ -541,7 +541,7 @@ struct P8Cfg {
     static_assert(HP * 16 * 64 * 4 <= STG * 16, "a wave's staging holds the four planes it hands over");
 };
 
-template <bool GELU, bool D4>
+template <bool GELU, bool D4, class E>
 __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, const uint4 *__restrict__ wfrag,
                                                   const uint16_t *__restrict__ bias, int bias_shift,
                                                   uint16_t *__restrict__ y, int64_t N, int C_in, int C_out,
@@ -609,10 +609,10 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
         const int c0 = cq * NCH;
         uint4 *dst = xb + ((tl >> 5) * KSS + (c0 >> 4)) * G * 64 + ((c0 >> 3) & 1) * 32 + (tl & 31);
         float pl[G][NCH];
-        dft_ch<G, NCH, D4>(src[0], pl);
+        dft_ch<G, NCH, D4, E>(src[0], pl);
 #pragma unroll
         for (int p = 0; p < G; ++p)
-            reinterpret_cast<uint32_t *>(dst + p * 64)[(c0 >> 1) & 3] = pack_bf16x2(pl[p][0], pl[p][1]);
+            reinterpret_cast<uint32_t *>(dst + p * 64)[(c0 >> 1) & 3] = pack2<E>(pl[p][0], pl[p][1]);
     };
     // a wave's staged block: role r finishes token block r
     auto read_staged = [&](int j) {
@@ -668,31 +668,31 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
                 // D4, role 0: the four characters, one product each; role 1: the 2 x 2 irrep,
                 // Y_ab += W_0b X_a0 + W_1b X_a1 (local planes 0..3 = entries 00, 01, 10, 11)
                 if constexpr (R == 0) {
-                    acc[b][0] = mfma32x32x16(w[0], xf[0], acc[b][0]);
+                    acc[b][0] = mma32<E>(w[0], xf[0], acc[b][0]);
 #pragma unroll
-                    for (int q = 1; q < 4; ++q) acc[b][q] = mfma32x32x16(w[q], xf[q], acc0(q));
+                    for (int q = 1; q < 4; ++q) acc[b][q] = mma32<E>(w[q], xf[q], acc0(q));
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int ra = e >> 1, cb = e & 1;
-                        acc[b][e] = mfma32x32x16(w[cb], xf[2 * ra], acc0(e));
-                        acc[b][e] = mfma32x32x16(w[2 + cb], xf[2 * ra + 1], acc[b][e]);
+                        acc[b][e] = mma32<E>(w[cb], xf[2 * ra], acc0(e));
+                        acc[b][e] = mma32<E>(w[2 + cb], xf[2 * ra + 1], acc[b][e]);
                     }
                 }
             } else if constexpr (R == 0) {
-                acc[b][0] = mfma32x32x16(w[0], xf[0], acc[b][0]);
-                acc[b][1] = mfma32x32x16(w[1], xf[1], acc0(1));
-                acc[b][2] = mfma32x32x16(w[2], xf[2], acc0(2));
-                acc[b][2] = mfma32x32x16(wn[1], xf[3], acc[b][2]);
-                acc[b][3] = mfma32x32x16(w[3], xf[2], acc0(3));
-                acc[b][3] = mfma32x32x16(w[2], xf[3], acc[b][3]);
+                acc[b][0] = mma32<E>(w[0], xf[0], acc[b][0]);
+                acc[b][1] = mma32<E>(w[1], xf[1], acc0(1));
+                acc[b][2] = mma32<E>(w[2], xf[2], acc0(2));
+                acc[b][2] = mma32<E>(wn[1], xf[3], acc[b][2]);
+                acc[b][3] = mma32<E>(w[3], xf[2], acc0(3));
+                acc[b][3] = mma32<E>(w[2], xf[3], acc[b][3]);
             } else {
 #pragma unroll
                 for (int c = 0; c < HP; c += 2) {
-                    acc[b][c] = mfma32x32x16(w[c], xf[c], acc0(c));
-                    acc[b][c] = mfma32x32x16(wn[c / 2], xf[c + 1], acc[b][c]);
-                    acc[b][c + 1] = mfma32x32x16(w[c + 1], xf[c], acc0(c + 1));
-                    acc[b][c + 1] = mfma32x32x16(w[c], xf[c + 1], acc[b][c + 1]);
+                    acc[b][c] = mma32<E>(w[c], xf[c], acc0(c));
+                    acc[b][c] = mma32<E>(wn[c / 2], xf[c + 1], acc[b][c]);
+                    acc[b][c + 1] = mma32<E>(w[c + 1], xf[c], acc0(c + 1));
+                    acc[b][c + 1] = mma32<E>(w[c], xf[c + 1], acc[b][c + 1]);
                 }
             }
         };
@@ -723,11 +723,11 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
             int tid_b = threadIdx.x;
             asm volatile("" : "+v"(tid_b));
             if constexpr (R == 0) {  // the bias enters plane k = 0: one product of the bias column with ones
-                const uint4 ones = make_uint4((tid_b & 63) < 32 ? 0x3f80u : 0u, 0u, 0u, 0u);
+                const uint4 ones = make_uint4((tid_b & 63) < 32 ? E::kOne : 0u, 0u, 0u, 0u);
                 uint32_t bc = bcol;
                 asm volatile("" : "+v"(bc));
 #pragma unroll
-                for (int b = 0; b < WB; ++b) acc[b][0] = mfma32x32x16(make_uint4(bc, 0u, 0u, 0u), ones, f32x16{});
+                for (int b = 0; b < WB; ++b) acc[b][0] = mma32<E>(make_uint4(bc, 0u, 0u, 0u), ones, f32x16{});
             }
             const bool has_prev = k > 0;
             const __amdgpu_buffer_rsrc_t rs_prev = tile_rsrc(k > 0 ? k - 1 : 0);
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(P8Cfg::NT) void k_p8(const uint4 *__restrict__ x4, 
 #pragma unroll
                 for (int kq = 0; kq < G / 2; ++kq) {
                     const int piece = ol * G / 8 + kq;
-                    reinterpret_cast<uint4 *>(mine)[rcol_e * C::PR + (piece ^ (rcol_e & 7))] = pack_bf16x8(out + 8 * kq);
+                    reinterpret_cast<uint4 *>(mine)[rcol_e * C::PR + (piece ^ (rcol_e & 7))] = pack8<E>(out + 8 * kq);
                 }
             }
         }
@@ -804,8 +804,11 @@ static hipError_t launch_p8(const Plan *p, const void *x, const void *b, void *y
     const int64_t grid = per_o * tiles_o;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     const int xg = xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * C::G * 2);
-    auto kern = p->d4 ? (act == EQLIN_ACT_GELU ? k_p8<true, true> : k_p8<false, true>)
-                      : (act == EQLIN_ACT_GELU ? k_p8<true, false> : k_p8<false, false>);
+    const bool gelu = act == EQLIN_ACT_GELU, f16 = p->dtype == EQLIN_F16;
+    auto kern = p->d4 ? (f16 ? (gelu ? k_p8<true, true, F16> : k_p8<false, true, F16>)
+                             : (gelu ? k_p8<true, true, BF16> : k_p8<false, true, BF16>))
+                      : (f16 ? (gelu ? k_p8<true, false, F16> : k_p8<false, false, F16>)
+                             : (gelu ? k_p8<true, false, BF16> : k_p8<false, false, BF16>));
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), 0, s, (const uint4 *)x, (const uint4 *)p->planes,
                        (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS,
                        (int)tiles_t, tiles_o, xg);
@@ -830,8 +833,12 @@ static hipError_t launch_big(const Plan *p, const void *x, const void *b, void *
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     const int xg = xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * G * 2);
     const bool vec = (p->C_out * G) % 8 == 0, gelu = act == EQLIN_ACT_GELU;
-    auto kern = vec ? (gelu ? k_big<G, WA, WB, OW, TW, true, true> : k_big<G, WA, WB, OW, TW, true, false>)
-                    : (gelu ? k_big<G, WA, WB, OW, TW, false, true> : k_big<G, WA, WB, OW, TW, false, false>);
+    auto pick = [&](auto e) {
+        using E = decltype(e);
+        return vec ? (gelu ? k_big<G, WA, WB, OW, TW, true, true, E> : k_big<G, WA, WB, OW, TW, true, false, E>)
+                   : (gelu ? k_big<G, WA, WB, OW, TW, false, true, E> : k_big<G, WA, WB, OW, TW, false, false, E>);
+    };
+    auto kern = p->dtype == EQLIN_F16 ? pick(F16{}) : pick(BF16{});
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), 0, s, (const uint4 *)x, (const uint4 *)p->planes,
                        (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS,
                        (int)tiles_t, tiles_o, xg);

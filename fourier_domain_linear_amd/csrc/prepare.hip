@@ -18,9 +18,10 @@
 
 namespace eqlin {
 
-__device__ __forceinline__ float load_w(const void *W, bool is_bf16, size_t idx) {
-    return is_bf16 ? __uint_as_float((uint32_t)((const uint16_t *)W)[idx] << 16)
-                   : ((const float *)W)[idx];
+// One weight element as fp32; half = true: 16-bit elements of type E (bf16 or fp16), else fp32.
+template <class E>
+__device__ __forceinline__ float load_w(const void *W, bool half, size_t idx) {
+    return half ? elem_to_float<E>(((const uint16_t *)W)[idx]) : ((const float *)W)[idx];
 }
 
 // The group's forward transform and plane scale, cyclic or D4 (D4 only exists at G = 8).
@@ -77,8 +78,9 @@ __device__ __forceinline__ size_t frag_index(int G, int KS, int kind, int o, int
 }
 
 // One thread per (o, i) of the padded domain [NB_total * rows] x [KS * kc]; padding gets zeros.
-template <int G>
-__global__ void k_prep_frag(const void *__restrict__ W, bool w_is_bf16, bool d4, int C_out, int C_in, int KS,
+// planes are stored in E (the layer's half type); W is E as well (w_is_half) or fp32
+template <int G, class E>
+__global__ void k_prep_frag(const void *__restrict__ W, bool w_is_half, bool d4, int C_out, int C_in, int KS,
                             int NB_total, int kind, uint16_t *__restrict__ frag) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int ipad = KS * (kind == 2 ? 16 : 32), rows = kind == 2 ? 32 : 16;
@@ -87,13 +89,13 @@ __global__ void k_prep_frag(const void *__restrict__ W, bool w_is_bf16, bool d4,
     float v[G], P[G];
     const bool live = o < C_out && i < C_in;
 #pragma unroll
-    for (int d = 0; d < G; ++d) v[d] = live ? load_w(W, w_is_bf16, ((size_t)o * C_in + i) * G + d) : 0.f;
+    for (int d = 0; d < G; ++d) v[d] = live ? load_w<E>(W, w_is_half, ((size_t)o * C_in + i) * G + d) : 0.f;
     weight_planes<G>(d4, v, P);
 #pragma unroll
-    for (int p = 0; p < G; ++p) frag[frag_index(G, KS, kind, o, i, p)] = pack_bf16(P[p] * group_plane_scale(G, d4, p));
+    for (int p = 0; p < G; ++p) frag[frag_index(G, KS, kind, o, i, p)] = pack1<E>(P[p] * group_plane_scale(G, d4, p));
 }
 
-template <int G>
+template <int G, class E>
 __global__ void k_export_frag(const uint16_t *__restrict__ frag, bool d4, int C_out, int C_in, int KS, int kind,
                               float *__restrict__ out) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -101,7 +103,7 @@ __global__ void k_export_frag(const uint16_t *__restrict__ frag, bool d4, int C_
     const int o = (int)(t / C_in), i = (int)(t % C_in);
 #pragma unroll
     for (int p = 0; p < G; ++p) {
-        const float s = __uint_as_float((uint32_t)frag[frag_index(G, KS, kind, o, i, p)] << 16);
+        const float s = elem_to_float<E>(frag[frag_index(G, KS, kind, o, i, p)]);
         out[((size_t)p * C_out + o) * C_in + i] = s / group_plane_scale(G, d4, p);
     }
 }
@@ -164,20 +166,28 @@ static inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n
         default: return hipErrorInvalidValue;   \
     }
 
-hipError_t launch_prep_frag(const void *W, bool w_is_bf16, bool d4, int G, int C_out, int C_in, int KS,
+hipError_t launch_prep_frag(const void *W, bool w_is_half, bool f16, bool d4, int G, int C_out, int C_in, int KS,
                             int NB_total, int kind, void *frag, hipStream_t s) {
     const int64_t n = (int64_t)NB_total * KS * 512;
-    DISPATCH_G(G, hipLaunchKernelGGL(k_prep_frag<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s, W,
-                                     w_is_bf16, d4, C_out, C_in, KS, NB_total, kind, (uint16_t *)frag));
+    if (f16)
+        DISPATCH_G(G, hipLaunchKernelGGL((k_prep_frag<GG, F16>), dim3(blocks_for(n, 256)), dim3(256), 0, s, W,
+                                         w_is_half, d4, C_out, C_in, KS, NB_total, kind, (uint16_t *)frag))
+    else
+        DISPATCH_G(G, hipLaunchKernelGGL((k_prep_frag<GG, BF16>), dim3(blocks_for(n, 256)), dim3(256), 0, s, W,
+                                         w_is_half, d4, C_out, C_in, KS, NB_total, kind, (uint16_t *)frag))
     return hipGetLastError();
 }
 
-hipError_t launch_export_frag(const void *frag, bool d4, int G, int C_out, int C_in, int KS, int NB_total,
+hipError_t launch_export_frag(const void *frag, bool f16, bool d4, int G, int C_out, int C_in, int KS, int NB_total,
                               int kind, float *out, hipStream_t s) {
     (void)NB_total;
     const int64_t n = (int64_t)C_out * C_in;
-    DISPATCH_G(G, hipLaunchKernelGGL(k_export_frag<GG>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
-                                     (const uint16_t *)frag, d4, C_out, C_in, KS, kind, out));
+    if (f16)
+        DISPATCH_G(G, hipLaunchKernelGGL((k_export_frag<GG, F16>), dim3(blocks_for(n, 256)), dim3(256), 0, s,
+                                         (const uint16_t *)frag, d4, C_out, C_in, KS, kind, out))
+    else
+        DISPATCH_G(G, hipLaunchKernelGGL((k_export_frag<GG, BF16>), dim3(blocks_for(n, 256)), dim3(256), 0, s,
+                                         (const uint16_t *)frag, d4, C_out, C_in, KS, kind, out))
     return hipGetLastError();
 }
 

@@ -30,12 +30,12 @@ class Workload:
     C_in: int
     C_out: int
     N: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     group: str = "cyclic"  # or "d4" (G = 8)
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.dtype]
 
     @property
     def elem_bytes(self) -> int:
@@ -56,26 +56,28 @@ BENCH_WORKLOAD = WORKLOADS[1]
 
 
 def make_inputs(G: int, C_in: int, C_out: int, N: int, dtype: str = "bf16", seed: int = 0):
-    """Return CPU tensors (x[N, C_in, G], W[C_out, C_in, G], b[C_out]) in the workload dtype."""
-    if dtype not in ("f32", "bf16"):
-        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    """Return CPU tensors (x[N, C_in, G], W[C_out, C_in, G], b[C_out]) in the workload dtype (the same
+    fp32 draws, rounded to nearest even for bf16 / f16)."""
+    if dtype not in ("f32", "bf16", "f16"):
+        raise ValueError(f"dtype must be 'f32', 'bf16' or 'f16', got {dtype!r}")
     gen = torch.Generator().manual_seed(int(seed))
     x = torch.randn((N, C_in, G), generator=gen, dtype=torch.float32)
     W = torch.randn((C_out, C_in, G), generator=gen, dtype=torch.float32) * (C_in * G) ** -0.5
     b = torch.randn((C_out,), generator=gen, dtype=torch.float32) * 0.1
-    if dtype == "bf16":
-        x, W, b = x.to(torch.bfloat16), W.to(torch.bfloat16), b.to(torch.bfloat16)
+    if dtype != "f32":
+        half = torch.bfloat16 if dtype == "bf16" else torch.float16
+        x, W, b = x.to(half), W.to(half), b.to(half)
     return x, W, b
 
 
 def make_grad(G: int, C_out: int, N: int, dtype: str = "bf16", seed: int = 0):
     """An upstream gradient dy[N, C_out, G] ~ N(0, 1) (CPU tensor in the workload dtype) for the
     backward passes; seeded like make_inputs but from its own stream (seed + 7919)."""
-    if dtype not in ("f32", "bf16"):
-        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    if dtype not in ("f32", "bf16", "f16"):
+        raise ValueError(f"dtype must be 'f32', 'bf16' or 'f16', got {dtype!r}")
     gen = torch.Generator().manual_seed(int(seed) + 7919)
     dy = torch.randn((N, C_out, G), generator=gen, dtype=torch.float32)
-    return dy.to(torch.bfloat16) if dtype == "bf16" else dy
+    return dy if dtype == "f32" else dy.to(torch.bfloat16 if dtype == "bf16" else torch.float16)
 
 
 def workload_inputs(w: Workload, seed: int = 0, N: int | None = None):
@@ -105,3 +107,9 @@ D4_WORKLOADS = [
     Workload("d4_c256x1024_n12544_bf16", G=8, C_in=256, C_out=1024, N=64 * 14 * 14, dtype="bf16", group="d4"),
 ]
 BY_NAME.update({w.name: w for w in D4_WORKLOADS})
+
+
+# IEEE half precision (the pages' FP16 kernels) at the four half-precision workload shapes.
+F16_WORKLOADS = [Workload(w.name.replace("_bf16", "_f16"), G=w.G, C_in=w.C_in, C_out=w.C_out, N=w.N, dtype="f16")
+                 for w in WORKLOADS[1:]]
+BY_NAME.update({w.name: w for w in F16_WORKLOADS})

@@ -17,12 +17,13 @@
  * Layouts (row-major, contiguous, group index innermost):
  *   x[N][C_in][G], y[N][C_out][G], W[C_out][C_in][G], b[C_out].
  * Element type: EQLIN_BF16 (bfloat16 in and out, fp32 transforms and accumulation, one
- * round-to-nearest-even at the store) or EQLIN_F32 (fp32 throughout).
+ * round-to-nearest-even at the store), EQLIN_F16 (the same with IEEE half precision: the page's FP16
+ * kernels, "Implementación"; values beyond +-65504 overflow to infinity) or EQLIN_F32 (fp32 throughout).
  *
  * Memory. Every data pointer is a DEVICE pointer on the current HIP device. The caller owns x, W, b
  * and y; the handle owns the spectral weights (and the unrolled weight, when asked for) until
  * eqlin_destroy. x, y and W must be 16-byte aligned; b (optional) 4-byte aligned for f32, 2-byte
- * for bf16. x and y must not overlap.
+ * for bf16 and fp16. x and y must not overlap.
  *
  * Streams. All device work is enqueued on `stream` (NULL = the legacy default stream) and nothing
  * synchronises the host, except where an entry point says otherwise. A handle is immutable after
@@ -54,13 +55,13 @@ typedef struct eqlin_plan *eqlin_handle_t;
 typedef enum {
     EQLIN_OK = 0,
     EQLIN_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, G not in {1,2,4,8}, ... */
-    EQLIN_ERR_UNSUPPORTED = 2,   /* valid layer the kernels do not cover (bf16 with C_in % 8 != 0;
+    EQLIN_ERR_UNSUPPORTED = 2,   /* valid layer the kernels do not cover (bf16/fp16 with C_in % 8 != 0;
                                     C_out * G or C_in * G above 2^20) */
     EQLIN_ERR_OUT_OF_MEMORY = 3, /* device allocation failed */
     EQLIN_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
 } eqlin_status_t;
 
-typedef enum { EQLIN_F32 = 0, EQLIN_BF16 = 1 } eqlin_dtype_t;
+typedef enum { EQLIN_F32 = 0, EQLIN_BF16 = 1, EQLIN_F16 = 2 } eqlin_dtype_t;
 
 /* Element-wise activation applied to the layer's output (after the bias, before the store's single
  * rounding). EQLIN_ACT_GELU is GELU in its exact form, y * Phi(y) = y/2 (1 + erf(y / sqrt 2)): the
@@ -94,16 +95,16 @@ typedef enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 } eqlin_act_t;
  *
  * Computes What[o, i, k] = sum_d W[o, i, d] exp(-2 pi i d k / G) for k = 0..G/2 (the DFT along the
  * group axis, same sign as the input's, no conjugate; "Enfoque Algorítmico") in fp32 and stores it
- * as G real planes in the layout the forward kernels read (bf16 for EQLIN_BF16). It takes the very
+ * as G real planes in the layout the forward kernels read (bf16 / fp16 for EQLIN_BF16 / EQLIN_F16). It takes the very
  * W a naive EQ-Linear uses: the method is a drop-in replacement that needs no retraining
  * ("Implementación": training-free, plug-and-play).
  *
  *   W      device [C_out][C_in][G] of `dtype`; read once, stream-ordered. The caller may free or
  *          overwrite W once `stream` has passed this call.
  *   C_out, C_in >= 1; G in {1, 2, 4, 8}; C_out * G and C_in * G <= 2^20 (else UNSUPPORTED).
- *          EQLIN_BF16 needs C_in % 8 == 0 (else UNSUPPORTED).
+ *          EQLIN_BF16 and EQLIN_F16 need C_in % 8 == 0 (else UNSUPPORTED).
  *   flags  EQLIN_PREPARE_EXPANDED to also build the unrolled weight for eqlin_forward_expanded;
- *          EQLIN_PREPARE_BACKWARD to also build the weights of eqlin_backward_data (EQLIN_BF16 then
+ *          EQLIN_PREPARE_BACKWARD to also build the weights of eqlin_backward_data (bf16/fp16 then
  *          also needs C_out % 8 == 0, else UNSUPPORTED); EQLIN_PREPARE_D4 for the dihedral group
  *          (G must be 8, else INVALID_ARG; W's group axis in the element order above).
  *   out    receives the new handle (set to NULL on failure).
@@ -114,7 +115,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
 
 /*
  * eqlin_forward -- the spectral forward, one fused kernel: load a token tile (G contiguous), group
- * DFT in registers, per-frequency channel products on the matrix cores (bf16 in, fp32 accumulate;
+ * DFT in registers, per-frequency channel products on the matrix cores (bf16 or fp16 in, fp32 accumulate;
  * a complex frequency as four real products), inverse DFT + bias in registers, one store
  * ("Enfoque Algorítmico"; "Implementación": fused dataflow with no intermediate global writes).
  *
@@ -170,9 +171,9 @@ eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, i
  *     dW[o, i, d] = sum_n sum_{h < G} dy[n, o, h] * x[n, i, (h - d) mod G],   db[o] = sum_{n, h} dy[n, o, h]
  *
  * computed per frequency as C_k = sum_n DY_k conj(X_k) (the same group DFT as the forward) followed
- * by the inverse DFT. bf16 with G = 4 or 8: x and dy are transformed into bf16 planes, multiplied on
+ * by the inverse DFT. bf16 with G = 4 or 8 (cyclic): x and dy are transformed into bf16 planes, multiplied on
  * the matrix cores with fp32 accumulation over token splits, and the splits summed in fp32; other
- * cases (fp32, G = 1 or 2) evaluate the definition in fp32 on the vector ALU.
+ * cases (fp32, fp16, G = 1 or 2, D4) evaluate the definition in fp32 on the vector ALU.
  *   x      device [N][C_in][G], dy device [N][C_out][G], both of the handle's dtype.
  *   dW     device float [C_out][C_in][G] (overwritten); db device float [C_out] or NULL (overwritten).
  *   workspace, workspace_bytes: device scratch of at least eqlin_backward_weights_workspace(h, N)
@@ -192,7 +193,8 @@ eqlin_status_t eqlin_destroy(eqlin_handle_t h);
  * eqlin_export_spectral_weights -- copy the stored spectral weights out, for checking.
  * out: device float [G][C_out][C_in], plane order: k = 0 (real); k = G/2 (real, when G >= 2);
  * then Re and Im of each k = 1..G/2-1 in turn. Values are What itself (the forward's internal
- * 1/G and 2/G scalings are undone exactly), as stored: bf16-rounded for an EQLIN_BF16 handle. A D4
+ * 1/G and 2/G scalings are undone exactly), as stored: rounded to the handle's half type for EQLIN_BF16
+ * and EQLIN_F16. A D4
  * handle's planes are sum_g W[., ., g] chi_k(g) for its four characters chi_k = 1, (-1)^b, (-1)^a,
  * (-1)^(a+b), then the entries (0,0), (0,1), (1,0), (1,1) of sum_g W[., ., g] rho(g), rho(r^a s^b) =
  * R^a S^b with R = [[0, -1], [1, 0]] and S = diag(1, -1).

@@ -55,6 +55,7 @@ def test_prepare_argument_errors(lib):
     assert _prepare(lib, fake, 0, 8, 4)[0] == eq.EQLIN_ERR_INVALID_ARG         # C_out < 1
     assert _prepare(lib, fake, 4, -1, 4)[0] == eq.EQLIN_ERR_INVALID_ARG
     assert _prepare(lib, fake, 4, 8, 4, dtype=7)[0] == eq.EQLIN_ERR_INVALID_ARG
+    assert _prepare(lib, fake, 4, 12, 4, dtype=eq.EQLIN_F16)[0] == eq.EQLIN_ERR_UNSUPPORTED  # f16, C_in % 8
     assert _prepare(lib, fake, 4, 8, 4, flags=0x10)[0] == eq.EQLIN_ERR_INVALID_ARG
     assert _prepare(lib, ctypes.c_void_p(0x10008), 4, 8, 4)[0] == eq.EQLIN_ERR_INVALID_ARG  # misaligned
     assert _prepare(lib, fake, 4, 12, 4, dtype=1)[0] == eq.EQLIN_ERR_UNSUPPORTED  # bf16, C_in % 8
