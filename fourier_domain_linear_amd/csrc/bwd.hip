@@ -388,6 +388,253 @@ __global__ __launch_bounds__(256) void k_bw_bias(const void *__restrict__ dy, in
 }
 
 // ------------------------------------------------------------------------------------------------
+// Small channel counts (bf16, cyclic G = 4 or 8, C_in_pad * C_out_pad * G <= 40960): one fused pass.
+// At such sizes the three-pass path spends its time writing and re-reading transformed planes and on
+// 128-wide tiles padding 64 or 96 channels; here each workgroup owns a contiguous token range and the
+// whole C_out x C_in x G spectrum of it in registers (8 waves, at most 5 32x32 accumulator blocks
+// each), so x and dy are read once and only the fp32 partial spectra leave. Per super-chunk of 64
+// tokens every thread issues all its loads at once (at most two items of 8 tokens x 16 bytes), the
+// group DFT writes bf16 K-major fragments (tokens along K, as in pass 1) to LDS, and the waves run
+// their blocks' products over the four 16-token steps; the next super-chunk's loads fly meanwhile.
+// Partials go to part[split][plane][o][i] and db partials to db_part[split][o]; k_bw_small_reduce sums
+// them in a fixed order.
+struct SmallBwCfg {
+    static constexpr int NT = 512, ST = 64, KT = ST / 16, MAXI = 2, MAXB = 5;
+};
+
+template <int G>
+__global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dy,
+                                                  int64_t N, int C_in, int C_out, int tok_wg, int CB_in, int CB_out,
+                                                  float *__restrict__ part, float *__restrict__ db_part) {
+    using C = SmallBwCfg;
+    constexpr int CPU = 8 / G;  // channels per 16-byte unit of a token row
+    extern __shared__ uint4 frag[];  // [KT][CB_in][G] x fragments, then [KT][CB_out][G] dy fragments
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int C_in_pad = CB_in * 32, C_out_pad = CB_out * 32;
+    const int DYB = C::KT * CB_in * G;  // first dy fragment
+    const int64_t n_begin = (int64_t)blockIdx.x * tok_wg;
+    const int64_t n_end = N - n_begin < tok_wg ? N : n_begin + tok_wg;
+    // items (16-byte unit u of a token row, 8-token group tg) per super-chunk: x's first, then dy's;
+    // C_in * G % 64 == 0 makes the x/dy boundary fall between waves, so the tensor is wave-uniform
+    const int ux = C_in / CPU, uy = C_out / CPU;  // 16-byte units per token row
+    const int nx = ux * 8, items = (ux + uy) * 8;
+    auto item = [&](int i, bool &isx, int &tg, int &u) {
+        isx = __builtin_amdgcn_readfirstlane(i < nx ? 1 : 0) != 0;
+        const int k = isx ? i : i - nx, uu = isx ? ux : uy;
+        tg = k / uu;
+        u = k % uu;
+    };
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, (int)(N * C_in * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc((void *)dy, (short)0, (int)(N * C_out * G * 2), 0x00020000);
+
+    // zero the fragments once: channels past C_in / C_out are never written and must read as zeros
+    for (int k = t; k < (DYB + C::KT * CB_out * G) * 64; k += C::NT) frag[k] = make_uint4(0u, 0u, 0u, 0u);
+
+    uint4 raw[C::MAXI][8];
+    auto load = [&](int64_t nb) {  // the super-chunk at token nb: every load in flight at once
+#pragma unroll
+        for (int it = 0; it < C::MAXI; ++it) {
+            const int i = t + it * C::NT;
+            bool isx;
+            int tg, u;
+            item(i, isx, tg, u);
+            const int row = (isx ? C_in : C_out) * G * 2, col = u * 16;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t n = nb + tg * 8 + j;
+                const int off = (i < items && n < n_end) ? (int)(n * row) + col : 0x7fffffff;  // dead: zeros
+                typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(isx ? rx : ry, off, 0, 0);
+                raw[it][j] = make_uint4(v.x, v.y, v.z, v.w);
+            }
+        }
+    };
+    float dbacc[C::MAXI][CPU];
+#pragma unroll
+    for (int it = 0; it < C::MAXI; ++it)
+#pragma unroll
+        for (int c = 0; c < CPU; ++c) dbacc[it][c] = 0.f;
+    auto transform = [&]() {  // raw -> DFT -> bf16 fragments in LDS (+ dy's plane 0 into dbacc)
+#pragma unroll
+        for (int it = 0; it < C::MAXI; ++it) {
+            const int i = t + it * C::NT;
+            if (i >= items) continue;
+            bool isx;
+            int tg, u;
+            item(i, isx, tg, u);
+            const int c0 = u * CPU;
+            const int step = tg >> 1, half = tg & 1;
+#pragma unroll
+            for (int c = 0; c < CPU; ++c) {
+                float pl[G][8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float v[G], P[G];
+#pragma unroll
+                    for (int g = 0; g < G; ++g) v[g] = bf16_at(raw[it][j], c * G + g);
+                    forward_planes<G>(v, P);
+#pragma unroll
+                    for (int q = 0; q < G; ++q) pl[q][j] = P[q];
+                    if (!isx) dbacc[it][c] += P[0];
+                }
+                const int ch = c0 + c;
+                const int base = isx ? (step * CB_in + (ch >> 5)) * G : DYB + (step * CB_out + (ch >> 5)) * G;
+                const int lf = (ch & 31) + 32 * half;
+#pragma unroll
+                for (int q = 0; q < G; ++q) frag[(base + q) * 64 + lf] = pack_bf16x8(pl[q]);
+            }
+        }
+    };
+
+    // accumulator blocks: b = p * tiles + (ob * CB_in + ib), dealt round-robin to the waves (so every
+    // wave gets a mix of real and complex planes)
+    const int tiles = CB_in * CB_out, nbk = tiles * G;
+    f32x16 acc[C::MAXB];
+#pragma unroll
+    for (int q = 0; q < C::MAXB; ++q) acc[q] = f32x16{};
+    // per owned block: its plane and the offsets of its dy (rows = outputs) and x (columns = inputs)
+    // fragments in token step 0 (decoded once, not in the product loop)
+    int bp[C::MAXB], boa[C::MAXB], bob[C::MAXB];
+#pragma unroll
+    for (int q = 0; q < C::MAXB; ++q) {
+        const int b = wave + 8 * q, tile = b % tiles;
+        bp[q] = b < nbk ? b / tiles : -1;
+        boa[q] = (DYB + (tile / CB_in) * G) * 64;
+        bob[q] = ((tile % CB_in) * G) * 64;
+    }
+    auto products = [&](int steps) {
+        for (int k = 0; k < steps; ++k)
+#pragma unroll
+            for (int q = 0; q < C::MAXB; ++q) {
+                const int pp = bp[q];
+                if (pp < 0) continue;  // wave-uniform
+                const uint4 *A = frag + boa[q] + k * CB_out * G * 64 + lane;
+                const uint4 *B = frag + bob[q] + k * CB_in * G * 64 + lane;
+                if (pp < 2) {
+                    acc[q] = mfma32x32x16(A[pp * 64], B[pp * 64], acc[q]);
+                } else if ((pp & 1) == 0) {  // Re C_k = DYr Xr + DYi Xi
+                    acc[q] = mfma32x32x16(A[pp * 64], B[pp * 64], acc[q]);
+                    acc[q] = mfma32x32x16(A[(pp + 1) * 64], B[(pp + 1) * 64], acc[q]);
+                } else {  // Im C_k = DYi Xr - DYr Xi
+                    acc[q] = mfma32x32x16(A[pp * 64], B[(pp - 1) * 64], acc[q]);
+                    acc[q] = mfma32x32x16(neg_bf16x8(A[(pp - 1) * 64]), B[pp * 64], acc[q]);
+                }
+            }
+    };
+
+    load(n_begin);
+    for (int64_t nb = n_begin; nb < n_end; nb += C::ST) {
+        __syncthreads();  // the previous super-chunk's products are done with the fragments
+        transform();
+        __syncthreads();
+        if (nb + C::ST < n_end) load(nb + C::ST);
+        const int64_t left = n_end - nb;
+        products(left >= C::ST ? C::KT : (int)((left + 15) / 16));
+    }
+
+    // partial spectra of this token range, fp32
+    const int64_t plane_sz = (int64_t)C_out_pad * C_in_pad;
+#pragma unroll
+    for (int q = 0; q < C::MAXB; ++q) {
+        const int b = wave + 8 * q;
+        if (b >= nbk) continue;
+        const int pp = b / tiles, tile = b % tiles, ob = tile / CB_in, ib = tile % CB_in;
+        float *dst = part + ((int64_t)blockIdx.x * G + pp) * plane_sz + (int64_t)(ob * 32) * C_in_pad + ib * 32 +
+                     (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[(int64_t)(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * C_in_pad] = acc[q][v];
+    }
+    // db: this range's sum over tokens and h, the 8 token groups added in a fixed order (LDS)
+    __syncthreads();  // every wave is done with the fragments
+    float *red = reinterpret_cast<float *>(frag);  // [8][C_out]
+#pragma unroll
+    for (int it = 0; it < C::MAXI; ++it) {
+        const int i = t + it * C::NT;
+        if (i >= items) continue;
+        bool isx;
+        int tg, u;
+        item(i, isx, tg, u);
+        if (isx) continue;
+#pragma unroll
+        for (int c = 0; c < CPU; ++c) red[tg * C_out + u * CPU + c] = dbacc[it][c];
+    }
+    __syncthreads();
+    for (int o = t; o < C_out; o += C::NT) {
+        float a = 0.f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) a += red[g * C_out + o];
+        db_part[(int64_t)blockIdx.x * C_out_pad + o] = a;
+    }
+}
+
+// Sum of the fused pass's partial spectra over its token ranges in a fixed order (32 interleaved shares,
+// then the shares in turn), scaled inverse DFT -> dW; the trailing workgroups sum the db partials.
+// 32 consecutive (o, i) positions of the padded [C_out][C_in_pad] grid per workgroup, all G planes.
+template <int G>
+__global__ __launch_bounds__(1024) void k_bw_small_reduce(const float *__restrict__ part, const float *__restrict__ db_part,
+                                                         int splits, int C_out, int C_in, int C_out_pad, int C_in_pad,
+                                                         int n_main, float *__restrict__ dW, float *__restrict__ db) {
+    constexpr int NS = 32, KMAX = 8;  // split shares; splits per share (splits <= NS * KMAX)
+    __shared__ float red[NS][G][33];
+    const int t = threadIdx.x, pl = t & 31, sg = t >> 5;
+    if ((int)blockIdx.x < n_main) {
+        const int64_t pos = (int64_t)blockIdx.x * 32 + pl;
+        const int o = (int)(pos / C_in_pad), i = (int)(pos % C_in_pad);
+        const int64_t plane_sz = (int64_t)C_out_pad * C_in_pad;
+        float a[G];
+#pragma unroll
+        for (int p = 0; p < G; ++p) a[p] = 0.f;
+        if (o < C_out) {
+            const float *src = part + (int64_t)o * C_in_pad + i;
+            // every load of the share issued before the first add (the shares are short)
+            float v[KMAX][G];
+#pragma unroll
+            for (int kk = 0; kk < KMAX; ++kk) {
+                const int k = sg + kk * NS;
+#pragma unroll
+                for (int p = 0; p < G; ++p) v[kk][p] = k < splits ? src[((int64_t)k * G + p) * plane_sz] : 0.f;
+            }
+#pragma unroll
+            for (int kk = 0; kk < KMAX; ++kk)
+#pragma unroll
+                for (int p = 0; p < G; ++p) a[p] += v[kk][p];
+        }
+#pragma unroll
+        for (int p = 0; p < G; ++p) red[sg][p][pl] = a[p];
+        __syncthreads();
+        if (sg == 0 && o < C_out && i < C_in) {
+            float Y[G], out[G];
+#pragma unroll
+            for (int p = 0; p < G; ++p) {
+                float v = 0.f;
+#pragma unroll
+                for (int k = 0; k < NS; ++k) v += red[k][p][pl];
+                Y[p] = v * plane_scale(G, p);
+            }
+            inverse_planes<G>(Y, out);
+#pragma unroll
+            for (int d = 0; d < G; ++d) dW[((int64_t)o * C_in + i) * G + d] = out[d];
+        }
+    } else {
+        if (!db) return;  // uniform over the workgroup
+        const int o = ((int)blockIdx.x - n_main) * 32 + pl;
+        float a = 0.f;
+        if (o < C_out)
+            for (int k = sg; k < splits; k += NS) a += db_part[(int64_t)k * C_out_pad + o];
+        red[sg][0][pl] = a;
+        __syncthreads();
+        if (sg == 0 && o < C_out) {
+            float v = 0.f;
+#pragma unroll
+            for (int k = 0; k < NS; ++k) v += red[k][0][pl];
+            db[o] = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Host side: workspace layout and launch.
 namespace {
 
@@ -428,6 +675,58 @@ BwLayout bw_layout(const Plan *p, int64_t N) {
     L.off_db = al(L.off_part + (size_t)L.splits * G * L.C_out_pad * L.C_in_pad * 4);
     L.total = al(L.off_db + (size_t)L.ptiles * L.C_out_pad * 4);
     return L;
+}
+
+// The fused small-channel pass (k_bw_small): its conditions and workspace.
+struct SmallLayout {
+    bool ok = false;
+    int CB_in = 0, CB_out = 0, tok_wg = 0, splits = 0;
+    size_t lds = 0, off_part = 0, off_db = 0, total = 0;
+};
+
+SmallLayout small_layout(const Plan *p, int64_t N) {
+    SmallLayout L;
+    const int G = p->G;
+    if (p->dtype != EQLIN_BF16 || p->d4 || (G != 4 && G != 8) || N <= 0) return L;
+    L.CB_in = (p->C_in + 31) / 32;
+    L.CB_out = (p->C_out + 31) / 32;
+    if (L.CB_in * L.CB_out * G > 8 * SmallBwCfg::MAXB) return L;           // accumulator blocks per workgroup
+    if ((p->C_in + p->C_out) * G > SmallBwCfg::MAXI * SmallBwCfg::NT) return L;  // load items per thread
+    if ((p->C_in * G) % 64 != 0 || p->C_out % 8 != 0) return L;               // wave-uniform x/dy items
+    if (N * p->C_in * G * 2 > 0x7fffffff || N * p->C_out * G * 2 > 0x7fffffff) return L;  // 32-bit offsets
+    L.lds = (size_t)SmallBwCfg::KT * (L.CB_in + L.CB_out) * G * 1024;
+    if (L.lds > 160 * 1024) return L;
+    // one token range per compute unit (each range costs one full C_out x C_in x G partial spectrum)
+    const int ranges = device_num_cus();
+    const int64_t per = (N + ranges - 1) / ranges;
+    L.tok_wg = (int)((per + SmallBwCfg::ST - 1) / SmallBwCfg::ST * SmallBwCfg::ST);
+    L.splits = (int)((N + L.tok_wg - 1) / L.tok_wg);
+    if (L.splits > 256) return L;  // the reduction's shares hold at most 256 ranges
+    auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+    L.off_part = 0;
+    L.off_db = al((size_t)L.splits * G * (L.CB_out * 32) * (L.CB_in * 32) * 4);
+    L.total = al(L.off_db + (size_t)L.splits * (L.CB_out * 32) * 4);
+    L.ok = true;
+    return L;
+}
+
+template <int G>
+hipError_t launch_small(const Plan *p, const SmallLayout &L, const void *x, const void *dy, float *dW, float *db,
+                        int64_t N, void *ws, hipStream_t s) {
+    char *w = static_cast<char *>(ws);
+    float *part = reinterpret_cast<float *>(w + L.off_part), *dbp = reinterpret_cast<float *>(w + L.off_db);
+    if (L.lds > 65536) {
+        const hipError_t e =
+            hipFuncSetAttribute((const void *)k_bw_small<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_bw_small<G>, dim3(L.splits), dim3(SmallBwCfg::NT), L.lds, s, (const uint16_t *)x,
+                       (const uint16_t *)dy, N, p->C_in, p->C_out, L.tok_wg, L.CB_in, L.CB_out, part, dbp);
+    const int n_main = (int)(((int64_t)p->C_out * L.CB_in * 32 + 31) / 32);
+    const int n_db = db ? (p->C_out + 31) / 32 : 0;
+    hipLaunchKernelGGL(k_bw_small_reduce<G>, dim3(n_main + n_db), dim3(1024), 0, s, (const float *)part,
+                       (const float *)dbp, L.splits, p->C_out, p->C_in, L.CB_out * 32, L.CB_in * 32, n_main, dW, db);
+    return hipGetLastError();
 }
 
 BwLayout layout_for(const Plan *p, int64_t N) {
@@ -485,12 +784,17 @@ hipError_t launch_direct_g(const Plan *p, const void *x, const void *dy, float *
 }  // namespace
 
 size_t bw_workspace_bytes(const Plan *p, int64_t N) {
+    const SmallLayout S = small_layout(p, N);
+    if (S.ok) return S.total;
     if (!mfma_path(p) || N <= 0) return 0;
     return layout_for(p, N).total;
 }
 
 hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N,
                                    void *ws, hipStream_t s) {
+    const SmallLayout S = small_layout(p, N);
+    if (S.ok) return p->G == 8 ? launch_small<8>(p, S, x, dy, dW, db, N, ws, s)
+                               : launch_small<4>(p, S, x, dy, dW, db, N, ws, s);
     if (mfma_path(p)) return p->G == 8 ? launch_mfma<8>(p, x, dy, dW, db, N, ws, s)
                                        : launch_mfma<4>(p, x, dy, dW, db, N, ws, s);
     if (p->dtype == EQLIN_BF16) return launch_direct_g<BF16>(p, x, dy, dW, db, N, s);
@@ -499,6 +803,8 @@ hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy,
 }
 
 const char *bw_kernel_name(const Plan *p) {
+    // (the fused pass serves every token count at these channel counts up to the 2 GB offset limit)
+    if (small_layout(p, 1).ok) return "bf16 fused dft + mfma32x32x16 per token range + reduce (small channels)";
     return mfma_path(p) ? "bf16 dft planes + plane-split mfma32x32x16 split-K + reduce" : "direct fp32 valu";
 }
 

@@ -88,6 +88,24 @@ def test_backward_full_size_sampled(w, cuda_device):
     _check(db[torch.as_tensor(osub, device=db.device)], rb, w.dtype, f"{w.name} db sampled")
 
 
+@pytest.mark.parametrize("G,C,N", [(8, 64, 70001), (4, 96, 50003)])
+def test_backward_weights_long_token_ranges(G, C, N, cuda_device):
+    # several 64-token super-chunks per workgroup and a ragged last range (the fused small-channel pass)
+    x, W, _ = make_inputs(G, C, C, N, "bf16", seed=13)
+    dy = make_grad(G, C, N, "bf16", seed=13)
+    h = _handle(W, cuda_device)
+    dW, db = eq.backward_weights(h, x.to(cuda_device), dy.to(cuda_device))
+    torch.cuda.synchronize()
+    print(f"[kernel] {h.describe()}", flush=True)
+    rng = np.random.default_rng(4)
+    osub = np.unique(np.concatenate([[0, C - 1], rng.choice(C, 10, replace=False)]))
+    isub = np.unique(np.concatenate([[0, C - 1], rng.choice(C, 10, replace=False)]))
+    rW, rb = oracle.backward_weights(x[:, isub], dy[:, osub])
+    got = dW[torch.as_tensor(osub, device=dW.device)][:, torch.as_tensor(isub, device=dW.device)]
+    _check(got, rW, "bf16", f"dW G={G} C={C} N={N} sampled channels")
+    _check(db[torch.as_tensor(osub, device=db.device)], rb, "bf16", f"db G={G} C={C} N={N}")
+
+
 def test_backward_weights_empty_and_tiny(cuda_device):
     x, W, _ = make_inputs(8, 32, 64, 1, "bf16", seed=5)
     h = _handle(W, cuda_device)
