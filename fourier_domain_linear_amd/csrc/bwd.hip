@@ -541,10 +541,14 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
         const int b = wave + 8 * q;
         if (b >= nbk) continue;
         const int pp = b / tiles, tile = b % tiles, ob = tile / CB_in, ib = tile % CB_in;
-        float *dst = part + ((int64_t)blockIdx.x * G + pp) * plane_sz + (int64_t)(ob * 32) * C_in_pad + ib * 32 +
-                     (lane & 31);
+        float *dst = part + ((int64_t)blockIdx.x * G + pp) * plane_sz +
+                     (int64_t)(ob * 32 + 4 * (lane >> 5)) * C_in_pad + ib * 32 + (lane & 31);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) dst[(int64_t)(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * C_in_pad] = acc[q][v];
+        for (int v4 = 0; v4 < 4; ++v4) {  // rows 8 * v4 + 4 * (lane / 32) + 0..3
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dst[v * C_in_pad] = acc[q][4 * v4 + v];
+            dst += 8 * C_in_pad;
+        }
     }
     // db: this range's sum over tokens and h, the 8 token groups added in a fixed order (LDS)
     __syncthreads();  // every wave is done with the fragments
@@ -569,14 +573,14 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
     }
 }
 
-// Sum of the fused pass's partial spectra over its token ranges in a fixed order (32 interleaved shares,
+// Sum of the fused pass's partial spectra over its token ranges in a fixed order (16 interleaved shares,
 // then the shares in turn), scaled inverse DFT -> dW; the trailing workgroups sum the db partials.
 // 32 consecutive (o, i) positions of the padded [C_out][C_in_pad] grid per workgroup, all G planes.
 template <int G>
-__global__ __launch_bounds__(1024) void k_bw_small_reduce(const float *__restrict__ part, const float *__restrict__ db_part,
+__global__ __launch_bounds__(512) void k_bw_small_reduce(const float *__restrict__ part, const float *__restrict__ db_part,
                                                          int splits, int C_out, int C_in, int C_out_pad, int C_in_pad,
                                                          int n_main, float *__restrict__ dW, float *__restrict__ db) {
-    constexpr int NS = 32, KMAX = 8;  // split shares; splits per share (splits <= NS * KMAX)
+    constexpr int NS = 16, KMAX = 16;  // split shares; splits per share (splits <= NS * KMAX)
     __shared__ float red[NS][G][33];
     const int t = threadIdx.x, pl = t & 31, sg = t >> 5;
     if ((int)blockIdx.x < n_main) {
@@ -724,7 +728,7 @@ hipError_t launch_small(const Plan *p, const SmallLayout &L, const void *x, cons
                        (const uint16_t *)dy, N, p->C_in, p->C_out, L.tok_wg, L.CB_in, L.CB_out, part, dbp);
     const int n_main = (int)(((int64_t)p->C_out * L.CB_in * 32 + 31) / 32);
     const int n_db = db ? (p->C_out + 31) / 32 : 0;
-    hipLaunchKernelGGL(k_bw_small_reduce<G>, dim3(n_main + n_db), dim3(1024), 0, s, (const float *)part,
+    hipLaunchKernelGGL(k_bw_small_reduce<G>, dim3(n_main + n_db), dim3(512), 0, s, (const float *)part,
                        (const float *)dbp, L.splits, p->C_out, p->C_in, L.CB_out * 32, L.CB_in * 32, n_main, dW, db);
     return hipGetLastError();
 }
