@@ -24,7 +24,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["fourier_domain_linear_amd/csrc/fwd_bf16.hip", "fourier_domain_linear_amd/csrc/device_common.h",
-                  "fourier_domain_linear_amd/csrc/dft.h"]
+                  "fourier_domain_linear_amd/csrc/dft.h", "fourier_domain_linear_amd/csrc/act.h"]
 
 
 def kernel_source_hash() -> str:

@@ -159,3 +159,26 @@ def test_mlp_block_empty_and_one_token(cuda_device):
     _check(y, oracle.mlp_block(x, W1, b1, W2, b2), "bf16", "block N=1")
     y0 = eq.mlp_block(h1, b1.to(cuda_device), h2, b2.to(cuda_device), x[:0].to(cuda_device))
     assert tuple(y0.shape) == (0, 32, 4)
+
+
+def test_block_graph_replay_matches_eager(cuda_device):
+    # the block (two launches, GELU in the first) captured in one HIP graph: every replay equals the
+    # eager result, with unrelated eager work and synchronisations between replays; D4 and fp16 too
+    for group, dtype, G in (("cyclic", "bf16", 4), ("d4", "bf16", 8), ("cyclic", "f16", 4)):
+        x, W1, b1, W2, b2 = make_block_inputs(G, 64, 256, 1000, dtype, seed=12)
+        h1 = eq.prepare_weights(W1.to(cuda_device), group=group)
+        h2 = eq.prepare_weights(W2.to(cuda_device), group=group)
+        xd, b1d, b2d = x.to(cuda_device), b1.to(cuda_device), b2.to(cuda_device)
+        ref = eq.mlp_block(h1, b1d, h2, b2d, xd)
+        hid = torch.empty((1000, 256, G), dtype=ref.dtype, device=cuda_device)
+        y = torch.empty_like(ref)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            eq.mlp_block(h1, b1d, h2, b2d, xd, hid, y)
+        for r in range(3):
+            y.fill_(float("nan"))
+            eq.forward(h1, xd, None, act="gelu")  # unrelated eager work
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, ref), (group, dtype, r)
