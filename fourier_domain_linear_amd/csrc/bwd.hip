@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256) void k_bw_bias(const void *__restrict__ dy, in
 // group DFT writes bf16 K-major fragments (tokens along K, as in pass 1) to LDS, and the waves run
 // their blocks' products over the four 16-token steps; the next super-chunk's loads fly meanwhile.
 // Partials go to part[split][plane][o][i] and db partials to db_part[split][o]; k_bw_small_reduce sums
-// them in a fixed order.
+// them in a fixed order and k_bw_small_inverse applies the inverse DFT.
 struct SmallBwCfg {
     static constexpr int NT = 512, ST = 64, KT = ST / 16, MAXI = 2, MAXB = 5;
 };
@@ -573,53 +573,41 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
     }
 }
 
-// Sum of the fused pass's partial spectra over its token ranges in a fixed order (16 interleaved shares,
-// then the shares in turn), scaled inverse DFT -> dW; the trailing workgroups sum the db partials.
-// 32 consecutive (o, i) positions of the padded [C_out][C_in_pad] grid per workgroup, all G planes.
+// Sum of the fused pass's partial spectra over its token ranges, in a fixed order: one workgroup per
+// (group of 32 consecutive (o, i) positions of the padded [C_out][C_in_pad] grid, plane p), 16
+// interleaved shares of the ranges with every load of a share issued before the first add, then the
+// shares in turn; the scaled plane sums go to `psum` [G][C_out_pad][C_in_pad]. The trailing
+// workgroups sum the db partials. (k_bw_small_inverse then applies the inverse DFT: a second launch,
+// because making the plane sums of other workgroups visible inside this one takes device-scope
+// fences, and each of those writes back an XCD's L2.)
 template <int G>
 __global__ __launch_bounds__(512) void k_bw_small_reduce(const float *__restrict__ part, const float *__restrict__ db_part,
-                                                         int splits, int C_out, int C_in, int C_out_pad, int C_in_pad,
-                                                         int n_main, float *__restrict__ dW, float *__restrict__ db) {
+                                                         int splits, int C_out, int C_out_pad, int C_in_pad, int n_main,
+                                                         float *__restrict__ psum, float *__restrict__ db) {
     constexpr int NS = 16, KMAX = 16;  // split shares; splits per share (splits <= NS * KMAX)
-    __shared__ float red[NS][G][33];
+    __shared__ float red[NS][33];
     const int t = threadIdx.x, pl = t & 31, sg = t >> 5;
+    const int64_t plane_sz = (int64_t)C_out_pad * C_in_pad;
     if ((int)blockIdx.x < n_main) {
-        const int64_t pos = (int64_t)blockIdx.x * 32 + pl;
-        const int o = (int)(pos / C_in_pad), i = (int)(pos % C_in_pad);
-        const int64_t plane_sz = (int64_t)C_out_pad * C_in_pad;
-        float a[G];
+        const int pg = (int)blockIdx.x / G, p = (int)blockIdx.x % G;
+        const int64_t pos = (int64_t)pg * 32 + pl;  // < C_out * C_in_pad
+        const float *src = part + p * plane_sz + pos;
+        float v[KMAX];
 #pragma unroll
-        for (int p = 0; p < G; ++p) a[p] = 0.f;
-        if (o < C_out) {
-            const float *src = part + (int64_t)o * C_in_pad + i;
-            // every load of the share issued before the first add (the shares are short)
-            float v[KMAX][G];
-#pragma unroll
-            for (int kk = 0; kk < KMAX; ++kk) {
-                const int k = sg + kk * NS;
-#pragma unroll
-                for (int p = 0; p < G; ++p) v[kk][p] = k < splits ? src[((int64_t)k * G + p) * plane_sz] : 0.f;
-            }
-#pragma unroll
-            for (int kk = 0; kk < KMAX; ++kk)
-#pragma unroll
-                for (int p = 0; p < G; ++p) a[p] += v[kk][p];
+        for (int kk = 0; kk < KMAX; ++kk) {
+            const int k = sg + kk * NS;
+            v[kk] = k < splits ? src[(int64_t)k * G * plane_sz] : 0.f;
         }
+        float a = 0.f;
 #pragma unroll
-        for (int p = 0; p < G; ++p) red[sg][p][pl] = a[p];
+        for (int kk = 0; kk < KMAX; ++kk) a += v[kk];
+        red[sg][pl] = a;
         __syncthreads();
-        if (sg == 0 && o < C_out && i < C_in) {
-            float Y[G], out[G];
+        if (sg == 0) {
+            float sum = 0.f;
 #pragma unroll
-            for (int p = 0; p < G; ++p) {
-                float v = 0.f;
-#pragma unroll
-                for (int k = 0; k < NS; ++k) v += red[k][p][pl];
-                Y[p] = v * plane_scale(G, p);
-            }
-            inverse_planes<G>(Y, out);
-#pragma unroll
-            for (int d = 0; d < G; ++d) dW[((int64_t)o * C_in + i) * G + d] = out[d];
+            for (int k = 0; k < NS; ++k) sum += red[k][pl];
+            psum[p * plane_sz + pos] = sum * plane_scale(G, p);
         }
     } else {
         if (!db) return;  // uniform over the workgroup
@@ -627,15 +615,31 @@ __global__ __launch_bounds__(512) void k_bw_small_reduce(const float *__restrict
         float a = 0.f;
         if (o < C_out)
             for (int k = sg; k < splits; k += NS) a += db_part[(int64_t)k * C_out_pad + o];
-        red[sg][0][pl] = a;
+        red[sg][pl] = a;
         __syncthreads();
         if (sg == 0 && o < C_out) {
-            float v = 0.f;
+            float sum = 0.f;
 #pragma unroll
-            for (int k = 0; k < NS; ++k) v += red[k][0][pl];
-            db[o] = v;
+            for (int k = 0; k < NS; ++k) sum += red[k][pl];
+            db[o] = sum;
         }
     }
+}
+
+// dW[o, i, :] = inverse DFT of the scaled plane sums; one thread per (o, i).
+template <int G>
+__global__ __launch_bounds__(256) void k_bw_small_inverse(const float *__restrict__ psum, int C_out, int C_in,
+                                                          int C_out_pad, int C_in_pad, float *__restrict__ dW) {
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (k >= (int64_t)C_out * C_in) return;
+    const int o = (int)(k / C_in), i = (int)(k % C_in);
+    const int64_t plane_sz = (int64_t)C_out_pad * C_in_pad;
+    float Y[G], out[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) Y[q] = psum[q * plane_sz + (int64_t)o * C_in_pad + i];
+    inverse_planes<G>(Y, out);
+#pragma unroll
+    for (int d = 0; d < G; ++d) dW[k * G + d] = out[d];
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -685,7 +689,8 @@ BwLayout bw_layout(const Plan *p, int64_t N) {
 struct SmallLayout {
     bool ok = false;
     int CB_in = 0, CB_out = 0, tok_wg = 0, splits = 0;
-    size_t lds = 0, off_part = 0, off_db = 0, total = 0;
+    size_t lds = 0, off_part = 0, off_db = 0, off_psum = 0, total = 0;
+    int n_groups = 0;  // reduction position groups (32 positions of the padded grid)
 };
 
 SmallLayout small_layout(const Plan *p, int64_t N) {
@@ -709,7 +714,9 @@ SmallLayout small_layout(const Plan *p, int64_t N) {
     auto al = [](size_t v) { return (v + 255) / 256 * 256; };
     L.off_part = 0;
     L.off_db = al((size_t)L.splits * G * (L.CB_out * 32) * (L.CB_in * 32) * 4);
-    L.total = al(L.off_db + (size_t)L.splits * (L.CB_out * 32) * 4);
+    L.off_psum = al(L.off_db + (size_t)L.splits * (L.CB_out * 32) * 4);
+    L.n_groups = (int)((int64_t)p->C_out * L.CB_in * 32 / 32);
+    L.total = al(L.off_psum + (size_t)G * (L.CB_out * 32) * (L.CB_in * 32) * 4);
     L.ok = true;
     return L;
 }
@@ -719,6 +726,7 @@ hipError_t launch_small(const Plan *p, const SmallLayout &L, const void *x, cons
                         int64_t N, void *ws, hipStream_t s) {
     char *w = static_cast<char *>(ws);
     float *part = reinterpret_cast<float *>(w + L.off_part), *dbp = reinterpret_cast<float *>(w + L.off_db);
+    float *psum = reinterpret_cast<float *>(w + L.off_psum);
     if (L.lds > 65536) {
         const hipError_t e =
             hipFuncSetAttribute((const void *)k_bw_small<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
@@ -726,10 +734,13 @@ hipError_t launch_small(const Plan *p, const SmallLayout &L, const void *x, cons
     }
     hipLaunchKernelGGL(k_bw_small<G>, dim3(L.splits), dim3(SmallBwCfg::NT), L.lds, s, (const uint16_t *)x,
                        (const uint16_t *)dy, N, p->C_in, p->C_out, L.tok_wg, L.CB_in, L.CB_out, part, dbp);
-    const int n_main = (int)(((int64_t)p->C_out * L.CB_in * 32 + 31) / 32);
+    const int n_main = L.n_groups * G;
     const int n_db = db ? (p->C_out + 31) / 32 : 0;
     hipLaunchKernelGGL(k_bw_small_reduce<G>, dim3(n_main + n_db), dim3(512), 0, s, (const float *)part,
-                       (const float *)dbp, L.splits, p->C_out, p->C_in, L.CB_out * 32, L.CB_in * 32, n_main, dW, db);
+                       (const float *)dbp, L.splits, p->C_out, L.CB_out * 32, L.CB_in * 32, n_main, psum, db);
+    const int64_t n_inv = ((int64_t)p->C_out * p->C_in + 255) / 256;
+    hipLaunchKernelGGL(k_bw_small_inverse<G>, dim3((unsigned)n_inv), dim3(256), 0, s, (const float *)psum, p->C_out,
+                       p->C_in, L.CB_out * 32, L.CB_in * 32, dW);
     return hipGetLastError();
 }
 
