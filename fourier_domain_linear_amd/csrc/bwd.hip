@@ -392,14 +392,19 @@ __global__ __launch_bounds__(256) void k_bw_bias(const void *__restrict__ dy, in
 // At such sizes the three-pass path spends its time writing and re-reading transformed planes and on
 // 128-wide tiles padding 64 or 96 channels; here each workgroup owns a contiguous token range and the
 // whole C_out x C_in x G spectrum of it in registers (8 waves, at most 5 32x32 accumulator blocks
-// each), so x and dy are read once and only the fp32 partial spectra leave. Per super-chunk of 64
-// tokens every thread issues all its loads at once (at most two items of 8 tokens x 16 bytes), the
-// group DFT writes bf16 K-major fragments (tokens along K, as in pass 1) to LDS, and the waves run
-// their blocks' products over the four 16-token steps; the next super-chunk's loads fly meanwhile.
-// Partials go to part[split][plane][o][i] and db partials to db_part[split][o]; k_bw_small_reduce sums
-// them in a fixed order and k_bw_small_inverse applies the inverse DFT.
+// each), so x and dy are read once and only the fp32 partial spectra leave. The range is walked in
+// super-chunks of 32 tokens through two LDS fragment buffers: in step s the waves issue the loads of
+// super-chunk s + 2 (one item of 8 tokens x 16 bytes per thread), run the products of super-chunk s
+// from one buffer and write the group DFT of super-chunk s + 1 (bf16, K-major fragments: tokens along
+// K, as in pass 1) into the other, so the transform's vector ALU and the products overlap and each
+// load has a whole step to arrive. Partials go to part[split][plane][o][i] and db partials to
+// db_part[split][o]; k_bw_small_reduce sums them in a fixed order and k_bw_small_inverse applies the
+// inverse DFT.
 struct SmallBwCfg {
-    static constexpr int NT = 512, ST = 64, KT = ST / 16, MAXI = 2, MAXB = 5;
+    static constexpr int NT = 512, ST = 32, KT = ST / 16;
+    // accumulator blocks per wave: 5 at G = 4 (96 x 96 x 4), 4 at G = 8 (64 x 64 x 8; G = 8's transform
+    // needs the registers)
+    static constexpr int maxb(int G) { return G == 8 ? 4 : 5; }
 };
 
 template <int G>
@@ -408,110 +413,89 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
                                                   float *__restrict__ part, float *__restrict__ db_part) {
     using C = SmallBwCfg;
     constexpr int CPU = 8 / G;  // channels per 16-byte unit of a token row
-    extern __shared__ uint4 frag[];  // [KT][CB_in][G] x fragments, then [KT][CB_out][G] dy fragments
+    constexpr int MAXB = C::maxb(G);
+    extern __shared__ uint4 frag[];  // two buffers of [KT][CB_in][G] x fragments then [KT][CB_out][G] dy fragments
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int C_in_pad = CB_in * 32, C_out_pad = CB_out * 32;
-    const int DYB = C::KT * CB_in * G;  // first dy fragment
+    const int DYB = C::KT * CB_in * G;              // first dy fragment of a buffer
+    const int FR = DYB + C::KT * CB_out * G;        // fragments per buffer
     const int64_t n_begin = (int64_t)blockIdx.x * tok_wg;
     const int64_t n_end = N - n_begin < tok_wg ? N : n_begin + tok_wg;
-    // items (16-byte unit u of a token row, 8-token group tg) per super-chunk: x's first, then dy's;
-    // C_in * G % 64 == 0 makes the x/dy boundary fall between waves, so the tensor is wave-uniform
-    const int ux = C_in / CPU, uy = C_out / CPU;  // 16-byte units per token row
-    const int nx = ux * 8, items = (ux + uy) * 8;
-    auto item = [&](int i, bool &isx, int &tg, int &u) {
-        isx = __builtin_amdgcn_readfirstlane(i < nx ? 1 : 0) != 0;
-        const int k = isx ? i : i - nx, uu = isx ? ux : uy;
-        tg = k / uu;
-        u = k % uu;
-    };
-    const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, (int)(N * C_in * G * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t ry =
-        __builtin_amdgcn_make_buffer_rsrc((void *)dy, (short)0, (int)(N * C_out * G * 2), 0x00020000);
+    const int nsc = (int)((n_end - n_begin + C::ST - 1) / C::ST);  // super-chunks of this range
+    // this thread's item (16-byte unit u of a token row, 8-token group tg) of every super-chunk: x's
+    // items first, then dy's; C_in * G % 128 == 0 puts the boundary between waves (wave-uniform tensor)
+    const int ux = C_in / CPU, uy = C_out / CPU;
+    const int nx = ux * 4, items = (ux + uy) * 4;
+    const bool live = t < items;
+    const bool isx = __builtin_amdgcn_readfirstlane(t < nx ? 1 : 0) != 0;
+    const int ki = isx ? t : t - nx, uu = isx ? ux : uy;
+    const int tg = ki / uu, u = ki % uu;
+    const int row = (isx ? C_in : C_out) * G * 2, col = u * 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(isx ? x : dy), (short)0, (int)(N * (isx ? C_in : C_out) * G * 2), 0x00020000);
 
-    // zero the fragments once: channels past C_in / C_out are never written and must read as zeros
-    for (int k = t; k < (DYB + C::KT * CB_out * G) * 64; k += C::NT) frag[k] = make_uint4(0u, 0u, 0u, 0u);
+    for (int k = t; k < 2 * FR * 64; k += C::NT) frag[k] = make_uint4(0u, 0u, 0u, 0u);  // padded channels
 
-    uint4 raw[C::MAXI][8];
-    auto load = [&](int64_t nb) {  // the super-chunk at token nb: every load in flight at once
+    uint4 raw[2][8];
+    auto load = [&](int sc, uint4 (&dst)[8]) {  // all 8 tokens of this thread's item in flight at once
+        const int64_t nb = n_begin + (int64_t)sc * C::ST + tg * 8;
 #pragma unroll
-        for (int it = 0; it < C::MAXI; ++it) {
-            const int i = t + it * C::NT;
-            bool isx;
-            int tg, u;
-            item(i, isx, tg, u);
-            const int row = (isx ? C_in : C_out) * G * 2, col = u * 16;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t n = nb + tg * 8 + j;
-                const int off = (i < items && n < n_end) ? (int)(n * row) + col : 0x7fffffff;  // dead: zeros
-                typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(isx ? rx : ry, off, 0, 0);
-                raw[it][j] = make_uint4(v.x, v.y, v.z, v.w);
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int64_t n = nb + j;
+            const int off = (live && n < n_end) ? (int)(n * row) + col : 0x7fffffff;  // dead: zeros
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            dst[j] = make_uint4(v.x, v.y, v.z, v.w);
         }
     };
-    float dbacc[C::MAXI][CPU];
+    float dbacc[CPU];
 #pragma unroll
-    for (int it = 0; it < C::MAXI; ++it)
+    for (int c = 0; c < CPU; ++c) dbacc[c] = 0.f;
+    auto transform = [&](const uint4 (&src)[8], int buf) {  // DFT -> bf16 fragments (+ dy's plane 0)
+        if (!live) return;
+        const int step = tg >> 1, half = tg & 1;
 #pragma unroll
-        for (int c = 0; c < CPU; ++c) dbacc[it][c] = 0.f;
-    auto transform = [&]() {  // raw -> DFT -> bf16 fragments in LDS (+ dy's plane 0 into dbacc)
+        for (int c = 0; c < CPU; ++c) {
+            float pl[G][8];
 #pragma unroll
-        for (int it = 0; it < C::MAXI; ++it) {
-            const int i = t + it * C::NT;
-            if (i >= items) continue;
-            bool isx;
-            int tg, u;
-            item(i, isx, tg, u);
-            const int c0 = u * CPU;
-            const int step = tg >> 1, half = tg & 1;
+            for (int j = 0; j < 8; ++j) {
+                float v[G], P[G];
 #pragma unroll
-            for (int c = 0; c < CPU; ++c) {
-                float pl[G][8];
+                for (int g = 0; g < G; ++g) v[g] = bf16_at(src[j], c * G + g);
+                forward_planes<G>(v, P);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    float v[G], P[G];
-#pragma unroll
-                    for (int g = 0; g < G; ++g) v[g] = bf16_at(raw[it][j], c * G + g);
-                    forward_planes<G>(v, P);
-#pragma unroll
-                    for (int q = 0; q < G; ++q) pl[q][j] = P[q];
-                    if (!isx) dbacc[it][c] += P[0];
-                }
-                const int ch = c0 + c;
-                const int base = isx ? (step * CB_in + (ch >> 5)) * G : DYB + (step * CB_out + (ch >> 5)) * G;
-                const int lf = (ch & 31) + 32 * half;
-#pragma unroll
-                for (int q = 0; q < G; ++q) frag[(base + q) * 64 + lf] = pack_bf16x8(pl[q]);
+                for (int q = 0; q < G; ++q) pl[q][j] = P[q];
+                if (!isx) dbacc[c] += P[0];
             }
+            const int ch = u * CPU + c;
+            const int base = buf * FR + (isx ? (step * CB_in + (ch >> 5)) * G : DYB + (step * CB_out + (ch >> 5)) * G);
+            const int lf = (ch & 31) + 32 * half;
+#pragma unroll
+            for (int q = 0; q < G; ++q) frag[(base + q) * 64 + lf] = pack_bf16x8(pl[q]);
         }
     };
 
     // accumulator blocks: b = p * tiles + (ob * CB_in + ib), dealt round-robin to the waves (so every
-    // wave gets a mix of real and complex planes)
+    // wave gets a mix of real and complex planes); plane and fragment offsets decoded once
     const int tiles = CB_in * CB_out, nbk = tiles * G;
-    f32x16 acc[C::MAXB];
+    f32x16 acc[MAXB];
+    int bp[MAXB], boa[MAXB], bob[MAXB];
 #pragma unroll
-    for (int q = 0; q < C::MAXB; ++q) acc[q] = f32x16{};
-    // per owned block: its plane and the offsets of its dy (rows = outputs) and x (columns = inputs)
-    // fragments in token step 0 (decoded once, not in the product loop)
-    int bp[C::MAXB], boa[C::MAXB], bob[C::MAXB];
-#pragma unroll
-    for (int q = 0; q < C::MAXB; ++q) {
+    for (int q = 0; q < MAXB; ++q) {
+        acc[q] = f32x16{};
         const int b = wave + 8 * q, tile = b % tiles;
         bp[q] = b < nbk ? b / tiles : -1;
         boa[q] = (DYB + (tile / CB_in) * G) * 64;
         bob[q] = ((tile % CB_in) * G) * 64;
     }
-    auto products = [&](int steps) {
+    auto products = [&](int buf, int steps) {
         for (int k = 0; k < steps; ++k)
 #pragma unroll
-            for (int q = 0; q < C::MAXB; ++q) {
+            for (int q = 0; q < MAXB; ++q) {
                 const int pp = bp[q];
                 if (pp < 0) continue;  // wave-uniform
-                const uint4 *A = frag + boa[q] + k * CB_out * G * 64 + lane;
-                const uint4 *B = frag + bob[q] + k * CB_in * G * 64 + lane;
+                const uint4 *A = frag + buf * FR * 64 + boa[q] + k * CB_out * G * 64 + lane;  // dy: rows = outputs
+                const uint4 *B = frag + buf * FR * 64 + bob[q] + k * CB_in * G * 64 + lane;   // x: columns = inputs
                 if (pp < 2) {
                     acc[q] = mfma32x32x16(A[pp * 64], B[pp * 64], acc[q]);
                 } else if ((pp & 1) == 0) {  // Re C_k = DYr Xr + DYi Xi
@@ -523,21 +507,34 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
                 }
             }
     };
-
-    load(n_begin);
-    for (int64_t nb = n_begin; nb < n_end; nb += C::ST) {
-        __syncthreads();  // the previous super-chunk's products are done with the fragments
-        transform();
+    auto steps_of = [&](int sc) {  // 16-token steps holding tokens of this range
+        const int64_t left = n_end - n_begin - (int64_t)sc * C::ST;
+        return left >= C::ST ? C::KT : (int)((left + 15) / 16);
+    };
+    // step s: loads of s + 2 into the register set s's data came in, products of s (buffer s % 2),
+    // transform of s + 1 (registers (s + 1) % 2 -> buffer (s + 1) % 2)
+    auto stage = [&](auto rc, int sc) {
+        constexpr int R = decltype(rc)::value;  // sc % 2
+        if (sc + 2 < nsc) load(sc + 2, raw[R]);
+        products(R, steps_of(sc));
+        if (sc + 1 < nsc) transform(raw[1 - R], 1 - R);
         __syncthreads();
-        if (nb + C::ST < n_end) load(nb + C::ST);
-        const int64_t left = n_end - nb;
-        products(left >= C::ST ? C::KT : (int)((left + 15) / 16));
+    };
+
+    __syncthreads();  // zero fill done
+    load(0, raw[0]);
+    if (nsc > 1) load(1, raw[1]);
+    transform(raw[0], 0);
+    __syncthreads();
+    for (int sc = 0; sc < nsc; sc += 2) {
+        stage(IC2<0>{}, sc);
+        if (sc + 1 < nsc) stage(IC2<1>{}, sc + 1);
     }
 
     // partial spectra of this token range, fp32
     const int64_t plane_sz = (int64_t)C_out_pad * C_in_pad;
 #pragma unroll
-    for (int q = 0; q < C::MAXB; ++q) {
+    for (int q = 0; q < MAXB; ++q) {
         const int b = wave + 8 * q;
         if (b >= nbk) continue;
         const int pp = b / tiles, tile = b % tiles, ob = tile / CB_in, ib = tile % CB_in;
@@ -550,25 +547,17 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
             dst += 8 * C_in_pad;
         }
     }
-    // db: this range's sum over tokens and h, the 8 token groups added in a fixed order (LDS)
-    __syncthreads();  // every wave is done with the fragments
-    float *red = reinterpret_cast<float *>(frag);  // [8][C_out]
+    // db: this range's sum over tokens and h, the 4 token groups added in a fixed order (LDS; every wave
+    // is past its last products: the loop ends on a barrier)
+    float *red = reinterpret_cast<float *>(frag);  // [4][C_out]
+    if (live && !isx)
 #pragma unroll
-    for (int it = 0; it < C::MAXI; ++it) {
-        const int i = t + it * C::NT;
-        if (i >= items) continue;
-        bool isx;
-        int tg, u;
-        item(i, isx, tg, u);
-        if (isx) continue;
-#pragma unroll
-        for (int c = 0; c < CPU; ++c) red[tg * C_out + u * CPU + c] = dbacc[it][c];
-    }
+        for (int c = 0; c < CPU; ++c) red[tg * C_out + u * CPU + c] = dbacc[c];
     __syncthreads();
     for (int o = t; o < C_out; o += C::NT) {
         float a = 0.f;
 #pragma unroll
-        for (int g = 0; g < 8; ++g) a += red[g * C_out + o];
+        for (int g = 0; g < 4; ++g) a += red[g * C_out + o];
         db_part[(int64_t)blockIdx.x * C_out_pad + o] = a;
     }
 }
@@ -699,11 +688,11 @@ SmallLayout small_layout(const Plan *p, int64_t N) {
     if (p->dtype != EQLIN_BF16 || p->d4 || (G != 4 && G != 8) || N <= 0) return L;
     L.CB_in = (p->C_in + 31) / 32;
     L.CB_out = (p->C_out + 31) / 32;
-    if (L.CB_in * L.CB_out * G > 8 * SmallBwCfg::MAXB) return L;           // accumulator blocks per workgroup
-    if ((p->C_in + p->C_out) * G > SmallBwCfg::MAXI * SmallBwCfg::NT) return L;  // load items per thread
-    if ((p->C_in * G) % 64 != 0 || p->C_out % 8 != 0) return L;               // wave-uniform x/dy items
+    if (L.CB_in * L.CB_out * G > 8 * SmallBwCfg::maxb(G)) return L;  // accumulator blocks per workgroup
+    if ((p->C_in + p->C_out) * G / 2 > SmallBwCfg::NT) return L;  // one load item per thread
+    if ((p->C_in * G) % 128 != 0 || p->C_out % 8 != 0) return L;  // wave-uniform x/dy items
     if (N * p->C_in * G * 2 > 0x7fffffff || N * p->C_out * G * 2 > 0x7fffffff) return L;  // 32-bit offsets
-    L.lds = (size_t)SmallBwCfg::KT * (L.CB_in + L.CB_out) * G * 1024;
+    L.lds = (size_t)2 * SmallBwCfg::KT * (L.CB_in + L.CB_out) * G * 1024;
     if (L.lds > 160 * 1024) return L;
     // one token range per compute unit (each range costs one full C_out x C_in x G partial spectrum)
     const int ranges = device_num_cus();
