@@ -388,7 +388,9 @@ __global__ __launch_bounds__(256) void k_bw_bias(const void *__restrict__ dy, in
 }
 
 // ------------------------------------------------------------------------------------------------
-// Small channel counts (bf16, cyclic G = 4 or 8, C_in_pad * C_out_pad * G <= 40960): one fused pass.
+// Small channel counts (bf16, G = 4 or 8 cyclic or D4, C_in_pad * C_out_pad * G <= 40960): one fused pass.
+// (D4: the character planes give G_k = sum DY_k X_k, the 2 x 2 irrep G_cb = sum_a X_ac DY_ab, the
+// adjoint of Y = X W; the inverse transform with the forward's scalings then gives dW.)
 // At such sizes the three-pass path spends its time writing and re-reading transformed planes and on
 // 128-wide tiles padding 64 or 96 channels; here each workgroup owns a contiguous token range and the
 // whole C_out x C_in x G spectrum of it in registers (8 waves, at most 5 32x32 accumulator blocks
@@ -407,7 +409,7 @@ struct SmallBwCfg {
     static constexpr int maxb(int G) { return G == 8 ? 4 : 5; }
 };
 
-template <int G>
+template <int G, bool D4>
 __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dy,
                                                   int64_t N, int C_in, int C_out, int tok_wg, int CB_in, int CB_out,
                                                   float *__restrict__ part, float *__restrict__ db_part) {
@@ -462,7 +464,7 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
                 float v[G], P[G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) v[g] = bf16_at(src[j], c * G + g);
-                forward_planes<G>(v, P);
+                group_forward<G, D4>(v, P);
 #pragma unroll
                 for (int q = 0; q < G; ++q) pl[q][j] = P[q];
                 if (!isx) dbacc[c] += P[0];
@@ -496,6 +498,16 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
                 if (pp < 0) continue;  // wave-uniform
                 const uint4 *A = frag + buf * FR * 64 + boa[q] + k * CB_out * G * 64 + lane;  // dy: rows = outputs
                 const uint4 *B = frag + buf * FR * 64 + bob[q] + k * CB_in * G * 64 + lane;   // x: columns = inputs
+                if constexpr (D4) {
+                    if (pp < 4) {  // a character: G_k = sum DY_k X_k
+                        acc[q] = mfma32x32x16(A[pp * 64], B[pp * 64], acc[q]);
+                    } else {  // the 2 x 2 irrep, entry (c, b): G_cb = sum_a X_ac DY_ab
+                        const int c = (pp - 4) >> 1, bb = (pp - 4) & 1;
+                        acc[q] = mfma32x32x16(A[(4 + bb) * 64], B[(4 + c) * 64], acc[q]);
+                        acc[q] = mfma32x32x16(A[(6 + bb) * 64], B[(6 + c) * 64], acc[q]);
+                    }
+                    continue;
+                }
                 if (pp < 2) {
                     acc[q] = mfma32x32x16(A[pp * 64], B[pp * 64], acc[q]);
                 } else if ((pp & 1) == 0) {  // Re C_k = DYr Xr + DYi Xi
@@ -569,7 +581,7 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
 // workgroups sum the db partials. (k_bw_small_inverse then applies the inverse DFT: a second launch,
 // because making the plane sums of other workgroups visible inside this one takes device-scope
 // fences, and each of those writes back an XCD's L2.)
-template <int G>
+template <int G, bool D4>
 __global__ __launch_bounds__(512) void k_bw_small_reduce(const float *__restrict__ part, const float *__restrict__ db_part,
                                                          int splits, int C_out, int C_out_pad, int C_in_pad, int n_main,
                                                          float *__restrict__ psum, float *__restrict__ db) {
@@ -596,7 +608,7 @@ __global__ __launch_bounds__(512) void k_bw_small_reduce(const float *__restrict
             float sum = 0.f;
 #pragma unroll
             for (int k = 0; k < NS; ++k) sum += red[k][pl];
-            psum[p * plane_sz + pos] = sum * plane_scale(G, p);
+            psum[p * plane_sz + pos] = sum * group_plane_scale(G, D4, p);
         }
     } else {
         if (!db) return;  // uniform over the workgroup
@@ -616,7 +628,7 @@ __global__ __launch_bounds__(512) void k_bw_small_reduce(const float *__restrict
 }
 
 // dW[o, i, :] = inverse DFT of the scaled plane sums; one thread per (o, i).
-template <int G>
+template <int G, bool D4>
 __global__ __launch_bounds__(256) void k_bw_small_inverse(const float *__restrict__ psum, int C_out, int C_in,
                                                           int C_out_pad, int C_in_pad, float *__restrict__ dW) {
     const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -626,7 +638,7 @@ __global__ __launch_bounds__(256) void k_bw_small_inverse(const float *__restric
     float Y[G], out[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) Y[q] = psum[q * plane_sz + (int64_t)o * C_in_pad + i];
-    inverse_planes<G>(Y, out);
+    group_inverse<G, D4>(Y, out);
 #pragma unroll
     for (int d = 0; d < G; ++d) dW[k * G + d] = out[d];
 }
@@ -685,7 +697,7 @@ struct SmallLayout {
 SmallLayout small_layout(const Plan *p, int64_t N) {
     SmallLayout L;
     const int G = p->G;
-    if (p->dtype != EQLIN_BF16 || p->d4 || (G != 4 && G != 8) || N <= 0) return L;
+    if (p->dtype != EQLIN_BF16 || (G != 4 && G != 8) || N <= 0) return L;
     L.CB_in = (p->C_in + 31) / 32;
     L.CB_out = (p->C_out + 31) / 32;
     if (L.CB_in * L.CB_out * G > 8 * SmallBwCfg::maxb(G)) return L;  // accumulator blocks per workgroup
@@ -710,7 +722,7 @@ SmallLayout small_layout(const Plan *p, int64_t N) {
     return L;
 }
 
-template <int G>
+template <int G, bool D4>
 hipError_t launch_small(const Plan *p, const SmallLayout &L, const void *x, const void *dy, float *dW, float *db,
                         int64_t N, void *ws, hipStream_t s) {
     char *w = static_cast<char *>(ws);
@@ -718,17 +730,17 @@ hipError_t launch_small(const Plan *p, const SmallLayout &L, const void *x, cons
     float *psum = reinterpret_cast<float *>(w + L.off_psum);
     if (L.lds > 65536) {
         const hipError_t e =
-            hipFuncSetAttribute((const void *)k_bw_small<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
+            hipFuncSetAttribute((const void *)k_bw_small<G, D4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_bw_small<G>, dim3(L.splits), dim3(SmallBwCfg::NT), L.lds, s, (const uint16_t *)x,
+    hipLaunchKernelGGL((k_bw_small<G, D4>), dim3(L.splits), dim3(SmallBwCfg::NT), L.lds, s, (const uint16_t *)x,
                        (const uint16_t *)dy, N, p->C_in, p->C_out, L.tok_wg, L.CB_in, L.CB_out, part, dbp);
     const int n_main = L.n_groups * G;
     const int n_db = db ? (p->C_out + 31) / 32 : 0;
-    hipLaunchKernelGGL(k_bw_small_reduce<G>, dim3(n_main + n_db), dim3(512), 0, s, (const float *)part,
+    hipLaunchKernelGGL((k_bw_small_reduce<G, D4>), dim3(n_main + n_db), dim3(512), 0, s, (const float *)part,
                        (const float *)dbp, L.splits, p->C_out, L.CB_out * 32, L.CB_in * 32, n_main, psum, db);
     const int64_t n_inv = ((int64_t)p->C_out * p->C_in + 255) / 256;
-    hipLaunchKernelGGL(k_bw_small_inverse<G>, dim3((unsigned)n_inv), dim3(256), 0, s, (const float *)psum, p->C_out,
+    hipLaunchKernelGGL((k_bw_small_inverse<G, D4>), dim3((unsigned)n_inv), dim3(256), 0, s, (const float *)psum, p->C_out,
                        p->C_in, L.CB_out * 32, L.CB_in * 32, dW);
     return hipGetLastError();
 }
@@ -797,8 +809,9 @@ size_t bw_workspace_bytes(const Plan *p, int64_t N) {
 hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N,
                                    void *ws, hipStream_t s) {
     const SmallLayout S = small_layout(p, N);
-    if (S.ok) return p->G == 8 ? launch_small<8>(p, S, x, dy, dW, db, N, ws, s)
-                               : launch_small<4>(p, S, x, dy, dW, db, N, ws, s);
+    if (S.ok) return p->G == 8 ? (p->d4 ? launch_small<8, true>(p, S, x, dy, dW, db, N, ws, s)
+                                        : launch_small<8, false>(p, S, x, dy, dW, db, N, ws, s))
+                               : launch_small<4, false>(p, S, x, dy, dW, db, N, ws, s);
     if (mfma_path(p)) return p->G == 8 ? launch_mfma<8>(p, x, dy, dW, db, N, ws, s)
                                        : launch_mfma<4>(p, x, dy, dW, db, N, ws, s);
     if (p->dtype == EQLIN_BF16) return launch_direct_g<BF16>(p, x, dy, dW, db, N, s);

@@ -87,7 +87,8 @@ typedef enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 } eqlin_act_t;
  * (the cyclic layer is the case g^-1 h = h - g mod G). The kernels use D4's Fourier transform over its
  * irreducible representations (four characters and one 2-D representation): per channel pair four
  * real products and one 2 x 2 matrix product, twelve real products against 64 for the unrolled block.
- * Every entry point takes a D4 handle; the backward weights then run on the vector ALU (fp32).
+ * Every entry point takes a D4 handle; the backward weights run on the matrix cores for small channel
+ * counts (bf16) and on the vector ALU (fp32) otherwise.
  */
 
 /*
@@ -173,7 +174,9 @@ eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, i
  * computed per frequency as C_k = sum_n DY_k conj(X_k) (the same group DFT as the forward) followed
  * by the inverse DFT. bf16 with G = 4 or 8 (cyclic): x and dy are transformed into bf16 planes, multiplied on
  * the matrix cores with fp32 accumulation over token splits, and the splits summed in fp32; other
- * cases (fp32, fp16, G = 1 or 2, D4) evaluate the definition in fp32 on the vector ALU.
+ * cases (fp32, fp16, G = 1 or 2, D4) evaluate the definition in fp32 on the vector ALU, except that
+ * small channel counts in bf16 (C_in * C_out * G up to about 40960; G = 4, 8 or D4) run one fused
+ * matrix-core pass per token range.
  *   x      device [N][C_in][G], dy device [N][C_out][G], both of the handle's dtype.
  *   dW     device float [C_out][C_in][G] (overwritten); db device float [C_out] or NULL (overwritten).
  *   workspace, workspace_bytes: device scratch of at least eqlin_backward_weights_workspace(h, N)
