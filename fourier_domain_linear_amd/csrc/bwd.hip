@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void k_bw_bias(const void *__restrict__ dy, in
 }
 
 // ------------------------------------------------------------------------------------------------
-// Small channel counts (bf16, G = 4 or 8 cyclic or D4, C_in_pad * C_out_pad * G <= 40960): one fused pass.
+// Small channel counts (bf16 or fp16, G = 4 or 8 cyclic or D4, C_in_pad * C_out_pad * G <= 40960): one fused pass.
 // (D4: the character planes give G_k = sum DY_k X_k, the 2 x 2 irrep G_cb = sum_a X_ac DY_ab, the
 // adjoint of Y = X W; the inverse transform with the forward's scalings then gives dW.)
 // At such sizes the three-pass path spends its time writing and re-reading transformed planes and on
@@ -409,7 +409,7 @@ struct SmallBwCfg {
     static constexpr int maxb(int G) { return G == 8 ? 4 : 5; }
 };
 
-template <int G, bool D4>
+template <int G, bool D4, class E>
 __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dy,
                                                   int64_t N, int C_in, int C_out, int tok_wg, int CB_in, int CB_out,
                                                   float *__restrict__ part, float *__restrict__ db_part) {
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
             for (int j = 0; j < 8; ++j) {
                 float v[G], P[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) v[g] = bf16_at(src[j], c * G + g);
+                for (int g = 0; g < G; ++g) v[g] = elem_at<E>(src[j], c * G + g);
                 group_forward<G, D4>(v, P);
 #pragma unroll
                 for (int q = 0; q < G; ++q) pl[q][j] = P[q];
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
             const int base = buf * FR + (isx ? (step * CB_in + (ch >> 5)) * G : DYB + (step * CB_out + (ch >> 5)) * G);
             const int lf = (ch & 31) + 32 * half;
 #pragma unroll
-            for (int q = 0; q < G; ++q) frag[(base + q) * 64 + lf] = pack_bf16x8(pl[q]);
+            for (int q = 0; q < G; ++q) frag[(base + q) * 64 + lf] = pack8<E>(pl[q]);
         }
     };
 
@@ -500,22 +500,22 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
                 const uint4 *B = frag + buf * FR * 64 + bob[q] + k * CB_in * G * 64 + lane;   // x: columns = inputs
                 if constexpr (D4) {
                     if (pp < 4) {  // a character: G_k = sum DY_k X_k
-                        acc[q] = mfma32x32x16(A[pp * 64], B[pp * 64], acc[q]);
+                        acc[q] = mma32<E>(A[pp * 64], B[pp * 64], acc[q]);
                     } else {  // the 2 x 2 irrep, entry (c, b): G_cb = sum_a X_ac DY_ab
                         const int c = (pp - 4) >> 1, bb = (pp - 4) & 1;
-                        acc[q] = mfma32x32x16(A[(4 + bb) * 64], B[(4 + c) * 64], acc[q]);
-                        acc[q] = mfma32x32x16(A[(6 + bb) * 64], B[(6 + c) * 64], acc[q]);
+                        acc[q] = mma32<E>(A[(4 + bb) * 64], B[(4 + c) * 64], acc[q]);
+                        acc[q] = mma32<E>(A[(6 + bb) * 64], B[(6 + c) * 64], acc[q]);
                     }
                     continue;
                 }
                 if (pp < 2) {
-                    acc[q] = mfma32x32x16(A[pp * 64], B[pp * 64], acc[q]);
+                    acc[q] = mma32<E>(A[pp * 64], B[pp * 64], acc[q]);
                 } else if ((pp & 1) == 0) {  // Re C_k = DYr Xr + DYi Xi
-                    acc[q] = mfma32x32x16(A[pp * 64], B[pp * 64], acc[q]);
-                    acc[q] = mfma32x32x16(A[(pp + 1) * 64], B[(pp + 1) * 64], acc[q]);
+                    acc[q] = mma32<E>(A[pp * 64], B[pp * 64], acc[q]);
+                    acc[q] = mma32<E>(A[(pp + 1) * 64], B[(pp + 1) * 64], acc[q]);
                 } else {  // Im C_k = DYi Xr - DYr Xi
-                    acc[q] = mfma32x32x16(A[pp * 64], B[(pp - 1) * 64], acc[q]);
-                    acc[q] = mfma32x32x16(neg_bf16x8(A[(pp - 1) * 64]), B[pp * 64], acc[q]);
+                    acc[q] = mma32<E>(A[pp * 64], B[(pp - 1) * 64], acc[q]);
+                    acc[q] = mma32<E>(neg_bf16x8(A[(pp - 1) * 64]), B[pp * 64], acc[q]);
                 }
             }
     };
@@ -697,7 +697,8 @@ struct SmallLayout {
 SmallLayout small_layout(const Plan *p, int64_t N) {
     SmallLayout L;
     const int G = p->G;
-    if (p->dtype != EQLIN_BF16 || (G != 4 && G != 8) || N <= 0) return L;
+    if (p->dtype == EQLIN_F32 || (G != 4 && G != 8) || N <= 0) return L;
+    if (p->dtype == EQLIN_F16 && G == 4) return L;  // the fp16 G = 4 instance would spill registers
     L.CB_in = (p->C_in + 31) / 32;
     L.CB_out = (p->C_out + 31) / 32;
     if (L.CB_in * L.CB_out * G > 8 * SmallBwCfg::maxb(G)) return L;  // accumulator blocks per workgroup
@@ -722,18 +723,28 @@ SmallLayout small_layout(const Plan *p, int64_t N) {
     return L;
 }
 
+// the fused pass's instance for the element type (fp16 only at G = 8: see small_layout)
+typedef void (*SmallFn)(const uint16_t *, const uint16_t *, int64_t, int, int, int, int, int, float *, float *);
+template <int G, bool D4>
+SmallFn kernel_small(eqlin_dtype_t dt) {
+    if constexpr (G == 8)
+        if (dt == EQLIN_F16) return k_bw_small<G, D4, F16>;
+    return k_bw_small<G, D4, BF16>;
+}
+
 template <int G, bool D4>
 hipError_t launch_small(const Plan *p, const SmallLayout &L, const void *x, const void *dy, float *dW, float *db,
                         int64_t N, void *ws, hipStream_t s) {
     char *w = static_cast<char *>(ws);
     float *part = reinterpret_cast<float *>(w + L.off_part), *dbp = reinterpret_cast<float *>(w + L.off_db);
     float *psum = reinterpret_cast<float *>(w + L.off_psum);
+    const SmallFn kfn = kernel_small<G, D4>(p->dtype);
     if (L.lds > 65536) {
         const hipError_t e =
-            hipFuncSetAttribute((const void *)k_bw_small<G, D4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
+            hipFuncSetAttribute((const void *)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_bw_small<G, D4>), dim3(L.splits), dim3(SmallBwCfg::NT), L.lds, s, (const uint16_t *)x,
+    hipLaunchKernelGGL(kfn, dim3(L.splits), dim3(SmallBwCfg::NT), L.lds, s, (const uint16_t *)x,
                        (const uint16_t *)dy, N, p->C_in, p->C_out, L.tok_wg, L.CB_in, L.CB_out, part, dbp);
     const int n_main = L.n_groups * G;
     const int n_db = db ? (p->C_out + 31) / 32 : 0;
@@ -821,7 +832,7 @@ hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy,
 
 const char *bw_kernel_name(const Plan *p) {
     // (the fused pass serves every token count at these channel counts up to the 2 GB offset limit)
-    if (small_layout(p, 1).ok) return "bf16 fused dft + mfma32x32x16 per token range + reduce (small channels)";
+    if (small_layout(p, 1).ok) return "fused dft + mfma32x32x16 per token range + reduce (small channels)";
     return mfma_path(p) ? "bf16 dft planes + plane-split mfma32x32x16 split-K + reduce" : "direct fp32 valu";
 }
 

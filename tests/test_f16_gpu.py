@@ -88,3 +88,18 @@ def test_spectral_weights_and_backward(cuda_device):
     _check(dx, ref_dx, "f16 dx", rms(ref_dx))
     _check(dW, ref_dW, "f16 dW", rms(ref_dW))
     _check(db, ref_db, "f16 db", rms(ref_db))
+
+
+@pytest.mark.parametrize("group", ["cyclic", "d4"])
+def test_backward_weights_fused_g8(group, cuda_device):
+    # fp16 at G = 8 and small channel counts: the fused matrix-core weight gradient
+    x, W, _ = make_inputs(8, 64, 64, 3001, "f16", seed=34)
+    dy = make_grad(8, 64, 3001, "f16", seed=34)
+    h = eq.prepare_weights(W.to(cuda_device), group=group)
+    assert "fused" in h.describe()
+    dW, db = eq.backward_weights(h, x.to(cuda_device), dy.to(cuda_device))
+    torch.cuda.synchronize()
+    rW, rb = (d4.backward_weights(x, dy) if group == "d4" else oracle.backward_weights(x, dy))
+    rms = lambda a: float(np.sqrt(np.mean(a * a)))
+    _check(dW, rW, f"f16 {group} dW fused", rms(rW))
+    _check(db, rb, f"f16 {group} db fused", rms(rb))
