@@ -14,14 +14,14 @@
 namespace eqlin {
 
 // GELU(v) = v * Phi(v), Phi the standard normal CDF (the activation the ViT-on-mobile page names,
-// "El Efecto GELU"; the exact form, not the tanh approximation). With Q(|v|) = 1 - Phi(|v|), the
+// "El Efecto GELU"; the erf form v * Phi(v), not the tanh approximation). With Q(|v|) = 1 - Phi(|v|), the
 // upper tail, GELU(v) = max(v, 0) - |v| * Q(|v|) for either sign of v. Q comes from Abramowitz &
 // Stegun's rational approximation 7.1.28 (Hastings): erf(z) = 1 - (1 + a1 z + ... + a6 z^6)^-16 with
 // |error| <= 3e-7 for z >= 0, so Q(u) = (1 - erf(u / sqrt 2)) / 2 = (1/2) p(u)^-16, where p has the
 // 1/sqrt(2) scaling folded into its coefficients (c_k = a_k / 2^(k/2)). One reciprocal, six fused
 // multiply-adds and four squarings, branch-free: the error in GELU is at most 1.5e-7 |v| plus fp32
 // rounding, well under a bf16 output's rounding and the fp32 path's tolerance.
-__host__ __device__ __forceinline__ float gelu_exact(float v) {
+__host__ __device__ __forceinline__ float gelu_erf_form(float v) {
     constexpr float c1 = 0.04986734696679053f, c2 = 0.02114100615f, c3 = 0.0032776263241471684f,
                     c4 = 3.8003575e-05f, c5 = 4.889063564344402e-05f, c6 = 5.382975e-06f;
     const float u = fabsf(v);
@@ -51,7 +51,7 @@ template <bool GELU, int M>
 __device__ __forceinline__ void apply_act(float (&out)[M]) {
     if constexpr (GELU) {
 #pragma unroll
-        for (int j = 0; j < M; ++j) out[j] = gelu_exact(out[j]);
+        for (int j = 0; j < M; ++j) out[j] = gelu_erf_form(out[j]);
     }
 }
 
