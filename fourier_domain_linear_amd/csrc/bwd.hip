@@ -698,7 +698,6 @@ SmallLayout small_layout(const Plan *p, int64_t N) {
     SmallLayout L;
     const int G = p->G;
     if (p->dtype == EQLIN_F32 || (G != 4 && G != 8) || N <= 0) return L;
-    if (p->dtype == EQLIN_F16 && G == 4) return L;  // the fp16 G = 4 instance would spill registers
     L.CB_in = (p->C_in + 31) / 32;
     L.CB_out = (p->C_out + 31) / 32;
     if (L.CB_in * L.CB_out * G > 8 * SmallBwCfg::maxb(G)) return L;  // accumulator blocks per workgroup
@@ -723,12 +722,11 @@ SmallLayout small_layout(const Plan *p, int64_t N) {
     return L;
 }
 
-// the fused pass's instance for the element type (fp16 only at G = 8: see small_layout)
+// the fused pass's instance for the element type
 typedef void (*SmallFn)(const uint16_t *, const uint16_t *, int64_t, int, int, int, int, int, float *, float *);
 template <int G, bool D4>
 SmallFn kernel_small(eqlin_dtype_t dt) {
-    if constexpr (G == 8)
-        if (dt == EQLIN_F16) return k_bw_small<G, D4, F16>;
+    if (dt == EQLIN_F16) return k_bw_small<G, D4, F16>;
     return k_bw_small<G, D4, BF16>;
 }
 
