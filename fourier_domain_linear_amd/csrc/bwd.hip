@@ -18,8 +18,8 @@
 // transform with its 1/G and 2/G plane scalings. In real planes, a complex frequency is four real
 // products: Re C = DYr Xr + DYi Xi, Im C = DYi Xr - DYr Xi.
 //
-// bf16, G = 4 or 8 (matrix cores), three passes over a caller-provided workspace:
-//   1. k_bw_planes: x and dy -> DFT planes (fp32, rounded once to bf16) in 32x32x16 fragment order
+// bf16 or fp16, G = 4 or 8 (matrix cores), three passes over a caller-provided workspace:
+//   1. k_bw_planes: x and dy -> DFT planes (fp32, rounded once to the half type) in 32x32x16 fragment order
 //      with tokens along K: chunk (channel block cb of 32, token step kt of 16, plane p) is 1 KB, lane
 //      l holds channel cb*32 + l%32, tokens kt*16 + 8*(l/32) .. +7. Each token's transform is done
 //      once (in the product pass every x tile meets many dy tiles). Tokens past N are zeros. The dy
@@ -44,11 +44,11 @@
 namespace eqlin {
 
 // ------------------------------------------------------------------------------------------------
-// Pass 1: group DFT of a [N][C][G] bf16 tensor into K-major fragments.
+// Pass 1: group DFT of a [N][C][G] bf16 / fp16 tensor into K-major fragments.
 constexpr int kBwTok = 64;         // tokens per pass-1 workgroup (4 token steps of 16)
 constexpr int kBwRow = kBwTok + 8;  // LDS row of one (plane, channel): padded against bank conflicts
 
-template <int G>
+template <int G, class E>
 __global__ __launch_bounds__(256) void k_bw_planes(const uint16_t *__restrict__ src, int64_t N, int C, int KT,
                                                    uint4 *__restrict__ frag, float *__restrict__ db_part) {
     __shared__ __attribute__((aligned(16))) uint16_t sp[G][32][kBwRow];
@@ -67,10 +67,10 @@ __global__ __launch_bounds__(256) void k_bw_planes(const uint16_t *__restrict__ 
     for (int j = 0; j < 8; ++j) {
         float v[G], P[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) v[g] = bf16_at(r[(j * G + g) >> 3], (j * G + g) & 7);
+        for (int g = 0; g < G; ++g) v[g] = elem_at<E>(r[(j * G + g) >> 3], (j * G + g) & 7);
         forward_planes<G>(v, P);
 #pragma unroll
-        for (int pl = 0; pl < G; ++pl) sp[pl][cg * 8 + j][tl] = pack_bf16(P[pl]);
+        for (int pl = 0; pl < G; ++pl) sp[pl][cg * 8 + j][tl] = pack1<E>(P[pl]);
         red[cg * 8 + j][tl] = P[0];  // plane 0 is the sum over the group samples
     }
     __syncthreads();
@@ -116,7 +116,7 @@ __device__ __forceinline__ void bw_lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <int G>
+template <int G, class E>
 __global__ __launch_bounds__(512) void k_bw_gemm(const uint4 *__restrict__ xf, const uint4 *__restrict__ dyf,
                                                  float *__restrict__ part, int KT, int tiles_i, int splits,
                                                  int C_in_pad, int C_out_pad) {
@@ -198,15 +198,15 @@ __global__ __launch_bounds__(512) void k_bw_gemm(const uint4 *__restrict__ xf, c
                 for (int c = 0; c < HP; c += 2) {
                     if constexpr (R == 0) {
                         if (c == 0) {
-                            acc[b][0] = mfma32x32x16(a[0], bf[0], acc[b][0]);
-                            acc[b][1] = mfma32x32x16(a[1], bf[1], acc[b][1]);
+                            acc[b][0] = mma32<E>(a[0], bf[0], acc[b][0]);
+                            acc[b][1] = mma32<E>(a[1], bf[1], acc[b][1]);
                             continue;
                         }
                     }
-                    acc[b][c] = mfma32x32x16(a[c], bf[c], acc[b][c]);
-                    acc[b][c] = mfma32x32x16(a[c + 1], bf[c + 1], acc[b][c]);
-                    acc[b][c + 1] = mfma32x32x16(a[c + 1], bf[c], acc[b][c + 1]);
-                    acc[b][c + 1] = mfma32x32x16(an[c], bf[c + 1], acc[b][c + 1]);
+                    acc[b][c] = mma32<E>(a[c], bf[c], acc[b][c]);
+                    acc[b][c] = mma32<E>(a[c + 1], bf[c + 1], acc[b][c]);
+                    acc[b][c + 1] = mma32<E>(a[c + 1], bf[c], acc[b][c + 1]);
+                    acc[b][c + 1] = mma32<E>(an[c], bf[c + 1], acc[b][c + 1]);
                 }
             }
         };
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(256) void k_bw_dbsum(const float *__restrict__ db_p
 }
 
 // ------------------------------------------------------------------------------------------------
-// Direct kernel (fp32 or bf16 inputs, any G): the definition in fp32. Workgroup: 16 x 16 (o, i)
+// Direct kernel (fp32, bf16 or fp16 inputs, any G): the definition in fp32. Workgroup: 16 x 16 (o, i)
 // pairs, 256 threads (one pair each, all G shifts d); token tiles of 32 through LDS.
 // Index of h d^-1: (h - d) mod G, or in D4, with h = r^c s^e and d = r^a s^b: d^-1 = r^a' s^b (a' = -a
 // for a rotation, a for a reflection) and the product rule r^c s^e r^a' s^b = r^(c + (-1)^e a') s^(e + b).
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256) void k_bw_bias(const void *__restrict__ dy, in
 // each), so x and dy are read once and only the fp32 partial spectra leave. The range is walked in
 // super-chunks of 32 tokens through two LDS fragment buffers: in step s the waves issue the loads of
 // super-chunk s + 2 (one item of 8 tokens x 16 bytes per thread), run the products of super-chunk s
-// from one buffer and write the group DFT of super-chunk s + 1 (bf16, K-major fragments: tokens along
+// from one buffer and write the group DFT of super-chunk s + 1 (half type, K-major fragments: tokens along
 // K, as in pass 1) into the other, so the transform's vector ALU and the products overlap and each
 // load has a whole step to arrive. Partials go to part[split][plane][o][i] and db partials to
 // db_part[split][o]; k_bw_small_reduce sums them in a fixed order and k_bw_small_inverse applies the
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
     float dbacc[CPU];
 #pragma unroll
     for (int c = 0; c < CPU; ++c) dbacc[c] = 0.f;
-    auto transform = [&](const uint4 (&src)[8], int buf) {  // DFT -> bf16 fragments (+ dy's plane 0)
+    auto transform = [&](const uint4 (&src)[8], int buf) {  // DFT -> half-type fragments (+ dy's plane 0)
         if (!live) return;
         const int step = tg >> 1, half = tg & 1;
 #pragma unroll
@@ -647,7 +647,7 @@ __global__ __launch_bounds__(256) void k_bw_small_inverse(const float *__restric
 // Host side: workspace layout and launch.
 namespace {
 
-bool mfma_path(const Plan *p) { return p->dtype == EQLIN_BF16 && (p->G == 4 || p->G == 8) && !p->d4; }
+bool mfma_path(const Plan *p) { return p->dtype != EQLIN_F32 && (p->G == 4 || p->G == 8) && !p->d4; }
 
 struct BwLayout {
     int KT = 0, CB_in = 0, CB_out = 0, tiles_i = 0, tiles_o = 0, splits = 0, ptiles = 0;
@@ -759,7 +759,7 @@ BwLayout layout_for(const Plan *p, int64_t N) {
     return bw_layout<4>(p, N);
 }
 
-template <int G>
+template <int G, class E>
 hipError_t launch_mfma(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N, void *ws,
                        hipStream_t s) {
     const BwLayout L = bw_layout<G>(p, N);
@@ -767,12 +767,12 @@ hipError_t launch_mfma(const Plan *p, const void *x, const void *dy, float *dW, 
     uint4 *xf = reinterpret_cast<uint4 *>(w + L.off_x), *dyf = reinterpret_cast<uint4 *>(w + L.off_dy);
     float *part = reinterpret_cast<float *>(w + L.off_part), *dbp = reinterpret_cast<float *>(w + L.off_db);
     if ((int64_t)L.ptiles > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_bw_planes<G>, dim3(L.ptiles, L.CB_in), dim3(256), 0, s, (const uint16_t *)x, N, p->C_in,
+    hipLaunchKernelGGL((k_bw_planes<G, E>), dim3(L.ptiles, L.CB_in), dim3(256), 0, s, (const uint16_t *)x, N, p->C_in,
                        L.KT, xf, (float *)nullptr);
-    hipLaunchKernelGGL(k_bw_planes<G>, dim3(L.ptiles, L.CB_out), dim3(256), 0, s, (const uint16_t *)dy, N, p->C_out,
+    hipLaunchKernelGGL((k_bw_planes<G, E>), dim3(L.ptiles, L.CB_out), dim3(256), 0, s, (const uint16_t *)dy, N, p->C_out,
                        L.KT, dyf, dbp);
     const int grid = L.tiles_i * L.tiles_o * L.splits;
-    hipLaunchKernelGGL(k_bw_gemm<G>, dim3(grid), dim3(512), 0, s, (const uint4 *)xf, (const uint4 *)dyf, part,
+    hipLaunchKernelGGL((k_bw_gemm<G, E>), dim3(grid), dim3(512), 0, s, (const uint4 *)xf, (const uint4 *)dyf, part,
                        L.KT, L.tiles_i, L.splits, L.C_in_pad, L.C_out_pad);
     const int64_t rgrid = (int64_t)p->C_out * (L.C_in_pad / 32);
     if (rgrid > 0x7fffffff) return hipErrorInvalidValue;
@@ -821,8 +821,11 @@ hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy,
     if (S.ok) return p->G == 8 ? (p->d4 ? launch_small<8, true>(p, S, x, dy, dW, db, N, ws, s)
                                         : launch_small<8, false>(p, S, x, dy, dW, db, N, ws, s))
                                : launch_small<4, false>(p, S, x, dy, dW, db, N, ws, s);
-    if (mfma_path(p)) return p->G == 8 ? launch_mfma<8>(p, x, dy, dW, db, N, ws, s)
-                                       : launch_mfma<4>(p, x, dy, dW, db, N, ws, s);
+    if (mfma_path(p)) {
+        if (p->dtype == EQLIN_F16)
+            return p->G == 8 ? launch_mfma<8, F16>(p, x, dy, dW, db, N, ws, s) : launch_mfma<4, F16>(p, x, dy, dW, db, N, ws, s);
+        return p->G == 8 ? launch_mfma<8, BF16>(p, x, dy, dW, db, N, ws, s) : launch_mfma<4, BF16>(p, x, dy, dW, db, N, ws, s);
+    }
     if (p->dtype == EQLIN_BF16) return launch_direct_g<BF16>(p, x, dy, dW, db, N, s);
     if (p->dtype == EQLIN_F16) return launch_direct_g<F16>(p, x, dy, dW, db, N, s);
     return launch_direct_g<float>(p, x, dy, dW, db, N, s);
@@ -831,7 +834,7 @@ hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy,
 const char *bw_kernel_name(const Plan *p) {
     // (the fused pass serves every token count at these channel counts up to the 2 GB offset limit)
     if (small_layout(p, 1).ok) return "fused dft + mfma32x32x16 per token range + reduce (small channels)";
-    return mfma_path(p) ? "bf16 dft planes + plane-split mfma32x32x16 split-K + reduce" : "direct fp32 valu";
+    return mfma_path(p) ? "dft planes + plane-split mfma32x32x16 split-K + reduce" : "direct fp32 valu";
 }
 
 }  // namespace eqlin

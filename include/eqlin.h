@@ -172,11 +172,11 @@ eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, i
  *     dW[o, i, d] = sum_n sum_{h < G} dy[n, o, h] * x[n, i, (h - d) mod G],   db[o] = sum_{n, h} dy[n, o, h]
  *
  * computed per frequency as C_k = sum_n DY_k conj(X_k) (the same group DFT as the forward) followed
- * by the inverse DFT. bf16 with G = 4 or 8 (cyclic): x and dy are transformed into bf16 planes, multiplied on
- * the matrix cores with fp32 accumulation over token splits, and the splits summed in fp32; other
- * cases (fp32, fp16, G = 1 or 2, D4) evaluate the definition in fp32 on the vector ALU, except that
- * small channel counts in bf16 (C_in * C_out * G up to about 40960; G = 4, 8 or D4) run one fused
- * matrix-core pass per token range.
+ * by the inverse DFT. bf16 or fp16 with G = 4 or 8 (cyclic): x and dy are transformed into half-type
+ * planes, multiplied on the matrix cores with fp32 accumulation over token splits, and the splits
+ * summed in fp32; small channel counts (C_in * C_out * G up to about 40960; G = 4, 8 or D4) run one
+ * fused matrix-core pass per token range instead; other cases (fp32, G = 1 or 2, D4 at large channel
+ * counts) evaluate the definition in fp32 on the vector ALU.
  *   x      device [N][C_in][G], dy device [N][C_out][G], both of the handle's dtype.
  *   dW     device float [C_out][C_in][G] (overwritten); db device float [C_out] or NULL (overwritten).
  *   workspace, workspace_bytes: device scratch of at least eqlin_backward_weights_workspace(h, N)
