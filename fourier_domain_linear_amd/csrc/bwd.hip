@@ -48,7 +48,7 @@ namespace eqlin {
 constexpr int kBwTok = 64;         // tokens per pass-1 workgroup (4 token steps of 16)
 constexpr int kBwRow = kBwTok + 8;  // LDS row of one (plane, channel): padded against bank conflicts
 
-template <int G, class E>
+template <int G, class E, bool D4>
 __global__ __launch_bounds__(256) void k_bw_planes(const uint16_t *__restrict__ src, int64_t N, int C, int KT,
                                                    uint4 *__restrict__ frag, float *__restrict__ db_part) {
     __shared__ __attribute__((aligned(16))) uint16_t sp[G][32][kBwRow];
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_bw_planes(const uint16_t *__restrict__ 
         float v[G], P[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) v[g] = elem_at<E>(r[(j * G + g) >> 3], (j * G + g) & 7);
-        forward_planes<G>(v, P);
+        group_forward<G, D4>(v, P);
 #pragma unroll
         for (int pl = 0; pl < G; ++pl) sp[pl][cg * 8 + j][tl] = pack1<E>(P[pl]);
         red[cg * 8 + j][tl] = P[0];  // plane 0 is the sum over the group samples
@@ -116,7 +116,7 @@ __device__ __forceinline__ void bw_lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <int G, class E>
+template <int G, class E, bool D4>
 __global__ __launch_bounds__(512) void k_bw_gemm(const uint4 *__restrict__ xf, const uint4 *__restrict__ dyf,
                                                  float *__restrict__ part, int KT, int tiles_i, int splits,
                                                  int C_in_pad, int C_out_pad) {
@@ -194,6 +194,22 @@ __global__ __launch_bounds__(512) void k_bw_gemm(const uint4 *__restrict__ xf, c
                 uint4 bf[HP];
 #pragma unroll
                 for (int r = 0; r < HP; ++r) bf[r] = buf[(b * G + R * HP + r) * 64 + lane];
+                if constexpr (D4) {
+                    // role 0: the characters, G_k = sum DY_k X_k; role 1: the 2 x 2 irrep, entry
+                    // (c, b') at local plane 2c + b': G_cb' = sum_a X_ac DY_ab'
+                    if constexpr (R == 0) {
+#pragma unroll
+                        for (int q = 0; q < HP; ++q) acc[b][q] = mma32<E>(a[q], bf[q], acc[b][q]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int c = e >> 1, bb = e & 1;
+                            acc[b][e] = mma32<E>(a[bb], bf[c], acc[b][e]);
+                            acc[b][e] = mma32<E>(a[2 + bb], bf[2 + c], acc[b][e]);
+                        }
+                    }
+                    continue;
+                }
 #pragma unroll
                 for (int c = 0; c < HP; c += 2) {
                     if constexpr (R == 0) {
@@ -259,7 +275,7 @@ __global__ __launch_bounds__(512) void k_bw_gemm(const uint4 *__restrict__ xf, c
 // inputs i of one output o (whole 128-byte lines of every partial plane): thread (sub, i) sums the
 // splits sub, sub + 8, ... of each plane; the 8 shares are added in a fixed order in LDS, then 32
 // threads run the inverse transforms.
-template <int G>
+template <int G, bool D4>
 __global__ __launch_bounds__(256) void k_bw_reduce(const float *__restrict__ part, int splits, int C_out, int C_in,
                                                    int C_out_pad, int C_in_pad, float *__restrict__ dW) {
     __shared__ float red[G][8][33];
@@ -281,9 +297,9 @@ __global__ __launch_bounds__(256) void k_bw_reduce(const float *__restrict__ par
         for (int p = 0; p < G; ++p) {
             const float a = (red[p][0][il] + red[p][1][il]) + (red[p][2][il] + red[p][3][il]);
             const float b = (red[p][4][il] + red[p][5][il]) + (red[p][6][il] + red[p][7][il]);
-            Y[p] = (a + b) * plane_scale(G, p);
+            Y[p] = (a + b) * group_plane_scale(G, D4, p);
         }
-        inverse_planes<G>(Y, out);
+        group_inverse<G, D4>(Y, out);
 #pragma unroll
         for (int d = 0; d < G; ++d) dW[((int64_t)o * C_in + i) * G + d] = out[d];
     }
@@ -647,7 +663,7 @@ __global__ __launch_bounds__(256) void k_bw_small_inverse(const float *__restric
 // Host side: workspace layout and launch.
 namespace {
 
-bool mfma_path(const Plan *p) { return p->dtype != EQLIN_F32 && (p->G == 4 || p->G == 8) && !p->d4; }
+bool mfma_path(const Plan *p) { return p->dtype != EQLIN_F32 && (p->G == 4 || p->G == 8); }
 
 struct BwLayout {
     int KT = 0, CB_in = 0, CB_out = 0, tiles_i = 0, tiles_o = 0, splits = 0, ptiles = 0;
@@ -759,7 +775,7 @@ BwLayout layout_for(const Plan *p, int64_t N) {
     return bw_layout<4>(p, N);
 }
 
-template <int G, class E>
+template <int G, class E, bool D4 = false>
 hipError_t launch_mfma(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N, void *ws,
                        hipStream_t s) {
     const BwLayout L = bw_layout<G>(p, N);
@@ -767,16 +783,16 @@ hipError_t launch_mfma(const Plan *p, const void *x, const void *dy, float *dW, 
     uint4 *xf = reinterpret_cast<uint4 *>(w + L.off_x), *dyf = reinterpret_cast<uint4 *>(w + L.off_dy);
     float *part = reinterpret_cast<float *>(w + L.off_part), *dbp = reinterpret_cast<float *>(w + L.off_db);
     if ((int64_t)L.ptiles > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_bw_planes<G, E>), dim3(L.ptiles, L.CB_in), dim3(256), 0, s, (const uint16_t *)x, N, p->C_in,
+    hipLaunchKernelGGL((k_bw_planes<G, E, D4>), dim3(L.ptiles, L.CB_in), dim3(256), 0, s, (const uint16_t *)x, N, p->C_in,
                        L.KT, xf, (float *)nullptr);
-    hipLaunchKernelGGL((k_bw_planes<G, E>), dim3(L.ptiles, L.CB_out), dim3(256), 0, s, (const uint16_t *)dy, N, p->C_out,
+    hipLaunchKernelGGL((k_bw_planes<G, E, D4>), dim3(L.ptiles, L.CB_out), dim3(256), 0, s, (const uint16_t *)dy, N, p->C_out,
                        L.KT, dyf, dbp);
     const int grid = L.tiles_i * L.tiles_o * L.splits;
-    hipLaunchKernelGGL((k_bw_gemm<G, E>), dim3(grid), dim3(512), 0, s, (const uint4 *)xf, (const uint4 *)dyf, part,
+    hipLaunchKernelGGL((k_bw_gemm<G, E, D4>), dim3(grid), dim3(512), 0, s, (const uint4 *)xf, (const uint4 *)dyf, part,
                        L.KT, L.tiles_i, L.splits, L.C_in_pad, L.C_out_pad);
     const int64_t rgrid = (int64_t)p->C_out * (L.C_in_pad / 32);
     if (rgrid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_bw_reduce<G>, dim3((unsigned)rgrid), dim3(256), 0, s, (const float *)part, L.splits,
+    hipLaunchKernelGGL((k_bw_reduce<G, D4>), dim3((unsigned)rgrid), dim3(256), 0, s, (const float *)part, L.splits,
                        p->C_out, p->C_in, L.C_out_pad, L.C_in_pad, dW);
     if (db)
         hipLaunchKernelGGL(k_bw_dbsum, dim3((p->C_out + 3) / 4), dim3(256), 0, s, (const float *)dbp, L.ptiles,
@@ -822,7 +838,11 @@ hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy,
                                         : launch_small<8, false>(p, S, x, dy, dW, db, N, ws, s))
                                : launch_small<4, false>(p, S, x, dy, dW, db, N, ws, s);
     if (mfma_path(p)) {
-        if (p->dtype == EQLIN_F16)
+        const bool f16 = p->dtype == EQLIN_F16;
+        if (p->d4)
+            return f16 ? launch_mfma<8, F16, true>(p, x, dy, dW, db, N, ws, s)
+                       : launch_mfma<8, BF16, true>(p, x, dy, dW, db, N, ws, s);
+        if (f16)
             return p->G == 8 ? launch_mfma<8, F16>(p, x, dy, dW, db, N, ws, s) : launch_mfma<4, F16>(p, x, dy, dW, db, N, ws, s);
         return p->G == 8 ? launch_mfma<8, BF16>(p, x, dy, dW, db, N, ws, s) : launch_mfma<4, BF16>(p, x, dy, dW, db, N, ws, s);
     }

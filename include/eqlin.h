@@ -87,8 +87,7 @@ typedef enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 } eqlin_act_t;
  * (the cyclic layer is the case g^-1 h = h - g mod G). The kernels use D4's Fourier transform over its
  * irreducible representations (four characters and one 2-D representation): per channel pair four
  * real products and one 2 x 2 matrix product, twelve real products against 64 for the unrolled block.
- * Every entry point takes a D4 handle; the backward weights run on the matrix cores for small channel
- * counts (bf16) and on the vector ALU (fp32) otherwise.
+ * Every entry point takes a D4 handle.
  */
 
 /*
@@ -172,11 +171,11 @@ eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, i
  *     dW[o, i, d] = sum_n sum_{h < G} dy[n, o, h] * x[n, i, (h - d) mod G],   db[o] = sum_{n, h} dy[n, o, h]
  *
  * computed per frequency as C_k = sum_n DY_k conj(X_k) (the same group DFT as the forward) followed
- * by the inverse DFT. bf16 or fp16 with G = 4 or 8 (cyclic): x and dy are transformed into half-type
- * planes, multiplied on the matrix cores with fp32 accumulation over token splits, and the splits
- * summed in fp32; small channel counts (C_in * C_out * G up to about 40960; G = 4, 8 or D4) run one
- * fused matrix-core pass per token range instead; other cases (fp32, G = 1 or 2, D4 at large channel
- * counts) evaluate the definition in fp32 on the vector ALU.
+ * by the inverse DFT (D4: its irreps' adjoint products and inverse). bf16 or fp16 with G = 4, 8 or D4:
+ * x and dy are transformed into half-type planes, multiplied on the matrix cores with fp32
+ * accumulation over token splits, and the splits summed in fp32; small channel counts (C_in * C_out * G
+ * up to about 40960) run one fused matrix-core pass per token range instead; other cases (fp32,
+ * G = 1 or 2) evaluate the definition in fp32 on the vector ALU.
  *   x      device [N][C_in][G], dy device [N][C_out][G], both of the handle's dtype.
  *   dW     device float [C_out][C_in][G] (overwritten); db device float [C_out] or NULL (overwritten).
  *   workspace, workspace_bytes: device scratch of at least eqlin_backward_weights_workspace(h, N)

@@ -107,6 +107,7 @@ def test_gelu_and_spectral_weights(cuda_device):
 
 @pytest.mark.parametrize("dtype,C_in,C_out,N", [("bf16", 64, 64, 517), ("bf16", 64, 64, 30001),
                                                 ("bf16", 32, 64, 1000), ("bf16", 256, 1024, 300),
+                                                ("bf16", 192, 768, 2000),
                                                 ("f32", 16, 24, 70)])
 def test_backward(dtype, C_in, C_out, N, cuda_device):
     print(f"[case] d4 backward {dtype} {C_in}->{C_out} N={N}", flush=True)

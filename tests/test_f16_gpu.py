@@ -105,16 +105,17 @@ def test_backward_weights_fused_g8(group, cuda_device):
     _check(db, rb, f"f16 {group} db fused", rms(rb))
 
 
-@pytest.mark.parametrize("G,C_in,C_out,N", [(4, 192, 768, 300), (8, 256, 1024, 130)])
-def test_backward_weights_large_channels(G, C_in, C_out, N, cuda_device):
+@pytest.mark.parametrize("G,C_in,C_out,N,group", [(4, 192, 768, 300, "cyclic"), (8, 256, 1024, 130, "cyclic"),
+                                                   (8, 256, 1024, 130, "d4")])
+def test_backward_weights_large_channels(G, C_in, C_out, N, group, cuda_device):
     # fp16 at large channel counts: the three-pass matrix-core weight gradient
     x, W, _ = make_inputs(G, C_in, C_out, N, "f16", seed=35)
     dy = make_grad(G, C_out, N, "f16", seed=35)
-    h = eq.prepare_weights(W.to(cuda_device))
+    h = eq.prepare_weights(W.to(cuda_device), group=group)
     assert "split-K" in h.describe()
     dW, db = eq.backward_weights(h, x.to(cuda_device), dy.to(cuda_device))
     torch.cuda.synchronize()
-    rW, rb = oracle.backward_weights(x, dy)
+    rW, rb = d4.backward_weights(x, dy) if group == "d4" else oracle.backward_weights(x, dy)
     rms = lambda a: float(np.sqrt(np.mean(a * a)))
     _check(dW, rW, f"f16 dW G={G} {C_in}x{C_out}", rms(rW))
     _check(db, rb, f"f16 db G={G} {C_in}x{C_out}", rms(rb))
