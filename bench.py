@@ -83,6 +83,22 @@ def time_eager(torch, launch, K: int, R: int):
     return start.elapsed_time(end) / K
 
 
+def time_each(torch, launch, n: int, R: int):
+    """Per-launch durations: n eager launches, each between its own pair of events on the launch
+    stream (the pair adds a little to each figure). Returns {"median", "min"} in microseconds."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, e) in enumerate(ev):
+        a.record(stream)
+        launch(i % R)
+        e.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(e) * 1e3 for a, e in ev)
+    return {"median": round(us[n // 2], 3), "min": round(us[0], 3), "launches": n,
+            "timing": "eager launches, an event pair around each"}
+
+
 def cpu_baseline(w, x, W, b, budget_s: float = 12.0):
     """The fp64 oracle, as it stands, on the host cores over a bounded sample of the workload: whole
     passes over the workload's tokens until about `budget_s` seconds have run, or (when one pass
@@ -253,6 +269,8 @@ def main():
             "kernel": "spectral forward (one launch per step)",
             "algorithmic_bytes_per_launch": B, "algorithmic_flops_per_launch": F,
             "mfma_frac": round(F / t / 1e12 / peak_c, 4), "hbm_frac": round(B / t / 1e9 / rl.PEAK_HBM_GBS, 4)}
+    each = time_each(torch, spectral, max(100, min(K, 500)), R)
+    log(f"[bench] spectral per launch: median {each['median']:.2f} us, min {each['min']:.2f} us")
 
     extra = {}
     if not args.no_expanded:
@@ -260,6 +278,7 @@ def main():
             expanded(i % R)
         torch.cuda.synchronize()
         ms_e = timer(torch, expanded, K, R)
+        each_e = time_each(torch, expanded, max(100, min(K, 500)), R)
         Fd = rl.dense_flops(w.N, w.C_in, w.C_out, w.G)
         Bd = rl.dense_bytes(w.N, w.C_in, w.C_out, w.G, eb)
         te = ms_e / 1e3
@@ -267,7 +286,8 @@ def main():
         extra["expanded_baseline"] = {
             "ms_per_step": round(ms_e, 6), "tokens_per_s": w.N / te, "bound": bd_,
             "roof_frac": round(tr / te, 4), "mfma_frac": round(Fd / te / 1e12 / peak_c, 4),
-            "hbm_frac": round(Bd / te / 1e9 / rl.PEAK_HBM_GBS, 4), "effective_tflops": round(Fd / te / 1e12, 2)}
+            "hbm_frac": round(Bd / te / 1e9 / rl.PEAK_HBM_GBS, 4), "effective_tflops": round(Fd / te / 1e12, 2),
+            "per_launch_us": each_e}
         extra["speedup_vs_expanded"] = round(ms_e / ms, 3)
         log(f"[bench] expanded: {ms_e * 1e3:.2f} us/step  speedup {ms_e / ms:.2f}x")
     if args.backward:
@@ -312,6 +332,7 @@ def main():
         extra["block"] = bench_block(torch, eq, rl, timer, dev, K, Wm, not args.no_expanded)
     extra["effective_tflops"] = round(rl.dense_flops(w.N, w.C_in, w.C_out, w.G) / t / 1e12, 2)
     extra["useful_tflops"] = round(F / t / 1e12, 2)
+    extra["per_launch_us"] = each
 
     line = {
         "metric": METRIC, "value": w.N / t, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,

@@ -9,6 +9,11 @@
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes B \
         --workload NAME --cmd "..." --out profiles/traffic_NAME.json
 
+    # matrix-core utilisation from one counter run (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA
+    # SQ_INSTS_VALU GRBM_GUI_ACTIVE)
+    python -m fourier_domain_linear_amd.profiling mfma DIR --kernel k_p8 --workload NAME \
+        --cmd "..." --out profiles/mfma_NAME.txt
+
 DIR is a rocprofv3 output directory (-d); the CSV files are found by name inside it.
 """
 from __future__ import annotations
@@ -66,6 +71,21 @@ def counter_per_dispatch(d: str, kernel: str, counter: str):
     return list(per.values())
 
 
+def dispatches(d: str, kernel: str):
+    """Per dispatch of kernels whose name contains `kernel`: (kernel name, duration in ns, {counter:
+    value summed over its hardware instances})."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    meta = {}
+    with open(_find(d, "*counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"]:
+                per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+                meta[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if not per:
+        raise ValueError(f"no counter samples for kernels matching {kernel!r} in {d}")
+    return [(meta[k][0], meta[k][1], dict(v)) for k, v in per.items()]
+
+
 def _avg(v):
     return sum(v) / len(v)
 
@@ -106,6 +126,49 @@ def cmd_traffic(a):
     print(json.dumps(rec, indent=1))
 
 
+def cmd_mfma(a):
+    """Matrix-core busy fraction: SQ_VALU_MFMA_BUSY_CYCLES counts, summed over every SIMD, the cycles
+    its matrix core is busy (32 per 32x32x16 and 16 per 16x16x32 bf16 instruction); GRBM_GUI_ACTIVE
+    counts the busy cycles of each XCD's graphics engine over the dispatch (summed over the XCDs)."""
+    from fourier_domain_linear_amd import roofline as rl
+    from fourier_domain_linear_amd.workloads import BY_NAME
+
+    rows = dispatches(a.dir, a.kernel)
+    names = sorted({r[0] for r in rows})
+    dur = _avg([r[1] for r in rows])
+    c = {k: _avg([r[2].get(k, 0.0) for r in rows]) for k in
+         ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE")}
+    cyc = c["GRBM_GUI_ACTIVE"] / a.xcds
+    busy_grbm = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (a.simds * cyc) if cyc else float("nan")
+    busy_dur = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (a.simds * dur * a.clock_ghz)
+    w = BY_NAME[a.workload]
+    flop = rl.spectral_flops(w.N, w.C_in, w.C_out, w.G, w.group)
+    issued = c["SQ_INSTS_MFMA"] * a.inst_flop
+    lines = [
+        "# matrix-core utilisation per launch (rocprofv3 --pmc, one pass)",
+        f"# command: {a.cmd}",
+        f"workload: {a.workload}",
+        "kernel: " + " / ".join(names),
+        f"dispatches averaged: {len(rows)}",
+        f"duration (counters on), us: {dur / 1e3:.3f}",
+        f"SQ_INSTS_MFMA: {c['SQ_INSTS_MFMA']:.0f}  (x {a.inst_flop} FLOP = {issued:.4g} issued;"
+        f" useful {flop:.4g}, ratio {issued / flop:.4f})",
+        f"SQ_VALU_MFMA_BUSY_CYCLES: {c['SQ_VALU_MFMA_BUSY_CYCLES']:.0f}",
+        f"SQ_INSTS_VALU: {c['SQ_INSTS_VALU']:.0f}  ({c['SQ_INSTS_VALU'] / max(1.0, c['SQ_INSTS_MFMA']):.2f} per MFMA)",
+        f"GRBM_GUI_ACTIVE: {c['GRBM_GUI_ACTIVE']:.0f}  ({cyc:.0f} per XCD over {a.xcds} XCDs: the engines' busy"
+        f" window, dispatch set-up included)",
+        f"matrix-core busy fraction, over the kernel duration at {a.clock_ghz} GHz: {busy_dur:.4f}",
+        f"matrix-core busy fraction, over the GRBM_GUI_ACTIVE window: {busy_grbm:.4f}",
+        f"useful TFLOP/s at the profiled duration: {flop / dur / 1e3:.1f}"
+        f" ({flop / dur / 1e3 / rl.PEAK_BF16_TFLOPS:.4f} of the 2.5 PFLOP/s bf16 peak)",
+    ]
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -124,8 +187,19 @@ def main(argv=None):
     t.add_argument("--workload", required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--simds", type=int, default=1024)
+    m.add_argument("--xcds", type=int, default=8)
+    m.add_argument("--clock-ghz", type=float, default=2.4)
+    m.add_argument("--inst-flop", type=int, default=32768,
+                   help="FLOP per matrix-core instruction (32x32x16: 32768, 16x16x32: 16384)")
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--out")
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.what](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -43,3 +43,34 @@ def test_bytes_and_roof():
 def test_bad_group():
     with pytest.raises(ValueError):
         roofline.real_products(3)
+
+
+def test_mfma_counter_summary(tmp_path):
+    # two dispatches of one kernel, each counter split over two hardware instances; another kernel's
+    # rows must be ignored
+    from fourier_domain_linear_amd import profiling
+
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for d, t0 in ((1, 1000), (2, 5000)):
+        for name, v in (("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 240), ("SQ_INSTS_MFMA", 30), ("SQ_INSTS_VALU", 60),
+                        ("GRBM_GUI_ACTIVE", 8 * 1200)):
+            for _ in range(2):
+                rows.append([d, "k_demo<4>", name, v / 2, t0, t0 + 1000])
+    rows.append([3, "other", "SQ_INSTS_MFMA", 1e9, 0, 1])
+    d = tmp_path / "run"
+    d.mkdir()
+    with open(d / "x_counter_collection.csv", "w") as f:
+        f.write(",".join(hdr) + "\n")
+        for r in rows:
+            f.write(",".join(f'"{c}"' if isinstance(c, str) else str(c) for c in r) + "\n")
+    out = tmp_path / "s.txt"
+    profiling.main(["mfma", str(d), "--kernel", "k_demo", "--workload", "p4_c96_n25088_bf16", "--cmd", "c",
+                    "--out", str(out)])
+    text = out.read_text()
+    assert "dispatches averaged: 2" in text
+    assert "SQ_INSTS_MFMA: 30 " in text
+    # 1024*240 busy cycles over 1024 SIMDs x 1000 ns x 2.4 GHz -> 0.1; over 1200 GRBM cycles per XCD -> 0.2
+    assert "over the kernel duration at 2.4 GHz: 0.1000" in text
+    assert "over the GRBM_GUI_ACTIVE window: 0.2000" in text
+    assert "(2.00 per MFMA)" in text
