@@ -70,9 +70,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    # EQLIN_ORACLE_LIB: a deliberately broken build of eqlin_oracle.c, used only by the test that
+    # checks that the pins catch planted mistakes
+    path = os.environ.get("EQLIN_ORACLE_LIB") or _LIB
+    if path == _LIB and not os.path.exists(_LIB):
         build(force=False)
-    lib = ctypes.CDLL(_LIB)
+    lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     i64 = ctypes.c_int64
     lib.eqlin_oracle_forward.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int]
