@@ -222,7 +222,10 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
     constexpr int NU = KS / SG::U;
     extern __shared__ uint4 lds[];
     constexpr int NW = kStreamWaves;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // the wave index through a scalar register: the compiler then knows that the block index and the
+    // buffer resources derived from it are wave-uniform (no per-lane loop around each buffer access)
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int g = lane >> 4;
     const int nb0 = blockIdx.y * nb_tile;
     const int64_t blocks = (N + 15) >> 4;
