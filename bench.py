@@ -126,8 +126,29 @@ def cpu_baseline(w, x, W, b, budget_s: float = 12.0):
         dt = time.perf_counter() - t0
         tokens = n
         sample = f"first {n} of {w.N} tokens of the workload"
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
-            "seconds": round(dt, 3)}
+    out = {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
+           "seconds": round(dt, 3), "cpu_model": _cpu_model()}
+    if w.group != "d4":
+        # the same oracle on one thread, over the first tokens that fit about a quarter of the budget
+        t0 = time.perf_counter()
+        fwd(x[:pilot], W, b, threads=1)
+        n1 = min(w.N, max(pilot, int(budget_s / 4 / max(1e-12, (time.perf_counter() - t0) / pilot))))
+        t0 = time.perf_counter()
+        fwd(x[:n1], W, b, threads=1)
+        out["single_thread"] = {"value": n1 / (time.perf_counter() - t0), "unit": "tokens/s",
+                                "sample": f"first {n1} of {w.N} tokens"}
+    return out
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def bench_block(torch, eq, rl, timer, dev, K: int, Wm: int, with_expanded: bool):
