@@ -1,5 +1,6 @@
 /*
- * eqlin.h -- C ABI of the MI355X (gfx950) EQ-Linear forward library, libeqlin.so.
+ * eqlin.h -- C ABI of the MI355X (gfx950) EQ-Linear library, libeqlin.so: the spectral forward, its
+ * dense comparator, the fused-activation variants and the gradients.
  *
  * The operation. A cyclic-group equivariant linear layer (EQ-Linear) over tokens shaped
  * [channels, G], G the order of the rotation group (p4: G = 4; p8: G = 8; G = 1 and 2 also work):
