@@ -311,6 +311,30 @@ def main():
             "per_launch_us": each_e}
         extra["speedup_vs_expanded"] = round(ms_e / ms, 3)
         log(f"[bench] expanded: {ms_e * 1e3:.2f} us/step  speedup {ms_e / ms:.2f}x")
+        if w.group == "cyclic":
+            # context only, never the baseline: the same unrolled product through torch's F.linear
+            # (the vendor GEMM library), the comparator the page measures against
+            E = eq.export_expanded_weight(h)
+            b_exp = bd.repeat_interleave(w.G)
+            xf = [t.view(w.N, w.C_in * w.G) for t in xs]
+
+            def torch_linear(i):
+                torch.nn.functional.linear(xf[i], E, b_exp)
+
+            # eager launches (a library GEMM is kept out of graph capture: its internal memsets are
+            # not checked here for replay safety)
+            try:
+                for i in range(Wm):
+                    torch_linear(i % R)
+                torch.cuda.synchronize()
+                ms_t = time_eager(torch, torch_linear, K, R)
+                extra["torch_linear_context"] = {"ms_per_step": round(ms_t, 6), "tokens_per_s": w.N / (ms_t / 1e3),
+                                                 "spectral_speedup": round(ms_t / ms, 3),
+                                                 "timing": "eager launches"}
+                log(f"[bench] torch F.linear on the unrolled weight (context): {ms_t * 1e3:.2f} us/step")
+            except RuntimeError as e:  # context only: never fail the bench over it
+                extra["torch_linear_context"] = {"error": str(e)[:200]}
+            del E, b_exp, xf
     if args.backward:
         # the gradients of the same layer: dx on the forward kernels (transposed, group-reversed W),
         # dW and db by the frequency-domain products over tokens; dy is a seeded upstream gradient
