@@ -801,6 +801,10 @@ static hipError_t launch_p8(const Plan *p, const void *x, const void *b, void *y
     if (tiles_t > 0x7fffffff || (int64_t)C::BT * p->C_out * C::G * 2 > 0x7fffffff) return hipErrorInvalidValue;
     int64_t per_o = std::max(1, p->fwd.num_cus / tiles_o);
     per_o = std::min<int64_t>(per_o, tiles_t);
+    // the fewest token streams per output tile that keep the number of tile rounds: every stream then
+    // gets the same number of tiles (196 tiles: 28 streams of 7, not 32 of which 4 run a 7th)
+    const int64_t rounds = (tiles_t + per_o - 1) / per_o;
+    per_o = (tiles_t + rounds - 1) / rounds;
     const int64_t grid = per_o * tiles_o;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     const int xg = xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * C::G * 2);
