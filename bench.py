@@ -6,14 +6,16 @@ per-frequency products, inverse DFT + bias, store -- one fused kernel). Default 
 (G = 4), C_in = C_out = 96, N = 8x56x56 = 25088 tokens, bf16 in/out, synthetic seeded inputs.
 
 Timing. Inputs are resident in HBM before the timed region. W warmup steps run eagerly; then K steps
-are captured into one HIP graph (so the ~6 us kernels are not bounded by host launch latency) and
+are captured into one HIP graph (so the ~10 us kernels are not bounded by host launch latency) and
 replayed once untimed and once timed, between HIP events on the launch stream, with
 torch.cuda.synchronize() on both sides. The K steps rotate over R buffer sets totalling >= 1 GiB,
 more than the 256 MB Infinity Cache, so x is read from HBM, not from the cache.
 ms_per_step = event time / K; value = tokens / (ms_per_step / 1e3).
 
-The same is done for eqlin_forward_expanded (the unrolled dense product, the comparator), and the
-fp64 oracle is timed on the host cores over a bounded sample (cpu_baseline).
+Per-launch median and minimum come from a separate pass of eager launches, each between its own
+pair of events. The same is done for eqlin_forward_expanded (the unrolled dense product, the
+comparator); torch's F.linear on the unrolled weight is timed as context only; and the fp64 oracle
+is timed on the host cores over a bounded sample (cpu_baseline, with a one-thread figure).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
