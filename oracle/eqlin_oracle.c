@@ -43,6 +43,17 @@
 #include <omp.h>
 #endif
 
+/* Threads for one call: nthreads > 0 asks for that many, else OpenMP's default. Passed as a clause
+ * of the call's parallel loop, so one call's request does not change the next call's default. */
+static int team_size(int nthreads) {
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
 int eqlin_oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
@@ -75,12 +86,9 @@ int eqlin_oracle_forward(const double *x, const double *W, const double *b, doub
     double *E = (double *)malloc((size_t)(rows * cols) * sizeof(double));
     if (!E) return -2;
     eqlin_oracle_expand(W, C_out, C_in, G, E);
-#ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(static)
+    const int nt = team_size(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(static) num_threads(nt)
     for (int64_t n = 0; n < N; ++n) {
         const double *xn = x + n * cols;
         double *yn = y + n * rows;
@@ -129,12 +137,9 @@ int eqlin_oracle_backward_data(const double *dy, const double *W, double *dx, in
     double *E = (double *)malloc((size_t)(rows * cols) * sizeof(double));
     if (!E) return -2;
     eqlin_oracle_expand(W, C_out, C_in, G, E);
-#ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(static)
+    const int nt = team_size(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(static) num_threads(nt)
     for (int64_t n = 0; n < N; ++n) {
         const double *dyn = dy + n * rows;
         double *dxn = dx + n * cols;
@@ -156,12 +161,9 @@ int eqlin_oracle_backward_weights(const double *x, const double *dy, double *dW,
     if (N > 0 && (!x || !dy)) return -1;
     const int64_t rows = C_out * G, cols = C_in * G;
     int failed = 0;
-#ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(static) reduction(| : failed)
+    const int nt = team_size(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(static) num_threads(nt) reduction(| : failed)
     for (int64_t o = 0; o < C_out; ++o) {
         /* the G rows of dE that belong to output channel o */
         double *dE = (double *)malloc((size_t)(G * cols) * sizeof(double));
