@@ -73,21 +73,6 @@ __device__ __forceinline__ void negate_imag(const uint4 (&a)[G], uint4 (&an)[G])
     for (int p = 0; p < G; ++p) an[p] = (p >= 3 && (p & 1)) ? neg_bf16x8(a[p]) : a[p];
 }
 
-// One lane's share of a 32-channel step (token n, channels i0..i0+7, all G samples) with the token
-// index clamped to N-1 and the channel group to the last real one, so every lane issues the same G
-// loads (no branches, no zero fill). Rows past N
-// only feed outputs that are never stored; a channel group past C_in only meets zero weight
-// columns (the prepared weights are zero-padded), so its (finite) duplicate data contributes 0.
-template <int G>
-__device__ __forceinline__ void load_x_clamped(const uint4 *__restrict__ x4, int64_t n, int64_t N,
-                                               int C_in, int i0, uint4 (&r)[G]) {
-    const int64_t nc = n < N ? n : N - 1;
-    const int ic = i0 < C_in ? i0 : C_in - 8;
-    const uint4 *p = x4 + ((nc * C_in + ic) >> 3) * G;
-#pragma unroll
-    for (int q = 0; q < G; ++q) r[q] = p[q];
-}
-
 // The 2G-2 real products with the weights as the A operand (rows = outputs) and the x planes as
 // the B operand (columns = tokens): D lane l holds outputs 4*(l/16)+v of token l%16. D4: the four
 // characters' products, then Y(rho) = X(rho) W(rho) entry by entry, Y_ab += W_cb X_ac over c = 0, 1
