@@ -2,8 +2,10 @@
 """Benchmark of the EQ-Linear spectral forward on one MI355X.
 
 A step is one eqlin_forward over one batch of the workload (the whole hot path: load, group DFT,
-per-frequency products, inverse DFT + bias, store -- one fused kernel). Default workload: p4
-(G = 4), C_in = C_out = 96, N = 8x56x56 = 25088 tokens, bf16 in/out, synthetic seeded inputs.
+per-frequency products, inverse DFT + bias, store -- one fused kernel). Default workload: the largest
+configured one, p8 (G = 8), C_in = 256 -> C_out = 1024, N = 64x14x14 = 12544 tokens, bf16 in/out,
+synthetic seeded inputs (matrix-core bound). The line also carries a table ("configs") with every
+configured workload's spectral and expanded times, roofline fractions and speedup.
 
 Timing. Inputs are resident in HBM before the timed region. W warmup steps run eagerly; then K steps
 are captured into one HIP graph (so the ~10 us kernels are not bounded by host launch latency) and
@@ -48,7 +50,7 @@ def load_traffic(workload: str):
         rec = json.load(f)
     from fourier_domain_linear_amd.profiling import kernel_source_hash
 
-    if rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("source_sha256") != kernel_source_hash(rec.get("sources")):
         log(f"[bench] {path} was taken on other kernel sources: traffic = null")
         return None
     return rec.get("traffic_bytes_per_launch")
@@ -153,6 +155,52 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def bench_backward(torch, eq, rl, w, st, dev, K: int, Wm: int, timer, with_expanded: bool):
+    """Time the gradients of the headline layer: eqlin_backward_data (dx on the forward kernels over the
+    transposed, group-reversed weight) and eqlin_backward_weights (dW, db by frequency-domain products
+    over tokens); dy is a seeded upstream gradient."""
+    import ctypes
+
+    from fourier_domain_linear_amd.workloads import make_grad
+
+    h, xs, R, F, B, peak_c = st["h"], st["xs"], st["R"], st["F"], st["B"], st["peak_c"]
+    eb = w.elem_bytes
+    dy0 = make_grad(w.G, w.C_out, w.N, w.dtype, seed=0).to(dev)
+    dys = [dy0] + [dy0.clone() for _ in range(R - 1)]
+    dxs = [torch.empty_like(xs[0]) for _ in range(R)]
+    ws = torch.empty((max(1, eq.backward_weights_workspace(h, w.N)),), dtype=torch.uint8, device=dev)
+    dW = torch.empty((w.C_out, w.C_in, w.G), dtype=torch.float32, device=dev)
+    db = torch.empty((w.C_out,), dtype=torch.float32, device=dev)
+    lib = eq.load_library()
+
+    def bwd_data(i):
+        eq.backward_data(h, dys[i], dxs[i])
+
+    def bwd_weights(i):
+        st_ = lib.eqlin_backward_weights(ctypes.c_void_p(h.ptr), ctypes.c_void_p(xs[i].data_ptr()),
+                                         ctypes.c_void_p(dys[i].data_ptr()), ctypes.c_void_p(dW.data_ptr()),
+                                         ctypes.c_void_p(db.data_ptr()), w.N, ctypes.c_void_p(ws.data_ptr()),
+                                         ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st_ != 0:
+            raise RuntimeError(f"eqlin_backward_weights: {eq.status_string(st_)}")
+
+    res = {}
+    for name, fn, Bk in (("data", bwd_data, B),
+                         ("weights", bwd_weights,
+                          w.N * (w.C_in + w.C_out) * w.G * eb + w.C_out * w.C_in * w.G * 4 + w.C_out * 4)):
+        for i in range(Wm):
+            fn(i % R)
+        torch.cuda.synchronize()
+        ms_b = timer(torch, fn, K, R)
+        tb = ms_b / 1e3
+        res[name] = {"us_per_step": round(ms_b * 1e3, 3), "tokens_per_s": w.N / tb,
+                     "useful_tflops": round(F / tb / 1e12, 2), "mfma_frac": round(F / tb / 1e12 / peak_c, 4),
+                     "algorithmic_bytes": Bk, "hbm_frac": round(Bk / tb / 1e9 / rl.PEAK_HBM_GBS, 4)}
+        log(f"[bench] backward {name}: {ms_b * 1e3:.2f} us/step")
+    res["kernels"] = h.describe().split("|")[3:]
+    return res
+
+
 def bench_block(torch, eq, rl, timer, dev, K: int, Wm: int, with_expanded: bool):
     """Time the MLP block (layer 1 with GELU in its epilogue, then layer 2; two launches per step) on
     its seeded inputs, its two layers alone, and the same block on the unrolled weights."""
@@ -203,18 +251,126 @@ def bench_block(torch, eq, rl, timer, dev, K: int, Wm: int, with_expanded: bool)
     return res
 
 
+def measure_forward(torch, eq, rl, w, dev, K: int, Wm: int, timer, with_expanded: bool = True,
+                    with_torch: bool = False, with_each: bool = True, backward: bool = False):
+    """Time eqlin_forward (and eqlin_forward_expanded) on workload w's seeded inputs, resident in HBM
+    and rotated over >= 1 GiB of buffer sets. Returns (record, state) where record holds the figures
+    and state the tensors and handle a caller may reuse."""
+    x, W, b = workload_inputs_for(w)
+    eb = w.elem_bytes
+    set_bytes = w.N * (w.C_in + w.C_out) * w.G * eb
+    R = max(3, math.ceil((1 << 30) / set_bytes))
+    xd0 = x.to(dev)
+    xs = [xd0] + [xd0.clone() for _ in range(R - 1)]
+    ys = [torch.empty((w.N, w.C_out, w.G), dtype=w.torch_dtype, device=dev) for _ in range(R)]
+    bd = b.to(dev)
+    h = eq.prepare_weights(W.to(dev), expanded=with_expanded, backward=backward, group=w.group)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: {h.describe()}  rotating buffer sets: {R} ({R * set_bytes / 2**20:.0f} MiB)")
+
+    def spectral(i):
+        eq.forward(h, xs[i], bd, ys[i])
+
+    def expanded(i):
+        eq.forward_expanded(h, xs[i], bd, ys[i])
+
+    for i in range(Wm):
+        spectral(i % R)
+    torch.cuda.synchronize()
+    ms = timer(torch, spectral, K, R)
+    log(f"[bench] {w.name} spectral: {ms * 1e3:.2f} us/step")
+    F = rl.spectral_flops(w.N, w.C_in, w.C_out, w.G, w.group)
+    B = rl.spectral_bytes(w.N, w.C_in, w.C_out, w.G, eb)
+    # fp16 matrix cores have the bf16 dense peak on this chip (2.5 PFLOP/s)
+    peak_c = rl.PEAK_BF16_TFLOPS if w.dtype in ("bf16", "f16") else rl.PEAK_FP32_TFLOPS
+    _, bound = rl.roof_time_s(F, B, peak_c)
+    t = ms / 1e3
+    rec = {"workload": w.name, "us_per_step": round(ms * 1e3, 3), "tokens_per_s": w.N / t, "bound": bound,
+           "frac": round((B / t / 1e9 / rl.PEAK_HBM_GBS) if bound == "hbm" else (F / t / 1e12 / peak_c), 4),
+           "mfma_frac": round(F / t / 1e12 / peak_c, 4), "hbm_frac": round(B / t / 1e9 / rl.PEAK_HBM_GBS, 4),
+           "useful_tflops": round(F / t / 1e12, 2),
+           "effective_tflops": round(rl.dense_flops(w.N, w.C_in, w.C_out, w.G) / t / 1e12, 2),
+           "kernel": h.describe().split("|")[1].strip().removeprefix("forward: ")}
+    state = {"x": x, "W": W, "b": b, "xs": xs, "ys": ys, "bd": bd, "h": h, "R": R, "ms": ms, "F": F, "B": B,
+             "peak_c": peak_c, "bound": bound, "spectral": spectral}
+    if with_each:
+        rec["per_launch_us"] = time_each(torch, spectral, max(100, min(K, 500)), R)
+        log(f"[bench] {w.name} spectral per launch: median {rec['per_launch_us']['median']:.2f} us, "
+            f"min {rec['per_launch_us']['min']:.2f} us")
+    if with_expanded:
+        for i in range(Wm):
+            expanded(i % R)
+        torch.cuda.synchronize()
+        ms_e = timer(torch, expanded, K, R)
+        Fd = rl.dense_flops(w.N, w.C_in, w.C_out, w.G)
+        Bd = rl.dense_bytes(w.N, w.C_in, w.C_out, w.G, eb)
+        te = ms_e / 1e3
+        tr, bd_ = rl.roof_time_s(Fd, Bd, peak_c)
+        exp = {"us_per_step": round(ms_e * 1e3, 3), "tokens_per_s": w.N / te, "bound": bd_,
+               "roof_frac": round(tr / te, 4), "mfma_frac": round(Fd / te / 1e12 / peak_c, 4),
+               "hbm_frac": round(Bd / te / 1e9 / rl.PEAK_HBM_GBS, 4), "effective_tflops": round(Fd / te / 1e12, 2),
+               "kernel": h.describe().split("|")[2].strip().removeprefix("expanded: ")}
+        if with_each:
+            exp["per_launch_us"] = time_each(torch, expanded, max(100, min(K, 500)), R)
+        rec["expanded"] = exp
+        rec["speedup_vs_expanded"] = round(ms_e / ms, 3)
+        log(f"[bench] {w.name} expanded: {ms_e * 1e3:.2f} us/step  speedup {ms_e / ms:.2f}x")
+        if with_torch and w.group == "cyclic":
+            # context only, never the baseline: the same unrolled product through torch's F.linear
+            # (the vendor GEMM library), the comparator the page measures against
+            E = eq.export_expanded_weight(h)
+            b_exp = bd.repeat_interleave(w.G)
+            xf = [v.view(w.N, w.C_in * w.G) for v in xs]
+
+            def torch_linear(i):
+                torch.nn.functional.linear(xf[i], E, b_exp)
+
+            # eager launches (a library GEMM is kept out of graph capture: its internal memsets are
+            # not checked here for replay safety)
+            try:
+                for i in range(Wm):
+                    torch_linear(i % R)
+                torch.cuda.synchronize()
+                ms_t = time_eager(torch, torch_linear, K, R)
+                rec["torch_linear_context"] = {"us_per_step": round(ms_t * 1e3, 3),
+                                               "tokens_per_s": w.N / (ms_t / 1e3),
+                                               "spectral_speedup": round(ms_t / ms, 3), "timing": "eager launches"}
+                log(f"[bench] torch F.linear on the unrolled weight (context): {ms_t * 1e3:.2f} us/step")
+            except RuntimeError as e:  # context only: never fail the bench over it
+                rec["torch_linear_context"] = {"error": str(e)[:200]}
+            del E, b_exp, xf
+    return rec, state
+
+
+_INPUT_CACHE = {}
+
+
+def workload_inputs_for(w):
+    from fourier_domain_linear_amd.workloads import workload_inputs
+
+    if w.name not in _INPUT_CACHE:
+        _INPUT_CACHE.clear()
+        _INPUT_CACHE[w.name] = workload_inputs(w, seed=0)
+    return _INPUT_CACHE[w.name]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default=None, help="workload name (default: the p4, 96-channel one)")
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: the largest, p8 256->1024 channels, 12544 tokens)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-expanded", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload table (every configured workload, spectral and expanded)")
+    ap.add_argument("--config-steps", type=int, default=200, help="timed steps per workload of the table")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--backward", action="store_true",
-                    help="also time eqlin_backward_data and eqlin_backward_weights (reported under 'backward')")
+                    help="also time eqlin_backward_data and eqlin_backward_weights, and the same gradients "
+                         "through the unrolled weight (reported under 'backward')")
     ap.add_argument("--block", action="store_true",
                     help="also time the transformer MLP block EQ-Linear(C->4C), GELU, EQ-Linear(4C->C) at the "
                          "p4 192-channel shape, spectral and expanded (reported under 'block')")
@@ -241,7 +397,7 @@ def main():
 
     import fourier_domain_linear_amd as eq
     from fourier_domain_linear_amd import roofline as rl
-    from fourier_domain_linear_amd.workloads import BENCH_WORKLOAD, BY_NAME, make_grad, workload_inputs
+    from fourier_domain_linear_amd.workloads import BENCH_WORKLOAD, BY_NAME, WORKLOADS
 
     w = BY_NAME[args.workload] if args.workload else BENCH_WORKLOAD
     if not torch.cuda.is_available():
@@ -250,38 +406,12 @@ def main():
     dev = torch.device("cuda:0")
     eq.load_library()
 
-    log(f"[bench] workload {w.name}: G={w.G} C_in={w.C_in} C_out={w.C_out} N={w.N} {w.dtype}")
-    x, W, b = workload_inputs(w, seed=0)
-    eb = w.elem_bytes
-    set_bytes = w.N * (w.C_in + w.C_out) * w.G * eb
-    R = max(3, math.ceil((1 << 30) / set_bytes))
-    xd0 = x.to(dev)
-    xs = [xd0] + [xd0.clone() for _ in range(R - 1)]
-    ys = [torch.empty((w.N, w.C_out, w.G), dtype=w.torch_dtype, device=dev) for _ in range(R)]
-    bd = b.to(dev)
-    h = eq.prepare_weights(W.to(dev), expanded=not args.no_expanded, backward=args.backward, group=w.group)
-    torch.cuda.synchronize()
-    log(f"[bench] {h.describe()}  rotating buffer sets: {R} ({R * set_bytes / 2**20:.0f} MiB)")
-
-    def spectral(i):
-        eq.forward(h, xs[i], bd, ys[i])
-
-    def expanded(i):
-        eq.forward_expanded(h, xs[i], bd, ys[i])
-
     K, Wm = args.steps, args.warmup
     timer = time_eager if args.no_graph else time_graph
-    for i in range(Wm):
-        spectral(i % R)
-    torch.cuda.synchronize()
-    ms = timer(torch, spectral, K, R)
-    log(f"[bench] spectral: {ms * 1e3:.2f} us/step")
-
-    F = rl.spectral_flops(w.N, w.C_in, w.C_out, w.G, w.group)
-    B = rl.spectral_bytes(w.N, w.C_in, w.C_out, w.G, eb)
-    # fp16 matrix cores have the bf16 dense peak on this chip (2.5 PFLOP/s)
-    peak_c = rl.PEAK_BF16_TFLOPS if w.dtype in ("bf16", "f16") else rl.PEAK_FP32_TFLOPS
-    _, bound = rl.roof_time_s(F, B, peak_c)
+    log(f"[bench] workload {w.name}: G={w.G} C_in={w.C_in} C_out={w.C_out} N={w.N} {w.dtype} ({w.group})")
+    rec, st = measure_forward(torch, eq, rl, w, dev, K, Wm, timer, with_expanded=not args.no_expanded,
+                              with_torch=True, with_each=True, backward=args.backward)
+    ms, F, B, peak_c, bound = st["ms"], st["F"], st["B"], st["peak_c"], st["bound"]
     t = ms / 1e3
     if bound == "hbm":
         achieved, peak, unit = B / t / 1e9, rl.PEAK_HBM_GBS, "GB/s"
@@ -289,97 +419,43 @@ def main():
         achieved, peak, unit = F / t / 1e12, peak_c, "TFLOP/s"
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name),
-            "kernel": "spectral forward (one launch per step)",
+            "kernel": rec["kernel"] + " (one launch per step)",
             "algorithmic_bytes_per_launch": B, "algorithmic_flops_per_launch": F,
-            "mfma_frac": round(F / t / 1e12 / peak_c, 4), "hbm_frac": round(B / t / 1e9 / rl.PEAK_HBM_GBS, 4)}
-    each = time_each(torch, spectral, max(100, min(K, 500)), R)
-    log(f"[bench] spectral per launch: median {each['median']:.2f} us, min {each['min']:.2f} us")
+            "mfma_frac": rec["mfma_frac"], "hbm_frac": rec["hbm_frac"]}
 
     extra = {}
-    if not args.no_expanded:
-        for i in range(Wm):
-            expanded(i % R)
-        torch.cuda.synchronize()
-        ms_e = timer(torch, expanded, K, R)
-        each_e = time_each(torch, expanded, max(100, min(K, 500)), R)
-        Fd = rl.dense_flops(w.N, w.C_in, w.C_out, w.G)
-        Bd = rl.dense_bytes(w.N, w.C_in, w.C_out, w.G, eb)
-        te = ms_e / 1e3
-        tr, bd_ = rl.roof_time_s(Fd, Bd, peak_c)
-        extra["expanded_baseline"] = {
-            "ms_per_step": round(ms_e, 6), "tokens_per_s": w.N / te, "bound": bd_,
-            "roof_frac": round(tr / te, 4), "mfma_frac": round(Fd / te / 1e12 / peak_c, 4),
-            "hbm_frac": round(Bd / te / 1e9 / rl.PEAK_HBM_GBS, 4), "effective_tflops": round(Fd / te / 1e12, 2),
-            "per_launch_us": each_e}
-        extra["speedup_vs_expanded"] = round(ms_e / ms, 3)
-        log(f"[bench] expanded: {ms_e * 1e3:.2f} us/step  speedup {ms_e / ms:.2f}x")
-        if w.group == "cyclic":
-            # context only, never the baseline: the same unrolled product through torch's F.linear
-            # (the vendor GEMM library), the comparator the page measures against
-            E = eq.export_expanded_weight(h)
-            b_exp = bd.repeat_interleave(w.G)
-            xf = [t.view(w.N, w.C_in * w.G) for t in xs]
-
-            def torch_linear(i):
-                torch.nn.functional.linear(xf[i], E, b_exp)
-
-            # eager launches (a library GEMM is kept out of graph capture: its internal memsets are
-            # not checked here for replay safety)
-            try:
-                for i in range(Wm):
-                    torch_linear(i % R)
-                torch.cuda.synchronize()
-                ms_t = time_eager(torch, torch_linear, K, R)
-                extra["torch_linear_context"] = {"ms_per_step": round(ms_t, 6), "tokens_per_s": w.N / (ms_t / 1e3),
-                                                 "spectral_speedup": round(ms_t / ms, 3),
-                                                 "timing": "eager launches"}
-                log(f"[bench] torch F.linear on the unrolled weight (context): {ms_t * 1e3:.2f} us/step")
-            except RuntimeError as e:  # context only: never fail the bench over it
-                extra["torch_linear_context"] = {"error": str(e)[:200]}
-            del E, b_exp, xf
+    if "expanded" in rec:
+        e = rec["expanded"]
+        extra["expanded_baseline"] = {k: v for k, v in e.items()}
+        extra["expanded_baseline"]["ms_per_step"] = round(e["us_per_step"] / 1e3, 6)
+        extra["speedup_vs_expanded"] = rec["speedup_vs_expanded"]
+    if "torch_linear_context" in rec:
+        extra["torch_linear_context"] = rec["torch_linear_context"]
     if args.backward:
-        # the gradients of the same layer: dx on the forward kernels (transposed, group-reversed W),
-        # dW and db by the frequency-domain products over tokens; dy is a seeded upstream gradient
-        dy0 = make_grad(w.G, w.C_out, w.N, w.dtype, seed=0).to(dev)
-        dys = [dy0] + [dy0.clone() for _ in range(R - 1)]
-        dxs = [torch.empty_like(xd0) for _ in range(R)]
-        ws = torch.empty((max(1, eq.backward_weights_workspace(h, w.N)),), dtype=torch.uint8, device=dev)
-        dW = torch.empty((w.C_out, w.C_in, w.G), dtype=torch.float32, device=dev)
-        db = torch.empty((w.C_out,), dtype=torch.float32, device=dev)
-        lib = eq.load_library()
-        import ctypes
-
-        def bwd_data(i):
-            eq.backward_data(h, dys[i], dxs[i])
-
-        def bwd_weights(i):
-            st = lib.eqlin_backward_weights(ctypes.c_void_p(h.ptr), ctypes.c_void_p(xs[i].data_ptr()),
-                                            ctypes.c_void_p(dys[i].data_ptr()), ctypes.c_void_p(dW.data_ptr()),
-                                            ctypes.c_void_p(db.data_ptr()), w.N, ctypes.c_void_p(ws.data_ptr()),
-                                            ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-            if st != 0:
-                raise RuntimeError(f"eqlin_backward_weights: {eq.status_string(st)}")
-
-        res = {}
-        for name, fn, Bk in (("data", bwd_data, B),
-                             ("weights", bwd_weights,
-                              w.N * (w.C_in + w.C_out) * w.G * eb + w.C_out * w.C_in * w.G * 4 + w.C_out * 4)):
-            for i in range(Wm):
-                fn(i % R)
-            torch.cuda.synchronize()
-            ms_b = timer(torch, fn, K, R)
-            tb = ms_b / 1e3
-            res[name] = {"ms_per_step": round(ms_b, 6), "tokens_per_s": w.N / tb,
-                         "useful_tflops": round(F / tb / 1e12, 2), "mfma_frac": round(F / tb / 1e12 / peak_c, 4),
-                         "algorithmic_bytes": Bk, "hbm_frac": round(Bk / tb / 1e9 / rl.PEAK_HBM_GBS, 4)}
-            log(f"[bench] backward {name}: {ms_b * 1e3:.2f} us/step")
-        res["kernels"] = h.describe().split("|")[3:]
-        extra["backward"] = res
+        extra["backward"] = bench_backward(torch, eq, rl, w, st, dev, K, Wm, timer, not args.no_expanded)
     if args.block:
         extra["block"] = bench_block(torch, eq, rl, timer, dev, K, Wm, not args.no_expanded)
-    extra["effective_tflops"] = round(rl.dense_flops(w.N, w.C_in, w.C_out, w.G) / t / 1e12, 2)
-    extra["useful_tflops"] = round(F / t / 1e12, 2)
-    extra["per_launch_us"] = each
+    extra["effective_tflops"] = rec["effective_tflops"]
+    extra["useful_tflops"] = rec["useful_tflops"]
+    extra["per_launch_us"] = rec["per_launch_us"]
+    x, W, b = st["x"], st["W"], st["b"]
+    del st
+    if not args.no_configs:
+        # every configured workload (the headline's figures reused), spectral and expanded
+        table = {}
+        for wc in WORKLOADS:
+            if wc.name == w.name:
+                r = {k: v for k, v in rec.items() if k not in ("per_launch_us", "torch_linear_context")}
+                if "expanded" in r:
+                    r["expanded"] = {k: v for k, v in r["expanded"].items() if k != "per_launch_us"}
+            else:
+                r, _ = measure_forward(torch, eq, rl, wc, dev, min(K, args.config_steps),
+                                       min(Wm, args.config_steps), timer, with_expanded=not args.no_expanded,
+                                       with_each=False)
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+            table[wc.name] = r
+        extra["configs"] = table
 
     line = {
         "metric": METRIC, "value": w.N / t, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
@@ -387,7 +463,7 @@ def main():
         "dtype": w.dtype, "data": "synthetic (seeded Gaussian x, W, b; see fourier_domain_linear_amd/workloads.py)",
         "config": {"workload": w.name, "group": w.group, "G": w.G, "C_in": w.C_in, "C_out": w.C_out, "tokens": w.N,
                    "timing": ("eager launches" if args.no_graph else "one HIP graph of K launches")
-                   + f", {R} rotating buffer sets"},
+                   + ", rotating buffer sets over >= 1 GiB"},
         "roofline": roof,
     }
     line.update(extra)

@@ -30,9 +30,11 @@
 //      own), the x fragments through LDS (shared by all waves).
 //   3. k_bw_reduce: sum of the splits, inverse DFT (scaled) -> dW fp32; k_bw_dbsum: db from its
 //      partials.
-// Other cases (fp32, fp16, G = 1 or 2, the dihedral group D4): k_bw_direct, the definition above in fp32
-// with LDS token tiles. For D4 (element a + 4b = r^a s^b) the definition reads
-// dW[o, i, d] = sum_n sum_h dy[n, o, h] x[n, i, h d^-1] (the g with g^-1 h = d).
+// The dihedral group D4 and fp16 take the same matrix-core passes (D4: its irreps' adjoint products and
+// inverse); small channel counts take one fused pass per token range instead (k_bw_small). Other cases
+// (fp32, G = 1 or 2): k_bw_direct, the definition above in fp32 with LDS token tiles. For D4 (element
+// a + 4b = r^a s^b) the definition reads dW[o, i, d] = sum_n sum_h dy[n, o, h] x[n, i, h d^-1] (the g
+// with g^-1 h = d).
 #include <stdio.h>
 
 #include <algorithm>
@@ -657,6 +659,19 @@ __global__ __launch_bounds__(256) void k_bw_small_inverse(const float *__restric
     group_inverse<G, D4>(Y, out);
 #pragma unroll
     for (int d = 0; d < G; ++d) dW[k * G + d] = out[d];
+}
+
+// Zero fill (the gradients of an empty batch), a kernel rather than a memset so that a captured HIP
+// graph holds only kernel nodes.
+__global__ __launch_bounds__(256) void k_zero_f32(float *__restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -292,9 +292,9 @@ eqlin_status_t eqlin_backward_weights(eqlin_handle_t h, const void *x, const voi
     if (need > 0 && !aligned(workspace, 256)) return fail(EQLIN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     (void)hipGetLastError();
     hipError_t e;
-    if (N == 0) {  // no tokens: zero gradients
-        e = hipMemsetAsync(dW, 0, (size_t)h->C_out * h->C_in * h->G * sizeof(float), (hipStream_t)stream);
-        if (e == hipSuccess && db) e = hipMemsetAsync(db, 0, (size_t)h->C_out * sizeof(float), (hipStream_t)stream);
+    if (N == 0) {  // no tokens: zero gradients (fill kernels, no memset nodes under graph capture)
+        e = eqlin::launch_zero_f32(dW, (int64_t)h->C_out * h->C_in * h->G, (hipStream_t)stream);
+        if (e == hipSuccess && db) e = eqlin::launch_zero_f32(db, h->C_out, (hipStream_t)stream);
         return e == hipSuccess ? EQLIN_OK : hip_fail(e, "eqlin_backward_weights clear");
     }
     e = eqlin::launch_backward_weights(h, x, dy, dW, db, N, workspace, (hipStream_t)stream);

@@ -82,6 +82,8 @@ size_t bw_workspace_bytes(const Plan *p, int64_t N);
 hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy, float *dW, float *db, int64_t N,
                                    void *ws, hipStream_t s);
 const char *bw_kernel_name(const Plan *p);
+// p[0..n) = 0 on stream s (a fill kernel: no memset node when the caller captures a graph)
+hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
 
 // ---- prepare.hip ----
 // W [C_out][C_in][G] (16-bit elements of the half type when w_is_half, else fp32) -> fragment-ordered

@@ -30,6 +30,7 @@
 //               global memory into the A operands.
 //   (larger channel counts go to k_big in fwd_big.hip)
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -384,10 +385,13 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_stream(const uint4 *__res
 // ------------------------------------------------------------------------------------------------
 // Launchers and selection.
 
-// Raise the kernel's dynamic-LDS limit above 64 KB where needed (gfx950 has 160 KB per CU). A
-// refusal is not fatal here: the launch itself then reports the error.
+// Raise the kernel's dynamic-LDS limit above 64 KB where needed (gfx950 has 160 KB per CU). A refusal
+// makes the selection below fall back to the large-channel kernel (static LDS, no attribute needed).
+// EQLIN_FAULT_LDS_LIMIT=<bytes> (fault injection for the tests) refuses every request above <bytes>.
 static hipError_t set_lds_limit(const void *fn, size_t bytes) {
     if (bytes <= 65536) return hipSuccess;
+    if (const char *cap = getenv("EQLIN_FAULT_LDS_LIMIT"))
+        if (bytes > (size_t)strtoull(cap, nullptr, 10)) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     (void)hipGetLastError();
     return e;
@@ -491,7 +495,7 @@ bool select_bf16(int G, bool d4, int C_in, int C_out, KernelChoice *out) {
         out->kc = 32;
         out->ks_mult = 1;
         out->launch = e.launch;
-        (void)e.init(out->lds_bytes);
+        if (e.init(out->lds_bytes) != hipSuccess) break;  // LDS limit refused: the large-channel kernel
         snprintf(out->name, sizeof(out->name), "bf16 stream %s%d KS=%d nb_tile=%d tiles=%d waves=%d",
                  d4 ? "D" : "G=", d4 ? 4 : G, KS, nb_tile, tiles, kStreamWaves);
         return true;

@@ -28,14 +28,29 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = ["fourier_domain_linear_amd/csrc/fwd_bf16.hip", "fourier_domain_linear_amd/csrc/device_common.h",
-                  "fourier_domain_linear_amd/csrc/dft.h", "fourier_domain_linear_amd/csrc/act.h"]
+_COMMON = ["fourier_domain_linear_amd/csrc/device_common.h", "fourier_domain_linear_amd/csrc/dft.h",
+           "fourier_domain_linear_amd/csrc/act.h"]
+# the sources each forward kernel family is built from (a counter summary is valid only for these)
+KERNEL_SOURCES = {
+    "k_stream": ["fourier_domain_linear_amd/csrc/fwd_bf16.hip"] + _COMMON,
+    "k_big": ["fourier_domain_linear_amd/csrc/fwd_big.hip"] + _COMMON,
+    "k_p8": ["fourier_domain_linear_amd/csrc/fwd_big.hip"] + _COMMON,
+    "k_conv": ["fourier_domain_linear_amd/csrc/fwd_big.hip", "fourier_domain_linear_amd/csrc/conv.hip"] + _COMMON,
+}
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the forward kernel's sources (a counter summary is valid only for these)."""
+def sources_for(kernel: str) -> list:
+    """The source list of the kernel family whose name starts `kernel` (e.g. "k_p8<false, ...>")."""
+    for fam in sorted(KERNEL_SOURCES, key=len, reverse=True):
+        if kernel.startswith(fam):
+            return KERNEL_SOURCES[fam]
+    raise ValueError(f"unknown kernel family for {kernel!r}")
+
+
+def kernel_source_hash(sources: list | None = None) -> str:
+    """sha256 over a kernel family's sources (default: the stream kernel's)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES["k_stream"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -113,7 +128,8 @@ def cmd_traffic(a):
     w_scale = a.copy_bytes / _avg(cwrite)
     rd, wr = _avg(fetch) * f_scale, _avg(write) * w_scale
     rec = {
-        "workload": a.workload, "kernel": a.kernel, "source_sha256": kernel_source_hash(),
+        "workload": a.workload, "kernel": a.kernel, "sources": sources_for(a.kernel),
+        "source_sha256": kernel_source_hash(sources_for(a.kernel)),
         "fetch_kib_per_dispatch": _avg(fetch), "write_kib_per_dispatch": _avg(write),
         "copy_bytes": a.copy_bytes, "copy_fetch_kib": _avg(cfetch), "copy_write_kib": _avg(cwrite),
         "fetch_scale_bytes_per_kib": f_scale, "write_scale_bytes_per_kib": w_scale,

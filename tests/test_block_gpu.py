@@ -20,6 +20,7 @@ import torch
 import fourier_domain_linear_amd as eq
 import oracle
 from fourier_domain_linear_amd.workloads import BLOCK_WORKLOAD, make_block_inputs, make_inputs
+from fullsize import compare_all_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -140,17 +141,16 @@ def test_mlp_block_small(dtype, G, C, N, expanded, cuda_device):
 
 
 @pytest.mark.parametrize("expanded", [False, True], ids=["spectral", "expanded"])
-def test_mlp_block_full_size_sampled(expanded, cuda_device):
+def test_mlp_block_full_size_all_tokens(expanded, cuda_device):
     w = BLOCK_WORKLOAD
     print(f"[case] block full {w.name} expanded={expanded}", flush=True)
     x, W1, b1, W2, b2 = make_block_inputs(w.G, w.C_in, w.C_out, w.N, w.dtype, seed=0)
     y, _, _ = _block(cuda_device, x, W1, b1, W2, b2, expanded)
-    rng = np.random.default_rng(11)
-    idx = sorted(set([0, 1, 31, 32, 255, 256, w.N // 2, w.N - 33, w.N - 1]) |
-                 set(rng.choice(w.N, 160, replace=False).tolist()))
-    ref = oracle.mlp_block(x[idx], W1, b1, W2, b2)
-    _check(y[torch.as_tensor(idx, device=y.device)], ref, w.dtype,
-           f"block {w.name} sampled {len(idx)} {'expanded' if expanded else 'spectral'}")
+    e = compare_all_tokens({"y": y}, lambda lo, hi: oracle.mlp_block(x[lo:hi], W1, b1, W2, b2), w.N,
+                           chunk=2048)["y"]
+    print(f"[parity] block {w.name} all {w.N} tokens {'expanded' if expanded else 'spectral'}: "
+          f"rel_frob={e.rel:.3e} max_abs={e.max_abs:.3e}", flush=True)
+    assert e.finite and e.rel <= REL_BF16 and e.max_abs <= MAX_BF16, (e.rel, e.max_abs)
 
 
 def test_mlp_block_empty_and_one_token(cuda_device):

@@ -14,6 +14,7 @@ import torch
 import fourier_domain_linear_amd as eq
 from fourier_domain_linear_amd.workloads import D4_WORKLOADS, make_grad, make_inputs
 from oracle import dihedral as d4
+from fullsize import compare_all_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -53,19 +54,18 @@ def test_forward(dtype, C_in, C_out, N, expanded, with_bias, cuda_device):
            f"[{h.describe()}]")
 
 
-@pytest.mark.parametrize("expanded", [False, True], ids=["spectral", "expanded"])
 @pytest.mark.parametrize("w", D4_WORKLOADS, ids=[w.name for w in D4_WORKLOADS])
-def test_full_size_sampled(w, expanded, cuda_device):
-    print(f"[case] d4 full {w.name} expanded={expanded}", flush=True)
+def test_full_size_all_tokens(w, cuda_device):
+    print(f"[case] d4 full {w.name}", flush=True)
     x, W, b = make_inputs(w.G, w.C_in, w.C_out, w.N, w.dtype, seed=0)
-    h = eq.prepare_weights(W.to(cuda_device), expanded=expanded, group="d4")
-    y = (eq.forward_expanded if expanded else eq.forward)(h, x.to(cuda_device), b.to(cuda_device))
+    h = eq.prepare_weights(W.to(cuda_device), expanded=True, group="d4")
+    xd, bd = x.to(cuda_device), b.to(cuda_device)
+    outs = {"spectral": eq.forward(h, xd, bd), "expanded": eq.forward_expanded(h, xd, bd)}
     torch.cuda.synchronize()
-    rng = np.random.default_rng(5)
-    idx = sorted(set([0, 1, 15, 16, 31, 32, 63, 64, w.N // 2, w.N - 65, w.N - 1]) |
-                 set(rng.choice(w.N, 160, replace=False).tolist()))
-    _check(y[torch.as_tensor(idx, device=y.device)], d4.forward(x[idx], W, b), w.dtype,
-           f"{w.name} sampled {len(idx)} {'expanded' if expanded else 'spectral'}")
+    errs = compare_all_tokens(outs, lambda lo, hi: d4.forward(x[lo:hi], W, b), w.N, chunk=2048)
+    for k, e in errs.items():
+        print(f"[parity] {w.name} all {w.N} tokens {k}: rel_frob={e.rel:.3e} max_abs={e.max_abs:.3e}", flush=True)
+        assert e.finite and e.rel <= REL_BF16 and e.max_abs <= MAX_BF16, (w.name, k, e.rel, e.max_abs)
 
 
 @pytest.mark.parametrize("w", D4_WORKLOADS, ids=[w.name for w in D4_WORKLOADS])

@@ -15,6 +15,7 @@ import fourier_domain_linear_amd as eq
 import oracle
 from fourier_domain_linear_amd.workloads import F16_WORKLOADS, make_grad, make_inputs
 from oracle import dihedral as d4
+from fullsize import compare_all_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -49,14 +50,14 @@ def test_forward(G, C_in, C_out, N, expanded, cuda_device):
 
 
 @pytest.mark.parametrize("w", F16_WORKLOADS, ids=[w.name for w in F16_WORKLOADS])
-def test_full_size_sampled(w, cuda_device):
+def test_full_size_all_tokens(w, cuda_device):
     x, W, b = make_inputs(w.G, w.C_in, w.C_out, w.N, "f16", seed=0)
     h = eq.prepare_weights(W.to(cuda_device))
     y = eq.forward(h, x.to(cuda_device), b.to(cuda_device))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(6)
-    idx = sorted(set([0, 1, 15, 16, 63, 64, w.N // 2, w.N - 1]) | set(rng.choice(w.N, 160, replace=False).tolist()))
-    _check(y[torch.as_tensor(idx, device=y.device)], oracle.forward(x[idx], W, b), f"{w.name} sampled")
+    e = compare_all_tokens({"y": y}, lambda lo, hi: oracle.forward(x[lo:hi], W, b), w.N, chunk=2048)["y"]
+    print(f"[parity] {w.name} all {w.N} tokens: rel_frob={e.rel:.3e} max_abs={e.max_abs:.3e}", flush=True)
+    assert e.finite and e.rel <= REL_F16 and e.max_abs <= MAX_F16, (w.name, e.rel, e.max_abs)
 
 
 @pytest.mark.parametrize("C_in,C_out", [(64, 64), (256, 1024)])
