@@ -3,7 +3,7 @@ oracle/eqlin_oracle.c (a wrong index, a sign, a dropped term or bias), builds it
 tests/test_oracle.py against that build in a child process, which must then fail. An unmodified
 copy built the same way must pass, so a failure is the pins' doing and not the harness's. Every
 slip keeps all memory accesses in bounds. The Python parts of the oracle (the D4 group and its
-layer, the GELU and the MLP block) get the same treatment through a copy of the oracle package
+layer, the GELU and the MLP block, the p4 group convolution) get the same treatment through a copy of the oracle package
 that the child process imports instead of the real one."""
 import os
 import shutil
@@ -83,6 +83,18 @@ PY_MUTANTS = {
     "gelu_wrong_scale": ("__init__.py", "0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))", "0.5 * v * (1.0 + erf(v / 2.0))"),
     "mlp_block_without_activation": ("__init__.py", "hidden = gelu(forward(x, W1, b1, threads))",
                                      "hidden = forward(x, W1, b1, threads)"),
+    # the p4 group convolution: filter turned with R^h instead of R^-h
+    "conv_filter_turned_forward": ("conv.py", "fy, fx = rotate_offset(dy, dx, -h)",
+                                   "fy, fx = rotate_offset(dy, dx, h)"),
+    "conv_group_index_reversed": ("conv.py", "w = psi[:, :, (h - g) % G, fy + r, fx + r]",
+                                  "w = psi[:, :, (g - h) % G, fy + r, fx + r]"),
+    # a convolution instead of a cross-correlation over the pixels
+    "conv_offset_sign": ("conv.py", "xs = shifted(x, dy, dx)", "xs = shifted(x, -dy, -dx)"),
+    "conv_rotation_inverted": ("conv.py", "dy, dx = -dx, dy", "dy, dx = dx, -dy"),
+    "conv_bias_dropped": ("conv.py", "    if bias is not None:\n        y +=", "    if False:\n        y +="),
+    "conv_zero_padding_wraps": ("conv.py", "        s[:, y0:y1, x0:x1] = x[:, y0 + dy:y1 + dy, x0 + dx:x1 + dx]",
+                                "        s[:, y0:y1, x0:x1] = x[:, y0 + dy:y1 + dy, x0 + dx:x1 + dx]\n"
+                                "        s = np.roll(x, (-dy, -dx), axis=(1, 2))"),
 }
 
 
@@ -95,7 +107,7 @@ def _run_py_copy(tmp_path, edit=None):
     root = tmp_path / "root"
     shutil.copytree(os.path.join(ROOT, "oracle"), root / "oracle", ignore=shutil.ignore_patterns("__pycache__", "_build"))
     (root / "tests").mkdir()
-    for f in ("conftest.py", "test_oracle.py", "test_oracle_dihedral.py"):
+    for f in ("conftest.py", "test_oracle.py", "test_oracle_dihedral.py", "test_oracle_conv.py"):
         shutil.copy(os.path.join(ROOT, "tests", f), root / "tests" / f)
     if edit:
         fname, old, new = edit
