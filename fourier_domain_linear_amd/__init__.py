@@ -46,7 +46,7 @@ _ACTS = {None: EQLIN_ACT_NONE, "none": EQLIN_ACT_NONE, "gelu": EQLIN_ACT_GELU}
 EXPORTED = (
     "eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_forward_act",
     "eqlin_forward_expanded_act", "eqlin_backward_data",
-    "eqlin_backward_weights_workspace", "eqlin_backward_weights", "eqlin_destroy",
+    "eqlin_backward_weights_workspace", "eqlin_backward_weights", "eqlin_backward_weights_static", "eqlin_destroy",
     "eqlin_export_spectral_weights", "eqlin_export_expanded_weight", "eqlin_describe",
     "eqlin_status_string", "eqlin_last_error", "eqlin_version",
 )
@@ -80,6 +80,7 @@ def load_library() -> ctypes.CDLL:
     lib.eqlin_backward_weights_workspace.argtypes = [vp, i64]
     lib.eqlin_backward_weights_workspace.restype = ctypes.c_size_t
     lib.eqlin_backward_weights.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.eqlin_backward_weights_static.argtypes = [vp, vp, vp, vp, vp, i64, vp]
     lib.eqlin_destroy.argtypes = [vp]
     lib.eqlin_export_spectral_weights.argtypes = [vp, vp, vp]
     lib.eqlin_export_expanded_weight.argtypes = [vp, vp, vp]
@@ -92,6 +93,8 @@ def load_library() -> ctypes.CDLL:
     lib.eqlin_version.argtypes = []
     lib.eqlin_version.restype = ctypes.c_char_p
     for name in ("eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_destroy",
+                 "eqlin_forward_act", "eqlin_forward_expanded_act", "eqlin_backward_data", "eqlin_backward_weights",
+                 "eqlin_backward_weights_static",
                  "eqlin_export_spectral_weights", "eqlin_export_expanded_weight"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -289,6 +292,32 @@ def backward_weights(h: Handle, x: torch.Tensor, dy: torch.Tensor, with_bias: bo
             ctypes.c_void_p(dW.data_ptr()), ctypes.c_void_p(db.data_ptr()) if db is not None else None, N, wsp,
             need, _stream(x))
     _check(st, "eqlin_backward_weights")
+    return dW, db
+
+
+STATIC_SCRATCH_BYTES = 64 << 20  # EQLIN_STATIC_SCRATCH_BYTES
+
+
+def backward_weights_static(h: Handle, x: torch.Tensor, dy: torch.Tensor, with_bias: bool = True):
+    """eqlin_backward_weights_static: backward_weights with the library's static per-device scratch
+    instead of a workspace (no device allocation in the library; the gradient tensors are allocated
+    here unless passed in). Calls on one device must not overlap."""
+    _need_cuda(x, "x")
+    _need_cuda(dy, "dy")
+    if x.dtype != h.dtype or dy.dtype != h.dtype:
+        raise TypeError(f"x and dy must be {h.dtype}")
+    if x.dim() != 3 or x.shape[1:] != (h.C_in, h.G) or dy.dim() != 3 or dy.shape[1:] != (h.C_out, h.G) \
+            or x.shape[0] != dy.shape[0]:
+        raise ValueError(f"x must be [N, {h.C_in}, {h.G}] and dy [N, {h.C_out}, {h.G}]")
+    N = x.shape[0]
+    dW = torch.empty((h.C_out, h.C_in, h.G), dtype=torch.float32, device=x.device)
+    db = torch.empty((h.C_out,), dtype=torch.float32, device=x.device) if with_bias else None
+    with torch.cuda.device(x.device):
+        st = load_library().eqlin_backward_weights_static(
+            ctypes.c_void_p(h.ptr), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(dy.data_ptr()),
+            ctypes.c_void_p(dW.data_ptr()), ctypes.c_void_p(db.data_ptr()) if db is not None else None, N,
+            _stream(x))
+    _check(st, "eqlin_backward_weights_static")
     return dW, db
 
 

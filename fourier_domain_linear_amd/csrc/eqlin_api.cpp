@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "eqlin_internal.h"
@@ -108,7 +109,33 @@ eqlin_status_t check_forward_args(const Plan *h, const void *x, const void *b, c
     return EQLIN_OK;
 }
 
+// The scratch of eqlin_backward_weights_static: a static device array in this library's code object,
+// so each device the library runs on holds its own copy, from the first use until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device (static_scratch), and only that address is handed to kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+static __device__ __align__(256) unsigned char scratch[EQLIN_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on device `dev`, which must be the current device (looked up on the
+// first call for that device, then kept).
+static eqlin_status_t static_scratch(int dev, void **out) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(EQLIN_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(EQLIN_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return EQLIN_OK;
+}
 
 extern "C" {
 
@@ -152,6 +179,14 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
     if (st != EQLIN_OK) {
         free_plan(p);
         return st;
+    }
+    {  // set-up of this device: the address of eqlin_backward_weights_static's scratch
+        void *ws = nullptr;
+        st = static_scratch(p->device, &ws);
+        if (st != EQLIN_OK) {
+            free_plan(p);
+            return st;
+        }
     }
     if (flags & EQLIN_PREPARE_EXPANDED) {
         const size_t eb = dtype == EQLIN_F32 ? 4 : 2;
@@ -277,28 +312,57 @@ size_t eqlin_backward_weights_workspace(eqlin_handle_t h, int64_t N) {
     return eqlin::bw_workspace_bytes(h, N);
 }
 
-eqlin_status_t eqlin_backward_weights(eqlin_handle_t h, const void *x, const void *dy, float *dW, float *db,
-                                      int64_t N, void *workspace, size_t workspace_bytes, eqlin_stream_t stream) {
-    g_err[0] = 0;
+// The gradient passes of eqlin_backward_weights after its argument checks; ws: workspace of at least
+// eqlin::bw_workspace_bytes(h, N) bytes (or null when that is 0).
+static eqlin_status_t backward_weights_run(const Plan *h, const void *x, const void *dy, float *dW, float *db,
+                                           int64_t N, void *ws, hipStream_t stream) {
+    (void)hipGetLastError();
+    hipError_t e;
+    if (N == 0) {  // no tokens: zero gradients (fill kernels, no memset nodes under graph capture)
+        e = eqlin::launch_zero_f32(dW, (int64_t)h->C_out * h->C_in * h->G, stream);
+        if (e == hipSuccess && db) e = eqlin::launch_zero_f32(db, h->C_out, stream);
+        return e == hipSuccess ? EQLIN_OK : hip_fail(e, "eqlin_backward_weights clear");
+    }
+    e = eqlin::launch_backward_weights(h, x, dy, dW, db, N, ws, stream);
+    return e == hipSuccess ? EQLIN_OK : hip_fail(e, "eqlin_backward_weights launch");
+}
+
+static eqlin_status_t check_backward_weights_args(const Plan *h, const void *x, const void *dy, const float *dW,
+                                                  const float *db, int64_t N) {
     if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
     if (!dW) return fail(EQLIN_ERR_INVALID_ARG, "null dW");
     if (!aligned(dW, 4) || (db && !aligned(db, 4))) return fail(EQLIN_ERR_INVALID_ARG, "dW and db must be 4-byte aligned");
     // x plays the forward's x, dy the forward's y (shapes, alignment, overlap, device)
-    eqlin_status_t st = check_forward_args(h, x, nullptr, dy, N, h->C_in, h->C_out, h->G);
+    return check_forward_args(h, x, nullptr, dy, N, h->C_in, h->C_out, h->G);
+}
+
+eqlin_status_t eqlin_backward_weights(eqlin_handle_t h, const void *x, const void *dy, float *dW, float *db,
+                                      int64_t N, void *workspace, size_t workspace_bytes, eqlin_stream_t stream) {
+    g_err[0] = 0;
+    eqlin_status_t st = check_backward_weights_args(h, x, dy, dW, db, N);
     if (st != EQLIN_OK) return st;
     const size_t need = eqlin::bw_workspace_bytes(h, N);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(EQLIN_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
     if (need > 0 && !aligned(workspace, 256)) return fail(EQLIN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    (void)hipGetLastError();
-    hipError_t e;
-    if (N == 0) {  // no tokens: zero gradients (fill kernels, no memset nodes under graph capture)
-        e = eqlin::launch_zero_f32(dW, (int64_t)h->C_out * h->C_in * h->G, (hipStream_t)stream);
-        if (e == hipSuccess && db) e = eqlin::launch_zero_f32(db, h->C_out, (hipStream_t)stream);
-        return e == hipSuccess ? EQLIN_OK : hip_fail(e, "eqlin_backward_weights clear");
+    return backward_weights_run(h, x, dy, dW, db, N, workspace, (hipStream_t)stream);
+}
+
+eqlin_status_t eqlin_backward_weights_static(eqlin_handle_t h, const void *x, const void *dy, float *dW, float *db,
+                                             int64_t N, eqlin_stream_t stream) {
+    g_err[0] = 0;
+    eqlin_status_t st = check_backward_weights_args(h, x, dy, dW, db, N);
+    if (st != EQLIN_OK) return st;
+    const size_t need = eqlin::bw_workspace_bytes(h, N);
+    if (need > EQLIN_STATIC_SCRATCH_BYTES)
+        return fail(EQLIN_ERR_UNSUPPORTED, "N = %lld needs %zu bytes of scratch, above the static %zu (use "
+                    "eqlin_backward_weights with a workspace)", (long long)N, need, (size_t)EQLIN_STATIC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need > 0) {
+        st = static_scratch(h->device, &ws);
+        if (st != EQLIN_OK) return st;
     }
-    e = eqlin::launch_backward_weights(h, x, dy, dW, db, N, workspace, (hipStream_t)stream);
-    return e == hipSuccess ? EQLIN_OK : hip_fail(e, "eqlin_backward_weights launch");
+    return backward_weights_run(h, x, dy, dW, db, N, ws, (hipStream_t)stream);
 }
 
 eqlin_status_t eqlin_destroy(eqlin_handle_t h) {

@@ -189,6 +189,30 @@ size_t eqlin_backward_weights_workspace(eqlin_handle_t h, int64_t N);
 eqlin_status_t eqlin_backward_weights(eqlin_handle_t h, const void *x, const void *dy, float *dW, float *db,
                                       int64_t N, void *workspace, size_t workspace_bytes, eqlin_stream_t stream);
 
+/*
+ * eqlin_backward_weights_static -- eqlin_backward_weights with no workspace argument and no device
+ * allocation, for callers that cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The same gradients from the same kernels, with the same arguments
+ * (less the workspace), alignment, device and stream rules.
+ *
+ * Its scratch is a static device array of EQLIN_STATIC_SCRATCH_BYTES (64 MiB) inside the library:
+ * each device holds its own copy, from when the library first runs there until the process ends. Its
+ * device address is looked up once per device, when eqlin_prepare_weights (or else the first call of
+ * this function) runs there. A call whose scratch need, eqlin_backward_weights_workspace(h, N),
+ * exceeds the array returns EQLIN_ERR_UNSUPPORTED and enqueues nothing. (The fused small-channel pass
+ * keeps one partial spectrum per compute unit, so its need does not grow with N: the p4 96 x 96 and
+ * p8 64 x 64 layers fit at any token count. The large-channel passes hold transformed copies of x and
+ * dy, so they fit only small batches, e.g. about 1000 tokens at p4 192 -> 768.)
+ *
+ * Calls no hipMalloc, hipFree or other allocating routine. All calls on one device share its array,
+ * which keeps the last call's contents; no pass reads scratch that the same call has not written, so
+ * nothing needs to start at zero. Calls that overlap on one device (several streams, or several
+ * threads without an order between them) race on the array: the caller must order them.
+ */
+#define EQLIN_STATIC_SCRATCH_BYTES (64u << 20)
+eqlin_status_t eqlin_backward_weights_static(eqlin_handle_t h, const void *x, const void *dy, float *dW, float *db,
+                                             int64_t N, eqlin_stream_t stream);
+
 /* Frees the handle's device memory (hipFree, which synchronises the device). NULL is a no-op. */
 eqlin_status_t eqlin_destroy(eqlin_handle_t h);
 
