@@ -201,6 +201,73 @@ def bench_backward(torch, eq, rl, w, st, dev, K: int, Wm: int, timer, with_expan
     return res
 
 
+def bench_conv(torch, eq, rl, timer, dev, K: int, Wm: int):
+    """Time the p4 group convolution (eqlin_conv_forward: the EQ-Linear layer over the gathered channels,
+    gathered while x is loaded) and its unrolled comparator (eqlin_conv_forward_expanded), plus torch's
+    conv2d on the fully unrolled filter bank as context (the plain way to run a group convolution)."""
+    from fourier_domain_linear_amd.workloads import CONV_WORKLOAD as cw, make_conv_inputs
+
+    Ci, Co, k, N = cw.C_in, cw.C_out, cw.k, cw.N
+    log(f"[bench] conv {cw.name}: p4 {k}x{k} C_in={Ci} C_out={Co} {cw.B}x{cw.H}x{cw.W} {cw.dtype}")
+    x, psi, b = make_conv_inputs(Ci, Co, k, cw.B, cw.H, cw.W, cw.dtype, seed=0)
+    set_bytes = N * (Ci + Co) * 4 * 2
+    R = max(3, math.ceil((1 << 30) / set_bytes))
+    x0 = x.to(dev)
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    ys = [torch.empty((cw.B, cw.H, cw.W, Co, 4), dtype=cw.torch_dtype, device=dev) for _ in range(R)]
+    h = eq.prepare_conv_weights(psi.to(dev), expanded=True)
+    bd = b.to(dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {h.describe()}")
+    Cg = Ci * k * k  # gathered channels
+    F = rl.spectral_flops(N, Cg, Co, 4)
+    Fd = rl.dense_flops(N, Cg, Co, 4)
+    B = rl.spectral_bytes(N, Ci, Co, 4, 2) + (Cg - Ci) * Co * 4 * 2  # x, y, the gathered layer's planes, bias
+    res = {"workload": cw.name, "k": k, "C_in": Ci, "C_out": Co, "images": [cw.B, cw.H, cw.W], "tokens": N,
+           "gathered_channels": Cg, "kernels": h.describe(), "algorithmic_flops": F, "algorithmic_bytes": B}
+    for name, fn, flops in (("spectral", lambda i: eq.conv_forward(h, xs[i], bd, ys[i]), F),
+                            ("expanded", lambda i: eq.conv_forward_expanded(h, xs[i], bd, ys[i]), Fd)):
+        for i in range(Wm):
+            fn(i % R)
+        torch.cuda.synchronize()
+        ms = timer(torch, fn, K, R)
+        t = ms / 1e3
+        res[name] = {"us_per_step": round(ms * 1e3, 3), "tokens_per_s": N / t, "tflops": round(flops / t / 1e12, 2),
+                     "mfma_frac": round(flops / t / 1e12 / rl.PEAK_BF16_TFLOPS, 4),
+                     "hbm_frac": round(B / t / 1e9 / rl.PEAK_HBM_GBS, 4)}
+        log(f"[bench] conv {name}: {ms * 1e3:.2f} us/step")
+    tr, bound = rl.roof_time_s(F, B, rl.PEAK_BF16_TFLOPS)
+    res["bound"] = bound
+    res["frac"] = round(tr / (res["spectral"]["us_per_step"] / 1e6), 4)
+    res["speedup_vs_expanded"] = round(res["expanded"]["us_per_step"] / res["spectral"]["us_per_step"], 3)
+    # context: torch conv2d (the vendor convolution library) on the unrolled filter bank
+    # Wfull[(o, h), (i, g)] = psi[o, i, (h - g) mod 4] turned h quarter turns, input in NCHW
+    try:
+        Wf = torch.empty((Co, 4, Ci, 4, k, k), dtype=torch.float32)
+        pf = psi.float()
+        for hh in range(4):
+            for g in range(4):
+                Wf[:, hh, :, g] = torch.rot90(pf[:, :, (hh - g) % 4], hh, dims=(2, 3))
+        Wf = Wf.reshape(Co * 4, Ci * 4, k, k).to(cw.torch_dtype).to(dev)
+        xn = [v.reshape(cw.B, cw.H, cw.W, Ci * 4).permute(0, 3, 1, 2).contiguous() for v in xs[:2]]
+        bf = bd.repeat_interleave(4)
+
+        def torch_conv(i):
+            torch.nn.functional.conv2d(xn[i % 2], Wf, bf, padding=k // 2)
+
+        for i in range(Wm):
+            torch_conv(i)
+        torch.cuda.synchronize()
+        ms_t = time_eager(torch, torch_conv, K, 2)
+        res["torch_conv2d_context"] = {"us_per_step": round(ms_t * 1e3, 3),
+                                       "spectral_speedup": round(ms_t * 1e3 / res["spectral"]["us_per_step"], 3),
+                                       "timing": "eager launches, NCHW input, 2 buffer sets"}
+        log(f"[bench] torch conv2d on the unrolled filters (context): {ms_t * 1e3:.2f} us/step")
+    except RuntimeError as e:  # context only
+        res["torch_conv2d_context"] = {"error": str(e)[:200]}
+    return res
+
+
 def bench_block(torch, eq, rl, timer, dev, K: int, Wm: int, with_expanded: bool):
     """Time the MLP block (layer 1 with GELU in its epilogue, then layer 2; two launches per step) on
     its seeded inputs, its two layers alone, and the same block on the unrolled weights."""
@@ -374,6 +441,8 @@ def main():
     ap.add_argument("--block", action="store_true",
                     help="also time the transformer MLP block EQ-Linear(C->4C), GELU, EQ-Linear(4C->C) at the "
                          "p4 192-channel shape, spectral and expanded (reported under 'block')")
+    ap.add_argument("--conv", action="store_true",
+                    help="also time the p4 3x3 group convolution, spectral and expanded (reported under 'conv')")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (the counter calibration for traffic)")
     args = ap.parse_args()
@@ -435,6 +504,8 @@ def main():
         extra["backward"] = bench_backward(torch, eq, rl, w, st, dev, K, Wm, timer, not args.no_expanded)
     if args.block:
         extra["block"] = bench_block(torch, eq, rl, timer, dev, K, Wm, not args.no_expanded)
+    if args.conv:
+        extra["conv"] = bench_conv(torch, eq, rl, timer, dev, K, Wm)
     extra["effective_tflops"] = rec["effective_tflops"]
     extra["useful_tflops"] = rec["useful_tflops"]
     extra["per_launch_us"] = rec["per_launch_us"]

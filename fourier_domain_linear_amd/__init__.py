@@ -12,6 +12,8 @@ is missing, every call raises.
     dW, db = eq.backward_weights(h, x, dy)    # float32 gradients of W and b
     z = eq.forward(h, x, b, act="gelu")       # GELU(y), applied in the kernel's epilogue
     y = eq.mlp_block(h1, b1, h2, b2, x)       # EQ-Linear(C -> 4C), GELU, EQ-Linear(4C -> C)
+    hc = eq.prepare_conv_weights(psi)         # p4 group convolution, psi [C_out, C_in, 4, k, k]
+    y = eq.conv_forward(hc, x, b)             # x [B, H, W, C_in, 4] -> y [B, H, W, C_out, 4]
 
 Method: "Flash EQ-Linear: Accelerating Equivariant Linear Layers via Group-wise Discrete Fourier
 Transform" (explainer page, gist.science/es/paper/2607.21271).
@@ -49,6 +51,7 @@ EXPORTED = (
     "eqlin_backward_weights_workspace", "eqlin_backward_weights", "eqlin_backward_weights_static", "eqlin_destroy",
     "eqlin_export_spectral_weights", "eqlin_export_expanded_weight", "eqlin_describe",
     "eqlin_status_string", "eqlin_last_error", "eqlin_version",
+    "eqlin_prepare_conv_weights", "eqlin_conv_forward", "eqlin_conv_forward_expanded",
 )
 
 _lib = None
@@ -81,6 +84,9 @@ def load_library() -> ctypes.CDLL:
     lib.eqlin_backward_weights_workspace.restype = ctypes.c_size_t
     lib.eqlin_backward_weights.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
     lib.eqlin_backward_weights_static.argtypes = [vp, vp, vp, vp, vp, i64, vp]
+    lib.eqlin_prepare_conv_weights.argtypes = [vp, i32, i32, i32, i32, i32, u32, vp, ctypes.POINTER(vp)]
+    lib.eqlin_conv_forward.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp]
+    lib.eqlin_conv_forward_expanded.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp]
     lib.eqlin_destroy.argtypes = [vp]
     lib.eqlin_export_spectral_weights.argtypes = [vp, vp, vp]
     lib.eqlin_export_expanded_weight.argtypes = [vp, vp, vp]
@@ -94,7 +100,8 @@ def load_library() -> ctypes.CDLL:
     lib.eqlin_version.restype = ctypes.c_char_p
     for name in ("eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_destroy",
                  "eqlin_forward_act", "eqlin_forward_expanded_act", "eqlin_backward_data", "eqlin_backward_weights",
-                 "eqlin_backward_weights_static",
+                 "eqlin_backward_weights_static", "eqlin_prepare_conv_weights", "eqlin_conv_forward",
+                 "eqlin_conv_forward_expanded",
                  "eqlin_export_spectral_weights", "eqlin_export_expanded_weight"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -134,8 +141,9 @@ class Handle:
     """Owns an eqlin_handle_t; destroyed with the object (or explicitly via destroy())."""
 
     def __init__(self, ptr: int, C_out: int, C_in: int, G: int, dtype: torch.dtype, device, expanded: bool,
-                 backward: bool = False, group: str = "cyclic"):
+                 backward: bool = False, group: str = "cyclic", conv_k: int = 0):
         self.ptr = ptr
+        self.conv_k = conv_k
         self.C_out, self.C_in, self.G, self.group = C_out, C_in, G, group
         self.dtype, self.device, self.expanded, self.backward = dtype, device, expanded, backward
 
@@ -293,6 +301,61 @@ def backward_weights(h: Handle, x: torch.Tensor, dy: torch.Tensor, with_bias: bo
             need, _stream(x))
     _check(st, "eqlin_backward_weights")
     return dW, db
+
+
+def prepare_conv_weights(psi: torch.Tensor, expanded: bool = False) -> Handle:
+    """eqlin_prepare_conv_weights: psi [C_out, C_in, 4, k, k] (cuda, bf16 or fp16) -> Handle of the p4
+    group convolution y[b, p, o, h] = bias[o] + sum psi[o, i, (h - g) mod 4, R^-h delta] x[b, p + delta, i, g].
+    ``expanded`` also builds the unrolled comparator (conv_forward_expanded)."""
+    lib = load_library()
+    _need_cuda(psi, "psi")
+    if psi.dim() != 5 or psi.shape[2] != 4 or psi.shape[3] != psi.shape[4]:
+        raise ValueError(f"psi must be [C_out, C_in, 4, k, k], got {tuple(psi.shape)}")
+    C_out, C_in, G, k, _ = psi.shape
+    out = ctypes.c_void_p()
+    with torch.cuda.device(psi.device):
+        st = lib.eqlin_prepare_conv_weights(ctypes.c_void_p(psi.data_ptr()), C_out, C_in, G, k, _dtype_code(psi.dtype),
+                                            EQLIN_PREPARE_EXPANDED if expanded else 0, _stream(psi), ctypes.byref(out))
+    _check(st, "eqlin_prepare_conv_weights")
+    return Handle(out.value, C_out, C_in, G, psi.dtype, psi.device, expanded, conv_k=k)
+
+
+def _conv(fn, what: str, h: Handle, x: torch.Tensor, b: torch.Tensor | None, y: torch.Tensor | None):
+    if not h.conv_k:
+        raise ValueError("not a convolution handle (prepare_conv_weights)")
+    _need_cuda(x, "x")
+    if x.dtype != h.dtype or x.dim() != 5 or x.shape[3:] != (h.C_in, h.G):
+        raise ValueError(f"x must be [B, H, W, {h.C_in}, {h.G}] of {h.dtype}, got {tuple(x.shape)} {x.dtype}")
+    B, H, W = x.shape[:3]
+    if y is None:
+        y = torch.empty((B, H, W, h.C_out, h.G), dtype=x.dtype, device=x.device)
+    else:
+        _need_cuda(y, "y")
+        if y.dtype != h.dtype or tuple(y.shape) != (B, H, W, h.C_out, h.G):
+            raise ValueError(f"y must be [{B}, {H}, {W}, {h.C_out}, {h.G}] of {h.dtype}")
+    bp = None
+    if b is not None:
+        _need_cuda(b, "b")
+        if b.dtype != h.dtype or tuple(b.shape) != (h.C_out,):
+            raise ValueError(f"b must be [{h.C_out}] of {h.dtype}")
+        bp = ctypes.c_void_p(b.data_ptr())
+    with torch.cuda.device(x.device):
+        st = fn(ctypes.c_void_p(h.ptr), ctypes.c_void_p(x.data_ptr()), bp, ctypes.c_void_p(y.data_ptr()), B, H, W,
+                _stream(x))
+    _check(st, what)
+    return y
+
+
+def conv_forward(h: Handle, x: torch.Tensor, b: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """eqlin_conv_forward: x [B, H, W, C_in, 4] -> y [B, H, W, C_out, 4] (the spectral kernel)."""
+    return _conv(load_library().eqlin_conv_forward, "eqlin_conv_forward", h, x, b, y)
+
+
+def conv_forward_expanded(h: Handle, x: torch.Tensor, b: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """eqlin_conv_forward_expanded: the same through the unrolled gathered layer (needs expanded=True)."""
+    if not h.expanded:
+        raise ValueError("handle was prepared without expanded=True")
+    return _conv(load_library().eqlin_conv_forward_expanded, "eqlin_conv_forward_expanded", h, x, b, y)
 
 
 STATIC_SCRATCH_BYTES = 64 << 20  # EQLIN_STATIC_SCRATCH_BYTES

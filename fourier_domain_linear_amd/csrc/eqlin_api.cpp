@@ -43,14 +43,19 @@ void free_plan(Plan *p) {
     if (p->planes) (void)hipFree(p->planes);
     if (p->wexp) (void)hipFree(p->wexp);
     if (p->wt) (void)hipFree(p->wt);
+    if (p->conv_tab) (void)hipFree(p->conv_tab);
+    if (p->wconv) (void)hipFree(p->wconv);
     delete static_cast<eqlin_plan *>(p);
 }
 
-// Fill p->planes from a weight W[C_out][C_in][G] of p->dtype (W may be the unrolled E, G = 1).
+// Fill p->planes from a weight W[C_out][C_in][G] of p->dtype (W may be the unrolled E, G = 1). A plan
+// with conv_k > 0 gets the gathered-load kernel and its stage table.
 eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
     hipError_t e;
     if (p->dtype != EQLIN_F32) {  // bf16 or fp16: the matrix-core kernels
-        if (!eqlin::select_bf16(p->G, p->d4, p->C_in, p->C_out, &p->fwd))
+        const bool ok = p->conv_k > 0 ? eqlin::select_big_conv(p->G, p->C_in, p->C_out, &p->fwd)
+                                      : eqlin::select_bf16(p->G, p->d4, p->C_in, p->C_out, &p->fwd);
+        if (!ok)
             return fail(EQLIN_ERR_UNSUPPORTED, "no half-precision kernel for G=%d C_in=%d C_out=%d", p->G, p->C_in,
                         p->C_out);
         if (p->dtype == EQLIN_F16 && strncmp(p->fwd.name, "bf16", 4) == 0) memcpy(p->fwd.name, "f16 ", 4);
@@ -68,6 +73,18 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
         e = eqlin::launch_prep_frag(W, true, p->dtype == EQLIN_F16, p->d4, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->fwd.frag_kind,
                                     p->planes, s);
         if (e != hipSuccess) return hip_fail(e, "spectral weight preparation");
+        if (p->conv_k > 0) {  // the gathered loads' stage table (one entry per stage of 16 gathered channels)
+            const int n_stages = p->G == 1 ? p->KS / 4 : p->KS;
+            const std::vector<uint4> tab = eqlin::conv_stage_table(p->conv_cin, p->conv_k, 2, n_stages);
+            e = hipMalloc(&p->conv_tab, tab.size() * sizeof(uint4));
+            if (e != hipSuccess) {
+                p->conv_tab = nullptr;
+                return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc for the convolution's stage table");
+            }
+            // the host vector dies with this call: a synchronous copy (a few KB, at prepare only)
+            e = hipMemcpy(p->conv_tab, tab.data(), tab.size() * sizeof(uint4), hipMemcpyHostToDevice);
+            if (e != hipSuccess) return hip_fail(e, "convolution stage table");
+        }
     } else {
         if (!eqlin::select_f32(p->G, p->d4, p->C_in, p->C_out, &p->fwd))
             return fail(EQLIN_ERR_UNSUPPORTED, "no f32 kernel for G=%d", p->G);
@@ -270,6 +287,7 @@ eqlin_status_t eqlin_forward_act(eqlin_handle_t h, const void *x, const void *b,
                                  eqlin_stream_t stream) {
     g_err[0] = 0;
     if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
+    if (h->conv_k > 0) return fail(EQLIN_ERR_INVALID_ARG, "a convolution handle: use eqlin_conv_forward");
     if (!valid_act(act)) return fail(EQLIN_ERR_INVALID_ARG, "unknown activation %d", act);
     eqlin_status_t st = check_forward_args(h, x, b, y, N, h->C_in, h->C_out, h->G);
     if (st != EQLIN_OK || N == 0) return st;
@@ -285,6 +303,7 @@ eqlin_status_t eqlin_forward_expanded_act(eqlin_handle_t h, const void *x, const
                                           int act, eqlin_stream_t stream) {
     g_err[0] = 0;
     if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
+    if (h->conv_k > 0) return fail(EQLIN_ERR_INVALID_ARG, "a convolution handle: use eqlin_conv_forward_expanded");
     if (!h->expanded)
         return fail(EQLIN_ERR_INVALID_ARG, "handle was prepared without EQLIN_PREPARE_EXPANDED");
     if (!valid_act(act)) return fail(EQLIN_ERR_INVALID_ARG, "unknown activation %d", act);
@@ -330,6 +349,7 @@ static eqlin_status_t backward_weights_run(const Plan *h, const void *x, const v
 static eqlin_status_t check_backward_weights_args(const Plan *h, const void *x, const void *dy, const float *dW,
                                                   const float *db, int64_t N) {
     if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
+    if (h->conv_k > 0) return fail(EQLIN_ERR_INVALID_ARG, "a convolution handle has no gradient entry points");
     if (!dW) return fail(EQLIN_ERR_INVALID_ARG, "null dW");
     if (!aligned(dW, 4) || (db && !aligned(db, 4))) return fail(EQLIN_ERR_INVALID_ARG, "dW and db must be 4-byte aligned");
     // x plays the forward's x, dy the forward's y (shapes, alignment, overlap, device)
@@ -365,6 +385,136 @@ eqlin_status_t eqlin_backward_weights_static(eqlin_handle_t h, const void *x, co
     return backward_weights_run(h, x, dy, dW, db, N, ws, (hipStream_t)stream);
 }
 
+eqlin_status_t eqlin_prepare_conv_weights(const void *psi, int C_out, int C_in, int G, int k, eqlin_dtype_t dtype,
+                                          unsigned flags, eqlin_stream_t stream, eqlin_handle_t *out) {
+    g_err[0] = 0;
+    if (!out) return fail(EQLIN_ERR_INVALID_ARG, "null out");
+    *out = nullptr;
+    if (!psi) return fail(EQLIN_ERR_INVALID_ARG, "null psi");
+    if (G != 4) return fail(EQLIN_ERR_INVALID_ARG, "the convolution is over p4: G must be 4 (got %d)", G);
+    if (k < 1 || k > 15 || k % 2 == 0) return fail(EQLIN_ERR_INVALID_ARG, "k = %d: odd, 1..15", k);
+    if (C_out < 1 || C_in < 1) return fail(EQLIN_ERR_INVALID_ARG, "C_out = %d, C_in = %d must be >= 1", C_out, C_in);
+    if (!aligned(psi, 16)) return fail(EQLIN_ERR_INVALID_ARG, "psi must be 16-byte aligned");
+    if (dtype != EQLIN_BF16 && dtype != EQLIN_F16)
+        return fail(EQLIN_ERR_UNSUPPORTED, "the convolution runs in bf16 or fp16 (dtype %d)", (int)dtype);
+    if (C_in % 16 != 0 || C_out % 8 != 0)
+        return fail(EQLIN_ERR_UNSUPPORTED, "the convolution needs C_in %% 16 == 0 and C_out %% 8 == 0 (%d, %d)", C_in, C_out);
+    if (flags & ~EQLIN_PREPARE_EXPANDED) return fail(EQLIN_ERR_UNSUPPORTED, "flags 0x%x: only EQLIN_PREPARE_EXPANDED", flags);
+    const int64_t cg = (int64_t)C_in * k * k;  // gathered channels
+    if (cg * G > (1 << 20) || (int64_t)C_out * G > (1 << 20))
+        return fail(EQLIN_ERR_UNSUPPORTED, "channel counts beyond 2^20 unrolled columns");
+    hipStream_t s = (hipStream_t)stream;
+    Plan *p = new (std::nothrow) eqlin_plan();
+    if (!p) return fail(EQLIN_ERR_OUT_OF_MEMORY, "host allocation");
+    p->C_out = C_out;
+    p->C_in = (int)cg;
+    p->G = G;
+    p->dtype = dtype;
+    p->flags = flags;
+    p->conv_k = k;
+    p->conv_cin = C_in;
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+        free_plan(p);
+        return hip_fail(e, "hipGetDevice");
+    }
+    const size_t wbytes = (size_t)C_out * cg * G * 2;
+    e = hipMalloc(&p->wconv, wbytes);
+    if (e != hipSuccess) {
+        p->wconv = nullptr;
+        free_plan(p);
+        return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for the gathered weight", wbytes);
+    }
+    e = eqlin::launch_conv_weight(psi, 2, C_out, C_in, k, p->wconv, s);
+    if (e != hipSuccess) {
+        free_plan(p);
+        return hip_fail(e, "gathered weight");
+    }
+    eqlin_status_t st = build_spectral(p, p->wconv, s);
+    if (st != EQLIN_OK) {
+        free_plan(p);
+        return st;
+    }
+    {  // set-up of this device (as eqlin_prepare_weights)
+        void *ws = nullptr;
+        st = static_scratch(p->device, &ws);
+        if (st != EQLIN_OK) {
+            free_plan(p);
+            return st;
+        }
+    }
+    if (flags & EQLIN_PREPARE_EXPANDED) {  // the unrolled gathered layer, run as G = 1 with the same gather
+        const size_t ebytes = (size_t)C_out * G * cg * G * 2;
+        e = hipMalloc(&p->wexp, ebytes);
+        if (e != hipSuccess) {
+            p->wexp = nullptr;
+            free_plan(p);
+            return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for the unrolled weight", ebytes);
+        }
+        e = eqlin::launch_expand(p->wconv, 2, false, G, C_out, (int)cg, p->wexp, s);
+        if (e != hipSuccess) {
+            free_plan(p);
+            return hip_fail(e, "unrolled weight");
+        }
+        Plan *q = new (std::nothrow) eqlin_plan();
+        if (!q) {
+            free_plan(p);
+            return fail(EQLIN_ERR_OUT_OF_MEMORY, "host allocation");
+        }
+        q->C_out = C_out * G;
+        q->C_in = (int)cg * G;
+        q->G = 1;
+        q->dtype = dtype;
+        q->device = p->device;
+        q->bias_shift = 2;
+        q->conv_k = k;
+        q->conv_cin = C_in;
+        p->expanded = q;
+        st = build_spectral(q, p->wexp, s);
+        if (st != EQLIN_OK) {
+            free_plan(p);
+            return st;
+        }
+    }
+    *out = static_cast<eqlin_handle_t>(static_cast<eqlin_plan *>(p));
+    return EQLIN_OK;
+}
+
+static eqlin_status_t run_conv(const Plan *h, const Plan *run, const void *x, const void *b, void *y, int64_t B, int H,
+                               int W, eqlin_stream_t stream, const char *what) {
+    if (B < 0 || H < 0 || W < 0) return fail(EQLIN_ERR_INVALID_ARG, "B = %lld, H = %d, W = %d", (long long)B, H, W);
+    if (B == 0 || H == 0 || W == 0) return EQLIN_OK;
+    if ((int64_t)H * W > INT32_MAX || B > (INT64_C(1) << 40) / ((int64_t)H * W))
+        return fail(EQLIN_ERR_INVALID_ARG, "B x H x W overflows");
+    const int64_t N = B * H * W;
+    // x plays the layer's x with its real channel count, y the layer's y
+    eqlin_status_t st = check_forward_args(h, x, b, y, N, h->conv_cin, h->C_out, h->G);
+    if (st != EQLIN_OK) return st;
+    if (N * h->conv_cin * h->G * 2 >= (INT64_C(1) << 31))
+        return fail(EQLIN_ERR_UNSUPPORTED, "x of %lld bytes: the gathered loads address x with 32-bit offsets",
+                    (long long)(N * h->conv_cin * h->G * 2));
+    (void)hipGetLastError();
+    hipError_t e = run->fwd.conv_launch(run, x, b, y, N, H, W, (hipStream_t)stream);
+    return e == hipSuccess ? EQLIN_OK : hip_fail(e, what);
+}
+
+eqlin_status_t eqlin_conv_forward(eqlin_handle_t h, const void *x, const void *bias, void *y, int64_t B, int H, int W,
+                                  eqlin_stream_t stream) {
+    g_err[0] = 0;
+    if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
+    if (h->conv_k <= 0) return fail(EQLIN_ERR_INVALID_ARG, "not a convolution handle (eqlin_prepare_conv_weights)");
+    return run_conv(h, h, x, bias, y, B, H, W, stream, "eqlin_conv_forward launch");
+}
+
+eqlin_status_t eqlin_conv_forward_expanded(eqlin_handle_t h, const void *x, const void *bias, void *y, int64_t B,
+                                           int H, int W, eqlin_stream_t stream) {
+    g_err[0] = 0;
+    if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
+    if (h->conv_k <= 0) return fail(EQLIN_ERR_INVALID_ARG, "not a convolution handle (eqlin_prepare_conv_weights)");
+    if (!h->expanded) return fail(EQLIN_ERR_INVALID_ARG, "handle was prepared without EQLIN_PREPARE_EXPANDED");
+    return run_conv(h, h->expanded, x, bias, y, B, H, W, stream, "eqlin_conv_forward_expanded launch");
+}
+
 eqlin_status_t eqlin_destroy(eqlin_handle_t h) {
     g_err[0] = 0;
     free_plan(h);
@@ -396,6 +546,10 @@ eqlin_status_t eqlin_export_expanded_weight(eqlin_handle_t h, void *out, eqlin_s
 
 int eqlin_describe(eqlin_handle_t h, char *buf, size_t len) {
     if (!h) return snprintf(buf, len, "(null handle)");
+    if (h->conv_k > 0)
+        return snprintf(buf, len, "p4 conv %dx%d C_in=%d (gathered %d) C_out=%d %s | forward: %s | expanded: %s", h->conv_k,
+                        h->conv_k, h->conv_cin, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : "f16", h->fwd.name,
+                        h->expanded ? h->expanded->fwd.name : "(not prepared)");
     return snprintf(buf, len,
                     "%s%d C_in=%d C_out=%d %s | forward: %s | expanded: %s | backward data: %s | backward weights: %s",
                     h->d4 ? "D" : "G=", h->d4 ? 4 : h->G, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : h->dtype == EQLIN_F16 ? "f16" : "f32", h->fwd.name,

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/eqlin.h"
 
 namespace eqlin {
@@ -24,6 +26,9 @@ struct Plan;
 // act: an eqlin_act_t applied to every output value in the epilogue
 typedef hipError_t (*LaunchFn)(const Plan *p, const void *x, const void *b, void *y, int64_t N, int act,
                                hipStream_t s);
+// the p4 group convolution's forward (conv.hip): x, y one token per pixel of a [N / (H W)][H][W] grid
+typedef hipError_t (*ConvLaunchFn)(const Plan *p, const void *x, const void *b, void *y, int64_t N, int H, int W,
+                                   hipStream_t s);
 
 // Kernel choice for one plan. The weight layout (padding of C_in and C_out) depends on it.
 struct KernelChoice {
@@ -39,6 +44,7 @@ struct KernelChoice {
     int ks_mult = 1;        // K-steps are padded to a multiple of this
     size_t lds_bytes = 0;
     LaunchFn launch = nullptr;
+    ConvLaunchFn conv_launch = nullptr;  // convolution plans: the gathered-load instance
     char name[96] = {0};
 };
 
@@ -65,6 +71,13 @@ struct Plan {
     // (C_in and C_out swapped), whose forward is dx; plus Wt itself
     Plan *backward = nullptr;
     void *wt = nullptr;  // [C_in][C_out][G] of dtype
+
+    // p4 group convolution (eqlin_prepare_conv_weights): C_in above is the gathered channel count
+    // conv_cin * conv_k^2; conv_tab the kernels' per-stage source table (conv.hip); wconv the gathered
+    // weight W'[C_out][C_in][G] the spectral planes (and the unrolled weight) were built from
+    int conv_k = 0, conv_cin = 0;
+    void *conv_tab = nullptr;
+    void *wconv = nullptr;
 };
 
 // ---- fwd_bf16.hip ----
@@ -72,6 +85,8 @@ bool select_bf16(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 int device_num_cus();  // compute units of the current device (queried once)
 // ---- fwd_big.hip ----
 bool select_big(int G, bool d4, int C_in, int C_out, KernelChoice *out);
+// the gathered-load (convolution) instance for G = 4 (spectral) or G = 1 (the unrolled comparator)
+bool select_big_conv(int G, int C_in, int C_out, KernelChoice *out);
 // ---- fwd_f32.hip ----
 bool select_f32(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 
@@ -84,6 +99,12 @@ hipError_t launch_backward_weights(const Plan *p, const void *x, const void *dy,
 const char *bw_kernel_name(const Plan *p);
 // p[0..n) = 0 on stream s (a fill kernel: no memset node when the caller captures a graph)
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
+
+// ---- conv.hip ----
+// psi[C_out][C_in][4][k][k] -> the gathered layer's weight W'[C_out][C_in * k * k][4] (2- or 4-byte elements)
+hipError_t launch_conv_weight(const void *psi, int elem_bytes, int C_out, int C_in, int k, void *wp, hipStream_t s);
+// the kernels' per-stage source table for n_stages stages (host side; uploaded by the caller)
+std::vector<uint4> conv_stage_table(int C_in, int k, int elem_bytes, int n_stages);
 
 // ---- prepare.hip ----
 // W [C_out][C_in][G] (16-bit elements of the half type when w_is_half, else fp32) -> fragment-ordered

@@ -34,6 +34,7 @@
 // start), outputs staged per wave in LDS (XOR-swizzled), then written as whole 16-byte pieces with
 // range-checked non-temporal buffer stores.
 #include <stdio.h>
+#include <string.h>
 
 #include <algorithm>
 
@@ -171,15 +172,25 @@ struct BigCfg {
 // Persistent: each workgroup keeps output tile ot (its weights, bias and L2 set) and walks the token
 // tiles tt0, tt0 + tstep, ... (block_tile; tstep = gridDim.x / tiles_o). The load pipeline runs on
 // across tile boundaries, and a tile's outputs are stored while the next tile computes.
-template <int G, int WA, int WB, int OW, int TW, bool VEC, bool GELU, class E>
+//
+// CONV: the input channels are the gathered channels of a p4 group convolution (conv.hip): token n is
+// pixel n of a [B][img_h][img_w] grid, x holds x_elems elements per pixel, and stage s takes its
+// channels from conv_tab[s] -- a byte offset into the pixel's row (.x) and, for each group sample g,
+// the offset (dy, dx) of the pixel it is read from (bytes g of .y and .z, signed); pixels outside the
+// image read as zeros. An x item's G samples (its 2 channels, or 8 scalars at G = 1) then come from 4
+// loads, sample g from the g-th pixel: they are merged into the item's 16 bytes before the transform.
+template <int G, int WA, int WB, int OW, int TW, bool VEC, bool GELU, class E, bool CONV = false>
 __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ x4,
                                                       const uint4 *__restrict__ wfrag,
                                                       const uint16_t *__restrict__ bias, int bias_shift,
                                                       uint16_t *__restrict__ y, int64_t N, int C_in,
                                                       int C_out, int n_stages, int KS16, int tiles_t,
-                                                      int tiles_o, int xg) {
+                                                      int tiles_o, int xg, const uint4 *__restrict__ conv_tab,
+                                                      int img_h, int img_w, int x_elems) {
     using C = BigCfg<G, WA, WB, OW, TW>;
     constexpr int KSS = C::KSS, NCH = C::NCH;
+    static_assert(!CONV || (C::XU4 == 1 && (G == 4 || G == 1)), "gathered loads: one 16-byte piece per item");
+    constexpr int XL = CONV ? 4 : C::XU4;  // 16-byte loads per x item and stage
     __shared__ uint4 lds[C::LDS_U4];  // two x-plane buffers, then each wave's output staging
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wo = wave % OW, wt = wave / OW;
@@ -200,35 +211,76 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     // (item it of a thread is token tl + it * NT / (SC / NCH), same channels: a scalar row offset)
     static_assert(C::NT % (C::SC / NCH) == 0, "items of a thread differ by whole token rows");
-    const int x_row = C_in * G * 2;  // bytes per token row
+    const int x_row = (CONV ? x_elems : C_in * G) * 2;  // bytes per token row
     const int x_tl = tid / (C::SC / NCH), x_c0 = (tid % (C::SC / NCH)) * NCH;
     const int x_vo = x_tl * x_row + x_c0 * G * 2;
     const int x_vo_last = x_tl * x_row + (C_in - NCH) * G * 2;  // the row's last channels
-    auto x_rsrc = [&](int k) {
-        const int64_t n0 = (int64_t)(tt0 + k * tstep) * C::BT;
-        int64_t rows = N - n0 < C::BT ? N - n0 : C::BT;
-        rows = k < ntl ? rows : 0;
-        return __builtin_amdgcn_make_buffer_rsrc((void *)(x4 + (k < ntl ? n0 : 0) * C_in * G / 8), (short)0,
-                                                 (int)(rows * x_row), 0x00020000);
+    constexpr int IT_ROWS = C::NT / (C::SC / NCH);  // token rows between a thread's items
+    // The x source of token tile k: its buffer resource, and (CONV) each item's pixel and row offset.
+    struct XSrc {
+        __amdgpu_buffer_rsrc_t rs;
+        int py[C::ITEMS], px[C::ITEMS], off[C::ITEMS];
     };
-    // stage of the current tile (resource rs_c), or past its end: the next tile's (rs_n)
-    auto load_x = [&](__amdgpu_buffer_rsrc_t rs_c, __amdgpu_buffer_rsrc_t rs_n, int stage,
-                      uint4 (&dst)[C::ITEMS][C::XU4]) {
-        const bool next = stage >= n_stages;  // uniform
-        const __amdgpu_buffer_rsrc_t rs = next ? rs_n : rs_c;
-        stage = next ? stage - n_stages : stage;
-        const int soff = stage * C::SC * G * 2;
-        // channels past C_in (the stage count is padded) re-read the row's last channels: finite
-        // values that meet zero weight columns
-        const int vo = (stage * C::SC + x_c0 < C_in) ? x_vo : x_vo_last - soff;
+    auto x_src = [&](int k) {
+        XSrc r;
+        const int64_t n0 = (int64_t)(tt0 + k * tstep) * C::BT;
+        if constexpr (CONV) {  // the whole tensor; rows past N or past the last tile read as zeros
+            r.rs = __builtin_amdgcn_make_buffer_rsrc((void *)x4, (short)0, (int)(N * x_row), 0x00020000);
+            const int hw = img_h * img_w;
 #pragma unroll
-        for (int it = 0; it < C::ITEMS; ++it)
-#pragma unroll
-            for (int q = 0; q < C::XU4; ++q) {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, vo + 16 * q, soff + it * (C::NT / (C::SC / NCH)) * x_row, 0);
-                dst[it][q] = make_uint4(v.x, v.y, v.z, v.w);
+            for (int it = 0; it < C::ITEMS; ++it) {
+                const int64_t n = n0 + x_tl + it * IT_ROWS;
+                const bool ok = k < ntl && n < N;
+                const int nn = ok ? (int)n : 0, pix = nn % hw;
+                r.py[it] = ok ? pix / img_w : -(1 << 24);
+                r.px[it] = pix % img_w;
+                r.off[it] = nn * x_row + x_c0 * G * 2;
             }
+        } else {  // the tile's rows (rows past N read as zeros; past the last tile, an empty range)
+            int64_t rows = N - n0 < C::BT ? N - n0 : C::BT;
+            rows = k < ntl ? rows : 0;
+            r.rs = __builtin_amdgcn_make_buffer_rsrc((void *)(x4 + (k < ntl ? n0 : 0) * C_in * G / 8), (short)0,
+                                                     (int)(rows * x_row), 0x00020000);
+#pragma unroll
+            for (int it = 0; it < C::ITEMS; ++it) r.py[it] = r.px[it] = r.off[it] = 0;
+        }
+        return r;
+    };
+    // stage of the current tile (source src_c), or past its end: the next tile's (src_n)
+    auto load_x = [&](const XSrc &src_c, const XSrc &src_n, int stage, uint4 (&dst)[C::ITEMS][XL]) {
+        const bool next = stage >= n_stages;  // uniform
+        const __amdgpu_buffer_rsrc_t rs = next ? src_n.rs : src_c.rs;
+        stage = next ? stage - n_stages : stage;
+        if constexpr (CONV) {
+            const uint4 t = conv_tab[stage];  // wave-uniform
+#pragma unroll
+            for (int it = 0; it < C::ITEMS; ++it) {
+                const int py = next ? src_n.py[it] : src_c.py[it];
+                const int px = next ? src_n.px[it] : src_c.px[it];
+                const int off = (next ? src_n.off[it] : src_c.off[it]) + (int)t.x;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int sy = (int)(signed char)(t.y >> (8 * g)), sx = (int)(signed char)(t.z >> (8 * g));
+                    const bool in = ((unsigned)(py + sy) < (unsigned)img_h) & ((unsigned)(px + sx) < (unsigned)img_w);
+                    const int vo = in ? off + (sy * img_w + sx) * x_row : 0x7fffffff;  // outside: zeros
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0);
+                    dst[it][g] = make_uint4(v.x, v.y, v.z, v.w);
+                }
+            }
+        } else {
+            const int soff = stage * C::SC * G * 2;
+            // channels past C_in (the stage count is padded) re-read the row's last channels: finite
+            // values that meet zero weight columns
+            const int vo = (stage * C::SC + x_c0 < C_in) ? x_vo : x_vo_last - soff;
+#pragma unroll
+            for (int it = 0; it < C::ITEMS; ++it)
+#pragma unroll
+                for (int q = 0; q < C::XU4; ++q) {
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, vo + 16 * q, soff + it * IT_ROWS * x_row,
+                                                                          0);
+                    dst[it][q] = make_uint4(v.x, v.y, v.z, v.w);
+                }
+        }
     };
     // weights: one resource per wave (its WA output blocks), block and stage as a scalar offset
     const int wo_u = __builtin_amdgcn_readfirstlane(wave) % OW;
@@ -245,7 +297,20 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                 dst[a * KSS * G + r] = make_uint4(v.x, v.y, v.z, v.w);
             }
     };
-    auto dft_store = [&](const uint4 (&src)[C::ITEMS][C::XU4], uint4 *xb) {
+    auto dft_store = [&](const uint4 (&raw)[C::ITEMS][XL], uint4 *xb) {
+        // CONV: element e = j * 4 + g of an item (channel j, sample g) is element e of load g
+        uint4 src[C::ITEMS][C::XU4];
+#pragma unroll
+        for (int it = 0; it < C::ITEMS; ++it) {
+            if constexpr (CONV) {
+                auto mix = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b & 0xffff0000u); };
+                src[it][0] = make_uint4(mix(raw[it][0].x, raw[it][1].x), mix(raw[it][2].y, raw[it][3].y),
+                                        mix(raw[it][0].z, raw[it][1].z), mix(raw[it][2].w, raw[it][3].w));
+            } else {
+#pragma unroll
+                for (int q = 0; q < C::XU4; ++q) src[it][q] = raw[it][q];
+            }
+        }
 #pragma unroll
         for (int it = 0; it < C::ITEMS; ++it) {
             const int item = tid + it * C::NT;
@@ -306,11 +371,11 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     }
 
     // ---- prologue: weights of stage 0 and raw x of positions 0 and 1 requested; x(0) transformed ----
-    uint4 xr[2][C::ITEMS][C::XU4];
+    uint4 xr[2][C::ITEMS][XL];
     uint4 wr[2][C::WF];
     load_w(0, wr[0]);
     {
-        const __amdgpu_buffer_rsrc_t rs0 = x_rsrc(0);
+        const XSrc rs0 = x_src(0);
         load_x(rs0, rs0, 0, xr[0]);
         load_x(rs0, rs0, 1, xr[1]);
     }
@@ -349,10 +414,9 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     // stores.
     // The next stage's products then wait for its weights only, with the raw x still in flight
     // (vector-memory operations complete in issue order).
-    auto step = [&](auto first, __amdgpu_buffer_rsrc_t xrs_c, __amdgpu_buffer_rsrc_t xrs_n, int s,
-                    uint4 (&x_free)[C::ITEMS][C::XU4], const uint4 (&x_next)[C::ITEMS][C::XU4],
-                    const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF], const uint4 *planes,
-                    uint4 *planes_next, __amdgpu_buffer_rsrc_t rs_prev, bool has_prev) {
+    auto step = [&](auto first, const XSrc &xrs_c, const XSrc &xrs_n, int s, uint4 (&x_free)[C::ITEMS][XL],
+                    const uint4 (&x_next)[C::ITEMS][XL], const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF],
+                    const uint4 *planes, uint4 *planes_next, __amdgpu_buffer_rsrc_t rs_prev, bool has_prev) {
         constexpr int P = KSS * WB, H = P / 2;
         // the second half's planes are read with the first half's when they fit in 4 registers of 16
         // bytes, so its products do not wait for LDS after the first half's
@@ -383,7 +447,7 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
 #pragma unroll
         for (int q = H; q < P; ++q) products(first, q, xb[q - H], w_cur, w_neg);
         dft_store(x_next, planes_next);  // past the last position: unused planes, harmless
-        interleave_stage<(PRE ? 0 : (P - H) * G) + C::SPS, (P - H) * WA * real_products(G), C::ITEMS * C::XU4,
+        interleave_stage<(PRE ? 0 : (P - H) * G) + C::SPS, (P - H) * WA * real_products(G), C::ITEMS * XL,
                          C::VPM>();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -410,7 +474,7 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
         }
         const bool has_prev = k > 0 && vec_rows;
         const __amdgpu_buffer_rsrc_t rs_prev = tile_rsrc(k > 0 ? k - 1 : 0);
-        const __amdgpu_buffer_rsrc_t xrs_c = x_rsrc(k), xrs_n = x_rsrc(k + 1);
+        const XSrc xrs_c = x_src(k), xrs_n = x_src(k + 1);
         // n_stages is even (the channel padding sees to it); for G >= 2 the first pair is peeled so
         // the first products can start the accumulators of planes 1.. without clearing them (G = 1
         // has only the bias plane)
@@ -845,7 +909,33 @@ static hipError_t launch_big(const Plan *p, const void *x, const void *b, void *
     auto kern = p->dtype == EQLIN_F16 ? pick(F16{}) : pick(BF16{});
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), 0, s, (const uint4 *)x, (const uint4 *)p->planes,
                        (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS,
-                       (int)tiles_t, tiles_o, xg);
+                       (int)tiles_t, tiles_o, xg, (const uint4 *)nullptr, 0, 0, 0);
+    return hipGetLastError();
+}
+
+// The gathered-load instances (the p4 group convolution and its unrolled comparator): like launch_big,
+// plus the stage table and the image geometry (token n = pixel n of a [N / (H W)][H][W] grid).
+template <int G, int WA, int WB, int OW, int TW>
+static hipError_t launch_big_conv(const Plan *p, const void *x, const void *b, void *y, int64_t N, int img_h,
+                                  int img_w, hipStream_t s) {
+    using C = BigCfg<G, WA, WB, OW, TW>;
+    const int64_t tiles_t = (N + C::BT - 1) / C::BT;
+    const int tiles_o = p->NB_total / (C::BO / 32);
+    const int n_stages = p->KS / C::KSS;
+    const int x_elems = p->conv_cin * 4;  // elements per pixel row of x (C_in channels x 4 samples)
+    // x is one buffer resource addressed with 32-bit offsets; output rows as in launch_big
+    if (tiles_t > 0x7fffffff || (int64_t)C::BT * p->C_out * G * 2 > 0x7fffffff || N * x_elems * 2 > 0x7fffffff)
+        return hipErrorInvalidValue;
+    int64_t per_o = std::max(1, p->fwd.num_cus / tiles_o);
+    per_o = std::min<int64_t>(per_o, tiles_t);
+    const int64_t grid = per_o * tiles_o;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    const int xg = xcd_group(tiles_o, (size_t)C::BO * p->KS * 16 * G * 2);
+    auto kern = p->dtype == EQLIN_F16 ? k_big<G, WA, WB, OW, TW, true, false, F16, true>
+                                      : k_big<G, WA, WB, OW, TW, true, false, BF16, true>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), 0, s, (const uint4 *)x, (const uint4 *)p->planes,
+                       (const uint16_t *)b, p->bias_shift, (uint16_t *)y, N, p->C_in, p->C_out, n_stages, p->KS,
+                       (int)tiles_t, tiles_o, xg, (const uint4 *)p->conv_tab, img_h, img_w, x_elems);
     return hipGetLastError();
 }
 
@@ -869,6 +959,17 @@ static const BigEntry kBig[] = {
     {8, P8Cfg::BO, P8Cfg::BT, P8Cfg::KSS, P8Cfg::NT, P8Cfg::LDS, launch_p8, "planes split over 2 waves/SIMD, 4x2 waves"},
 };
 #undef BE
+
+bool select_big_conv(int G, int C_in, int C_out, KernelChoice *out) {
+    if (G != 4 && G != 1) return false;
+    if (!select_big(G, false, C_in, C_out, out)) return false;
+    if ((C_out * G) % 8 != 0) return false;  // whole 16-byte pieces per output row
+    out->conv_launch = G == 4 ? launch_big_conv<4, 1, 2, 8, 1> : launch_big_conv<1, 2, 4, 8, 1>;
+    out->launch = nullptr;  // a convolution plan runs only through conv_launch
+    const size_t n = strlen(out->name);
+    snprintf(out->name + n, sizeof(out->name) - n, " gathered");
+    return true;
+}
 
 bool select_big(int G, bool d4, int C_in, int C_out, KernelChoice *out) {
     (void)C_in;

@@ -114,3 +114,47 @@ BY_NAME.update({w.name: w for w in D4_WORKLOADS})
 F16_WORKLOADS = [Workload(w.name.replace("_bf16", "_f16"), G=w.G, C_in=w.C_in, C_out=w.C_out, N=w.N, dtype="f16")
                  for w in WORKLOADS[1:]]
 BY_NAME.update({w.name: w for w in F16_WORKLOADS})
+
+
+# The p4 group convolution with k x k kernels (the equivariant convolutions of "Limitaciones y Trabajo
+# Futuro"): one token per pixel of a [B, H, W] batch, x[B, H, W, C_in, 4], psi[C_out, C_in, 4, k, k].
+@dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    C_in: int
+    C_out: int
+    k: int
+    B: int
+    H: int
+    W: int
+    dtype: str = "bf16"
+
+    @property
+    def N(self) -> int:
+        return self.B * self.H * self.W
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.dtype]
+
+
+# a 3 x 3 convolution of a vision stage: 256 channels per orientation (1024 with the group axis) on
+# 4 feature maps of 64 x 64 pixels
+CONV_WORKLOAD = ConvWorkload("p4_conv3x3_c256_n4x64x64_bf16", C_in=256, C_out=256, k=3, B=4, H=64, W=64)
+
+
+def make_conv_inputs(C_in: int, C_out: int, k: int, B: int, H: int, W: int, dtype: str = "bf16", seed: int = 0):
+    """CPU tensors (x[B, H, W, C_in, 4], psi[C_out, C_in, 4, k, k], b[C_out]): x ~ N(0, 1),
+    psi ~ N(0, 1/(C_in*4*k*k)) (the layer's reading of the variance: outputs of about unit variance over
+    the C_in * 4 * k * k terms), b ~ N(0, 0.01); drawn in that order from one generator, fp32, then rounded
+    to nearest even for bf16 / f16."""
+    if dtype not in ("f32", "bf16", "f16"):
+        raise ValueError(f"dtype must be 'f32', 'bf16' or 'f16', got {dtype!r}")
+    gen = torch.Generator().manual_seed(int(seed))
+    x = torch.randn((B, H, W, C_in, 4), generator=gen, dtype=torch.float32)
+    psi = torch.randn((C_out, C_in, 4, k, k), generator=gen, dtype=torch.float32) * (C_in * 4 * k * k) ** -0.5
+    b = torch.randn((C_out,), generator=gen, dtype=torch.float32) * 0.1
+    if dtype != "f32":
+        half = torch.bfloat16 if dtype == "bf16" else torch.float16
+        x, psi, b = x.to(half), psi.to(half), b.to(half)
+    return x, psi, b

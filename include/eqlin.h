@@ -213,6 +213,47 @@ eqlin_status_t eqlin_backward_weights(eqlin_handle_t h, const void *x, const voi
 eqlin_status_t eqlin_backward_weights_static(eqlin_handle_t h, const void *x, const void *dy, float *dW, float *db,
                                              int64_t N, eqlin_stream_t stream);
 
+/*
+ * The p4 group convolution with k x k spatial kernels -- the equivariant convolutions the Flash
+ * EQ-Linear page names among the operators the method extends to ("Limitaciones y Trabajo Futuro"):
+ *
+ *     y[b, p, o, h] = bias[o] + sum_{i, g} sum_{delta} psi[o, i, (h - g) mod 4, R^-h delta] * x[b, p + delta, i, g]
+ *
+ * over the pixels p = (row, column) of H x W images, offsets delta = (dy, dx) with |dy|, |dx| <= k / 2,
+ * R(dy, dx) = (-dx, dy) the quarter turn of an offset (the filter turns with the output orientation h),
+ * pixels outside the image reading as zero. Turning the image a quarter and shifting the group axis by
+ * one commutes with it; k = 1 is the EQ-Linear layer (W = psi[:, :, :, 0, 0]). The library runs it as an
+ * EQ-Linear layer over C_in * k * k gathered channels -- for each orbit {R^j delta0} of offsets,
+ * gathered channel (i, delta0, u) holds sample g of pixel p + R^(g - u) delta0 -- whose weight
+ * psi[o, i, m, R^-(m + u) delta0] depends on h - g alone, so the group DFT diagonalises it; the gather
+ * happens while x is loaded (one load address per sample), in the layer's own spectral kernel.
+ *
+ * Layouts (row-major, contiguous): x[B][H][W][C_in][4], y[B][H][W][C_out][4] (one token per pixel, the
+ * layer's rows), psi[C_out][C_in][4][k][k] (psi[o][i][d][ky][kx]: the filter at offset
+ * (ky - k/2, kx - k/2)), bias[C_out]. Element type EQLIN_BF16 or EQLIN_F16 (fp32 transforms and
+ * accumulation, one rounding of y).
+ *
+ * eqlin_prepare_conv_weights -- psi -> the gathered layer's spectral weights (and, with
+ * EQLIN_PREPARE_EXPANDED, its unrolled weight for eqlin_conv_forward_expanded).
+ *   G must be 4 and k odd in 1..15 (else EQLIN_ERR_INVALID_ARG); C_in % 16 == 0, C_out % 8 == 0, dtype
+ *   EQLIN_BF16 or EQLIN_F16 and flags within EQLIN_PREPARE_EXPANDED (else EQLIN_ERR_UNSUPPORTED).
+ *   Allocates device memory; synchronises nothing; psi may be freed once `stream` has passed the call.
+ *   The handle serves eqlin_conv_forward(_expanded), eqlin_describe, eqlin_export_* (the gathered
+ *   layer's weights, C_in * k * k input channels) and eqlin_destroy; the layer's entry points reject it.
+ * eqlin_conv_forward -- y from x for B images of H x W pixels (B, H, W >= 0; an empty batch enqueues
+ *   nothing). bias may be NULL. B * H * W * C_in * 8 must stay below 2^31 (x is addressed with 32-bit
+ *   offsets; else EQLIN_ERR_UNSUPPORTED). Alignment, overlap, device and stream rules as eqlin_forward;
+ *   allocates nothing.
+ * eqlin_conv_forward_expanded -- the same through the unrolled gathered layer, one dense product on the
+ *   matrix cores (the comparator); needs EQLIN_PREPARE_EXPANDED (else EQLIN_ERR_INVALID_ARG).
+ */
+eqlin_status_t eqlin_prepare_conv_weights(const void *psi, int C_out, int C_in, int G, int k, eqlin_dtype_t dtype,
+                                          unsigned flags, eqlin_stream_t stream, eqlin_handle_t *out);
+eqlin_status_t eqlin_conv_forward(eqlin_handle_t h, const void *x, const void *bias, void *y, int64_t B, int H, int W,
+                                  eqlin_stream_t stream);
+eqlin_status_t eqlin_conv_forward_expanded(eqlin_handle_t h, const void *x, const void *bias, void *y, int64_t B,
+                                           int H, int W, eqlin_stream_t stream);
+
 /* Frees the handle's device memory (hipFree, which synchronises the device). NULL is a no-op. */
 eqlin_status_t eqlin_destroy(eqlin_handle_t h);
 
