@@ -198,6 +198,49 @@ def bench_backward(torch, eq, rl, w, st, dev, K: int, Wm: int, timer, with_expan
                      "algorithmic_bytes": Bk, "hbm_frac": round(Bk / tb / 1e9 / rl.PEAK_HBM_GBS, 4)}
         log(f"[bench] backward {name}: {ms_b * 1e3:.2f} us/step")
     res["kernels"] = h.describe().split("|")[3:]
+    if with_expanded and w.group == "cyclic":
+        # the naive layer's gradients (replicate the weight, multiply densely): dx = dy E on the
+        # hand-written G = 1 kernels over E^T, and dE = dy^T x through torch's matrix product (the vendor
+        # GEMM, as autograd computes a dense layer's weight gradient) folded back onto W along the
+        # circulant diagonals, dW[o, i, d] = sum_h dE[o G + h, i G + (h - d) mod G]
+        dxe = [torch.empty_like(xs[0]) for _ in range(R)]
+
+        def bwd_data_exp(i):
+            eq.backward_data_expanded(h, dys[i], dxe[i])
+
+        G, Co, Ci = w.G, w.C_out, w.C_in
+        nset = min(R, 3)
+        dyT = [dys[i].view(w.N, Co * G).t().contiguous() for i in range(nset)]  # outside the timed region
+        xf = [xs[i].view(w.N, Ci * G) for i in range(nset)]
+        hh = torch.arange(G, device=dev)
+        index = ((hh[:, None] - hh[None, :]) % G).expand(Co, Ci, G, G)  # [o, i, h, d] -> g = (h - d) mod G
+
+        def bwd_weights_naive(i):
+            dE = torch.mm(dyT[i % nset], xf[i % nset])  # [Co G, Ci G]
+            torch.gather(dE.view(Co, G, Ci, G).permute(0, 2, 1, 3), 3, index).sum(dim=2)
+
+        exp = {}
+        for name, fn, timer_ in (("data_expanded", bwd_data_exp, timer), ("weights_naive", bwd_weights_naive, time_eager)):
+            try:
+                for i in range(Wm):
+                    fn(i % R)
+                torch.cuda.synchronize()
+                exp[name] = {"us_per_step": round(timer_(torch, fn, K, R) * 1e3, 3)}
+                log(f"[bench] backward {name}: {exp[name]['us_per_step']:.2f} us/step")
+            except RuntimeError as e:  # the torch leg is a comparator: report, never fail the bench
+                exp[name] = {"error": str(e)[:200]}
+        exp["weights_naive"]["timing"] = "eager launches: torch.mm (dy^T x) + gather/sum fold"
+        exp["data_expanded"]["kernel"] = "hand-written G = 1 product over E^T (eqlin_backward_data_expanded)"
+        res["expanded"] = exp
+        if "us_per_step" in exp["data_expanded"]:
+            res["data"]["speedup_vs_expanded"] = round(exp["data_expanded"]["us_per_step"] / res["data"]["us_per_step"], 3)
+        if "us_per_step" in exp["weights_naive"]:
+            res["weights"]["speedup_vs_naive"] = round(exp["weights_naive"]["us_per_step"] / res["weights"]["us_per_step"], 3)
+        if "us_per_step" in exp["data_expanded"] and "us_per_step" in exp["weights_naive"]:
+            tot_s = res["data"]["us_per_step"] + res["weights"]["us_per_step"]
+            tot_e = exp["data_expanded"]["us_per_step"] + exp["weights_naive"]["us_per_step"]
+            res["speedup_vs_expanded"] = round(tot_e / tot_s, 3)
+            log(f"[bench] backward (dx + dW): spectral {tot_s:.1f} us, naive {tot_e:.1f} us, {tot_e / tot_s:.2f}x")
     return res
 
 

@@ -47,7 +47,7 @@ _ACTS = {None: EQLIN_ACT_NONE, "none": EQLIN_ACT_NONE, "gelu": EQLIN_ACT_GELU}
 # Every symbol include/eqlin.h declares.
 EXPORTED = (
     "eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_forward_act",
-    "eqlin_forward_expanded_act", "eqlin_backward_data",
+    "eqlin_forward_expanded_act", "eqlin_backward_data", "eqlin_backward_data_expanded",
     "eqlin_backward_weights_workspace", "eqlin_backward_weights", "eqlin_backward_weights_static", "eqlin_destroy",
     "eqlin_export_spectral_weights", "eqlin_export_expanded_weight", "eqlin_describe",
     "eqlin_status_string", "eqlin_last_error", "eqlin_version",
@@ -80,6 +80,7 @@ def load_library() -> ctypes.CDLL:
     lib.eqlin_forward_act.argtypes = [vp, vp, vp, vp, i64, i32, vp]
     lib.eqlin_forward_expanded_act.argtypes = [vp, vp, vp, vp, i64, i32, vp]
     lib.eqlin_backward_data.argtypes = [vp, vp, vp, i64, vp]
+    lib.eqlin_backward_data_expanded.argtypes = [vp, vp, vp, i64, vp]
     lib.eqlin_backward_weights_workspace.argtypes = [vp, i64]
     lib.eqlin_backward_weights_workspace.restype = ctypes.c_size_t
     lib.eqlin_backward_weights.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
@@ -100,6 +101,7 @@ def load_library() -> ctypes.CDLL:
     lib.eqlin_version.restype = ctypes.c_char_p
     for name in ("eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_expanded", "eqlin_destroy",
                  "eqlin_forward_act", "eqlin_forward_expanded_act", "eqlin_backward_data", "eqlin_backward_weights",
+                 "eqlin_backward_data_expanded",
                  "eqlin_backward_weights_static", "eqlin_prepare_conv_weights", "eqlin_conv_forward",
                  "eqlin_conv_forward_expanded",
                  "eqlin_export_spectral_weights", "eqlin_export_expanded_weight"):
@@ -268,6 +270,28 @@ def backward_data(h: Handle, dy: torch.Tensor, dx: torch.Tensor | None = None) -
         st = load_library().eqlin_backward_data(ctypes.c_void_p(h.ptr), ctypes.c_void_p(dy.data_ptr()),
                                                 ctypes.c_void_p(dx.data_ptr()), N, _stream(dy))
     _check(st, "eqlin_backward_data")
+    return dx
+
+
+def backward_data_expanded(h: Handle, dy: torch.Tensor, dx: torch.Tensor | None = None) -> torch.Tensor:
+    """eqlin_backward_data_expanded: the same dx as one dense product with the unrolled weight (needs
+    prepare_weights(W, expanded=True, backward=True))."""
+    if not (h.backward and h.expanded):
+        raise ValueError("handle was prepared without expanded=True and backward=True")
+    _need_cuda(dy, "dy")
+    if dy.dtype != h.dtype or dy.dim() != 3 or dy.shape[1] != h.C_out or dy.shape[2] != h.G:
+        raise ValueError(f"dy must be [N, {h.C_out}, {h.G}] of {h.dtype}, got {tuple(dy.shape)} {dy.dtype}")
+    N = dy.shape[0]
+    if dx is None:
+        dx = torch.empty((N, h.C_in, h.G), dtype=dy.dtype, device=dy.device)
+    else:
+        _need_cuda(dx, "dx")
+        if dx.dtype != h.dtype or tuple(dx.shape) != (N, h.C_in, h.G):
+            raise ValueError(f"dx must be [{N}, {h.C_in}, {h.G}] of {h.dtype}")
+    with torch.cuda.device(dy.device):
+        st = load_library().eqlin_backward_data_expanded(ctypes.c_void_p(h.ptr), ctypes.c_void_p(dy.data_ptr()),
+                                                         ctypes.c_void_p(dx.data_ptr()), N, _stream(dy))
+    _check(st, "eqlin_backward_data_expanded")
     return dx
 
 

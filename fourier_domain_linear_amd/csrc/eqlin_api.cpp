@@ -101,6 +101,31 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
     return EQLIN_OK;
 }
 
+// The unrolled comparator of plan p, whose weight W[C_out][C_in][G] (p's dtype) is given: E = unroll(W)
+// and a G = 1 plan over it (p->wexp, p->expanded).
+eqlin_status_t add_expanded(Plan *p, const void *W, hipStream_t s) {
+    const int G = p->G;
+    const size_t eb = p->dtype == EQLIN_F32 ? 4 : 2;
+    const size_t ebytes = (size_t)p->C_out * G * p->C_in * G * eb;
+    hipError_t e = hipMalloc(&p->wexp, ebytes);
+    if (e != hipSuccess) {
+        p->wexp = nullptr;
+        return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for the unrolled weight", ebytes);
+    }
+    e = eqlin::launch_expand(W, (int)eb, p->d4, G, p->C_out, p->C_in, p->wexp, s);
+    if (e != hipSuccess) return hip_fail(e, "unrolled weight");
+    Plan *q = new (std::nothrow) eqlin_plan();
+    if (!q) return fail(EQLIN_ERR_OUT_OF_MEMORY, "host allocation");
+    q->C_out = p->C_out * G;
+    q->C_in = p->C_in * G;
+    q->G = 1;
+    q->dtype = p->dtype;
+    q->device = p->device;
+    q->bias_shift = ilog2(G);
+    p->expanded = q;  // owned by p from here (freed with it)
+    return build_spectral(q, p->wexp, s);
+}
+
 eqlin_status_t check_forward_args(const Plan *h, const void *x, const void *b, const void *y, int64_t N,
                                   int C_in, int C_out, int G) {
     if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
@@ -206,32 +231,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
         }
     }
     if (flags & EQLIN_PREPARE_EXPANDED) {
-        const size_t eb = dtype == EQLIN_F32 ? 4 : 2;
-        const size_t ebytes = (size_t)C_out * G * C_in * G * eb;
-        e = hipMalloc(&p->wexp, ebytes);
-        if (e != hipSuccess) {
-            p->wexp = nullptr;
-            free_plan(p);
-            return fail(EQLIN_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) for the unrolled weight", ebytes);
-        }
-        e = eqlin::launch_expand(W, (int)eb, d4, G, C_out, C_in, p->wexp, s);
-        if (e != hipSuccess) {
-            free_plan(p);
-            return hip_fail(e, "unrolled weight");
-        }
-        Plan *q = new (std::nothrow) eqlin_plan();
-        if (!q) {
-            free_plan(p);
-            return fail(EQLIN_ERR_OUT_OF_MEMORY, "host allocation");
-        }
-        q->C_out = C_out * G;
-        q->C_in = C_in * G;
-        q->G = 1;
-        q->dtype = dtype;
-        q->device = p->device;
-        q->bias_shift = ilog2(G);
-        p->expanded = q;
-        st = build_spectral(q, p->wexp, s);
+        st = add_expanded(p, W, s);
         if (st != EQLIN_OK) {
             free_plan(p);
             return st;
@@ -264,6 +264,8 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
         q->device = p->device;
         p->backward = q;
         st = build_spectral(q, p->wt, s);
+        // with both flags, the data gradient's own unrolled comparator: the G = 1 product with E^T
+        if (st == EQLIN_OK && (flags & EQLIN_PREPARE_EXPANDED)) st = add_expanded(q, p->wt, s);
         if (st != EQLIN_OK) {
             free_plan(p);
             return st;
@@ -324,6 +326,18 @@ eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, i
     eqlin_status_t st = check_forward_args(h, dy, nullptr, dx, N, h->C_out, h->C_in, h->G);
     if (st != EQLIN_OK || N == 0) return st;
     return run_forward(h->backward, dy, nullptr, dx, N, EQLIN_ACT_NONE, stream, "eqlin_backward_data launch");
+}
+
+eqlin_status_t eqlin_backward_data_expanded(eqlin_handle_t h, const void *dy, void *dx, int64_t N,
+                                            eqlin_stream_t stream) {
+    g_err[0] = 0;
+    if (!h) return fail(EQLIN_ERR_INVALID_ARG, "null handle");
+    if (!h->backward || !h->backward->expanded)
+        return fail(EQLIN_ERR_INVALID_ARG, "handle was not prepared with EQLIN_PREPARE_BACKWARD | EQLIN_PREPARE_EXPANDED");
+    eqlin_status_t st = check_forward_args(h, dy, nullptr, dx, N, h->C_out, h->C_in, h->G);
+    if (st != EQLIN_OK || N == 0) return st;
+    return run_forward(h->backward->expanded, dy, nullptr, dx, N, EQLIN_ACT_NONE, stream,
+                       "eqlin_backward_data_expanded launch");
 }
 
 size_t eqlin_backward_weights_workspace(eqlin_handle_t h, int64_t N) {

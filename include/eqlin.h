@@ -167,6 +167,16 @@ eqlin_status_t eqlin_forward_expanded_act(eqlin_handle_t h, const void *x, const
 eqlin_status_t eqlin_backward_data(eqlin_handle_t h, const void *dy, void *dx, int64_t N, eqlin_stream_t stream);
 
 /*
+ * eqlin_backward_data_expanded -- the naive comparator of eqlin_backward_data: dx_flat = dy_flat E, the
+ * dense product with the unrolled weight E[o*G+h][i*G+g] = W[o, i, (h-g) mod G] (the gradient of the
+ * replicate-then-multiply layer of "Declaración del Problema"), on the matrix cores as one G = 1
+ * product over E^T. Same arguments and rules as eqlin_backward_data; needs a handle prepared with both
+ * EQLIN_PREPARE_BACKWARD and EQLIN_PREPARE_EXPANDED (else EQLIN_ERR_INVALID_ARG). Allocates nothing.
+ */
+eqlin_status_t eqlin_backward_data_expanded(eqlin_handle_t h, const void *dy, void *dx, int64_t N,
+                                            eqlin_stream_t stream);
+
+/*
  * eqlin_backward_weights -- the weight and bias gradients (same passages):
  *
  *     dW[o, i, d] = sum_n sum_{h < G} dy[n, o, h] * x[n, i, (h - d) mod G],   db[o] = sum_{n, h} dy[n, o, h]

@@ -147,3 +147,40 @@ def test_backward_bf16_needs_c_out_multiple_of_8(cuda_device):
     with pytest.raises(eq.EqlinError) as ei:
         eq.prepare_weights(W.to(cuda_device), backward=True)
     assert ei.value.status == eq.EQLIN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("w", WORKLOADS, ids=[w.name for w in WORKLOADS])
+def test_backward_data_expanded_full_size(w, cuda_device):
+    # the naive comparator of dx (one dense product with the unrolled weight), every token
+    x, W, _ = make_inputs(w.G, w.C_in, w.C_out, w.N, w.dtype, seed=0)
+    dy = make_grad(w.G, w.C_out, w.N, w.dtype, seed=0)
+    h = eq.prepare_weights(W.to(cuda_device), expanded=True, backward=True)
+    dx = eq.backward_data_expanded(h, dy.to(cuda_device))
+    torch.cuda.synchronize()
+    e = compare_all_tokens({"dx": dx}, lambda lo, hi: oracle.backward_data(dy[lo:hi], W), w.N, chunk=2048)["dx"]
+    print(f"[parity] {w.name} expanded dx all {w.N} tokens: rel_frob={e.rel:.3e} max_abs={e.max_abs:.3e} "
+          f"rms_ref={e.rms:.3e}", flush=True)
+    assert e.finite
+    if w.dtype == "bf16":
+        assert e.rel <= REL_BF16 and e.max_abs <= MAX_BF16 * e.rms, (w.name, e.rel, e.max_abs, e.rms)
+    else:
+        assert e.rel <= REL_F32, (w.name, e.rel)
+
+
+@pytest.mark.parametrize("G,C_in,C_out,N", [(4, 40, 24, 70), (8, 136, 200, 203), (2, 64, 32, 333), (1, 48, 40, 100)])
+def test_backward_data_expanded_small(G, C_in, C_out, N, cuda_device):
+    x, W, _ = make_inputs(G, C_in, C_out, N, "bf16", seed=12)
+    dy = make_grad(G, C_out, N, "bf16", seed=12)
+    h = eq.prepare_weights(W.to(cuda_device), expanded=True, backward=True)
+    dx = eq.backward_data_expanded(h, dy.to(cuda_device))
+    torch.cuda.synchronize()
+    _check(dx, oracle.backward_data(dy, W), "bf16", f"expanded dx G={G} {C_in}x{C_out} N={N}")
+    # without EQLIN_PREPARE_EXPANDED the entry point refuses
+    import ctypes
+
+    h2 = eq.prepare_weights(W.to(cuda_device), backward=True)
+    dyd = dy.to(cuda_device)
+    st = eq.load_library().eqlin_backward_data_expanded(
+        ctypes.c_void_p(h2.ptr), ctypes.c_void_p(dyd.data_ptr()), ctypes.c_void_p(dx.data_ptr()), N,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == eq.EQLIN_ERR_INVALID_ARG
