@@ -282,6 +282,9 @@ def bench_conv(torch, eq, rl, timer, dev, K: int, Wm: int):
     tr, bound = rl.roof_time_s(F, B, rl.PEAK_BF16_TFLOPS)
     res["bound"] = bound
     res["frac"] = round(tr / (res["spectral"]["us_per_step"] / 1e6), 4)
+    # HBM bytes per launch of the spectral kernel, from the committed counter summary (null when it
+    # was taken on other kernel sources): the gather reads each pixel's row k^2 times from the caches
+    res["traffic"] = load_traffic(cw.name)
     res["speedup_vs_expanded"] = round(res["expanded"]["us_per_step"] / res["spectral"]["us_per_step"], 3)
     # context: torch conv2d (the vendor convolution library) on the unrolled filter bank
     # Wfull[(o, h), (i, g)] = psi[o, i, (h - g) mod 4] turned h quarter turns, input in NCHW

@@ -22,12 +22,17 @@
 // h - g alone, so the convolution is an EQ-Linear layer over C_in * k^2 gathered channels (the centre
 // orbit contributes x[p, i, g] itself with W'[o, (i, centre), m] = psi[o, i, m, 0]), which the group
 // DFT diagonalises as before. The forward kernels gather xt while loading x (CONV in fwd_big.hip):
-// sample g of a gathered channel is sample g of the pixel at offset R^(g - u) delta0, so the gather is
-// only a choice of load address per sample, never a shuffle of loaded values.
+// the four gathered channels u of one (orbit, channel block) read the same four rows of x -- the
+// block at the four rotated offsets R^m delta0 -- sample g of channel u from row (g - u) mod 4, so
+// each row is loaded once and the gather is a choice of 16-bit halves among rows in registers.
 //
-// Gathered channel order (the K axis the kernels stream in stages of 16 channels): stage s < nib
-// (nib = C_in / 16) is the centre, channels i = 16 s .. 16 s + 15; stage nib + t, t = 4 (q nib + ib) + u,
-// is orbit q, channels 16 ib .. 16 ib + 15, gathered channel u.
+// Gathered channel order (the K axis the kernels stream in stages of 16 channels, four stages to a
+// group that reads the same four 16-channel rows of x): nib = C_in / 16 channel blocks, taken four at
+// a time (a quad Q: blocks 4Q .. 4Q + 3). A quad's groups are its centre group, stage u being channel
+// block 4Q + u (blocks past nib are zero-weight filling), then for each of its blocks ib the orbit
+// groups q = 0 .. n_orb - 1 (n_orb = (k^2 - 1) / 4), stage u the gathered channel u of (q, ib) and
+// row m the block at offset R^m delta0. All reads of a block's rows then fall within one quad's
+// groups, so the rows that neighbouring token tiles share are still in the L2 when they are re-read.
 #include <algorithm>
 #include <vector>
 
@@ -52,45 +57,55 @@ __host__ __device__ inline void orbit_rep(int r, int q, int &dy, int &dx) {
     dx = q % (r + 1);
 }
 
-// stage s -> (orbit q or -1 for the centre, channel block ib, gathered channel u)
-__host__ __device__ inline void conv_stage(int s, int nib, int &q, int &ib, int &u) {
-    if (s < nib) {
-        q = -1;
-        ib = s;
-        u = 0;
-        return;
-    }
-    const int t = s - nib;
-    u = t & 3;
-    ib = (t >> 2) % nib;
-    q = (t >> 2) / nib;
+__host__ __device__ inline int centre_groups(int nib) { return (nib + 3) / 4; }
+
+__host__ __device__ inline int gathered(int C_in, int k) {
+    const int nib = C_in / 16;
+    return 64 * (centre_groups(nib) + (k * k - 1) / 4 * nib);
 }
 
-// W'[o][c'][m] (c' the gathered channel, order above) from psi[o][i][m][ky][kx]: a gather, exact.
-// T: the 2- or 4-byte element (the value is copied bit for bit).
+int conv_gathered_channels(int C_in, int k) { return gathered(C_in, k); }
+
+// group T -> (orbit q, or -1 for the centre; channel block ib of an orbit group, or the centre group's
+// first block). n_orb: orbits of nonzero offsets.
+__host__ __device__ inline void conv_group(int T, int nib, int n_orb, int &q, int &ib) {
+    const int per_quad = 1 + 4 * n_orb, Q = T / per_quad, t = T % per_quad;
+    if (t == 0) {
+        q = -1;
+        ib = 4 * Q;
+        return;
+    }
+    q = (t - 1) % n_orb;
+    ib = 4 * Q + (t - 1) / n_orb;
+}
+
+// W'[o][c'][m] (c' the gathered channel, order above) from psi[o][i][m][ky][kx]: a gather, exact
+// (zeros for the filling channels). T: the 2- or 4-byte element (the value is copied bit for bit).
 template <typename T>
 __global__ __launch_bounds__(256) void k_conv_weight(const T *__restrict__ psi, int C_out, int C_in, int k,
                                                      T *__restrict__ wp) {
-    const int cg = C_in * k * k, nib = C_in / 16, r = k / 2;
+    const int cg = gathered(C_in, k), nib = C_in / 16, r = k / 2;
     const int64_t total = (int64_t)C_out * cg * 4;
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
         const int m = (int)(e & 3);
         const int c = (int)((e >> 2) % cg);
         const int o = (int)((e >> 2) / cg);
-        int q, ib, u;
-        conv_stage(c / 16, nib, q, ib, u);
-        const int i = ib * 16 + c % 16;
+        const int stage = c / 16, u = stage & 3;
+        int q, ib;
+        conv_group(stage >> 2, nib, (k * k - 1) / 4, q, ib);
+        if (q < 0) ib += u;  // centre: stage u is block 4 T + u
         int fy = 0, fx = 0;
         if (q >= 0) {
             orbit_rep(r, q, fy, fx);
             turn(fy, fx, -(m + u));  // R^-(m + u) delta0
         }
-        wp[e] = psi[((((int64_t)o * C_in + i) * 4 + m) * k + fy + r) * k + fx + r];
+        const int i = ib * 16 + c % 16;
+        wp[e] = ib < nib ? psi[((((int64_t)o * C_in + i) * 4 + m) * k + fy + r) * k + fx + r] : T(0);
     }
 }
 
 hipError_t launch_conv_weight(const void *psi, int elem_bytes, int C_out, int C_in, int k, void *wp, hipStream_t s) {
-    const int64_t total = (int64_t)C_out * C_in * k * k * 4;
+    const int64_t total = (int64_t)C_out * conv_gathered_channels(C_in, k) * 4;
     const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
     if (elem_bytes == 2)
         hipLaunchKernelGGL(k_conv_weight<uint16_t>, dim3(blocks), dim3(256), 0, s, (const uint16_t *)psi, C_out, C_in, k,
@@ -101,27 +116,31 @@ hipError_t launch_conv_weight(const void *psi, int elem_bytes, int C_out, int C_
     return hipGetLastError();
 }
 
-// The kernels' per-stage source table: .x the stage's byte offset into a pixel's row of x (channel
-// block ib: 16 channels x 4 samples x elem bytes), bytes g of .y / .z the pixel offset (dy, dx) that
-// sample g is read from, R^(g - u) delta0 (0 for the centre). Stages past the real ones (padding to
-// the kernels' stage multiple) repeat the first centre stage; their weights are zero.
-std::vector<uint4> conv_stage_table(int C_in, int k, int elem_bytes, int n_stages) {
-    const int nib = C_in / 16, r = k / 2, real = nib * k * k;
-    std::vector<uint4> tab((size_t)n_stages);
-    for (int s = 0; s < n_stages; ++s) {
-        int q, ib, u;
-        conv_stage(s < real ? s : 0, nib, q, ib, u);
-        uint32_t ys = 0, xs = 0;
-        for (int g = 0; g < 4; ++g) {
-            int dy = 0, dx = 0;
+// The kernels' per-group source table: row m's byte offset into a pixel's row of x (channel block:
+// 16 channels x 4 samples x elem bytes) in 16 bits m of .x, .y, and the pixel offset (dy, dx) it is
+// read from in byte m of .z, .w (R^m delta0 for an orbit group, 0 for the centre). Centre filling
+// rows re-read the last block (zero weights); groups past the real ones (the stage count is padded)
+// repeat the first centre group, their weights zero as well.
+std::vector<uint4> conv_group_table(int C_in, int k, int elem_bytes, int n_groups) {
+    const int nib = C_in / 16, r = k / 2, real = conv_gathered_channels(C_in, k) / 64;
+    std::vector<uint4> tab((size_t)n_groups);
+    for (int T = 0; T < n_groups; ++T) {
+        int q, ib;
+        conv_group(T < real ? T : 0, nib, (k * k - 1) / 4, q, ib);
+        uint32_t chan[4], ys = 0, xs = 0;
+        for (int m = 0; m < 4; ++m) {
+            int dy = 0, dx = 0, blk = ib;
             if (q >= 0) {
                 orbit_rep(r, q, dy, dx);
-                turn(dy, dx, g - u);
+                turn(dy, dx, m);
+            } else {
+                blk = std::min(ib + m, nib - 1);
             }
-            ys |= (uint32_t)(uint8_t)(int8_t)dy << (8 * g);
-            xs |= (uint32_t)(uint8_t)(int8_t)dx << (8 * g);
+            chan[m] = (uint32_t)(blk * 16 * 4 * elem_bytes);
+            ys |= (uint32_t)(uint8_t)(int8_t)dy << (8 * m);
+            xs |= (uint32_t)(uint8_t)(int8_t)dx << (8 * m);
         }
-        tab[s] = make_uint4((uint32_t)(ib * 16 * 4 * elem_bytes), ys, xs, 0u);
+        tab[T] = make_uint4(chan[0] | chan[1] << 16, chan[2] | chan[3] << 16, ys, xs);
     }
     return tab;
 }

@@ -73,9 +73,9 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
         e = eqlin::launch_prep_frag(W, true, p->dtype == EQLIN_F16, p->d4, p->G, p->C_out, p->C_in, p->KS, p->NB_total, p->fwd.frag_kind,
                                     p->planes, s);
         if (e != hipSuccess) return hip_fail(e, "spectral weight preparation");
-        if (p->conv_k > 0) {  // the gathered loads' stage table (one entry per stage of 16 gathered channels)
+        if (p->conv_k > 0) {  // the gathered loads' table (one entry per group of four stages of 16 channels)
             const int n_stages = p->G == 1 ? p->KS / 4 : p->KS;
-            const std::vector<uint4> tab = eqlin::conv_stage_table(p->conv_cin, p->conv_k, 2, n_stages);
+            const std::vector<uint4> tab = eqlin::conv_group_table(p->conv_cin, p->conv_k, 2, n_stages / 4);
             e = hipMalloc(&p->conv_tab, tab.size() * sizeof(uint4));
             if (e != hipSuccess) {
                 p->conv_tab = nullptr;
@@ -414,7 +414,8 @@ eqlin_status_t eqlin_prepare_conv_weights(const void *psi, int C_out, int C_in, 
     if (C_in % 16 != 0 || C_out % 8 != 0)
         return fail(EQLIN_ERR_UNSUPPORTED, "the convolution needs C_in %% 16 == 0 and C_out %% 8 == 0 (%d, %d)", C_in, C_out);
     if (flags & ~EQLIN_PREPARE_EXPANDED) return fail(EQLIN_ERR_UNSUPPORTED, "flags 0x%x: only EQLIN_PREPARE_EXPANDED", flags);
-    const int64_t cg = (int64_t)C_in * k * k;  // gathered channels
+    if (C_in > 8192) return fail(EQLIN_ERR_UNSUPPORTED, "the convolution takes C_in <= 8192 (got %d)", C_in);
+    const int64_t cg = eqlin::conv_gathered_channels(C_in, k);
     if (cg * G > (1 << 20) || (int64_t)C_out * G > (1 << 20))
         return fail(EQLIN_ERR_UNSUPPORTED, "channel counts beyond 2^20 unrolled columns");
     hipStream_t s = (hipStream_t)stream;

@@ -101,10 +101,15 @@ const char *bw_kernel_name(const Plan *p);
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
 
 // ---- conv.hip ----
-// psi[C_out][C_in][4][k][k] -> the gathered layer's weight W'[C_out][C_in * k * k][4] (2- or 4-byte elements)
+// gathered channels of the layer a k x k convolution over C_in channels runs as: C_in * k * k, plus the
+// zero channels that fill the centre's last group of four stages
+int conv_gathered_channels(int C_in, int k);
+// psi[C_out][C_in][4][k][k] -> the gathered layer's weight W'[C_out][conv_gathered_channels][4] (2- or
+// 4-byte elements; the filling channels' weights are zero)
 hipError_t launch_conv_weight(const void *psi, int elem_bytes, int C_out, int C_in, int k, void *wp, hipStream_t s);
-// the kernels' per-stage source table for n_stages stages (host side; uploaded by the caller)
-std::vector<uint4> conv_stage_table(int C_in, int k, int elem_bytes, int n_stages);
+// the kernels' source table, one entry per group of four stages, for n_groups groups (host side;
+// uploaded by the caller)
+std::vector<uint4> conv_group_table(int C_in, int k, int elem_bytes, int n_groups);
 
 // ---- prepare.hip ----
 // W [C_out][C_in][G] (16-bit elements of the half type when w_is_half, else fp32) -> fragment-ordered

@@ -174,11 +174,15 @@ struct BigCfg {
 // across tile boundaries, and a tile's outputs are stored while the next tile computes.
 //
 // CONV: the input channels are the gathered channels of a p4 group convolution (conv.hip): token n is
-// pixel n of a [B][img_h][img_w] grid, x holds x_elems elements per pixel, and stage s takes its
-// channels from conv_tab[s] -- a byte offset into the pixel's row (.x) and, for each group sample g,
-// the offset (dy, dx) of the pixel it is read from (bytes g of .y and .z, signed); pixels outside the
-// image read as zeros. An x item's G samples (its 2 channels, or 8 scalars at G = 1) then come from 4
-// loads, sample g from the g-th pixel: they are merged into the item's 16 bytes before the transform.
+// pixel n of a [B][img_h][img_w] grid and x holds x_elems elements per pixel. The stages come in groups
+// of four that read the same four rows (16-channel pieces of a pixel's row): conv_tab[group] gives for
+// row m its byte offset into the pixel's row (16 bits m of .x, .y) and the offset (dy, dx) of the
+// pixel it is read from (byte m of .z, .w, signed); pixels outside the image read as zeros. A centre
+// group (all offsets zero) is four channel blocks of the pixel itself, stage u reading row u; an orbit
+// group is the four rotated neighbours R^m delta0 of one channel block, stage u taking sample g from
+// row (g - u) mod 4 -- a gathered channel. Each row is loaded once per group (one row per stage, six
+// stages ahead of the group's first use), so the four stages of a group cost one load per stage; the
+// stage loop runs in bodies of 8 stages, so u and the two row sets are compile-time choices.
 template <int G, int WA, int WB, int OW, int TW, bool VEC, bool GELU, class E, bool CONV = false>
 __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ x4,
                                                       const uint4 *__restrict__ wfrag,
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     using C = BigCfg<G, WA, WB, OW, TW>;
     constexpr int KSS = C::KSS, NCH = C::NCH;
     static_assert(!CONV || (C::XU4 == 1 && (G == 4 || G == 1)), "gathered loads: one 16-byte piece per item");
-    constexpr int XL = CONV ? 4 : C::XU4;  // 16-byte loads per x item and stage
+    constexpr int XL = CONV ? 4 : C::XU4;  // raw x per item and ring slot: CONV, a group's four rows
     __shared__ uint4 lds[C::LDS_U4];  // two x-plane buffers, then each wave's output staging
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wo = wave % OW, wt = wave / OW;
@@ -248,26 +252,10 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     };
     // stage of the current tile (source src_c), or past its end: the next tile's (src_n)
     auto load_x = [&](const XSrc &src_c, const XSrc &src_n, int stage, uint4 (&dst)[C::ITEMS][XL]) {
-        const bool next = stage >= n_stages;  // uniform
-        const __amdgpu_buffer_rsrc_t rs = next ? src_n.rs : src_c.rs;
-        stage = next ? stage - n_stages : stage;
-        if constexpr (CONV) {
-            const uint4 t = conv_tab[stage];  // wave-uniform
-#pragma unroll
-            for (int it = 0; it < C::ITEMS; ++it) {
-                const int py = next ? src_n.py[it] : src_c.py[it];
-                const int px = next ? src_n.px[it] : src_c.px[it];
-                const int off = (next ? src_n.off[it] : src_c.off[it]) + (int)t.x;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int sy = (int)(signed char)(t.y >> (8 * g)), sx = (int)(signed char)(t.z >> (8 * g));
-                    const bool in = ((unsigned)(py + sy) < (unsigned)img_h) & ((unsigned)(px + sx) < (unsigned)img_w);
-                    const int vo = in ? off + (sy * img_w + sx) * x_row : 0x7fffffff;  // outside: zeros
-                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0);
-                    dst[it][g] = make_uint4(v.x, v.y, v.z, v.w);
-                }
-            }
-        } else {
+        if constexpr (!CONV) {  // (CONV loads rows of stage groups: load_row)
+            const bool next = stage >= n_stages;  // uniform
+            const __amdgpu_buffer_rsrc_t rs = next ? src_n.rs : src_c.rs;
+            stage = next ? stage - n_stages : stage;
             const int soff = stage * C::SC * G * 2;
             // channels past C_in (the stage count is padded) re-read the row's last channels: finite
             // values that meet zero weight columns
@@ -282,6 +270,42 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                 }
         }
     };
+    // CONV: the table entry of stage group `group` (past the tile's groups: the next tile's), wave-uniform
+    const int n_groups = n_stages >> 2;
+    auto group_entry = [&](int group) { return conv_tab[group < n_groups ? group : group - n_groups]; };
+    // CONV: row r of a stage group (table entry t; next: a group of the next tile) into dst[.][r]
+    auto load_row = [&](const XSrc &src_c, const XSrc &src_n, bool next, const uint4 &t, int r,
+                        uint4 (&dst)[C::ITEMS][XL]) {
+        const __amdgpu_buffer_rsrc_t rs = next ? src_n.rs : src_c.rs;
+        const int chan = (int)(((r < 2 ? t.x : t.y) >> (16 * (r & 1))) & 0xffffu);
+        const int sy = (int)(signed char)(t.z >> (8 * r)), sx = (int)(signed char)(t.w >> (8 * r));
+        const int d = chan + (sy * img_w + sx) * x_row;  // uniform
+#pragma unroll
+        for (int it = 0; it < C::ITEMS; ++it) {
+            const int py = next ? src_n.py[it] : src_c.py[it];
+            const int px = next ? src_n.px[it] : src_c.px[it];
+            const int off = next ? src_n.off[it] : src_c.off[it];
+            const bool in = ((unsigned)(py + sy) < (unsigned)img_h) & ((unsigned)(px + sx) < (unsigned)img_w);
+            const int vo = in ? off + d : 0x7fffffff;  // outside the image: zeros
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0);
+            dst[it][r] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
+    // CONV: the item of stage u of a group from its rows. Element e = j * 4 + g (channel j, sample g);
+    // orbit: element e of row (g - u) mod 4; centre: element e of row u.
+    auto merge = [&](auto uc, bool centre, const uint4 (&rows)[C::ITEMS][XL], uint4 (&src)[C::ITEMS][C::XU4]) {
+        constexpr int u = decltype(uc)::value;
+        auto mix = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b & 0xffff0000u); };
+#pragma unroll
+        for (int it = 0; it < C::ITEMS; ++it) {
+            const uint4 *R = rows[it];
+            const uint4 o = make_uint4(mix(R[(4 - u) & 3].x, R[(5 - u) & 3].x), mix(R[(6 - u) & 3].y, R[(7 - u) & 3].y),
+                                       mix(R[(4 - u) & 3].z, R[(5 - u) & 3].z), mix(R[(6 - u) & 3].w, R[(7 - u) & 3].w));
+            const uint4 c = R[u];
+            src[it][0] = make_uint4(centre ? c.x : o.x, centre ? c.y : o.y, centre ? c.z : o.z, centre ? c.w : o.w);
+        }
+    };
+    auto is_centre = [](const uint4 &t) { return (t.z | t.w) == 0u; };  // a centre group: no pixel offsets
     // weights: one resource per wave (its WA output blocks), block and stage as a scalar offset
     const int wo_u = __builtin_amdgcn_readfirstlane(wave) % OW;
     const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -297,20 +321,8 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
                 dst[a * KSS * G + r] = make_uint4(v.x, v.y, v.z, v.w);
             }
     };
-    auto dft_store = [&](const uint4 (&raw)[C::ITEMS][XL], uint4 *xb) {
-        // CONV: element e = j * 4 + g of an item (channel j, sample g) is element e of load g
-        uint4 src[C::ITEMS][C::XU4];
-#pragma unroll
-        for (int it = 0; it < C::ITEMS; ++it) {
-            if constexpr (CONV) {
-                auto mix = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b & 0xffff0000u); };
-                src[it][0] = make_uint4(mix(raw[it][0].x, raw[it][1].x), mix(raw[it][2].y, raw[it][3].y),
-                                        mix(raw[it][0].z, raw[it][1].z), mix(raw[it][2].w, raw[it][3].w));
-            } else {
-#pragma unroll
-                for (int q = 0; q < C::XU4; ++q) src[it][q] = raw[it][q];
-            }
-        }
+    // the transform of one stage's x items (for CONV the items merged from their group's rows)
+    auto dft_store = [&](const uint4 (&src)[C::ITEMS][C::XU4], uint4 *xb) {
 #pragma unroll
         for (int it = 0; it < C::ITEMS; ++it) {
             const int item = tid + it * C::NT;
@@ -371,15 +383,27 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     }
 
     // ---- prologue: weights of stage 0 and raw x of positions 0 and 1 requested; x(0) transformed ----
+    // (CONV: the rows of stage group 0 and rows 0, 1 of group 1 -- what stages -6 .. -1 would load)
     uint4 xr[2][C::ITEMS][XL];
     uint4 wr[2][C::WF];
     load_w(0, wr[0]);
     {
         const XSrc rs0 = x_src(0);
-        load_x(rs0, rs0, 0, xr[0]);
-        load_x(rs0, rs0, 1, xr[1]);
+        if constexpr (CONV) {
+            const uint4 t0 = group_entry(0), t1 = group_entry(1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) load_row(rs0, rs0, false, t0, r, xr[0]);
+            load_row(rs0, rs0, false, t1, 0, xr[1]);
+            load_row(rs0, rs0, false, t1, 1, xr[1]);
+            uint4 xm[C::ITEMS][C::XU4];
+            merge(IC<0>{}, is_centre(t0), xr[0], xm);
+            dft_store(xm, lds);
+        } else {
+            load_x(rs0, rs0, 0, xr[0]);
+            load_x(rs0, rs0, 1, xr[1]);
+            dft_store(xr[0], lds);
+        }
     }
-    dft_store(xr[0], lds);
     lds_barrier();
 
     f32x16 acc[WA][WB][G];
@@ -414,9 +438,13 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
     // stores.
     // The next stage's products then wait for its weights only, with the raw x still in flight
     // (vector-memory operations complete in issue order).
-    auto step = [&](auto first, const XSrc &xrs_c, const XSrc &xrs_n, int s, uint4 (&x_free)[C::ITEMS][XL],
+    // CONV (bc: the stage's place b in its body of 8): the item of stage s + 1 is merged from its group's
+    // rows in the first half, ahead of the second half's row load, which at b = 2 and 6 overwrites a row
+    // of the set that merge reads; the load is row (b + 2) mod 4 of group (s + 6) / 4.
+    auto step = [&](auto first, auto bc, const XSrc &xrs_c, const XSrc &xrs_n, int s, uint4 (&x_free)[C::ITEMS][XL],
                     const uint4 (&x_next)[C::ITEMS][XL], const uint4 (&w_cur)[C::WF], uint4 (&w_next)[C::WF],
-                    const uint4 *planes, uint4 *planes_next, __amdgpu_buffer_rsrc_t rs_prev, bool has_prev) {
+                    const uint4 *planes, uint4 *planes_next, __amdgpu_buffer_rsrc_t rs_prev, bool has_prev,
+                    const uint4 (&tg)[4], int g0) {
         constexpr int P = KSS * WB, H = P / 2;
         // the second half's planes are read with the first half's when they fit in 4 registers of 16
         // bytes, so its products do not wait for LDS after the first half's
@@ -433,11 +461,18 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
         if constexpr (PRE)
 #pragma unroll
             for (int q = H; q < P; ++q) read_planes(q, planes, xb[q - H]);
+        constexpr int b = decltype(bc)::value;
+        uint4 xm[C::ITEMS][C::XU4];
+        // (CONV: stage s + 1 is in group g0 + (b + 1) / 4, the row load's group is g0 + (b + 6) / 4)
+        if constexpr (CONV) merge(IC<(b + 1) % 4>{}, is_centre(tg[(b + 1) / 4]), xr[((b + 1) / 4) % 2], xm);
 #pragma unroll
         for (int q = 0; q < H; ++q) products(first, q, xa[q], w_cur, w_neg);
         interleave_stage<(PRE ? P : H) * G, H * WA * real_products(G), C::WF, 1>();
         __builtin_amdgcn_sched_barrier(0);
-        load_x(xrs_c, xrs_n, s + 2, x_free);
+        if constexpr (CONV)
+            load_row(xrs_c, xrs_n, g0 + (b + 6) / 4 >= n_groups, tg[(b + 6) / 4], (b + 2) % 4, xr[((b + 6) / 4) % 2]);
+        else
+            load_x(xrs_c, xrs_n, s + 2, x_free);
         uint4 sv[C::SPS];
 #pragma unroll
         for (int i = 0; i < C::SPS; ++i) sv[i] = read_staged(min(s * C::SPS + i, C::NSTORE - 1));
@@ -446,9 +481,12 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
             for (int q = H; q < P; ++q) read_planes(q, planes, xb[q - H]);
 #pragma unroll
         for (int q = H; q < P; ++q) products(first, q, xb[q - H], w_cur, w_neg);
-        dft_store(x_next, planes_next);  // past the last position: unused planes, harmless
-        interleave_stage<(PRE ? 0 : (P - H) * G) + C::SPS, (P - H) * WA * real_products(G), C::ITEMS * XL,
-                         C::VPM>();
+        if constexpr (CONV)
+            dft_store(xm, planes_next);
+        else
+            dft_store(x_next, planes_next);  // past the last position: unused planes, harmless
+        constexpr int XLOADS = CONV ? C::ITEMS : C::ITEMS * XL;  // x loads per stage
+        interleave_stage<(PRE ? 0 : (P - H) * G) + C::SPS, (P - H) * WA * real_products(G), XLOADS, C::VPM>();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < C::SPS; ++i) {
@@ -478,15 +516,54 @@ __global__ __launch_bounds__(OW * TW * 64) void k_big(const uint4 *__restrict__ 
         // n_stages is even (the channel padding sees to it); for G >= 2 the first pair is peeled so
         // the first products can start the accumulators of planes 1.. without clearing them (G = 1
         // has only the bias plane)
-        int s0 = 0;
-        if constexpr (G >= 2) {
-            step(IC<1>{}, xrs_c, xrs_n, 0, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
-            step(IC<0>{}, xrs_c, xrs_n, 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
-            s0 = 2;
-        }
-        for (int s = s0; s < n_stages; s += 2) {
-            step(IC<0>{}, xrs_c, xrs_n, s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev, has_prev);
-            step(IC<0>{}, xrs_c, xrs_n, s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev, has_prev);
+        if constexpr (CONV) {
+            // n_stages is a multiple of 8: bodies of 8 stages, so each stage's place in its group of
+            // four and the row set it uses are fixed; planes 1.. start from zero (no peeled first stage)
+#pragma unroll
+            for (int a = 0; a < WA; ++a)
+#pragma unroll
+                for (int b = 0; b < WB; ++b)
+#pragma unroll
+                    for (int p = 1; p < G; ++p) acc[a][b][p] = f32x16{};
+            uint4(&x0)[C::ITEMS][XL] = xr[0];
+            for (int s = 0; s < n_stages; s += 8) {
+                // the table entries of the body's groups, read before its first stage: scalar loads
+                // share the LDS wait counter, so waiting for one inside a stage would also wait for
+                // that stage's LDS reads (the barrier that ended the last stage has drained the LDS)
+                const int g0 = s >> 2;
+                uint4 tg[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) tg[j] = group_entry(g0 + j);
+                __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+                __builtin_amdgcn_sched_barrier(0);
+#define CONV_STEP(B, WC, WN, PL, PN)                                                                        \
+    step(IC<0>{}, IC<B>{}, xrs_c, xrs_n, s + B, x0, x0, wr[WC], wr[WN], PL, PN, rs_prev, has_prev, tg, g0)
+                CONV_STEP(0, 0, 1, lds, lds + C::XST);
+                CONV_STEP(1, 1, 0, lds + C::XST, lds);
+                CONV_STEP(2, 0, 1, lds, lds + C::XST);
+                CONV_STEP(3, 1, 0, lds + C::XST, lds);
+                CONV_STEP(4, 0, 1, lds, lds + C::XST);
+                CONV_STEP(5, 1, 0, lds + C::XST, lds);
+                CONV_STEP(6, 0, 1, lds, lds + C::XST);
+                CONV_STEP(7, 1, 0, lds + C::XST, lds);
+#undef CONV_STEP
+            }
+        } else {
+            const uint4 no_tab[4] = {};
+            int s0 = 0;
+            if constexpr (G >= 2) {
+                step(IC<1>{}, IC<0>{}, xrs_c, xrs_n, 0, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev,
+                     has_prev, no_tab, 0);
+                step(IC<0>{}, IC<0>{}, xrs_c, xrs_n, 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev,
+                     has_prev, no_tab, 0);
+                s0 = 2;
+            }
+            for (int s = s0; s < n_stages; s += 2) {
+                step(IC<0>{}, IC<0>{}, xrs_c, xrs_n, s, xr[0], xr[1], wr[0], wr[1], lds, lds + C::XST, rs_prev,
+                     has_prev, no_tab, 0);
+                step(IC<0>{}, IC<0>{}, xrs_c, xrs_n, s + 1, xr[1], xr[0], wr[1], wr[0], lds + C::XST, lds, rs_prev,
+                     has_prev, no_tab, 0);
+            }
         }
         // stores of the previous tile that did not fit in this tile's stages
         if (has_prev)
@@ -922,6 +999,7 @@ static hipError_t launch_big_conv(const Plan *p, const void *x, const void *b, v
     const int64_t tiles_t = (N + C::BT - 1) / C::BT;
     const int tiles_o = p->NB_total / (C::BO / 32);
     const int n_stages = p->KS / C::KSS;
+    if (n_stages % 8 != 0) return hipErrorInvalidValue;  // the stage loop's bodies of 8
     const int x_elems = p->conv_cin * 4;  // elements per pixel row of x (C_in channels x 4 samples)
     // x is one buffer resource addressed with 32-bit offsets; output rows as in launch_big
     if (tiles_t > 0x7fffffff || (int64_t)C::BT * p->C_out * G * 2 > 0x7fffffff || N * x_elems * 2 > 0x7fffffff)
@@ -960,14 +1038,40 @@ static const BigEntry kBig[] = {
 };
 #undef BE
 
-bool select_big_conv(int G, int C_in, int C_out, KernelChoice *out) {
-    if (G != 4 && G != 1) return false;
-    if (!select_big(G, false, C_in, C_out, out)) return false;
-    if ((C_out * G) % 8 != 0) return false;  // whole 16-byte pieces per output row
-    out->conv_launch = G == 4 ? launch_big_conv<4, 1, 2, 8, 1> : launch_big_conv<1, 2, 4, 8, 1>;
+// The gathered-load tiles: G = 4 as the layer's (8 waves, two per SIMD); the unrolled comparator
+// (G = 1) on 4 waves, one per SIMD: its two x items per thread keep two sets of four rows each in
+// registers, which 8 waves' 256 registers per wave cannot hold beside the 2x4 blocks' accumulators
+// (spilled: 606 us vs 333 us at 3x3 256->256 over 4x64x64 pixels).
+template <int G, int WA, int WB, int OW, int TW>
+static void conv_choice(KernelChoice *out) {
+    using C = BigCfg<G, WA, WB, OW, TW>;
+    out->kind = KIND_BIG;
+    out->frag_kind = 2;
+    out->rows_per_block = 32;
+    out->kc = 16;
+    out->ks_mult = 8 * C::KSS;  // stages in bodies of 8 (two groups of four that share their rows)
+    out->nb_tile = C::BO / 32;
+    out->tokens_per_block = C::BT;
+    out->block_threads = C::NT;
+    out->lds_bytes = C::LDS;
+    out->num_cus = device_num_cus();
     out->launch = nullptr;  // a convolution plan runs only through conv_launch
-    const size_t n = strlen(out->name);
-    snprintf(out->name + n, sizeof(out->name) - n, " gathered");
+    out->conv_launch = launch_big_conv<G, WA, WB, OW, TW>;
+    snprintf(out->name, sizeof(out->name), "bf16 big G=%d BO=%d BT=%d (%dx%d blocks/wave, %dx%d waves) mfma32x32x16 gathered",
+             G, C::BO, C::BT, WA, WB, OW, TW);
+}
+
+bool select_big_conv(int G, int C_in, int C_out, KernelChoice *out) {
+    (void)C_in;
+    if (G != 4 && G != 1) return false;
+    if ((C_out * G) % 8 != 0) return false;  // whole 16-byte pieces per output row
+    if (G == 4) {
+        if ((int64_t)BigCfg<4, 1, 2, 8, 1>::BT * C_out * G * 2 > 0x7fffffff) return false;
+        conv_choice<4, 1, 2, 8, 1>(out);
+    } else {
+        if ((int64_t)BigCfg<1, 2, 4, 4, 1>::BT * C_out * G * 2 > 0x7fffffff) return false;
+        conv_choice<1, 2, 4, 4, 1>(out);
+    }
     return true;
 }
 

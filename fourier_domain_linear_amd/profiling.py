@@ -7,7 +7,7 @@
     # each scaled by what the same counter reads for a plain device copy of known size
     python -m fourier_domain_linear_amd.profiling traffic --kernel k_stream \
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes B \
-        --workload NAME --cmd "..." --out profiles/traffic_NAME.json
+        --workload NAME --cmd "..." --out profiles/traffic_NAME.json [--family k_conv]
 
     # matrix-core utilisation from one counter run (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA
     # SQ_INSTS_VALU GRBM_GUI_ACTIVE)
@@ -127,9 +127,9 @@ def cmd_traffic(a):
     f_scale = a.copy_bytes / _avg(cfetch)
     w_scale = a.copy_bytes / _avg(cwrite)
     rd, wr = _avg(fetch) * f_scale, _avg(write) * w_scale
+    srcs = KERNEL_SOURCES[a.family] if a.family else sources_for(a.kernel)
     rec = {
-        "workload": a.workload, "kernel": a.kernel, "sources": sources_for(a.kernel),
-        "source_sha256": kernel_source_hash(sources_for(a.kernel)),
+        "workload": a.workload, "kernel": a.kernel, "sources": srcs, "source_sha256": kernel_source_hash(srcs),
         "fetch_kib_per_dispatch": _avg(fetch), "write_kib_per_dispatch": _avg(write),
         "copy_bytes": a.copy_bytes, "copy_fetch_kib": _avg(cfetch), "copy_write_kib": _avg(cwrite),
         "fetch_scale_bytes_per_kib": f_scale, "write_scale_bytes_per_kib": w_scale,
@@ -201,6 +201,9 @@ def main(argv=None):
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--workload", required=True)
+    t.add_argument("--family", choices=sorted(KERNEL_SOURCES), default=None,
+                   help="the kernel family whose sources the record covers (default: by the name's prefix; "
+                        "the gathered-load k_big instances are k_conv)")
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
     m = sub.add_parser("mfma")

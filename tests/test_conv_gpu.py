@@ -42,7 +42,8 @@ def _check(y_gpu, ref, label, dtype="bf16"):
 
 CASES = [  # B, H, W, C_in, C_out, k
     (2, 9, 7, 16, 8, 3), (1, 12, 12, 32, 256, 3), (3, 5, 6, 16, 264, 5), (1, 1, 1, 16, 8, 3),
-    (2, 17, 19, 48, 296, 3), (1, 6, 6, 64, 512, 1), (4, 2, 3, 16, 16, 5), (1, 30, 31, 32, 64, 3)]
+    (2, 17, 19, 48, 296, 3), (1, 6, 6, 64, 512, 1), (4, 2, 3, 16, 16, 5), (1, 30, 31, 32, 64, 3),
+    (2, 7, 9, 80, 40, 3), (1, 8, 5, 48, 24, 5)]
 
 
 @pytest.mark.parametrize("with_bias", [True, False], ids=["bias", "nobias"])
