@@ -236,7 +236,8 @@ eqlin_status_t eqlin_backward_weights_static(eqlin_handle_t h, const void *x, co
  * EQ-Linear layer over C_in * k * k gathered channels -- for each orbit {R^j delta0} of offsets,
  * gathered channel (i, delta0, u) holds sample g of pixel p + R^(g - u) delta0 -- whose weight
  * psi[o, i, m, R^-(m + u) delta0] depends on h - g alone, so the group DFT diagonalises it; the gather
- * happens while x is loaded (one load address per sample), in the layer's own spectral kernel.
+ * happens while x is loaded, in the layer's own spectral kernel: the four gathered channels u of one
+ * (orbit, 16-channel block) read the same four neighbour rows, each loaded once.
  *
  * Layouts (row-major, contiguous): x[B][H][W][C_in][4], y[B][H][W][C_out][4] (one token per pixel, the
  * layer's rows), psi[C_out][C_in][4][k][k] (psi[o][i][d][ky][kx]: the filter at offset
@@ -245,11 +246,14 @@ eqlin_status_t eqlin_backward_weights_static(eqlin_handle_t h, const void *x, co
  *
  * eqlin_prepare_conv_weights -- psi -> the gathered layer's spectral weights (and, with
  * EQLIN_PREPARE_EXPANDED, its unrolled weight for eqlin_conv_forward_expanded).
- *   G must be 4 and k odd in 1..15 (else EQLIN_ERR_INVALID_ARG); C_in % 16 == 0, C_out % 8 == 0, dtype
- *   EQLIN_BF16 or EQLIN_F16 and flags within EQLIN_PREPARE_EXPANDED (else EQLIN_ERR_UNSUPPORTED).
+ *   G must be 4 and k odd in 1..15 (else EQLIN_ERR_INVALID_ARG); C_in % 16 == 0, C_in <= 8192,
+ *   C_out % 8 == 0, dtype EQLIN_BF16 or EQLIN_F16 and flags within EQLIN_PREPARE_EXPANDED (else
+ *   EQLIN_ERR_UNSUPPORTED).
  *   Allocates device memory; synchronises nothing; psi may be freed once `stream` has passed the call.
  *   The handle serves eqlin_conv_forward(_expanded), eqlin_describe, eqlin_export_* (the gathered
- *   layer's weights, C_in * k * k input channels) and eqlin_destroy; the layer's entry points reject it.
+ *   layer's weights: C_in * k * k input channels, plus zero-weight filling channels up to a multiple of
+ *   64 centre channels when C_in / 16 is not a multiple of 4) and eqlin_destroy; the layer's entry
+ *   points reject it.
  * eqlin_conv_forward -- y from x for B images of H x W pixels (B, H, W >= 0; an empty batch enqueues
  *   nothing). bias may be NULL. B * H * W * C_in * 8 must stay below 2^31 (x is addressed with 32-bit
  *   offsets; else EQLIN_ERR_UNSUPPORTED). Alignment, overlap, device and stream rules as eqlin_forward;
