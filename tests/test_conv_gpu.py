@@ -9,8 +9,9 @@ kernel as the layer; the expanded comparator runs the same gathered layer as one
 Bars: the layer's -- bf16: relative Frobenius error <= 1e-2 AND max abs error <= 3e-2 (the inputs'
 variances give outputs of about unit scale, as for the layer); fp16: the bf16 bars / 8.
 Sizes: small images with ragged token counts (several tiles, a partial one, images smaller than the
-filter, one-pixel images), k = 1, 3, 5, C_out not a multiple of the output tile; and the benchmark's
-shape at full size with every output compared.
+filter, one-pixel images), k = 1, 3, 5, 7, 9, C_out not a multiple of the output tile, C_in / 16 not a
+multiple of 4 (the centre's last group part filling); and the benchmark's shape at full size with
+every output compared.
 """
 import ctypes
 
@@ -43,7 +44,7 @@ def _check(y_gpu, ref, label, dtype="bf16"):
 CASES = [  # B, H, W, C_in, C_out, k
     (2, 9, 7, 16, 8, 3), (1, 12, 12, 32, 256, 3), (3, 5, 6, 16, 264, 5), (1, 1, 1, 16, 8, 3),
     (2, 17, 19, 48, 296, 3), (1, 6, 6, 64, 512, 1), (4, 2, 3, 16, 16, 5), (1, 30, 31, 32, 64, 3),
-    (2, 7, 9, 80, 40, 3), (1, 8, 5, 48, 24, 5)]
+    (2, 7, 9, 80, 40, 3), (1, 8, 5, 48, 24, 5), (1, 9, 10, 32, 16, 7), (1, 5, 4, 16, 8, 9)]
 
 
 @pytest.mark.parametrize("with_bias", [True, False], ids=["bias", "nobias"])
@@ -143,6 +144,11 @@ def test_conv_argument_errors(cuda_device):
     assert lib.eqlin_conv_forward(H, X, None, Y, 2, 3, 5, s) == eq.EQLIN_OK
     assert lib.eqlin_conv_forward(H, X, None, Y, -1, 3, 5, s) == eq.EQLIN_ERR_INVALID_ARG
     assert lib.eqlin_conv_forward(H, X, None, Y, 2, 3, 0, s) == eq.EQLIN_OK  # empty image: nothing to do
+    # a batch whose x would span more than 2^31 bytes is refused on the host before any launch (with
+    # these small buffers the extents that size implies overlap y, which is checked first; the
+    # buffers are never touched)
+    assert lib.eqlin_conv_forward(H, X, None, Y, 5000, 64, 64, s) in (eq.EQLIN_ERR_INVALID_ARG,
+                                                                      eq.EQLIN_ERR_UNSUPPORTED)
     # a convolution handle is not a layer handle, and the other way round
     assert lib.eqlin_forward(H, X, None, Y, 30, s) == eq.EQLIN_ERR_INVALID_ARG
     assert lib.eqlin_conv_forward_expanded(H, X, None, Y, 2, 3, 5, s) == eq.EQLIN_ERR_INVALID_ARG  # no EXPANDED flag
