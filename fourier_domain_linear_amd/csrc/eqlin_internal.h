@@ -18,7 +18,9 @@ enum KernelKind {
     KIND_BIG = 1,       // bf16, large C: persistent workgroups, each keeping one output tile and
                         // walking token tiles on 32x32x16 matrix cores; x planes transformed once per
                         // stage into LDS, weights straight to registers, outputs stored a tile later
-    KIND_F32 = 2        // fp32: vector-ALU spectral kernel
+    KIND_F32 = 2,       // fp32: vector-ALU spectral kernel
+    KIND_RES = 3        // bf16, G = 4, C_in planes fit on chip: one token tile per workgroup, its
+                        // planes resident in LDS for every output block, weights streamed per wave
 };
 
 struct Plan;
@@ -87,6 +89,8 @@ int device_num_cus();  // compute units of the current device (queried once)
 bool select_big(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 // the gathered-load (convolution) instance for G = 4 (spectral) or G = 1 (the unrolled comparator)
 bool select_big_conv(int G, int C_in, int C_out, KernelChoice *out);
+// ---- fwd_res.hip ----
+bool select_res(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 // ---- fwd_f32.hip ----
 bool select_f32(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 
