@@ -40,16 +40,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel sources (else None)."""
+def load_traffic(workload: str, kernel_desc: str | None = None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the kernel
+    family the plan runs (kernel_desc: the plan's forward kernel name) and on its current sources (else
+    None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    from fourier_domain_linear_amd.profiling import kernel_source_hash
+    from fourier_domain_linear_amd.profiling import KERNEL_SOURCES, family_of_plan, kernel_source_hash
 
+    rec_family = next((f for f in sorted(KERNEL_SOURCES, key=len, reverse=True) if rec.get("kernel", "").startswith(f)),
+                      None)
+    if kernel_desc is not None and rec_family != family_of_plan(kernel_desc):
+        log(f"[bench] {path} was taken on another kernel ({rec.get('kernel')}): traffic = null")
+        return None
     if rec.get("source_sha256") != kernel_source_hash(rec.get("sources")):
         log(f"[bench] {path} was taken on other kernel sources: traffic = null")
         return None
@@ -533,7 +539,7 @@ def main():
     else:
         achieved, peak, unit = F / t / 1e12, peak_c, "TFLOP/s"
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name),
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name, rec["kernel"]),
             "kernel": rec["kernel"] + " (one launch per step)",
             "algorithmic_bytes_per_launch": B, "algorithmic_flops_per_launch": F,
             "mfma_frac": rec["mfma_frac"], "hbm_frac": rec["hbm_frac"]}

@@ -36,7 +36,21 @@ KERNEL_SOURCES = {
     "k_big": ["fourier_domain_linear_amd/csrc/fwd_big.hip"] + _COMMON,
     "k_p8": ["fourier_domain_linear_amd/csrc/fwd_big.hip"] + _COMMON,
     "k_conv": ["fourier_domain_linear_amd/csrc/fwd_big.hip", "fourier_domain_linear_amd/csrc/conv.hip"] + _COMMON,
+    "k_res": ["fourier_domain_linear_amd/csrc/fwd_res.hip"] + _COMMON,
 }
+
+
+def family_of_plan(desc: str) -> str:
+    """The kernel family a plan's forward runs, from its name in eqlin_describe's forward field."""
+    if "resident" in desc:
+        return "k_res"
+    if "stream" in desc:
+        return "k_stream"
+    if "gathered" in desc:
+        return "k_conv"
+    if "big" in desc:
+        return "k_p8" if ("G=8" in desc or "D4" in desc) else "k_big"
+    return "other"
 
 
 def sources_for(kernel: str) -> list:
