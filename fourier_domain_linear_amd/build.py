@@ -28,13 +28,17 @@ CXXFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
-SOURCES = ["eqlin_api.cpp", "prepare.hip", "fwd_bf16.hip", "fwd_big.hip", "fwd_res.hip", "fwd_f32.hip", "bwd.hip", "conv.hip"]
+# Per-file device flags. fwd_res8.hip: matrix-core results in ordinary vector registers (the weight ring
+# and plane operands, which loads can fill directly, take the accumulator registers instead), so the
+# epilogue reads its eleven accumulators without a copy per value and no register is spilled.
+FILE_FLAGS = {"fwd_res8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCES = ["eqlin_api.cpp", "prepare.hip", "fwd_bf16.hip", "fwd_big.hip", "fwd_res.hip", "fwd_res8.hip", "fwd_f32.hip", "bwd.hip", "conv.hip"]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *CXXFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CXXFLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)

@@ -55,11 +55,14 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
     if (p->dtype != EQLIN_F32) {  // bf16 or fp16: the matrix-core kernels
         bool ok = p->conv_k > 0 ? eqlin::select_big_conv(p->G, p->C_in, p->C_out, &p->fwd)
                                 : eqlin::select_bf16(p->G, p->d4, p->C_in, p->C_out, &p->fwd);
-        // p4 layers too wide for the stream kernel whose input planes fit on chip: the resident-planes
-        // kernel (one token tile per workgroup, each token transformed once) instead of the large-channel one
+        // layers too wide for the stream kernel whose input planes fit on chip: the resident-planes
+        // kernels (a token tile's planes kept for every output block, each token transformed once per
+        // workgroup) instead of the large-channel ones
         if (ok && p->conv_k == 0 && p->fwd.kind == eqlin::KIND_BIG) {
             eqlin::KernelChoice r;
-            if (eqlin::select_res(p->G, p->d4, p->C_in, p->C_out, &r)) p->fwd = r;
+            if (eqlin::select_res(p->G, p->d4, p->C_in, p->C_out, &r) ||
+                eqlin::select_res8(p->G, p->d4, p->C_in, p->C_out, &r))
+                p->fwd = r;
         }
         if (!ok)
             return fail(EQLIN_ERR_UNSUPPORTED, "no half-precision kernel for G=%d C_in=%d C_out=%d", p->G, p->C_in,

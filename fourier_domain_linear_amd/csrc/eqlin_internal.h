@@ -91,6 +91,7 @@ bool select_big(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 bool select_big_conv(int G, int C_in, int C_out, KernelChoice *out);
 // ---- fwd_res.hip ----
 bool select_res(int G, bool d4, int C_in, int C_out, KernelChoice *out);
+bool select_res8(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 // ---- fwd_f32.hip ----
 bool select_f32(int G, bool d4, int C_in, int C_out, KernelChoice *out);
 

@@ -43,7 +43,7 @@ KERNEL_SOURCES = {
 def family_of_plan(desc: str) -> str:
     """The kernel family a plan's forward runs, from its name in eqlin_describe's forward field."""
     if "resident" in desc:
-        return "k_res"
+        return "k_res8" if ("G=8" in desc or "D4" in desc) else "k_res"
     if "stream" in desc:
         return "k_stream"
     if "gathered" in desc:

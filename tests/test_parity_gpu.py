@@ -91,7 +91,8 @@ def test_workload_full_size_all_tokens(w, cuda_device):
 @pytest.mark.parametrize("with_bias", [True, False], ids=["bias", "nobias"])
 @pytest.mark.parametrize("expanded", [False, True], ids=["spectral", "expanded"])
 @pytest.mark.parametrize("G,C_in,C_out", [(4, 128, 4096), (8, 64, 2048), (4, 128, 4095), (2, 128, 4096),
-                                          (1, 256, 4096), (8, 200, 1024), (4, 200, 2048), (4, 384, 4095)])
+                                          (1, 256, 4096), (8, 200, 1024), (4, 200, 2048), (4, 384, 4095),
+                                          (8, 320, 1024)])
 def test_large_channel_multi_tile(G, C_in, C_out, expanded, with_bias, cuda_device):
     if expanded and G == 1:
         pytest.skip("G = 1 has no separate expanded form")
@@ -104,9 +105,9 @@ def test_large_channel_multi_tile(G, C_in, C_out, expanded, with_bias, cuda_devi
     h, y = _run(x, W, b, cuda_device, expanded)
     desc = h.describe()
     print(f"[kernel] {desc}", flush=True)
-    # (G = 4 with C_in up to 320: the resident-planes kernel, which keeps a token tile's planes on chip)
+    # (G = 4 and 8 with C_in up to 256: the resident-planes kernels, which keep a token tile's planes on chip)
     kern = desc.split("|")[2 if expanded else 1]
-    assert "big" in kern or (G == 4 and C_in <= 320 and not expanded and "resident" in kern), desc
+    assert "big" in kern or (G in (4, 8) and C_in <= 256 and not expanded and "resident" in kern), desc
     _check(y, oracle.forward(x, W, b), "bf16",
            f"G={G} {C_in}->{C_out} N={N} {'expanded' if expanded else 'spectral'} all tokens")
 
