@@ -14,10 +14,12 @@
 // (8 KB per 16 channels, 128 KB at 256) stay in LDS while the workgroup computes output blocks against
 // them, so a token is transformed once per workgroup that touches its tile, not once per output tile.
 //   - Work units are (token tile, quad of four 32-output blocks), tile-major. The workgroups are
-//     persistent, one per compute unit, and workgroup b takes units [b U / grid, (b + 1) U / grid) of
-//     the U units: every compute unit gets the same number of units to within one, whatever N is (at
-//     12544 tokens and 1024 outputs: 3136 units over 256 CUs, 12 or 13 each). A range covers parts of
-//     one or a few tiles; each tile's planes are filled during the first quad the workgroup runs on it.
+//     persistent, one per compute unit, and each takes a contiguous range of units. A range covers
+//     parts of one or a few tiles, and each tile's planes are filled during the first quad the
+//     workgroup runs on it; a filling quad costs about 2.5 later ones, so the launch balances the
+//     ranges on that cost, not on the unit count (at 12544 tokens and 1024 outputs: 3136 units over
+//     256 CUs; equal counts leave 32 CUs with 13 quads and three fills, the balanced ranges give at
+//     most 13 quads with two fills or 12 with three, and leave a few CUs idle).
 //   - Four waves, one per SIMD (512 registers each): wave w computes block 4 q + w of quad q and
 //     streams only that block's weight fragments from L2, through a register ring four 16-channel
 //     steps deep, so the waves wait for each other only while a tile's planes are being filled.
@@ -48,7 +50,7 @@ namespace {
 
 constexpr int kR8Waves = 4, kR8Threads = kR8Waves * 64;
 constexpr int kR8BT = 32;                    // tokens per tile (one matrix-core block)
-constexpr int kR8Ring = 4;                   // weight steps in flight per wave (16 channels each)
+constexpr int kR8Ring = 4;                   // weight steps in flight per wave (16 channels each; 4 or 8)
 constexpr int kR8MaxKS = 16;                 // 16-channel steps of planes (8 KB each; C_in <= 256), plus
 constexpr int kR8LdsSteps = kR8MaxKS + 2;    // two spare steps that past-the-end parts are written to
 constexpr int kR8StoreAux = 2;               // output stores non-temporal
@@ -75,7 +77,7 @@ __device__ __forceinline__ int r8_chunk(int ks, int p) { return (ks * 8 + p) * 6
 // accumulators from zero). The order keeps every accumulator's two products apart.
 template <bool F, bool D4, class E>
 __device__ __forceinline__ void r8_products(const uint4 (&x)[8], const uint4 (&w)[8], f32x16 (&acc)[kR8Acc]) {
-    auto c = [&](int a) { return F ? f32x16{} : acc[a]; };
+    auto c = [&](int a) __attribute__((always_inline)) { return F ? f32x16{} : acc[a]; };
     if constexpr (D4) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) acc[p] = mma32<E>(x[p], w[p], c(p));
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(kR8Threads) void k_res8(const uint4 *__restrict__ x
     // all weight fragments: block ob, step ks, plane p at chunk (ob KS + ks) 8 + p
     const __amdgpu_buffer_rsrc_t w_rs =
         __builtin_amdgcn_make_buffer_rsrc((void *)wfrag, (short)0, NQ * 4 * KS * G * 1024, 0x00020000);
-    auto load_w = [&](int q, int ks, uint4 (&dst)[8]) {
+    auto load_w = [&](int q, int ks, uint4 (&dst)[8]) __attribute__((always_inline)) {
         // (wave-uniform; said so, or the compiler may wrap each load in a loop over distinct values)
         const int soff = __builtin_amdgcn_readfirstlane(((4 * q + wave) * KS + ks) * G * 1024);
 #pragma unroll
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kR8Threads) void k_res8(const uint4 *__restrict__ x
     };
     // raw x of step s: thread (token tl, channel pair cq) reads channels 16 s + 2 cq, + 1 (32 bytes)
     const int tl = tid >> 3, cq = tid & 7;
-    auto load_x = [&](__amdgpu_buffer_rsrc_t x_rs, int s, uint4 (&dst)[2]) {
+    auto load_x = [&](__amdgpu_buffer_rsrc_t x_rs, int s, uint4 (&dst)[2]) __attribute__((always_inline)) {
         const int c = s * 16 + 2 * cq;
         const int vo = c < C_in ? tl * x_row + c * G * 2 : 0x7fffffff;  // channels past C_in: zeros
 #pragma unroll
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kR8Threads) void k_res8(const uint4 *__restrict__ x
     // transform of step s's pair into the planes: one 32-bit word (two channels) per plane
     uint32_t *const pw = reinterpret_cast<uint32_t *>(planes);
     const int slot = (tl + 32 * (cq >> 2)) * 4 + (cq & 3);
-    auto dft_store = [&](int s, const uint4 (&r)[2]) {
+    auto dft_store = [&](int s, const uint4 (&r)[2]) __attribute__((always_inline)) {
         float pl[G][2];
         dft_ch8<D4, E>(r, pl);
 #pragma unroll
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(kR8Threads) void k_res8(const uint4 *__restrict__ x
 
     // output column of this lane in block ob: o = 32 ob + lane % 32
     const int ocol = lane & 31, hrow = lane >> 5;
-    auto bias_bits = [&](int q) -> uint32_t {
+    auto bias_bits = [&](int q) __attribute__((always_inline)) -> uint32_t {
         const int o = 32 * (4 * q + wave) + ocol;
         return (bias && o < C_out) ? (uint32_t)bias[o] : 0u;
     };
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(kR8Threads) void k_res8(const uint4 *__restrict__ x
     // and first read here -- the opaque copy keeps the conversion, and so the wait for the load, out of
     // the block's steps; a load issued here would be waited for together with every weight load and
     // store issued before it)
-    auto epilogue = [&](__amdgpu_buffer_rsrc_t y_rs, int q, uint32_t bb) {
+    auto epilogue = [&](__amdgpu_buffer_rsrc_t y_rs, int q, uint32_t bb) __attribute__((always_inline)) {
         asm volatile("" : "+v"(bb));
         const float bv = elem_to_float<E>((uint16_t)bb);
         const int o = 32 * (4 * q + wave) + ocol;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(kR8Threads) void k_res8(const uint4 *__restrict__ x
 #pragma unroll
         for (int r = 0; r < R; ++r) load_w(q0, r, wr[r]);  // KS >= R
     }
-    auto read_x = [&](int ks, uint4 (&dst)[8]) {
+    auto read_x = [&](int ks, uint4 (&dst)[8]) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < G; ++p) dst[p] = planes[r8_chunk(ks, p) + lane];
     };
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(kR8Threads) void k_res8(const uint4 *__restrict__ x
     // PF (quads whose planes are complete): each step's planes were read during the step before, and
     // it reads the next step's (step KS: a spare step, read and unused) under its products; in a
     // filling quad every step reads its own after the barrier that published them.
-    auto steps = [&](auto first, auto d0, auto d1, auto pf, int q, int qn, int s, uint4 (&xq)[2][8]) {
+    auto steps = [&](auto first, auto d0, auto d1, auto pf, int q, int qn, int s, uint4 (&xq)[2][8]) __attribute__((always_inline)) {
         constexpr int D0 = decltype(d0)::value, D1 = decltype(d1)::value;
         constexpr bool PF = decltype(pf)::value;
         const bool wrap = s + R >= KS;
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(kR8Threads) void k_res8(const uint4 *__restrict__ x
         const int qe = min(qb + NQg, qa + (ue - u));
         const bool more_tiles = u + (qe - qa) < ue;  // then the range goes on with quad qb of tile t + 1
         // the quad this workgroup runs after q (past its last: q itself, whose weights are in range)
-        auto next_q = [&](int q) { return q + 1 < qe ? q + 1 : (more_tiles ? qb : q); };
+        auto next_q = [&](int q) __attribute__((always_inline)) { return q + 1 < qe ? q + 1 : (more_tiles ? qb : q); };
         const int64_t n0 = (int64_t)t * kR8BT;
         const int rows = (int)std::min<int64_t>(kR8BT, N - n0);
         // x of this tile (rows past the tile read as zeros); y of this tile (stores past it are dropped)
@@ -292,53 +294,51 @@ __global__ __launch_bounds__(kR8Threads) void k_res8(const uint4 *__restrict__ x
         const __amdgpu_buffer_rsrc_t y_rs =
             __builtin_amdgcn_make_buffer_rsrc((void *)(y + n0 * C_out * G), (short)0, rows * y_row, 0x00020000);
 
-        // ---- quad qa fills the planes on the way (parts of two steps: each part's raw x requested two
-        // parts ahead of its transform -- an HBM latency is longer than one part's products -- and
-        // transformed one part ahead of its products) ----
+        // ---- quad qa fills the planes on the way (parts of two steps: each part's raw x requested one
+        // part ahead of its transform and transformed one part ahead of its products) ----
         {
-            constexpr int PS = 2;  // steps per part (R / PS parts per ring body)
-            uint4 xp[4][PS][2];    // part k's raw x in xp[k % 4]
-            auto load_part = [&](int p, uint4 (&dst)[PS][2]) {
+            constexpr int PS = 2, NPB = R / PS;  // steps per part, parts per ring body
+            uint4 xp[2][PS][2];                  // part k's raw x in xp[k % 2]
+            auto load_part = [&](int p, uint4 (&dst)[PS][2]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int j = 0; j < PS; ++j) load_x(x_rs, p * PS + j, dst[j]);
             };
-            auto dft_part = [&](int p, const uint4 (&src)[PS][2]) {
+            auto dft_part = [&](int p, const uint4 (&src)[PS][2]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int j = 0; j < PS; ++j) dft_store(p * PS + j, src[j]);
             };
             const uint32_t bb = bias_bits(qa);
             const int qn = next_q(qa);
             load_part(0, xp[0]);
-            load_part(1, xp[1]);  // KS >= R = 2 PS
-            load_part(2, xp[2]);
+            load_part(1, xp[1]);  // KS >= R >= 2 PS
             // the previous tile's planes are no longer read by any wave
             r8_lds_barrier();
             dft_part(0, xp[0]);
-            // Body of ring steps s .. s + R - 1 = parts p = s / PS and p + 1: their products, the
-            // transforms of parts p + 1 and p + 2 and the requests of parts p + 3 and p + 4, each into
-            // the buffer its part's transform has just freed, unconditionally: parts past the last read
-            // as zeros (channels past C_in) and the one of them transformed goes to the two spare steps
-            // after the planes. Each body starts with the barrier that publishes the part its first half
-            // reads, so a load the compiler sinks into the next quad still comes before that barrier.
-            // ODD: p = 2 mod 4 (the buffers are registers, so their indices must be constants); the
-            // first body is its own copy: its first step starts the accumulators.
-            auto body0 = [&](auto first, auto odd, int s) {
-                constexpr int B = decltype(odd)::value ? 2 : 0;  // p mod 4
-                const int p = s / PS;
+            // Part J of the body at ring step s (part k = s / PS + J): the barrier that publishes it, its
+            // products, the transform of part k + 1 and the request of part k + 2 into the buffer just
+            // freed, unconditionally: parts past the last read as zeros (channels past C_in) and the one
+            // of them transformed goes to the two spare steps after the planes. A load the compiler sinks
+            // past the end of a part still comes before the next part's barrier. (The body starts at an
+            // even part, so each part's buffers are known constants.)
+            auto part = [&](auto first, auto jc, int s) __attribute__((always_inline)) {
+                constexpr int J = decltype(jc)::value;
+                const int k = s / PS + J;
                 r8_lds_barrier();
-                steps(first, IC8<0>{}, IC8<PS>{}, IC8<0>{}, qa, qn, s, xq);  // part p's products
-                dft_part(p + 1, xp[(B + 1) & 3]);
-                load_part(p + 3, xp[(B + 3) & 3]);
-                r8_lds_barrier();
-                steps(IC8<false>{}, IC8<PS>{}, IC8<R>{}, IC8<0>{}, qa, qn, s, xq);  // part p + 1's
-                dft_part(p + 2, xp[(B + 2) & 3]);
-                load_part(p + 4, xp[B]);
+                steps(first, IC8<J * PS>{}, IC8<(J + 1) * PS>{}, IC8<0>{}, qa, qn, s, xq);
+                dft_part(k + 1, xp[(J + 1) & 1]);
+                load_part(k + 2, xp[J & 1]);
             };
-            body0(IC8<true>{}, IC8<0>{}, 0);
-            for (int s = R; s < KS; s += 2 * R) {
-                body0(IC8<false>{}, IC8<1>{}, s);
-                if (s + R < KS) body0(IC8<false>{}, IC8<0>{}, s + R);
-            }
+            // the first body is its own copy: its first step starts the accumulators
+            auto body0 = [&](auto first, int s) __attribute__((always_inline)) {
+                part(first, IC8<0>{}, s);
+                part(IC8<false>{}, IC8<1>{}, s);
+                if constexpr (NPB == 4) {
+                    part(IC8<false>{}, IC8<2>{}, s);
+                    part(IC8<false>{}, IC8<3>{}, s);
+                }
+            };
+            body0(IC8<true>{}, 0);
+            for (int s = R; s < KS; s += R) body0(IC8<false>{}, s);
             epilogue(y_rs, qa, bb);
         }
         // ---- later quads of the tile: the planes are complete; no barrier ----

@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "k_p8": ["fourier_domain_linear_amd/csrc/fwd_big.hip"] + _COMMON,
     "k_conv": ["fourier_domain_linear_amd/csrc/fwd_big.hip", "fourier_domain_linear_amd/csrc/conv.hip"] + _COMMON,
     "k_res": ["fourier_domain_linear_amd/csrc/fwd_res.hip"] + _COMMON,
+    "k_res8": ["fourier_domain_linear_amd/csrc/fwd_res8.hip"] + _COMMON,
 }
 
 
