@@ -126,6 +126,15 @@ def cmd_stats(a):
              f"{'kernel':<90} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
     for name, calls, avg, mn, mx, tot, pct in sorted(rows, key=lambda r: -r[5]):
         lines.append(f"{name[:90]:<90} {calls:>6} {avg / 1e3:>9.3f} {mn / 1e3:>9.3f} {mx / 1e3:>9.3f} {pct:>6.2f}")
+    if a.bench_json:
+        # the profiled bench.py run's own figures (graph-timed under the profiler, same process)
+        with open(a.bench_json) as f:
+            line = json.load(f)
+        lines += ["", f"# the profiled run's bench line: workload {line['config']['workload']}, "
+                      f"{line['ms_per_step'] * 1e3:.3f} us per step graph-timed over {line['steps']} steps "
+                      f"(the averages above also count the warm-up and per-launch eager launches)"]
+        for name, rec in sorted((line.get("configs") or {}).items()):
+            lines.append(f"#   {name}: {rec['us_per_step']:.3f} us per step ({rec['kernel']})")
     text = "\n".join(lines) + "\n"
     if a.out:
         with open(a.out, "w") as f:
@@ -206,6 +215,7 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("dir")
     s.add_argument("--cmd", required=True)
+    s.add_argument("--bench-json", help="bench.py --json-out file of the profiled run")
     s.add_argument("--out")
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
