@@ -474,7 +474,10 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
     auto transform = [&](const uint4 (&src)[8], int buf) {  // DFT -> half-type fragments (+ dy's plane 0)
         if (!live) return;
         const int step = tg >> 1, half = tg & 1;
-#pragma unroll
+        // (fp16 at G = 4: one channel at a time; unrolled, the two channels' fp16 conversions were kept
+        // live together and 56 registers spilled)
+        constexpr int UNR = (__is_same(E, F16) && CPU > 1) ? 1 : CPU;
+#pragma unroll UNR
         for (int c = 0; c < CPU; ++c) {
             float pl[G][8];
 #pragma unroll
@@ -485,7 +488,10 @@ __global__ __launch_bounds__(512) void k_bw_small(const uint16_t *__restrict__ x
                 group_forward<G, D4>(v, P);
 #pragma unroll
                 for (int q = 0; q < G; ++q) pl[q][j] = P[q];
-                if (!isx) dbacc[c] += P[0];
+                if (!isx)
+#pragma unroll
+                    for (int cc = 0; cc < CPU; ++cc)  // (a compile-time index also when c is not)
+                        if (cc == c) dbacc[cc] += P[0];
             }
             const int ch = u * CPU + c;
             const int base = buf * FR + (isx ? (step * CB_in + (ch >> 5)) * G : DYB + (step * CB_out + (ch >> 5)) * G);
