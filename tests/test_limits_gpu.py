@@ -1,8 +1,9 @@
 """Tensors at the size limits: the forward (and its unrolled comparator) on x and y of more than 2^31
-bytes, for each kernel family -- the small-channel stream kernel, the large-channel kernel at G = 4
-and the G = 8 kernel -- which address x and y with 64-bit bases per token tile (or row block) and
-32-bit offsets inside it, so no index may wrap past 2^31 bytes; and the convolution at the largest
-batch its single 32-bit x range admits.
+bytes, for each kernel family -- the small-channel stream kernel, the resident-planes kernels at G = 4
+and G = 8 (C_in <= 256), the large-channel G = 8 kernel (C_in > 256) and the large-channel kernel the
+unrolled comparator runs on -- which address x and y with 64-bit bases per token tile (or row block)
+and 32-bit offsets inside it, so no index may wrap past 2^31 bytes; and the convolution at the
+largest batch its single 32-bit x range admits.
 
 x is drawn on the device (torch's generator, seeded) to keep host memory small; the oracle sees the
 same bf16 values of the sampled tokens, copied back: the first and last rows, the rows around the
@@ -31,18 +32,20 @@ def _sample_rows(N, C_in, C_out, G, rng):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("G,C_in,C_out,N,expanded", [
-    (4, 16, 16, 1 << 25, True),       # stream kernel: x and y 4.3 GB each
-    (4, 256, 256, 1_200_000, True),   # large-channel kernel: 2.46 GB each
-    (8, 256, 256, 640_000, False),    # G = 8 kernel: 2.6 GB each
-], ids=["stream_p4_c16_n33554432", "big_p4_c256_n1200000", "p8_c256_n640000"])
-def test_forward_beyond_2gib(G, C_in, C_out, N, expanded, cuda_device):
+@pytest.mark.parametrize("G,C_in,C_out,N,expanded,kernel", [
+    (4, 16, 16, 1 << 25, True, "stream"),             # x and y 4.3 GB each
+    (4, 256, 256, 1_200_000, True, "resident-planes"),  # (unrolled: the large-channel kernel at G = 1) 2.46 GB each
+    (8, 256, 256, 640_000, False, "resident-planes"),   # 2.6 GB each
+    (8, 512, 512, 300_000, False, "big"),               # 2.46 GB each
+], ids=["stream_p4_c16_n33554432", "res_p4_c256_n1200000", "res8_p8_c256_n640000", "big_p8_c512_n300000"])
+def test_forward_beyond_2gib(G, C_in, C_out, N, expanded, kernel, cuda_device):
     assert N * C_in * G * 2 > 1 << 31 and N * C_out * G * 2 > 1 << 31
     _, W, b = make_inputs(G, C_in, C_out, 1, "bf16", seed=3)
     gen = torch.Generator(device=cuda_device).manual_seed(17)
     x = torch.randn((N, C_in, G), generator=gen, device=cuda_device).to(torch.bfloat16)
     h = eq.prepare_weights(W.to(cuda_device), expanded=expanded)
     print(f"[case] G={G} {C_in}->{C_out} N={N} [{h.describe()}]", flush=True)
+    assert f"forward: bf16 {kernel} " in h.describe(), h.describe()  # the kernel family this case is for
     bd = b.to(cuda_device)
     outs = {"spectral": eq.forward(h, x, bd)}
     if expanded:
