@@ -74,3 +74,29 @@ def test_mfma_counter_summary(tmp_path):
     assert "over the kernel duration at 2.4 GHz: 0.1000" in text
     assert "over the GRBM_GUI_ACTIVE window: 0.2000" in text
     assert "(2.00 per MFMA)" in text
+
+
+def test_kernel_stats_summary_with_bench_line(tmp_path):
+    # the kernel-trace summary sorted by total time, with the profiled run's own bench figures appended
+    import json
+
+    from fourier_domain_linear_amd import profiling
+
+    d = tmp_path / "run"
+    d.mkdir()
+    with open(d / "k_kernel_stats.csv", "w") as f:
+        f.write('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n')
+        f.write('"k_small",10,1000,100.0,10.0,90,110,1\n')
+        f.write('"k_big",20,9000,450.0,90.0,400,500,1\n')
+    line = {"config": {"workload": "p8_c256x1024_n12544_bf16"}, "ms_per_step": 0.1145, "steps": 200,
+            "configs": {"p4_c96_n25088_bf16": {"us_per_step": 10.5, "kernel": "bf16 stream"}}}
+    bj = tmp_path / "b.json"
+    bj.write_text(json.dumps(line))
+    out = tmp_path / "s.txt"
+    profiling.main(["stats", str(d), "--cmd", "c", "--bench-json", str(bj), "--out", str(out)])
+    lines = out.read_text().splitlines()
+    rows = [l for l in lines if l.startswith("k_")]
+    assert rows[0].split()[0] == "k_big" and rows[1].split()[0] == "k_small"
+    assert rows[0].split()[1:3] == ["20", "0.450"]  # calls, average in microseconds
+    assert any("p8_c256x1024_n12544_bf16, 114.500 us per step graph-timed over 200 steps" in l for l in lines)
+    assert any("p4_c96_n25088_bf16: 10.500 us per step (bf16 stream)" in l for l in lines)
