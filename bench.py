@@ -371,11 +371,11 @@ def bench_block(torch, eq, rl, timer, dev, K: int, Wm: int, with_expanded: bool)
 
 
 def measure_forward(torch, eq, rl, w, dev, K: int, Wm: int, timer, with_expanded: bool = True,
-                    with_torch: bool = False, with_each: bool = True, backward: bool = False):
-    """Time eqlin_forward (and eqlin_forward_expanded) on workload w's seeded inputs, resident in HBM
-    and rotated over >= 1 GiB of buffer sets. Returns (record, state) where record holds the figures
-    and state the tensors and handle a caller may reuse."""
-    x, W, b = workload_inputs_for(w)
+                    with_torch: bool = False, with_each: bool = True, backward: bool = False, inputs=None):
+    """Time eqlin_forward (and eqlin_forward_expanded) on workload w's seeded inputs (or `inputs`, an
+    (x, W, b) of w's shape), resident in HBM and rotated over >= 1 GiB of buffer sets. Returns (record,
+    state) where record holds the figures and state the tensors and handle a caller may reuse."""
+    x, W, b = inputs if inputs is not None else workload_inputs_for(w)
     eb = w.elem_bytes
     set_bytes = w.N * (w.C_in + w.C_out) * w.G * eb
     R = max(3, math.ceil((1 << 30) / set_bytes))
@@ -461,6 +461,35 @@ def measure_forward(torch, eq, rl, w, dev, K: int, Wm: int, timer, with_expanded
     return rec, state
 
 
+def bench_shards(torch, eq, rl, timer, dev, K: int, Wm: int, parts):
+    """The kernel at one shard's shape: each bf16 workload's spectral forward on the first N/P tokens of
+    its inputs, for P in `parts`, timed like the headline on this one GPU. The layer is token-parallel
+    with no communication, so a shard of P is this launch on its own device; what the table shows is how
+    the kernel's efficiency holds up as the per-device token count falls (launch cost, wave
+    quantisation). No figure for several devices is derived from it."""
+    import dataclasses
+
+    from fourier_domain_linear_amd.workloads import WORKLOADS
+
+    out = {}
+    for wf in WORKLOADS:
+        if wf.dtype != "bf16":
+            continue
+        x, W, b = workload_inputs_for(wf)
+        per = {}
+        for P in parts:
+            n = wf.N // P
+            ws = dataclasses.replace(wf, name=f"{wf.name}_shard_1_of_{P}", N=n)
+            r, _ = measure_forward(torch, eq, rl, ws, dev, K, Wm, timer, with_expanded=False, with_each=False,
+                                   inputs=(x[:n].contiguous(), W, b))
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            per[str(P)] = {"tokens": n, "us_per_step": r["us_per_step"], "tokens_per_s": r["tokens_per_s"],
+                           "bound": r["bound"], "frac": r["frac"], "kernel": r["kernel"]}
+        out[wf.name] = per
+    return out
+
+
 _INPUT_CACHE = {}
 
 
@@ -495,6 +524,8 @@ def main():
                          "p4 192-channel shape, spectral and expanded (reported under 'block')")
     ap.add_argument("--conv", action="store_true",
                     help="also time the p4 3x3 group convolution, spectral and expanded (reported under 'conv')")
+    ap.add_argument("--shards", default=None, metavar="P,P,...",
+                    help="also time each bf16 workload's kernel on one shard of N/P tokens (one GPU)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (the counter calibration for traffic)")
     args = ap.parse_args()
@@ -558,6 +589,12 @@ def main():
         extra["block"] = bench_block(torch, eq, rl, timer, dev, K, Wm, not args.no_expanded)
     if args.conv:
         extra["conv"] = bench_conv(torch, eq, rl, timer, dev, K, Wm)
+    if args.shards:
+        parts = [int(v) for v in args.shards.split(",") if v]
+        if any(P < 1 for P in parts):
+            raise SystemExit("--shards: each P must be >= 1")
+        extra["shards"] = bench_shards(torch, eq, rl, timer, dev, min(K, args.config_steps),
+                                       min(Wm, args.config_steps), parts)
     extra["effective_tflops"] = rec["effective_tflops"]
     extra["useful_tflops"] = rec["useful_tflops"]
     extra["per_launch_us"] = rec["per_launch_us"]

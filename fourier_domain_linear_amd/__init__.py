@@ -39,6 +39,7 @@ EQLIN_F16 = 2
 EQLIN_PREPARE_EXPANDED = 1
 EQLIN_PREPARE_BACKWARD = 2
 EQLIN_PREPARE_D4 = 4
+EQLIN_PREPARE_FIXED_KERNEL = 8
 GROUPS = ("cyclic", "d4")
 EQLIN_ACT_NONE = 0
 EQLIN_ACT_GELU = 1
@@ -164,10 +165,12 @@ class Handle:
         return describe(self)
 
 
-def prepare_weights(W: torch.Tensor, expanded: bool = False, backward: bool = False, group: str = "cyclic") -> Handle:
+def prepare_weights(W: torch.Tensor, expanded: bool = False, backward: bool = False, group: str = "cyclic",
+                    fixed_kernel: bool = False) -> Handle:
     """eqlin_prepare_weights: W [C_out, C_in, G] (cuda, bf16 or fp32) -> Handle. ``expanded`` builds the
     unrolled comparator, ``backward`` the weights of backward_data. ``group``: "cyclic" (G = 1, 2, 4, 8)
-    or "d4", the dihedral group of the square (G = 8, element a + 4b = r^a s^b; EQLIN_PREPARE_D4)."""
+    or "d4", the dihedral group of the square (G = 8, element a + 4b = r^a s^b; EQLIN_PREPARE_D4).
+    ``fixed_kernel``: one forward kernel for every batch size (EQLIN_PREPARE_FIXED_KERNEL)."""
     if group not in GROUPS:
         raise ValueError(f"group must be one of {GROUPS}, got {group!r}")
     lib = load_library()
@@ -177,7 +180,7 @@ def prepare_weights(W: torch.Tensor, expanded: bool = False, backward: bool = Fa
     C_out, C_in, G = W.shape
     out = ctypes.c_void_p()
     flags = (EQLIN_PREPARE_EXPANDED if expanded else 0) | (EQLIN_PREPARE_BACKWARD if backward else 0) | \
-        (EQLIN_PREPARE_D4 if group == "d4" else 0)
+        (EQLIN_PREPARE_D4 if group == "d4" else 0) | (EQLIN_PREPARE_FIXED_KERNEL if fixed_kernel else 0)
     with torch.cuda.device(W.device):
         st = lib.eqlin_prepare_weights(ctypes.c_void_p(W.data_ptr()), C_out, C_in, G, _dtype_code(W.dtype),
                                        flags, _stream(W), ctypes.byref(out))

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 
@@ -58,11 +59,13 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
         // layers too wide for the stream kernel whose input planes fit on chip: the resident-planes
         // kernels (a token tile's planes kept for every output block, each token transformed once per
         // workgroup) instead of the large-channel ones
+        eqlin::KernelChoice big;
+        bool res4 = false;
         if (ok && p->conv_k == 0 && p->fwd.kind == eqlin::KIND_BIG) {
             eqlin::KernelChoice r;
-            if (eqlin::select_res(p->G, p->d4, p->C_in, p->C_out, &r) ||
-                eqlin::select_res8(p->G, p->d4, p->C_in, p->C_out, &r))
-                p->fwd = r;
+            big = p->fwd;
+            res4 = eqlin::select_res(p->G, p->d4, p->C_in, p->C_out, &r);
+            if (res4 || eqlin::select_res8(p->G, p->d4, p->C_in, p->C_out, &r)) p->fwd = r;
         }
         if (!ok)
             return fail(EQLIN_ERR_UNSUPPORTED, "no half-precision kernel for G=%d C_in=%d C_out=%d", p->G, p->C_in,
@@ -72,6 +75,18 @@ eqlin_status_t build_spectral(Plan *p, const void *W, hipStream_t s) {
         p->KS = (ks + p->fwd.ks_mult - 1) / p->fwd.ks_mult * p->fwd.ks_mult;
         const int nb = (p->C_out + p->fwd.rows_per_block - 1) / p->fwd.rows_per_block;
         p->NB_total = (nb + p->fwd.nb_tile - 1) / p->fwd.nb_tile * p->fwd.nb_tile;
+        // G = 4: at 32 tokens per compute unit or fewer (one 32-token block per resident tile) every CU of
+        // the resident-planes kernel still streams the whole weight set for its few tokens, and the
+        // large-channel kernel, which splits the outputs over the CUs, is faster (measured at
+        // 192 -> 768: 13.3 against 27.6 us at 3136 tokens, 24.1 against 29.5 at 6272, equal at 12544).
+        // It reads the same weights when both kernels pad the channels alike.
+        if (res4 && !(p->flags & EQLIN_PREPARE_FIXED_KERNEL) && big.frag_kind == p->fwd.frag_kind &&
+            big.kc == p->fwd.kc && big.rows_per_block == p->fwd.rows_per_block && p->KS % big.ks_mult == 0 &&
+            p->NB_total % big.nb_tile == 0) {
+            p->fwd_small = big;
+            p->small_max_n = (int64_t)32 * std::max(1, p->fwd.num_cus);
+            if (p->dtype == EQLIN_F16 && strncmp(p->fwd_small.name, "bf16", 4) == 0) memcpy(p->fwd_small.name, "f16 ", 4);
+        }
         p->planes_bytes = (size_t)p->NB_total * p->KS * p->G * 1024;
         e = hipMalloc(&p->planes, p->planes_bytes);
         if (e != hipSuccess) {
@@ -200,7 +215,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(EQLIN_ERR_INVALID_ARG, "G = %d not in {1, 2, 4, 8}", G);
     if (dtype != EQLIN_F32 && dtype != EQLIN_BF16 && dtype != EQLIN_F16)
         return fail(EQLIN_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
-    if (flags & ~(EQLIN_PREPARE_EXPANDED | EQLIN_PREPARE_BACKWARD | EQLIN_PREPARE_D4))
+    if (flags & ~(EQLIN_PREPARE_EXPANDED | EQLIN_PREPARE_BACKWARD | EQLIN_PREPARE_D4 | EQLIN_PREPARE_FIXED_KERNEL))
         return fail(EQLIN_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     const bool d4 = (flags & EQLIN_PREPARE_D4) != 0;
     if (d4 && G != 8) return fail(EQLIN_ERR_INVALID_ARG, "EQLIN_PREPARE_D4 needs G = 8 (got G = %d)", G);
@@ -287,7 +302,8 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
 static eqlin_status_t run_forward(const Plan *h, const void *x, const void *b, void *y, int64_t N, int act,
                                   eqlin_stream_t stream, const char *what) {
     (void)hipGetLastError();  // drop a stale error left by someone else's call on this thread
-    hipError_t e = h->fwd.launch(h, x, b, y, N, act, (hipStream_t)stream);
+    const eqlin::KernelChoice &k = (h->fwd_small.launch && N <= h->small_max_n) ? h->fwd_small : h->fwd;
+    hipError_t e = k.launch(h, x, b, y, N, act, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, what);
     return EQLIN_OK;
 }
@@ -574,9 +590,14 @@ int eqlin_describe(eqlin_handle_t h, char *buf, size_t len) {
         return snprintf(buf, len, "p4 conv %dx%d C_in=%d (gathered %d) C_out=%d %s | forward: %s | expanded: %s", h->conv_k,
                         h->conv_k, h->conv_cin, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : "f16", h->fwd.name,
                         h->expanded ? h->expanded->fwd.name : "(not prepared)");
+    char fw[224];
+    if (h->fwd_small.launch)
+        snprintf(fw, sizeof(fw), "%s; at N <= %lld: %s", h->fwd.name, (long long)h->small_max_n, h->fwd_small.name);
+    else
+        snprintf(fw, sizeof(fw), "%s", h->fwd.name);
     return snprintf(buf, len,
                     "%s%d C_in=%d C_out=%d %s | forward: %s | expanded: %s | backward data: %s | backward weights: %s",
-                    h->d4 ? "D" : "G=", h->d4 ? 4 : h->G, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : h->dtype == EQLIN_F16 ? "f16" : "f32", h->fwd.name,
+                    h->d4 ? "D" : "G=", h->d4 ? 4 : h->G, h->C_in, h->C_out, h->dtype == EQLIN_BF16 ? "bf16" : h->dtype == EQLIN_F16 ? "f16" : "f32", fw,
                     h->expanded ? h->expanded->fwd.name : "(not prepared)",
                     h->backward ? h->backward->fwd.name : "(not prepared)", eqlin::bw_kernel_name(h));
 }

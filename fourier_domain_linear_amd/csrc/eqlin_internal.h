@@ -64,6 +64,10 @@ struct Plan {
     int KS = 0;        // bf16: K-steps of fwd.kc channels (C_in padded up; a multiple of ks_mult)
     int NB_total = 0;  // bf16: output blocks of fwd.rows_per_block (C_out padded to the tile)
     KernelChoice fwd;
+    // bf16 / fp16: the kernel for batches of at most small_max_n tokens (launch == nullptr: none), run
+    // on the same spectral weights (its padding of KS and NB_total agrees with fwd's)
+    KernelChoice fwd_small;
+    int64_t small_max_n = 0;
 
     // unrolled weight (flags & EQLIN_PREPARE_EXPANDED): a G = 1 plan over E, plus E itself
     Plan *expanded = nullptr;

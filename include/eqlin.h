@@ -75,6 +75,7 @@ typedef enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 } eqlin_act_t;
 #define EQLIN_PREPARE_EXPANDED 1u /* also build the unrolled weight for eqlin_forward_expanded */
 #define EQLIN_PREPARE_BACKWARD 2u /* also build the data-gradient weights for eqlin_backward_data */
 #define EQLIN_PREPARE_D4 4u       /* the group is the dihedral group D4 (needs G = 8), see below */
+#define EQLIN_PREPARE_FIXED_KERNEL 8u /* one forward kernel for every batch size (see eqlin_forward) */
 
 /*
  * The dihedral group D4 (EQLIN_PREPARE_D4). The p4 rotations plus the mirror images: the reflection
@@ -107,7 +108,8 @@ typedef enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 } eqlin_act_t;
  *   flags  EQLIN_PREPARE_EXPANDED to also build the unrolled weight for eqlin_forward_expanded;
  *          EQLIN_PREPARE_BACKWARD to also build the weights of eqlin_backward_data (bf16/fp16 then
  *          also needs C_out % 8 == 0, else UNSUPPORTED); EQLIN_PREPARE_D4 for the dihedral group
- *          (G must be 8, else INVALID_ARG; W's group axis in the element order above).
+ *          (G must be 8, else INVALID_ARG; W's group axis in the element order above);
+ *          EQLIN_PREPARE_FIXED_KERNEL to run one forward kernel whatever the batch size (below).
  *   out    receives the new handle (set to NULL on failure).
  * Allocates device memory (hipMalloc) on the current device; synchronises nothing.
  */
@@ -124,6 +126,12 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
  *   x      device [N][C_in][G]; b device [C_out] or NULL (no bias); y device [N][C_out][G].
  *   N      >= 0 tokens; N == 0 enqueues nothing and returns EQLIN_OK.
  * Must be called with the handle's device current. Asynchronous on `stream`; allocates nothing.
+ * Kernel by batch size: a wide p4 layer (C_in <= 256, C_out >= 256) runs the resident-planes kernel,
+ * which gives each compute unit one token tile and every output, while N exceeds 32 tokens per compute
+ * unit; at smaller N it runs the large-channel kernel, which splits the outputs over the compute units
+ * instead (the same prepared weights; eqlin_describe names both). The two sum in different orders, so
+ * results can differ in the last bits between batch sizes on either side of that point; a handle
+ * prepared with EQLIN_PREPARE_FIXED_KERNEL always runs the first.
  */
 eqlin_status_t eqlin_forward(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N,
                              eqlin_stream_t stream);

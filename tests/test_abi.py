@@ -57,6 +57,10 @@ def test_prepare_argument_errors(lib):
     assert _prepare(lib, fake, 4, 8, 4, dtype=7)[0] == eq.EQLIN_ERR_INVALID_ARG
     assert _prepare(lib, fake, 4, 12, 4, dtype=eq.EQLIN_F16)[0] == eq.EQLIN_ERR_UNSUPPORTED  # f16, C_in % 8
     assert _prepare(lib, fake, 4, 8, 4, flags=0x10)[0] == eq.EQLIN_ERR_INVALID_ARG
+    # the known flags together pass the flag check (and fail on the next one, the bf16 C_in rule)
+    allf = eq.EQLIN_PREPARE_EXPANDED | eq.EQLIN_PREPARE_BACKWARD | eq.EQLIN_PREPARE_FIXED_KERNEL
+    assert _prepare(lib, fake, 8, 12, 4, dtype=1, flags=allf)[0] == eq.EQLIN_ERR_UNSUPPORTED
+    assert "C_in" in lib.eqlin_last_error().decode()
     assert _prepare(lib, ctypes.c_void_p(0x10008), 4, 8, 4)[0] == eq.EQLIN_ERR_INVALID_ARG  # misaligned
     assert _prepare(lib, fake, 4, 12, 4, dtype=1)[0] == eq.EQLIN_ERR_UNSUPPORTED  # bf16, C_in % 8
     assert "C_in" in lib.eqlin_last_error().decode()

@@ -7,8 +7,11 @@ what its indexing depends on: the tile size (BT = ceil(N / CUs) up to 64, so N b
 read as zeros), the largest C_in whose planes fit (256), C_in = 8 (one step padded to four), output blocks that do
 not split evenly over the eight waves and C_out not a multiple of 32 (masked stores), no bias, the GELU epilogue and fp16.
 Bars as for the other half-precision paths: bf16 relative Frobenius <= 1e-2 and max abs <= 3e-2;
-fp16 the same divided by 8 (three more significant bits in every rounding).
+fp16 the same divided by 8 (three more significant bits in every rounding). These tests prepare with
+EQLIN_PREPARE_FIXED_KERNEL, so the resident-planes kernel runs at every N; without it a batch of at most
+32 tokens per compute unit runs the large-channel kernel on the same weights (the last test).
 """
+import re
 import numpy as np
 import pytest
 import torch
@@ -51,7 +54,7 @@ def test_res_forward(C_in, C_out, N, with_bias, cuda_device):
     x, W, b = make_inputs(4, C_in, C_out, N, "bf16", seed=C_in + C_out + N)
     if not with_bias:
         b = None
-    h = eq.prepare_weights(W.to(cuda_device))
+    h = eq.prepare_weights(W.to(cuda_device), fixed_kernel=True)
     assert "resident" in h.describe().split("|")[1], h.describe()
     y = eq.forward(h, x.to(cuda_device), None if b is None else b.to(cuda_device))
     torch.cuda.synchronize()
@@ -63,7 +66,7 @@ def test_res_forward(C_in, C_out, N, with_bias, cuda_device):
 def test_res_gelu(C_in, C_out, N, dtype, cuda_device):
     print(f"[case] res GELU {dtype} {C_in}->{C_out} N={N}", flush=True)
     x, W, b = make_inputs(4, C_in, C_out, N, dtype, seed=7)
-    h = eq.prepare_weights(W.to(cuda_device))
+    h = eq.prepare_weights(W.to(cuda_device), fixed_kernel=True)
     y = eq.forward(h, x.to(cuda_device), b.to(cuda_device), act="gelu")
     torch.cuda.synchronize()
     _check(y, oracle.gelu(oracle.forward(x, W, b)), dtype, f"res GELU {dtype} {C_in}->{C_out} N={N}")
@@ -73,7 +76,7 @@ def test_res_gelu(C_in, C_out, N, dtype, cuda_device):
 def test_res_f16(C_in, C_out, N, cuda_device):
     print(f"[case] res f16 {C_in}->{C_out} N={N}", flush=True)
     x, W, b = make_inputs(4, C_in, C_out, N, "f16", seed=11)
-    h = eq.prepare_weights(W.to(cuda_device))
+    h = eq.prepare_weights(W.to(cuda_device), fixed_kernel=True)
     assert "resident" in h.describe().split("|")[1], h.describe()
     y = eq.forward(h, x.to(cuda_device), b.to(cuda_device))
     torch.cuda.synchronize()
@@ -91,3 +94,25 @@ def test_res_not_taken_outside_its_range(cuda_device):
         y = eq.forward(h, x.to(cuda_device), b.to(cuda_device))
         torch.cuda.synchronize()
         _check(y, oracle.forward(x, W, b), "bf16", f"fallback {C_in}->{C_out} [{desc}]")
+
+
+def test_batch_size_dispatch(cuda_device):
+    # default handle: the large-channel kernel up to the threshold eqlin_describe names, the resident one
+    # past it, both on the same spectral weights; a FIXED_KERNEL handle names one kernel only
+    C_in, C_out = 192, 768
+    x, W, b = make_inputs(4, C_in, C_out, 9000, "bf16", seed=21)
+    Wd, bd, xd = W.to(cuda_device), b.to(cuda_device), x.to(cuda_device)
+    h = eq.prepare_weights(Wd)
+    fwd = h.describe().split("|")[1]
+    m = re.search(r"at N <= (\d+): bf16 big", fwd)
+    assert m and "resident" in fwd.split(";")[0], fwd
+    limit = int(m.group(1))
+    assert limit % 32 == 0 and limit >= 32, limit
+    hf = eq.prepare_weights(Wd, fixed_kernel=True)
+    assert "at N <=" not in hf.describe(), hf.describe()
+    for n in sorted({1, 517, min(limit, 9000), min(limit + 1, 9000), 9000}):
+        for name, hh in (("default", h), ("fixed", hf)):
+            y = eq.forward(hh, xd[:n], bd)
+            torch.cuda.synchronize()
+            kern = "big" if (hh is h and n <= limit) else "resident"
+            _check(y, oracle.forward(x[:n], W, b), "bf16", f"dispatch {name} N={n} ({kern}, limit {limit})")
