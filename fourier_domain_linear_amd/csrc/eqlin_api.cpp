@@ -286,6 +286,7 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
         q->d4 = d4;
         q->dtype = dtype;
         q->device = p->device;
+        q->flags = flags & EQLIN_PREPARE_FIXED_KERNEL;  // dx runs this plan's forward kernels
         p->backward = q;
         st = build_spectral(q, p->wt, s);
         // with both flags, the data gradient's own unrolled comparator: the G = 1 product with E^T

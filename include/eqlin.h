@@ -131,7 +131,8 @@ eqlin_status_t eqlin_prepare_weights(const void *W, int C_out, int C_in, int G, 
  * unit; at smaller N it runs the large-channel kernel, which splits the outputs over the compute units
  * instead (the same prepared weights; eqlin_describe names both). The two sum in different orders, so
  * results can differ in the last bits between batch sizes on either side of that point; a handle
- * prepared with EQLIN_PREPARE_FIXED_KERNEL always runs the first.
+ * prepared with EQLIN_PREPARE_FIXED_KERNEL always runs the first (eqlin_backward_data, which runs
+ * these kernels on the transposed weight, follows the same rule).
  */
 eqlin_status_t eqlin_forward(eqlin_handle_t h, const void *x, const void *b, void *y, int64_t N,
                              eqlin_stream_t stream);
