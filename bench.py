@@ -9,8 +9,11 @@ configured workload's spectral and expanded times, roofline fractions and speedu
 
 Timing. Inputs are resident in HBM before the timed region. W warmup steps run eagerly; then K steps
 are captured into one HIP graph (so the ~10 us kernels are not bounded by host launch latency) and
-replayed once untimed and once timed, between HIP events on the launch stream, with
-torch.cuda.synchronize() on both sides. The K steps rotate over R buffer sets totalling >= 1 GiB,
+replayed untimed (one replay at a time) for at least SETTLE_S = 0.25 s and then once timed, between
+HIP events on the launch stream, with torch.cuda.synchronize() on both sides. The W warm-up steps are
+likewise followed by more of the same launches until SETTLE_S has passed: the GPU's clock rises over
+tens of milliseconds of sustained work, and a few steps timed right after a short warm-up (or after the
+idle gap of the capture) run well below it. The K steps rotate over R buffer sets totalling >= 1 GiB,
 more than the 256 MB Infinity Cache, so x is read from HBM, not from the cache.
 ms_per_step = event time / K; value = tokens / (ms_per_step / 1e3).
 
@@ -62,15 +65,40 @@ def load_traffic(workload: str, kernel_desc: str | None = None):
     return rec.get("traffic_bytes_per_launch")
 
 
+# The warm-up runs for at least this long: the GPU's clock rises over tens of milliseconds of sustained
+# work, and a few steps timed right after a short warm-up run below the steady clock (measured: 148 us
+# per step at 20 steps after 5 warm-up launches against 113-115 us at 500 after 50, headline workload).
+SETTLE_S = 0.25
+
+
+def warm_up(torch, launch, Wm: int, R: int):
+    """The W warm-up launches (launch(i) uses buffer set i % R), then more of the same, in synchronised
+    rounds of max(W, 64), until at least SETTLE_S seconds have passed since the first."""
+    t0 = time.perf_counter()
+    for i in range(Wm):
+        launch(i % R)
+    torch.cuda.synchronize()
+    n = max(Wm, 64)
+    while time.perf_counter() - t0 < SETTLE_S:
+        for i in range(n):
+            launch(i % R)
+        torch.cuda.synchronize()
+
+
 def time_graph(torch, launch, K: int, R: int):
-    """Capture K launches (launch(i) uses buffer set i % R) into one graph; replay once untimed and
-    once timed. Returns ms per launch."""
+    """Capture K launches (launch(i) uses buffer set i % R) into one graph; replay it untimed, one
+    replay at a time, until at least SETTLE_S seconds have passed (the capture leaves the GPU idle long
+    enough for its clock to drop again), then once timed. Returns ms per launch."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(K):
             launch(i % R)
-    g.replay()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= SETTLE_S:
+            break
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -194,9 +222,7 @@ def bench_backward(torch, eq, rl, w, st, dev, K: int, Wm: int, timer, with_expan
     for name, fn, Bk in (("data", bwd_data, B),
                          ("weights", bwd_weights,
                           w.N * (w.C_in + w.C_out) * w.G * eb + w.C_out * w.C_in * w.G * 4 + w.C_out * 4)):
-        for i in range(Wm):
-            fn(i % R)
-        torch.cuda.synchronize()
+        warm_up(torch, fn, Wm, R)
         ms_b = timer(torch, fn, K, R)
         tb = ms_b / 1e3
         res[name] = {"us_per_step": round(ms_b * 1e3, 3), "tokens_per_s": w.N / tb,
@@ -228,9 +254,7 @@ def bench_backward(torch, eq, rl, w, st, dev, K: int, Wm: int, timer, with_expan
         exp = {}
         for name, fn, timer_ in (("data_expanded", bwd_data_exp, timer), ("weights_naive", bwd_weights_naive, time_eager)):
             try:
-                for i in range(Wm):
-                    fn(i % R)
-                torch.cuda.synchronize()
+                warm_up(torch, fn, Wm, R)
                 exp[name] = {"us_per_step": round(timer_(torch, fn, K, R) * 1e3, 3)}
                 log(f"[bench] backward {name}: {exp[name]['us_per_step']:.2f} us/step")
             except RuntimeError as e:  # the torch leg is a comparator: report, never fail the bench
@@ -276,9 +300,7 @@ def bench_conv(torch, eq, rl, timer, dev, K: int, Wm: int):
            "gathered_channels": Cg, "kernels": h.describe(), "algorithmic_flops": F, "algorithmic_bytes": B}
     for name, fn, flops in (("spectral", lambda i: eq.conv_forward(h, xs[i], bd, ys[i]), F),
                             ("expanded", lambda i: eq.conv_forward_expanded(h, xs[i], bd, ys[i]), Fd)):
-        for i in range(Wm):
-            fn(i % R)
-        torch.cuda.synchronize()
+        warm_up(torch, fn, Wm, R)
         ms = timer(torch, fn, K, R)
         t = ms / 1e3
         res[name] = {"us_per_step": round(ms * 1e3, 3), "tokens_per_s": N / t, "tflops": round(flops / t / 1e12, 2),
@@ -307,9 +329,7 @@ def bench_conv(torch, eq, rl, timer, dev, K: int, Wm: int):
         def torch_conv(i):
             torch.nn.functional.conv2d(xn[i % 2], Wf, bf, padding=k // 2)
 
-        for i in range(Wm):
-            torch_conv(i)
-        torch.cuda.synchronize()
+        warm_up(torch, torch_conv, Wm, R)
         ms_t = time_eager(torch, torch_conv, K, 2)
         res["torch_conv2d_context"] = {"us_per_step": round(ms_t * 1e3, 3),
                                        "spectral_speedup": round(ms_t * 1e3 / res["spectral"]["us_per_step"], 3),
@@ -348,9 +368,7 @@ def bench_block(torch, eq, rl, timer, dev, K: int, Wm: int, with_expanded: bool)
         steps["expanded_block"] = lambda i: eq.mlp_block(h1, b1d, h2, b2d, xs[i], hs[i], ys[i], expanded=True)
     ms = {}
     for name, fn in steps.items():
-        for i in range(Wm):
-            fn(i % R)
-        torch.cuda.synchronize()
+        warm_up(torch, fn, Wm, R)
         ms[name] = timer(torch, fn, K, R)
         log(f"[bench] block {name}: {ms[name] * 1e3:.2f} us/step")
     F = rl.spectral_flops(N, C, H, G) + rl.spectral_flops(N, H, C, G)
@@ -393,9 +411,7 @@ def measure_forward(torch, eq, rl, w, dev, K: int, Wm: int, timer, with_expanded
     def expanded(i):
         eq.forward_expanded(h, xs[i], bd, ys[i])
 
-    for i in range(Wm):
-        spectral(i % R)
-    torch.cuda.synchronize()
+    warm_up(torch, spectral, Wm, R)
     ms = timer(torch, spectral, K, R)
     log(f"[bench] {w.name} spectral: {ms * 1e3:.2f} us/step")
     F = rl.spectral_flops(w.N, w.C_in, w.C_out, w.G, w.group)
@@ -417,9 +433,7 @@ def measure_forward(torch, eq, rl, w, dev, K: int, Wm: int, timer, with_expanded
         log(f"[bench] {w.name} spectral per launch: median {rec['per_launch_us']['median']:.2f} us, "
             f"min {rec['per_launch_us']['min']:.2f} us")
     if with_expanded:
-        for i in range(Wm):
-            expanded(i % R)
-        torch.cuda.synchronize()
+        warm_up(torch, expanded, Wm, R)
         ms_e = timer(torch, expanded, K, R)
         Fd = rl.dense_flops(w.N, w.C_in, w.C_out, w.G)
         Bd = rl.dense_bytes(w.N, w.C_in, w.C_out, w.G, eb)
@@ -447,9 +461,7 @@ def measure_forward(torch, eq, rl, w, dev, K: int, Wm: int, timer, with_expanded
             # eager launches (a library GEMM is kept out of graph capture: its internal memsets are
             # not checked here for replay safety)
             try:
-                for i in range(Wm):
-                    torch_linear(i % R)
-                torch.cuda.synchronize()
+                warm_up(torch, torch_linear, Wm, R)
                 ms_t = time_eager(torch, torch_linear, K, R)
                 rec["torch_linear_context"] = {"us_per_step": round(ms_t * 1e3, 3),
                                                "tokens_per_s": w.N / (ms_t / 1e3),
@@ -623,7 +635,8 @@ def main():
         "dtype": w.dtype, "data": "synthetic (seeded Gaussian x, W, b; see fourier_domain_linear_amd/workloads.py)",
         "config": {"workload": w.name, "group": w.group, "G": w.G, "C_in": w.C_in, "C_out": w.C_out, "tokens": w.N,
                    "timing": ("eager launches" if args.no_graph else "one HIP graph of K launches")
-                   + ", rotating buffer sets over >= 1 GiB"},
+                   + f" after >= {SETTLE_S} s of warm-up (launches, then untimed replays), rotating buffer sets"
+                   + " over >= 1 GiB"},
         "roofline": roof,
     }
     line.update(extra)
