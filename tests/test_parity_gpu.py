@@ -226,11 +226,15 @@ def test_abi_rejects_bad_pointers_with_device_tensors(cuda_device):
         eq.prepare_weights(torch.zeros((4, 12, 4), dtype=torch.bfloat16, device=cuda_device))
 
 
-def test_graph_replay_matches_eager(cuda_device):
+@pytest.mark.parametrize("wi,N", [(1, 4096), (2, 4096), (3, 9000), (4, 4096)],
+                         ids=["p4_c96", "p8_c64", "p4_c192x768", "p8_c256x1024"])
+def test_graph_replay_matches_eager(wi, N, cuda_device):
     # The benchmark times HIP-graph replays; every replay must equal the eager result, also with
-    # other eager work and synchronisations between replays.
-    w = WORKLOADS[1]
-    x, W, b = make_inputs(w.G, w.C_in, w.C_out, 4096, w.dtype, seed=9)
+    # other eager work and synchronisations between replays. One case per kernel the workloads run
+    # (p4/192->768 above the batch-size switch, so the resident-planes kernel; p8/256->1024 the G = 8
+    # resident kernel, whose range table is a by-value kernel argument captured with the graph).
+    w = WORKLOADS[wi]
+    x, W, b = make_inputs(w.G, w.C_in, w.C_out, N, w.dtype, seed=9)
     h = eq.prepare_weights(W.to(cuda_device), expanded=True)
     x0, x1, bd = x.to(cuda_device), (x.float() * 0.5).to(torch.bfloat16).to(cuda_device), b.to(cuda_device)
     ref0, ref1 = eq.forward(h, x0, bd), eq.forward_expanded(h, x1, bd)
