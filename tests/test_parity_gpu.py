@@ -180,9 +180,10 @@ def test_expanded_weight_is_exact_unrolling(G, dtype, cuda_device):
     np.testing.assert_array_equal(got, oracle.expand(W))
 
 
-def test_equivariance_full_size(cuda_device):
-    # cyclic shift of x along g shifts y along h (holds at any size)
-    w = WORKLOADS[1]
+@pytest.mark.parametrize("w", WORKLOADS[1:], ids=[w.name for w in WORKLOADS[1:]])
+def test_equivariance_full_size(w, cuda_device):
+    # cyclic shift of x along g shifts y along h (holds at any size), at every bf16 workload's full size
+    # in the benchmark's launch configuration
     x, W, b = make_inputs(w.G, w.C_in, w.C_out, w.N, w.dtype, seed=0)
     h = eq.prepare_weights(W.to(cuda_device))
     xd, bd = x.to(cuda_device), b.to(cuda_device)
